@@ -1,0 +1,431 @@
+// libgguf_qk: C ABI over the gfx950 kernels (declarations and contract in
+// include/gguf_qk.h). Host code only validates, picks launch shapes and
+// launches; every arithmetic step runs in the kernels.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/gguf_qk.h"
+#include "dequant.hpp"
+#include "gemm.hpp"
+#include "gemv.hpp"
+#include "probe.hpp"
+
+namespace gqk {
+
+// Per-device scratch for split-K partial sums and row-group counters. It is a
+// static device array (each GPU the library runs on holds its own copy for the
+// life of the process); nothing is allocated at call time. Counters are zero
+// at load and every kernel that uses one returns it to zero.
+constexpr int64_t kScratchPartials = int64_t(2) << 20;   // floats (8 MiB)
+constexpr int64_t kScratchCounters = int64_t(1) << 14;   // row-group counters
+constexpr int kMaxSplits = 16;                            // K ranges per row group
+struct ScratchArea {
+  float partials[kScratchPartials];
+  int counters[kScratchCounters * kCounterStride];
+};
+static __device__ __attribute__((aligned(256))) ScratchArea g_scratch;
+
+constexpr int kMaxDevices = 64;
+
+// Launch-shape knobs. Defaults are the measured best; GGUF_QK_TUNE (for
+// sweeps, e.g. "tasks=2048,q4k_slots=1,q80_slots=1") overrides them.
+struct Tuning {
+  int target_tasks = 2048;   // wave tasks a split-K GEMV aims for
+  int q4k_slots = 1;         // LDS chunks in flight per wave, Q4_K
+  int q80_slots = 1;         // LDS chunks in flight per wave, Q8_0
+};
+
+static const Tuning& tuning() {
+  static const Tuning t = [] {
+    Tuning r;
+    const char* e = std::getenv("GGUF_QK_TUNE");
+    if (!e) return r;
+    const char* p = e;
+    while (*p) {
+      const char* eq = std::strchr(p, '=');
+      if (!eq) break;
+      const std::string key(p, eq - p);
+      const int v = std::atoi(eq + 1);
+      if (key == "tasks" && v > 0) r.target_tasks = v;
+      if (key == "q4k_slots" && (v == 1 || v == 2)) r.q4k_slots = v;
+      if (key == "q80_slots" && (v == 1 || v == 2)) r.q80_slots = v;
+      const char* comma = std::strchr(eq, ',');
+      if (!comma) break;
+      p = comma + 1;
+    }
+    return r;
+  }();
+  return t;
+}
+
+struct DeviceState {
+  std::atomic<int> checked{0};   // 0 unknown, 1 gfx950, -1 unsupported
+  ScratchArea* scratch = nullptr;
+  std::mutex mu;
+};
+static DeviceState g_dev[kMaxDevices];
+
+// Returns GGUF_QK_OK and the scratch of the current device, or an error.
+static int current_device(ScratchArea** scratch) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return GGUF_QK_ERR_DEVICE;
+  }
+  DeviceState& st = g_dev[dev];
+  int c = st.checked.load(std::memory_order_acquire);
+  if (c == 0) {
+    std::lock_guard<std::mutex> lk(st.mu);
+    c = st.checked.load(std::memory_order_relaxed);
+    if (c == 0) {
+      hipDeviceProp_t prop;
+      bool ok = hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+                std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+      void* p = nullptr;
+      if (ok) ok = hipGetSymbolAddress(&p, HIP_SYMBOL(g_scratch)) == hipSuccess && p != nullptr;
+      (void)hipGetLastError();
+      st.scratch = static_cast<ScratchArea*>(p);
+      c = ok ? 1 : -1;
+      st.checked.store(c, std::memory_order_release);
+    }
+  }
+  if (c != 1) return GGUF_QK_ERR_DEVICE;
+  if (scratch) *scratch = st.scratch;
+  return GGUF_QK_OK;
+}
+
+static int launch_status() {
+  return hipGetLastError() == hipSuccess ? GGUF_QK_OK : GGUF_QK_ERR_LAUNCH;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static bool overlap(const void* a, int64_t an, const void* b, int64_t bn) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return an > 0 && bn > 0 && a0 < b0 + (uintptr_t)bn && b0 < a0 + (uintptr_t)an;
+}
+
+// Byte size of rows x row_bytes without overflow, or -1.
+static int64_t mat_bytes(int64_t rows, int64_t row_bytes) {
+  if (rows < 0 || row_bytes <= 0) return -1;
+  if (rows > 0 && row_bytes > INT64_MAX / rows) return -1;
+  return rows * row_bytes;
+}
+
+static int64_t row_bytes_of(int type, int64_t cols) {
+  if (cols <= 0) return GGUF_QK_ERR_SHAPE;
+  if (type == GGUF_QK_TYPE_Q8_0) {
+    if (cols % kQ80BlockWeights) return GGUF_QK_ERR_SHAPE;
+    if (cols / kQ80BlockWeights > INT64_MAX / kQ80BlockBytes) return GGUF_QK_ERR_SHAPE;
+    return cols / kQ80BlockWeights * kQ80BlockBytes;
+  }
+  if (type == GGUF_QK_TYPE_Q4_K) {
+    if (cols % kQ4KBlockWeights) return GGUF_QK_ERR_SHAPE;
+    if (cols / kQ4KBlockWeights > INT64_MAX / kQ4KBlockBytes) return GGUF_QK_ERR_SHAPE;
+    return cols / kQ4KBlockWeights * kQ4KBlockBytes;
+  }
+  return GGUF_QK_ERR_SHAPE;
+}
+
+// Common validation of (W, out-ish) element ranges for a [rows x cols] matrix.
+static int check_matrix(int type, const void* W, int64_t rows, int64_t cols, int64_t* wbytes) {
+  if (!W) return GGUF_QK_ERR_NULL;
+  if (rows < 0) return GGUF_QK_ERR_SHAPE;
+  const int64_t rb = row_bytes_of(type, cols);
+  if (rb < 0) return (int)rb;
+  const int64_t wb = mat_bytes(rows, rb);
+  if (wb < 0) return GGUF_QK_ERR_SHAPE;
+  if (!aligned16(W)) return GGUF_QK_ERR_ALIGN;
+  *wbytes = wb;
+  return GGUF_QK_OK;
+}
+
+static int grid_1d(int64_t n, int per) { return (int)((n + per - 1) / per); }
+
+}  // namespace gqk
+
+using namespace gqk;
+
+extern "C" {
+
+int gguf_qk_abi_version(void) { return GGUF_QK_ABI_VERSION; }
+
+const char* gguf_qk_strerror(int status) {
+  switch (status) {
+    case GGUF_QK_OK: return "ok";
+    case GGUF_QK_ERR_NULL: return "null pointer argument";
+    case GGUF_QK_ERR_SHAPE: return "invalid shape (rows/n_tokens < 0, cols <= 0, cols not a multiple of the block, or size overflow)";
+    case GGUF_QK_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case GGUF_QK_ERR_ALIAS: return "output overlaps an input";
+    case GGUF_QK_ERR_DEVICE: return "no HIP device, or the current device is not gfx950";
+    case GGUF_QK_ERR_LAUNCH: return "kernel launch failed";
+    case GGUF_QK_ERR_LIMIT: return "request exceeds a library limit";
+    default: return "unknown status";
+  }
+}
+
+int64_t gguf_row_bytes(int type, int64_t cols) { return row_bytes_of(type, cols); }
+
+static int dequant_common(int type, const void* W, void* out, int64_t out_elem_bytes,
+                          int64_t rows, int64_t cols, hipStream_t stream, int kind) {
+  int64_t wb = 0;
+  int st = check_matrix(type, W, rows, cols, &wb);
+  if (st) return st;
+  if (!out) return GGUF_QK_ERR_NULL;
+  if (!aligned16(out)) return GGUF_QK_ERR_ALIGN;
+  if (rows > 0 && cols > INT64_MAX / out_elem_bytes / rows) return GGUF_QK_ERR_SHAPE;
+  const int64_t ob = rows * cols * out_elem_bytes;
+  if (overlap(W, wb, out, ob)) return GGUF_QK_ERR_ALIAS;
+  if (rows == 0) return GGUF_QK_OK;
+  st = current_device(nullptr);
+  if (st) return st;
+  const int64_t quads = rows * cols / 4;
+  if (grid_1d(quads, 256) <= 0 || quads / 256 >= INT32_MAX) return GGUF_QK_ERR_LIMIT;
+  const dim3 grid(grid_1d(quads, 256)), block(256);
+  const uint8_t* w = static_cast<const uint8_t*>(W);
+  if (kind == 0)
+    hipLaunchKernelGGL(dequant_q8_0_kernel, grid, block, 0, stream, w, static_cast<float4*>(out), quads);
+  else if (kind == 1)
+    hipLaunchKernelGGL(dequant_q4_k_kernel, grid, block, 0, stream, w, static_cast<float4*>(out), quads);
+  else
+    hipLaunchKernelGGL(dequant_q4_k_bf16_kernel, grid, block, 0, stream, w, static_cast<uint2*>(out), quads);
+  return launch_status();
+}
+
+int dequant_q8_0(const void* W, float* out, int64_t rows, int64_t cols, hipStream_t stream) {
+  return dequant_common(GGUF_QK_TYPE_Q8_0, W, out, 4, rows, cols, stream, 0);
+}
+
+int dequant_q4_k(const void* W, float* out, int64_t rows, int64_t cols, hipStream_t stream) {
+  return dequant_common(GGUF_QK_TYPE_Q4_K, W, out, 4, rows, cols, stream, 1);
+}
+
+int dequant_q4_k_bf16(const void* W, uint16_t* out, int64_t rows, int64_t cols, hipStream_t stream) {
+  return dequant_common(GGUF_QK_TYPE_Q4_K, W, out, 2, rows, cols, stream, 2);
+}
+
+// Validates one GEMV (type, W, x, y, rows, cols). Returns its weight bytes.
+static int check_gemv(int type, const void* W, const float* x, const float* y, int64_t rows,
+                      int64_t cols, int64_t* wbytes) {
+  int st = check_matrix(type, W, rows, cols, wbytes);
+  if (st) return st;
+  if (!x || !y) return GGUF_QK_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return GGUF_QK_ERR_ALIGN;
+  if (rows > INT64_MAX / 4 || cols > INT64_MAX / 4) return GGUF_QK_ERR_SHAPE;
+  if (overlap(y, rows * 4, W, *wbytes) || overlap(y, rows * 4, x, cols * 4)) return GGUF_QK_ERR_ALIAS;
+  if (row_bytes_of(type, cols) * 64 > INT32_MAX) return GGUF_QK_ERR_LIMIT;   // 32-bit tile offsets
+  return GGUF_QK_OK;
+}
+
+// Launches one group of same-format GEMVs (already validated, rows > 0).
+// Q8_0 GEMVs with cols % 256 != 0 are not grouped (see launch_gemvs).
+static int launch_group(int type, const gguf_qk_gemv* const* v, int n, const ScratchArea* scratch,
+                        hipStream_t stream) {
+  GemvGroup grp{};
+  grp.n = n;
+  int64_t total_bytes = 0;
+  for (int i = 0; i < n; ++i) total_bytes += v[i]->rows * row_bytes_of(type, v[i]->cols);
+  int64_t tasks = 0, part_off = 0, cnt_off = 0;
+  for (int i = 0; i < n; ++i) {
+    const gguf_qk_gemv& g = *v[i];
+    const int nch = (int)(g.cols / 256);   // Q4_K super-blocks or Q8_0 8-block chunks
+    const int64_t RG = (g.rows + 63) / 64;
+    const int64_t bytes = g.rows * row_bytes_of(type, g.cols);
+    int64_t want = (int64_t)((double)tuning().target_tasks * (double)bytes / (double)total_bytes);
+    if (want < 1) want = 1;
+    int64_t P = (want + RG - 1) / RG;
+    if (P > nch) P = nch;
+    if (P > kMaxSplits) P = kMaxSplits;
+    if (P < 1) P = 1;
+    while (P > 1 && part_off + P * g.rows > kScratchPartials) --P;
+    if (P > 1 && cnt_off + RG > kScratchCounters) P = 1;
+    GemvDesc& d = grp.d[i];
+    d.W = static_cast<const uint8_t*>(g.W);
+    d.x = g.x;
+    d.y = g.y;
+    d.rows = g.rows;
+    d.nchunks = nch;
+    d.P = (int)P;
+    d.part_off = part_off;
+    d.cnt_off = (int)cnt_off;
+    tasks += RG * P;
+    d.task_end = tasks;
+    if (P > 1) {
+      part_off += P * g.rows;
+      cnt_off += RG;
+    }
+  }
+  const int64_t blocks = (tasks + kGemvWaves - 1) / kGemvWaves;
+  if (blocks > INT32_MAX) return GGUF_QK_ERR_LIMIT;
+  float* partials = const_cast<float*>(scratch->partials);
+  int* counters = const_cast<int*>(scratch->counters);
+  const dim3 grid((unsigned)blocks), block(kGemvWaves * 64);
+  if (type == GGUF_QK_TYPE_Q4_K) {
+    if (tuning().q4k_slots == 2)
+      hipLaunchKernelGGL((gemv_group_kernel<2, true>), grid, block, 0, stream, grp, partials, counters);
+    else
+      hipLaunchKernelGGL((gemv_group_kernel<1, true>), grid, block, 0, stream, grp, partials, counters);
+  } else {
+    if (tuning().q80_slots == 2)
+      hipLaunchKernelGGL((gemv_group_kernel<2, false>), grid, block, 0, stream, grp, partials, counters);
+    else
+      hipLaunchKernelGGL((gemv_group_kernel<1, false>), grid, block, 0, stream, grp, partials, counters);
+  }
+  return launch_status();
+}
+
+static int launch_rowwise_q8_0(const gguf_qk_gemv& g, hipStream_t stream) {
+  const int64_t blocks = (g.rows + 3) / 4;
+  if (blocks > INT32_MAX || g.cols / kQ80BlockWeights > INT32_MAX) return GGUF_QK_ERR_LIMIT;
+  hipLaunchKernelGGL(gemv_q8_0_rowwise_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(g.W), g.x, g.y, g.rows,
+                     (int)(g.cols / kQ80BlockWeights));
+  return launch_status();
+}
+
+// Launches the GEMVs of one step: same-format GEMVs go together, kMaxGroup at
+// a time; each launch follows the previous one on the stream.
+static int launch_step(const gguf_qk_gemv* list, int n, const ScratchArea* scratch,
+                       hipStream_t stream) {
+  for (int type : {GGUF_QK_TYPE_Q4_K, GGUF_QK_TYPE_Q8_0}) {
+    const gguf_qk_gemv* grp[kMaxGroup];
+    int k = 0;
+    for (int i = 0; i < n; ++i) {
+      const gguf_qk_gemv& g = list[i];
+      if (g.type != type || g.rows == 0) continue;
+      if (type == GGUF_QK_TYPE_Q8_0 && g.cols % 256) {
+        const int st = launch_rowwise_q8_0(g, stream);
+        if (st) return st;
+        continue;
+      }
+      grp[k++] = &g;
+      if (k == kMaxGroup) {
+        const int st = launch_group(type, grp, k, scratch, stream);
+        if (st) return st;
+        k = 0;
+      }
+    }
+    if (k) {
+      const int st = launch_group(type, grp, k, scratch, stream);
+      if (st) return st;
+    }
+  }
+  return GGUF_QK_OK;
+}
+
+static int matvec_common(int type, const void* W, const float* x, float* y, int64_t rows,
+                         int64_t cols, hipStream_t stream) {
+  int64_t wb = 0;
+  int st = check_gemv(type, W, x, y, rows, cols, &wb);
+  if (st) return st;
+  if (rows == 0) return GGUF_QK_OK;
+  ScratchArea* scratch = nullptr;
+  st = current_device(&scratch);
+  if (st) return st;
+  const gguf_qk_gemv g{W, x, y, rows, cols, type, 0, {0}};
+  return launch_step(&g, 1, scratch, stream);
+}
+
+int gguf_qmatvec_batch(const gguf_qk_gemv* list, int32_t n, hipStream_t stream) {
+  if (n < 0) return GGUF_QK_ERR_SHAPE;
+  if (n == 0) return GGUF_QK_OK;
+  if (!list) return GGUF_QK_ERR_NULL;
+  // validate everything before any HIP call
+  for (int32_t i = 0; i < n; ++i) {
+    int64_t wb = 0;
+    const gguf_qk_gemv& g = list[i];
+    if (g.type != GGUF_QK_TYPE_Q8_0 && g.type != GGUF_QK_TYPE_Q4_K) return GGUF_QK_ERR_SHAPE;
+    const int st = check_gemv(g.type, g.W, g.x, g.y, g.rows, g.cols, &wb);
+    if (st) return st;
+  }
+  // inside a step, no output may overlap another entry's output or input
+  for (int32_t i = 0; i < n;) {
+    int32_t j = i;
+    while (j < n && list[j].stage == list[i].stage) ++j;
+    for (int32_t a = i; a < j; ++a)
+      for (int32_t b = i; b < j; ++b) {
+        if (a == b) continue;
+        const int64_t wb = list[b].rows * row_bytes_of(list[b].type, list[b].cols);
+        if (overlap(list[a].y, list[a].rows * 4, list[b].y, list[b].rows * 4) ||
+            overlap(list[a].y, list[a].rows * 4, list[b].x, list[b].cols * 4) ||
+            overlap(list[a].y, list[a].rows * 4, list[b].W, wb))
+          return GGUF_QK_ERR_ALIAS;
+      }
+    i = j;
+  }
+  ScratchArea* scratch = nullptr;
+  int st = current_device(&scratch);
+  if (st) return st;
+  for (int32_t i = 0; i < n;) {
+    int32_t j = i;
+    while (j < n && list[j].stage == list[i].stage) ++j;
+    st = launch_step(list + i, j - i, scratch, stream);
+    if (st) return st;
+    i = j;
+  }
+  return GGUF_QK_OK;
+}
+
+int gguf_qmatvec_q8_0(const void* W, const float* x, float* y, int64_t rows, int64_t cols,
+                      hipStream_t stream) {
+  return matvec_common(GGUF_QK_TYPE_Q8_0, W, x, y, rows, cols, stream);
+}
+
+int gguf_qmatvec_q4_k(const void* W, const float* x, float* y, int64_t rows, int64_t cols,
+                      hipStream_t stream) {
+  return matvec_common(GGUF_QK_TYPE_Q4_K, W, x, y, rows, cols, stream);
+}
+
+int gguf_qmatmul_q4_k(const void* W, const uint16_t* X, uint16_t* Y, int64_t n_tokens,
+                      int64_t rows, int64_t cols, hipStream_t stream) {
+  int64_t wb = 0;
+  int st = check_matrix(GGUF_QK_TYPE_Q4_K, W, rows, cols, &wb);
+  if (st) return st;
+  if (!X || !Y) return GGUF_QK_ERR_NULL;
+  if (n_tokens < 0) return GGUF_QK_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(Y)) return GGUF_QK_ERR_ALIGN;
+  if (n_tokens > 0 && (cols > INT64_MAX / 2 / n_tokens || rows > INT64_MAX / 2 / n_tokens))
+    return GGUF_QK_ERR_SHAPE;
+  const int64_t xb = n_tokens * cols * 2, yb = n_tokens * rows * 2;
+  if (overlap(Y, yb, W, wb) || overlap(Y, yb, X, xb)) return GGUF_QK_ERR_ALIAS;
+  if (rows == 0 || n_tokens == 0) return GGUF_QK_OK;
+  st = current_device(nullptr);
+  if (st) return st;
+  const int64_t gx = (rows + kGemmBN - 1) / kGemmBN, gy = (n_tokens + kGemmBM - 1) / kGemmBM;
+  if (gx > INT32_MAX || gy > 65535) return GGUF_QK_ERR_LIMIT;
+  hipLaunchKernelGGL(gemm_q4_k_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(W), X, Y, n_tokens, rows,
+                     (int)(cols / kQ4KBlockWeights));
+  return launch_status();
+}
+
+int gguf_qk_probe_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!buf || !sink) return GGUF_QK_ERR_NULL;
+  if (bytes < 0 || bytes % 16) return GGUF_QK_ERR_SHAPE;
+  if (!aligned16(buf) || !aligned16(sink)) return GGUF_QK_ERR_ALIGN;
+  if (overlap(sink, 4, buf, bytes)) return GGUF_QK_ERR_ALIAS;
+  if (bytes == 0) return GGUF_QK_OK;
+  int st = current_device(nullptr);
+  if (st) return st;
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return GGUF_QK_ERR_DEVICE;
+  }
+  const int64_t n16 = bytes / 16;
+  int64_t blocks = (int64_t)cus * 8;
+  const int64_t need = (n16 + kProbeThreads - 1) / kProbeThreads;
+  if (blocks > need) blocks = need;
+  hipLaunchKernelGGL(probe_read_kernel, dim3((unsigned)blocks), dim3(kProbeThreads), 0, stream,
+                     static_cast<const u32x4*>(buf), n16, sink);
+  return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,164 @@
+/*
+ * gguf_qk.h -- C ABI of libgguf_qk.so: dequantization of GGUF block-quantized
+ * weight matrices (Q8_0, Q4_K) and the fused dequantize-and-multiply against
+ * activations on an AMD Instinct MI355X (gfx950).
+ *
+ * Formats (bytes exactly as a GGUF file stores them, never repacked):
+ *
+ *  Q8_0  34-byte blocks of 32 consecutive weights of one row: a little-endian
+ *        fp16 multiplier d, then 32 int8 values q; w = q * d.
+ *        ("GGUF Inferencer in R", section 2.1, byte blueprint of a Q8_0 tensor;
+ *        "GGUF: The File Format Powering Local LLM Inference", "How a Q8_0
+ *        block is stored".)
+ *
+ *  Q4_K  144-byte super-blocks of 256 weights of one row, 8 sub-blocks of 32,
+ *        each sub-block with a 6-bit scale and a 6-bit min
+ *        ("GGUF: The File Format...", k-quant paragraph and bits-per-weight
+ *        table). Field placement (GGUF's on-disk layout; not printed on those
+ *        pages): bytes 0-1 fp16 d, 2-3 fp16 dmin, 4-15 twelve bytes S holding
+ *        the 8 scales sc[j] and 8 mins m[j] (j<4: sc=S[j]&63, m=S[j+4]&63;
+ *        j>=4: sc=(S[j+4]&15)|((S[j-4]>>6)<<4), m=(S[j+4]>>4)|((S[j]>>6)<<4)),
+ *        16-143 quants: byte 32g+l holds weight 64g+l in its low nibble and
+ *        weight 64g+32+l in its high nibble. w = d*sc[j]*q - dmin*m[j].
+ *
+ * Matrix layout: W is rows x cols (cols = K fastest), stored as `rows` runs of
+ * gguf_row_bytes(type, cols) bytes with no padding between rows ("GGUF
+ * Inferencer in R", section 2.1: Q8_0 x cols/32 chunks per row, rows back to
+ * back). The matvec computes y[r] = sum_k w[r,k] x[k] (culpeo.ws blog, the
+ * naive-implementation post, matvec(w:[r,c], x:[c]) -> [r]).
+ *
+ * Conventions for every entry point below:
+ *  - All pointers are DEVICE pointers into memory the caller owns and
+ *    allocated (the output memory is always provided by the caller, as in the
+ *    culpeo.ws naive-implementation post). The library keeps no pointer after
+ *    returning.
+ *  - Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *    without synchronizing. Device-side faults surface at the caller's next
+ *    synchronization, as for any HIP operation.
+ *  - Arguments are validated before any HIP call; a failed call enqueues
+ *    nothing and returns a negative status. rows == 0 (or n_tokens == 0)
+ *    returns GGUF_QK_OK without launching anything.
+ *  - Outputs are fully overwritten (never accumulated into).
+ *  - W needs 16-byte alignment; x, y, X, Y need 16-byte alignment.
+ *  - The multiply entry points and the decode-stream entry points share one
+ *    per-device scratch area inside the library (partial sums and counters,
+ *    a static device array: nothing is allocated at call time). Calls that
+ *    run concurrently on one device (different streams overlapping in time)
+ *    race on it; issue them on one stream, or serialize them.
+ */
+#ifndef GGUF_QK_H
+#define GGUF_QK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GGUF_QK_ABI_VERSION 1
+
+/* Status codes. */
+#define GGUF_QK_OK 0
+#define GGUF_QK_ERR_NULL (-1)     /* a required pointer is NULL */
+#define GGUF_QK_ERR_SHAPE (-2)    /* rows/n_tokens < 0, cols <= 0, cols not a multiple of
+                                     32 (Q8_0) or 256 (Q4_K), or a byte size overflows */
+#define GGUF_QK_ERR_ALIGN (-3)    /* a pointer is not 16-byte aligned */
+#define GGUF_QK_ERR_ALIAS (-4)    /* an output range overlaps an input range */
+#define GGUF_QK_ERR_DEVICE (-5)   /* no HIP device, or the current device is not gfx950 */
+#define GGUF_QK_ERR_LAUNCH (-6)   /* the kernel launch failed */
+#define GGUF_QK_ERR_LIMIT (-7)    /* request exceeds a documented library limit */
+
+/* Tensor type ids as a GGUF tensor-info record stores them: 8 = Q8_0 ("GGUF
+ * Inferencer in R", section 2.1, example tensor entry); 12 = Q4_K (GGUF's id,
+ * not printed on those pages). */
+#define GGUF_QK_TYPE_Q8_0 8
+#define GGUF_QK_TYPE_Q4_K 12
+
+/* ABI version of the loaded library (GGUF_QK_ABI_VERSION it was built with). */
+int gguf_qk_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* gguf_qk_strerror(int status);
+
+/* Bytes of one row of `cols` weights of `type`, or a negative status
+ * (GGUF_QK_ERR_SHAPE for an unknown type or a cols the type cannot hold). */
+int64_t gguf_row_bytes(int type, int64_t cols);
+
+/* --- standalone dequantization ------------------------------------------ */
+
+/* out[r*cols + k] = w[r,k] as fp32 (row-major [rows x cols]). The value is
+ * bit-exact: Q8_0's q*d is exact in fp32; Q4_K's d*sc*q and dmin*m are exact
+ * and their difference is rounded once to nearest-even. */
+int dequant_q8_0(const void* W, float* out, int64_t rows, int64_t cols, hipStream_t stream);
+int dequant_q4_k(const void* W, float* out, int64_t rows, int64_t cols, hipStream_t stream);
+
+/* out = bf16 bit patterns of the fp32 dequant above, rounded to nearest-even
+ * (the tile type of the prefill path). */
+int dequant_q4_k_bf16(const void* W, uint16_t* out, int64_t rows, int64_t cols,
+                      hipStream_t stream);
+
+/* --- decode: fused dequant x vector (batch 1) ----------------------------- */
+
+/* y[r] = sum_k w[r,k] * x[k]; x fp32 [cols], y fp32 [rows]. fp32 arithmetic,
+ * any summation order; deterministic (two calls give identical bits).
+ * Q8_0 needs cols % 32 == 0, Q4_K cols % 256 == 0. */
+int gguf_qmatvec_q8_0(const void* W, const float* x, float* y, int64_t rows, int64_t cols,
+                      hipStream_t stream);
+int gguf_qmatvec_q4_k(const void* W, const float* x, float* y, int64_t rows, int64_t cols,
+                      hipStream_t stream);
+
+/* --- decode step: an ordered list of GEMVs -------------------------------- */
+
+/* One GEMV of a list: y[r] = sum_k w[r,k] x[k] as above. */
+typedef struct gguf_qk_gemv {
+  const void* W;   /* device, rows x gguf_row_bytes(type, cols) bytes */
+  const float* x;  /* device, cols floats */
+  float* y;        /* device, rows floats (written) */
+  int64_t rows;
+  int64_t cols;
+  int32_t type;    /* GGUF_QK_TYPE_Q8_0 or GGUF_QK_TYPE_Q4_K */
+  int32_t stage;   /* adjacent entries with equal stage form one step */
+  int32_t reserved[2];
+} gguf_qk_gemv;
+
+/* Runs the GEMVs of `list` (a HOST array of n entries, read during the call)
+ * as a sequence of steps on `stream`: adjacent entries with the same `stage`
+ * form one step and may run concurrently (in one launch when they share a
+ * format), so within a step no y may overlap another entry's y, x or W
+ * (GGUF_QK_ERR_ALIAS). Each step starts after the previous step has finished,
+ * exactly as if every step were issued separately on the stream, so an entry
+ * may read as x what an earlier step wrote as y. This is the decode step of a
+ * transformer layer: q/k/v read the same normalised input, so do gate/up
+ * ("GGUF Inferencer in R", section 5.2: Q, K and V come from the same normed
+ * input; G and U likewise). Every entry is validated before anything is
+ * enqueued. */
+int gguf_qmatvec_batch(const gguf_qk_gemv* list, int32_t n, hipStream_t stream);
+
+/* --- prefill: fused dequant x matrix (small batch, MFMA) ------------------ */
+
+/* Y[n, r] = sum_k X[n, k] * w[r, k] for n < n_tokens. X bf16 row-major
+ * [n_tokens x cols], Y bf16 row-major [n_tokens x rows]. The prefill is the
+ * decode math with the whole prompt as one matrix ("GGUF Inferencer in R",
+ * section 1 and section 4). Weights are dequantized to bf16 (nearest-even)
+ * tiles, multiplied on the matrix cores with fp32 accumulation, and Y is
+ * rounded to nearest-even bf16. */
+int gguf_qmatmul_q4_k(const void* W, const uint16_t* X, uint16_t* Y, int64_t n_tokens,
+                      int64_t rows, int64_t cols, hipStream_t stream);
+
+/* --- measurement ---------------------------------------------------------- */
+
+/* Streaming-read probe: reads `bytes` (a multiple of 16) from device buffer
+ * `buf` once with 16-byte vector loads spread over every compute unit, and
+ * writes nothing unless the XOR of all words equals 0x9E3779B9, in which case
+ * it stores that word to *sink. Timing it gives the device's achievable read
+ * bandwidth, the practical ceiling for the weight stream. */
+int gguf_qk_probe_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GGUF_QK_H */

@@ -1,0 +1,175 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad arguments before any HIP call. No compute call is made: every
+call here fails validation (or, with no device present, the device check)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gguf_block_quant_dequant_amd as g
+from gguf_block_quant_dequant_amd.build import LIB_PATH
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "gguf_qk.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB_PATH),
+                                reason="libgguf_qk.so not built (run the build step first)")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    body = text.split('extern "C" {', 1)[1]
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       body, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ["gguf_qmatvec_q8_0", "gguf_qmatvec_q4_k", "gguf_qmatmul_q4_k", "dequant_q8_0",
+              "dequant_q4_k", "dequant_q4_k_bf16", "gguf_row_bytes", "gguf_qk_strerror",
+              "gguf_qk_abi_version", "gguf_qmatvec_batch"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    L = ctypes.CDLL(LIB_PATH)
+    missing = [n for n in _declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_binding_names_match_header():
+    for n in _declared_functions():
+        assert hasattr(g, n), n
+
+
+def test_version_and_strerror():
+    assert g.gguf_qk_abi_version() == 1
+    for s in range(-7, 1):
+        assert g.gguf_qk_strerror(s)
+    assert g.gguf_qk_strerror(-99) == "unknown status"
+
+
+def test_row_bytes():
+    assert g.gguf_row_bytes(g.TYPE_Q8_0, 2048) == 2176
+    assert g.gguf_row_bytes(g.TYPE_Q8_0, 512) == 544
+    assert g.gguf_row_bytes(g.TYPE_Q4_K, 2048) == 1152
+    assert g.gguf_row_bytes(g.TYPE_Q4_K, 11008) == 6192
+    assert g.gguf_row_bytes(g.TYPE_Q4_K, 100) == g.ERR_SHAPE
+    assert g.gguf_row_bytes(g.TYPE_Q8_0, 33) == g.ERR_SHAPE
+    assert g.gguf_row_bytes(g.TYPE_Q8_0, 0) == g.ERR_SHAPE
+    assert g.gguf_row_bytes(99, 256) == g.ERR_SHAPE
+
+
+# Fake, never-dereferenced addresses: every call below fails validation first.
+A = 0x10000
+B = 0x20000
+C = 0x30000
+
+
+def _mv(name, W, x, y, rows, cols):
+    return getattr(g.lib(), name)(W, x, y, rows, cols, None)
+
+
+@pytest.mark.parametrize("name", ["gguf_qmatvec_q8_0", "gguf_qmatvec_q4_k"])
+def test_matvec_validation(name):
+    assert _mv(name, None, B, C, 4, 256) == g.ERR_NULL
+    assert _mv(name, A, None, C, 4, 256) == g.ERR_NULL
+    assert _mv(name, A, B, None, 4, 256) == g.ERR_NULL
+    assert _mv(name, A, B, C, -1, 256) == g.ERR_SHAPE
+    assert _mv(name, A, B, C, 4, 0) == g.ERR_SHAPE
+    assert _mv(name, A, B, C, 4, -256) == g.ERR_SHAPE
+    assert _mv(name, A, B, C, 4, 255) == g.ERR_SHAPE
+    assert _mv(name, A, B, C, 1 << 62, 1 << 40) == g.ERR_SHAPE      # byte size overflows
+    assert _mv(name, A + 2, B, C, 4, 256) == g.ERR_ALIGN
+    assert _mv(name, A, B + 4, C, 4, 256) == g.ERR_ALIGN
+    assert _mv(name, A, B, C + 8, 4, 256) == g.ERR_ALIGN
+    assert _mv(name, A, B, A + 16, 4, 256) == g.ERR_ALIAS           # y inside W
+    assert _mv(name, A, B, B, 4, 256) == g.ERR_ALIAS                # y == x
+    assert _mv(name, A, B, C, 0, 256) == g.OK                       # nothing to do
+
+
+def test_q4_k_matvec_rejects_q8_0_only_widths():
+    assert _mv("gguf_qmatvec_q4_k", A, B, C, 4, 32) == g.ERR_SHAPE
+    assert _mv("gguf_qmatvec_q8_0", A, B, C, 0, 32) == g.OK
+
+
+@pytest.mark.parametrize("name,cols", [("dequant_q8_0", 64), ("dequant_q4_k", 256),
+                                       ("dequant_q4_k_bf16", 256)])
+def test_dequant_validation(name, cols):
+    f = getattr(g.lib(), name)
+    assert f(None, B, 4, cols, None) == g.ERR_NULL
+    assert f(A, None, 4, cols, None) == g.ERR_NULL
+    assert f(A, B, -1, cols, None) == g.ERR_SHAPE
+    assert f(A, B, 4, cols + 1, None) == g.ERR_SHAPE
+    assert f(A + 1, B, 4, cols, None) == g.ERR_ALIGN
+    assert f(A, B + 2, 4, cols, None) == g.ERR_ALIGN
+    assert f(A, A + 16, 4, cols, None) == g.ERR_ALIAS
+    assert f(A, B, 0, cols, None) == g.OK
+
+
+def test_matmul_validation():
+    f = g.lib().gguf_qmatmul_q4_k
+    assert f(None, B, C, 8, 4, 256, None) == g.ERR_NULL
+    assert f(A, None, C, 8, 4, 256, None) == g.ERR_NULL
+    assert f(A, B, None, 8, 4, 256, None) == g.ERR_NULL
+    assert f(A, B, C, -1, 4, 256, None) == g.ERR_SHAPE
+    assert f(A, B, C, 8, -4, 256, None) == g.ERR_SHAPE
+    assert f(A, B, C, 8, 4, 128, None) == g.ERR_SHAPE
+    assert f(A, B + 2, C, 8, 4, 256, None) == g.ERR_ALIGN
+    assert f(A, B, B + 16, 8, 4, 256, None) == g.ERR_ALIAS          # Y overlaps X
+    assert f(A, B, C, 0, 4, 256, None) == g.OK
+    assert f(A, B, C, 8, 0, 256, None) == g.OK
+
+
+def _no_gpu_visible():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+@pytest.mark.skipif(not _no_gpu_visible(), reason="only meaningful where no GPU is visible")
+def test_valid_arguments_without_a_device_report_no_device():
+    # Arguments pass validation; with no device the call stops at the device
+    # check and never launches.
+    assert _mv("gguf_qmatvec_q4_k", A, B, C, 4, 256) == g.ERR_DEVICE
+    assert g.lib().dequant_q8_0(A, B, 4, 64, None) == g.ERR_DEVICE
+    assert g.lib().gguf_qmatmul_q4_k(A, B, C, 8, 4, 256, None) == g.ERR_DEVICE
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    W = torch.zeros((4, 144), dtype=torch.uint8)
+    x = torch.zeros(256, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        g.gguf_qmatvec_q4_k(W, x)
+
+
+def _entry(W, x, y, rows, cols, typ, stage):
+    return g.GemvEntry(W, x, y, rows, cols, typ, stage, (0, 0))
+
+
+def test_batch_validation():
+    f = g.lib().gguf_qmatvec_batch
+    arr = (g.GemvEntry * 2)(_entry(A, B, C, 4, 256, g.TYPE_Q4_K, 0),
+                            _entry(A, B, C + 4096, 4, 256, g.TYPE_Q4_K, 0))
+    p = ctypes.cast(arr, ctypes.c_void_p)
+    assert f(None, 1, None) == g.ERR_NULL
+    assert f(p, -1, None) == g.ERR_SHAPE
+    assert f(p, 0, None) == g.OK
+    bad = (g.GemvEntry * 1)(_entry(A, B, C, 4, 256, 3, 0))
+    assert f(ctypes.cast(bad, ctypes.c_void_p), 1, None) == g.ERR_SHAPE
+    bad = (g.GemvEntry * 1)(_entry(A, B, C, 4, 100, g.TYPE_Q4_K, 0))
+    assert f(ctypes.cast(bad, ctypes.c_void_p), 1, None) == g.ERR_SHAPE
+    bad = (g.GemvEntry * 1)(_entry(A, B + 4, C, 4, 256, g.TYPE_Q4_K, 0))
+    assert f(ctypes.cast(bad, ctypes.c_void_p), 1, None) == g.ERR_ALIGN
+    # same step: second y overlaps the first entry's x -> alias
+    bad = (g.GemvEntry * 2)(_entry(A, B, C, 4, 256, g.TYPE_Q4_K, 0),
+                            _entry(A, B, B, 4, 256, g.TYPE_Q4_K, 0))
+    assert f(ctypes.cast(bad, ctypes.c_void_p), 2, None) == g.ERR_ALIAS
+    # same step: two entries write the same y -> alias
+    bad = (g.GemvEntry * 2)(_entry(A, B, C, 4, 256, g.TYPE_Q4_K, 0),
+                            _entry(A + 4096, B, C, 4, 256, g.TYPE_Q4_K, 0))
+    assert f(ctypes.cast(bad, ctypes.c_void_p), 2, None) == g.ERR_ALIAS
