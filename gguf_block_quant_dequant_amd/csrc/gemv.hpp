@@ -67,6 +67,37 @@ typedef float xreg16 __attribute__((ext_vector_type(16)));
 #define GQK_SLOAD16(dst, base, off) \
   asm volatile("s_load_dwordx16 %0, %1, %2" : "=s"(dst) : "s"(base), "n"(off))
 #define GQK_SWAIT(reg) asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(reg))
+
+// Load x[0..15] of a 1 KiB activation range into xa and, in the same
+// round trip, touch its other 15 64-byte lines (one scalar dword each) so
+// that the step-by-step loads that follow hit the scalar cache instead of
+// each paying a miss. The touched words are discarded; their registers are
+// held until the wait so no late load can land in a reused register.
+__device__ __forceinline__ void sload_first_with_touch(xreg16& xa, const float* xs) {
+  uint32_t t[15];
+  asm volatile(
+      "s_load_dwordx16 %0, %16, 0\n"
+      "s_load_dword %1, %16, 64\n"
+      "s_load_dword %2, %16, 128\n"
+      "s_load_dword %3, %16, 192\n"
+      "s_load_dword %4, %16, 256\n"
+      "s_load_dword %5, %16, 320\n"
+      "s_load_dword %6, %16, 384\n"
+      "s_load_dword %7, %16, 448\n"
+      "s_load_dword %8, %16, 512\n"
+      "s_load_dword %9, %16, 576\n"
+      "s_load_dword %10, %16, 640\n"
+      "s_load_dword %11, %16, 704\n"
+      "s_load_dword %12, %16, 768\n"
+      "s_load_dword %13, %16, 832\n"
+      "s_load_dword %14, %16, 896\n"
+      "s_load_dword %15, %16, 960\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=s"(xa), "=s"(t[0]), "=s"(t[1]), "=s"(t[2]), "=s"(t[3]), "=s"(t[4]), "=s"(t[5]),
+        "=s"(t[6]), "=s"(t[7]), "=s"(t[8]), "=s"(t[9]), "=s"(t[10]), "=s"(t[11]), "=s"(t[12]),
+        "=s"(t[13]), "=s"(t[14])
+      : "s"(xs));
+}
 // The wait for step h + 1's activations also takes step h's accumulators as
 // inputs, which pins step h's multiply-adds before it (and, since volatile
 // statements keep their order, before the load for step h + 2).
@@ -197,8 +228,7 @@ __device__ __forceinline__ float q4k_wave_task(const uint8_t* __restrict__ W, co
     if (p < n) dma_chunk<9>(tile + (c0 + p) * kQ4KBlockBytes, off, slots + p * kQ4KChunk);
   float acc = 0.f;
   xreg16 xa;
-  GQK_SLOAD16(xa, xs0, 0);
-  GQK_SWAIT(xa);
+  sload_first_with_touch(xa, xs0);
   for (int i = 0; i < n; ++i) {
     uint8_t* slot = slots + (i % kSlots) * kQ4KChunk;
     // with two slots, chunk i+1's 9 loads (issued after x of i) may stay in flight
@@ -229,8 +259,7 @@ __device__ __forceinline__ float q80_wave_task(const uint8_t* __restrict__ W, co
     if (p < n) dma_chunk<17>(tile + (c0 + p) * kQ80ChunkRowBytes, off, slots + p * kQ80Chunk);
   const float* xs0 = x + (int64_t)c0 * 256;
   xreg16 xa;
-  GQK_SLOAD16(xa, xs0, 0);
-  GQK_SWAIT(xa);
+  sload_first_with_touch(xa, xs0);
   for (int i = 0; i < n; ++i) {
     uint8_t* slot = slots + (i % kSlots) * kQ80Chunk;
     if (kSlots >= 2 && i + 1 < n) GQK_WAIT_VMCNT(17);
@@ -296,12 +325,11 @@ __device__ __forceinline__ void splitk_finish(float acc, float* __restrict__ y, 
 // ---------------------------------------------------------------------------
 // GEMV kernels over a group of up to kMaxGroup same-format GEMVs (one GEMV, or
 // the GEMVs of one decode stage that read the same input, such as q/k/v).
-// Tasks are numbered across the group; task t of GEMV g is row group
-// t_local / P and K range t_local % P. One wave per task slot; waves loop over
-// tasks with stride (grid waves).
 // ---------------------------------------------------------------------------
-constexpr int kGemvWaves = 4;
+constexpr int kGemvWaves = 4;      // per-wave task kernel (Q8_0)
+constexpr int kBlockWaves = 8;     // block task kernel (Q4_K)
 constexpr int kMaxGroup = 4;
+constexpr int kMaxPrefetch = 4;
 
 struct GemvDesc {
   const uint8_t* W;
@@ -316,11 +344,35 @@ struct GemvDesc {
   int pad;
 };
 
-struct GemvGroup {
-  GemvDesc d[kMaxGroup];
+// Byte ranges to pull towards the device (into the memory-side Infinity
+// Cache) while this launch runs: the weights of the next step of a decode
+// pass, so that its loads find them on chip.
+struct Prefetch {
+  const uint8_t* p[kMaxPrefetch];
+  int64_t bytes[kMaxPrefetch];
   int n;
 };
 
+struct GemvGroup {
+  GemvDesc d[kMaxGroup];
+  int n;
+  Prefetch pf;
+};
+
+// Issue this wave's share of the prefetch ranges (wave `gw` of `nw` in the
+// grid) as direct global->LDS loads into a scratch window nothing reads, so
+// they hold no registers; the wave's next vmcnt wait also covers them.
+__device__ __forceinline__ void prefetch_share(const Prefetch& pf, int64_t gw, int64_t nw, int lane,
+                                               uint8_t* junk) {
+  for (int r = 0; r < pf.n; ++r) {
+    const int64_t n1k = pf.bytes[r] >> 10;                 // whole 1 KiB windows
+    const int64_t per = (n1k + nw - 1) / nw;
+    const int64_t w0 = gw * per, w1 = (w0 + per) < n1k ? (w0 + per) : n1k;
+    for (int64_t w = w0; w < w1; ++w) dma16(pf.p[r] + w * 1024 + 16 * lane, junk);
+  }
+}
+
+// Per-wave tasks (each wave one row group x K range). Used for Q8_0.
 template <int kSlots, bool kQ4K>
 __global__ __launch_bounds__(kGemvWaves * 64) void gemv_group_kernel(GemvGroup grp, float* partials,
                                                                     int* counters) {
@@ -351,6 +403,54 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_group_kernel(GemvGroup g
     const SplitK sk{partials + D.part_off, counters + (int64_t)D.cnt_off * kCounterStride};
     splitk_finish(acc, D.y, D.rows, row0, valid, rg, part, P, sk, lane);
   }
+}
+
+// Block tasks for Q4_K: a block of kBlockWaves waves owns one row group and
+// a range of up to kBlockWaves super-blocks along K, one per wave. The waves'
+// 64 partial sums are added in LDS in wave order; a row group whose K is cut
+// into P > 1 ranges (K > kBlockWaves super-blocks) finishes through the
+// split-K hand-off between blocks. The prefetch share is issued first so it
+// overlaps this block's own loads and multiply-adds.
+__global__ __launch_bounds__(kBlockWaves * 64) void gemv_q4k_block_kernel(GemvGroup grp,
+                                                                          float* partials,
+                                                                          int* counters) {
+  __shared__ __attribute__((aligned(16))) uint8_t slots[kBlockWaves][kQ4KChunk];
+  __shared__ __attribute__((aligned(16))) uint8_t junk[1024];
+  __shared__ float red[kBlockWaves][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (grp.pf.n)
+    prefetch_share(grp.pf, (int64_t)blockIdx.x * kBlockWaves + wave,
+                   (int64_t)gridDim.x * kBlockWaves, lane, junk);
+  const int64_t T = grp.d[grp.n - 1].task_end;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    int g = 0;
+    while (g + 1 < grp.n && t >= grp.d[g].task_end) ++g;
+    const GemvDesc& D = grp.d[g];
+    const int64_t lt = t - (g ? grp.d[g - 1].task_end : 0);
+    const int P = D.P;
+    const int rg = (int)(lt / P), part = (int)(lt % P);
+    const int n = D.nchunks;
+    const int c0 = (int)((int64_t)part * n / P), c1 = (int)((int64_t)(part + 1) * n / P);
+    const int64_t row0 = (int64_t)rg * 64;
+    const int valid = (int)((D.rows - row0) < 64 ? (D.rows - row0) : 64);
+    const uint32_t row_bytes = (uint32_t)n * kQ4KBlockBytes;
+    // wave w takes super-blocks c0 + w, c0 + w + kBlockWaves, ...
+    float acc = 0.f;
+    for (int c = c0 + wave; c < c1; c += kBlockWaves)
+      acc += q4k_wave_task<1>(D.W, D.x, row_bytes, row0, valid, c, c + 1, &slots[wave][0], lane);
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < kBlockWaves; ++w) s += red[w][lane];
+      const SplitK sk{partials + D.part_off, counters + (int64_t)D.cnt_off * kCounterStride};
+      splitk_finish(s, D.y, D.rows, row0, valid, rg, part, P, sk, lane);
+    }
+    __syncthreads();
+  }
+  GQK_WAIT_VMCNT(0);   // prefetch loads of waves without a task
 }
 
 // Q8_0 rows whose length is not a multiple of 256 weights (row bytes not a

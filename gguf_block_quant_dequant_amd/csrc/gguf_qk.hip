@@ -39,6 +39,7 @@ struct Tuning {
   int target_tasks = 2048;   // wave tasks a split-K GEMV aims for
   int q4k_slots = 1;         // LDS chunks in flight per wave, Q4_K
   int q80_slots = 1;         // LDS chunks in flight per wave, Q8_0
+  int prefetch = 0;          // decode batches pull the next step's weights on chip (measured slower)
 };
 
 static const Tuning& tuning() {
@@ -55,6 +56,7 @@ static const Tuning& tuning() {
       if (key == "tasks" && v > 0) r.target_tasks = v;
       if (key == "q4k_slots" && (v == 1 || v == 2)) r.q4k_slots = v;
       if (key == "q80_slots" && (v == 1 || v == 2)) r.q80_slots = v;
+      if (key == "prefetch") r.prefetch = v != 0;
       const char* comma = std::strchr(eq, ',');
       if (!comma) break;
       p = comma + 1;
@@ -224,11 +226,16 @@ static int check_gemv(int type, const void* W, const float* x, const float* y, i
 }
 
 // Launches one group of same-format GEMVs (already validated, rows > 0).
-// Q8_0 GEMVs with cols % 256 != 0 are not grouped (see launch_gemvs).
+// Q8_0 GEMVs with cols % 256 != 0 are not grouped (see launch_step).
+// Q4_K runs as block tasks (8 waves per row group and up to 8 super-blocks,
+// partials added in LDS); Q8_0 as per-wave tasks with split-K sized to the
+// task target. `pf` (may be null) lists weight ranges to pull into the
+// Infinity Cache while this launch runs.
 static int launch_group(int type, const gguf_qk_gemv* const* v, int n, const ScratchArea* scratch,
-                        hipStream_t stream) {
+                        hipStream_t stream, const Prefetch* pf) {
   GemvGroup grp{};
   grp.n = n;
+  if (pf) grp.pf = *pf;
   int64_t total_bytes = 0;
   for (int i = 0; i < n; ++i) total_bytes += v[i]->rows * row_bytes_of(type, v[i]->cols);
   int64_t tasks = 0, part_off = 0, cnt_off = 0;
@@ -236,13 +243,18 @@ static int launch_group(int type, const gguf_qk_gemv* const* v, int n, const Scr
     const gguf_qk_gemv& g = *v[i];
     const int nch = (int)(g.cols / 256);   // Q4_K super-blocks or Q8_0 8-block chunks
     const int64_t RG = (g.rows + 63) / 64;
-    const int64_t bytes = g.rows * row_bytes_of(type, g.cols);
-    int64_t want = (int64_t)((double)tuning().target_tasks * (double)bytes / (double)total_bytes);
-    if (want < 1) want = 1;
-    int64_t P = (want + RG - 1) / RG;
-    if (P > nch) P = nch;
-    if (P > kMaxSplits) P = kMaxSplits;
-    if (P < 1) P = 1;
+    int64_t P;
+    if (type == GGUF_QK_TYPE_Q4_K) {
+      P = (nch + kBlockWaves - 1) / kBlockWaves;
+    } else {
+      const int64_t bytes = g.rows * row_bytes_of(type, g.cols);
+      int64_t want = (int64_t)((double)tuning().target_tasks * (double)bytes / (double)total_bytes);
+      if (want < 1) want = 1;
+      P = (want + RG - 1) / RG;
+      if (P > nch) P = nch;
+      if (P > kMaxSplits) P = kMaxSplits;
+      if (P < 1) P = 1;
+    }
     while (P > 1 && part_off + P * g.rows > kScratchPartials) --P;
     if (P > 1 && cnt_off + RG > kScratchCounters) P = 1;
     GemvDesc& d = grp.d[i];
@@ -261,22 +273,21 @@ static int launch_group(int type, const gguf_qk_gemv* const* v, int n, const Scr
       cnt_off += RG;
     }
   }
-  const int64_t blocks = (tasks + kGemvWaves - 1) / kGemvWaves;
-  if (blocks > INT32_MAX) return GGUF_QK_ERR_LIMIT;
   float* partials = const_cast<float*>(scratch->partials);
   int* counters = const_cast<int*>(scratch->counters);
-  const dim3 grid((unsigned)blocks), block(kGemvWaves * 64);
   if (type == GGUF_QK_TYPE_Q4_K) {
-    if (tuning().q4k_slots == 2)
-      hipLaunchKernelGGL((gemv_group_kernel<2, true>), grid, block, 0, stream, grp, partials, counters);
-    else
-      hipLaunchKernelGGL((gemv_group_kernel<1, true>), grid, block, 0, stream, grp, partials, counters);
-  } else {
-    if (tuning().q80_slots == 2)
-      hipLaunchKernelGGL((gemv_group_kernel<2, false>), grid, block, 0, stream, grp, partials, counters);
-    else
-      hipLaunchKernelGGL((gemv_group_kernel<1, false>), grid, block, 0, stream, grp, partials, counters);
+    if (tasks > INT32_MAX) return GGUF_QK_ERR_LIMIT;
+    hipLaunchKernelGGL(gemv_q4k_block_kernel, dim3((unsigned)tasks), dim3(kBlockWaves * 64), 0,
+                       stream, grp, partials, counters);
+    return launch_status();
   }
+  const int64_t blocks = (tasks + kGemvWaves - 1) / kGemvWaves;
+  if (blocks > INT32_MAX) return GGUF_QK_ERR_LIMIT;
+  const dim3 grid((unsigned)blocks), block(kGemvWaves * 64);
+  if (tuning().q80_slots == 2)
+    hipLaunchKernelGGL((gemv_group_kernel<2, false>), grid, block, 0, stream, grp, partials, counters);
+  else
+    hipLaunchKernelGGL((gemv_group_kernel<1, false>), grid, block, 0, stream, grp, partials, counters);
   return launch_status();
 }
 
@@ -292,7 +303,7 @@ static int launch_rowwise_q8_0(const gguf_qk_gemv& g, hipStream_t stream) {
 // Launches the GEMVs of one step: same-format GEMVs go together, kMaxGroup at
 // a time; each launch follows the previous one on the stream.
 static int launch_step(const gguf_qk_gemv* list, int n, const ScratchArea* scratch,
-                       hipStream_t stream) {
+                       hipStream_t stream, const Prefetch* pf) {
   for (int type : {GGUF_QK_TYPE_Q4_K, GGUF_QK_TYPE_Q8_0}) {
     const gguf_qk_gemv* grp[kMaxGroup];
     int k = 0;
@@ -306,13 +317,13 @@ static int launch_step(const gguf_qk_gemv* list, int n, const ScratchArea* scrat
       }
       grp[k++] = &g;
       if (k == kMaxGroup) {
-        const int st = launch_group(type, grp, k, scratch, stream);
+        const int st = launch_group(type, grp, k, scratch, stream, pf);
         if (st) return st;
         k = 0;
       }
     }
     if (k) {
-      const int st = launch_group(type, grp, k, scratch, stream);
+      const int st = launch_group(type, grp, k, scratch, stream, pf);
       if (st) return st;
     }
   }
@@ -329,7 +340,7 @@ static int matvec_common(int type, const void* W, const float* x, float* y, int6
   st = current_device(&scratch);
   if (st) return st;
   const gguf_qk_gemv g{W, x, y, rows, cols, type, 0, {0}};
-  return launch_step(&g, 1, scratch, stream);
+  return launch_step(&g, 1, scratch, stream, nullptr);
 }
 
 int gguf_qmatvec_batch(const gguf_qk_gemv* list, int32_t n, hipStream_t stream) {
@@ -365,7 +376,18 @@ int gguf_qmatvec_batch(const gguf_qk_gemv* list, int32_t n, hipStream_t stream) 
   for (int32_t i = 0; i < n;) {
     int32_t j = i;
     while (j < n && list[j].stage == list[i].stage) ++j;
-    st = launch_step(list + i, j - i, scratch, stream);
+    // the next step's weights, pulled on chip while this step runs
+    Prefetch pf{};
+    if (tuning().prefetch && j < n) {
+      int32_t k = j;
+      while (k < n && list[k].stage == list[j].stage && pf.n < kMaxPrefetch) {
+        pf.p[pf.n] = static_cast<const uint8_t*>(list[k].W);
+        pf.bytes[pf.n] = list[k].rows * row_bytes_of(list[k].type, list[k].cols);
+        ++pf.n;
+        ++k;
+      }
+    }
+    st = launch_step(list + i, j - i, scratch, stream, pf.n ? &pf : nullptr);
     if (st) return st;
     i = j;
   }
