@@ -67,6 +67,8 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_window) {
 // writes, does not insert a wait for ALL outstanding vector loads before them;
 // the caller has already waited (GQK_WAIT_VMCNT) for the loads that filled
 // these bytes. Each block ends with lgkmcnt(0), so results are ready on exit.
+// Outputs are early-clobber: a read may return before the block's later reads
+// have issued, so no destination may share registers with the address.
 __device__ __forceinline__ void lds_read_9x16(uint32_t addr, uint32_t (&o)[36]) {
   i32x4 v0, v1, v2, v3, v4, v5, v6, v7, v8;
   asm volatile(
@@ -80,7 +82,7 @@ __device__ __forceinline__ void lds_read_9x16(uint32_t addr, uint32_t (&o)[36]) 
       "ds_read_b128 %7, %9 offset:112\n"
       "ds_read_b128 %8, %9 offset:128\n"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(v0), "=v"(v1), "=v"(v2), "=v"(v3), "=v"(v4), "=v"(v5), "=v"(v6), "=v"(v7), "=v"(v8)
+      : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3), "=&v"(v4), "=&v"(v5), "=&v"(v6), "=&v"(v7), "=&v"(v8)
       : "v"(addr)
       : "memory");
   const i32x4 v[9] = {v0, v1, v2, v3, v4, v5, v6, v7, v8};
@@ -112,8 +114,8 @@ __device__ __forceinline__ void lds_read_17x16(uint32_t addr, uint32_t (&o)[68])
       "ds_read_b128 %15, %17 offset:240\n"
       "ds_read_b128 %16, %17 offset:256\n"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(v0), "=v"(v1), "=v"(v2), "=v"(v3), "=v"(v4), "=v"(v5), "=v"(v6), "=v"(v7), "=v"(v8),
-        "=v"(v9), "=v"(v10), "=v"(v11), "=v"(v12), "=v"(v13), "=v"(v14), "=v"(v15), "=v"(v16)
+      : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3), "=&v"(v4), "=&v"(v5), "=&v"(v6), "=&v"(v7), "=&v"(v8),
+        "=&v"(v9), "=&v"(v10), "=&v"(v11), "=&v"(v12), "=&v"(v13), "=&v"(v14), "=&v"(v15), "=&v"(v16)
       : "v"(addr)
       : "memory");
   const i32x4 v[17] = {v0, v1, v2, v3, v4, v5, v6, v7, v8, v9, v10, v11, v12, v13, v14, v15, v16};

@@ -72,7 +72,10 @@ typedef float xreg16 __attribute__((ext_vector_type(16)));
 // round trip, touch its other 15 64-byte lines (one scalar dword each) so
 // that the step-by-step loads that follow hit the scalar cache instead of
 // each paying a miss. The touched words are discarded; their registers are
-// held until the wait so no late load can land in a reused register.
+// held until the wait so no late load can land in a reused register. Every
+// output is early-clobber: a load's data may return while later loads of the
+// block are still to issue, so no destination may share registers with the
+// base address.
 __device__ __forceinline__ void sload_first_with_touch(xreg16& xa, const float* xs) {
   uint32_t t[15];
   asm volatile(
@@ -93,9 +96,9 @@ __device__ __forceinline__ void sload_first_with_touch(xreg16& xa, const float* 
       "s_load_dword %14, %16, 896\n"
       "s_load_dword %15, %16, 960\n"
       "s_waitcnt lgkmcnt(0)"
-      : "=s"(xa), "=s"(t[0]), "=s"(t[1]), "=s"(t[2]), "=s"(t[3]), "=s"(t[4]), "=s"(t[5]),
-        "=s"(t[6]), "=s"(t[7]), "=s"(t[8]), "=s"(t[9]), "=s"(t[10]), "=s"(t[11]), "=s"(t[12]),
-        "=s"(t[13]), "=s"(t[14])
+      : "=&s"(xa), "=&s"(t[0]), "=&s"(t[1]), "=&s"(t[2]), "=&s"(t[3]), "=&s"(t[4]),
+        "=&s"(t[5]), "=&s"(t[6]), "=&s"(t[7]), "=&s"(t[8]), "=&s"(t[9]), "=&s"(t[10]),
+        "=&s"(t[11]), "=&s"(t[12]), "=&s"(t[13]), "=&s"(t[14])
       : "s"(xs));
 }
 // The wait for step h + 1's activations also takes step h's accumulators as
@@ -344,13 +347,17 @@ struct GemvDesc {
   int pad;
 };
 
-// Byte ranges to pull towards the device (into the memory-side Infinity
-// Cache) while this launch runs: the weights of the next step of a decode
-// pass, so that its loads find them on chip.
+// Byte ranges to pull into the memory-side Infinity Cache while a launch
+// runs: the weights (and inputs) of the next step of a decode pass, so that
+// its first loads find them on chip instead of paying the HBM round trip.
+// The reads are made by `blocks` extra blocks at the end of the grid; each
+// takes an equal share of the ranges, reads it with 16-byte loads and drops
+// the data. Every range is a multiple of 16 bytes and 16-byte aligned.
 struct Prefetch {
   const uint8_t* p[kMaxPrefetch];
   int64_t bytes[kMaxPrefetch];
   int n;
+  int blocks;
 };
 
 struct GemvGroup {
@@ -359,17 +366,37 @@ struct GemvGroup {
   Prefetch pf;
 };
 
-// Issue this wave's share of the prefetch ranges (wave `gw` of `nw` in the
-// grid) as direct global->LDS loads into a scratch window nothing reads, so
-// they hold no registers; the wave's next vmcnt wait also covers them.
-__device__ __forceinline__ void prefetch_share(const Prefetch& pf, int64_t gw, int64_t nw, int lane,
-                                               uint8_t* junk) {
+// Prefetch block `b` of pf.blocks: read its share of the ranges. Eight
+// 16-byte loads per thread are in flight before the first is consumed.
+__device__ __forceinline__ void prefetch_block(const Prefetch& pf, int b) {
+  if (pf.blocks <= 0 || b >= pf.blocks) return;
+  int64_t units = 0;
+  for (int r = 0; r < pf.n; ++r) units += pf.bytes[r] >> 4;
+  const int64_t per = (units + pf.blocks - 1) / pf.blocks;
+  const int64_t u0 = (int64_t)b * per;
+  const int64_t u1 = (u0 + per) < units ? (u0 + per) : units;
+  uint32_t acc = 0;
+  int64_t base = 0;
   for (int r = 0; r < pf.n; ++r) {
-    const int64_t n1k = pf.bytes[r] >> 10;                 // whole 1 KiB windows
-    const int64_t per = (n1k + nw - 1) / nw;
-    const int64_t w0 = gw * per, w1 = (w0 + per) < n1k ? (w0 + per) : n1k;
-    for (int64_t w = w0; w < w1; ++w) dma16(pf.p[r] + w * 1024 + 16 * lane, junk);
+    const int64_t nr = pf.bytes[r] >> 4;
+    const int64_t lo = (u0 > base ? u0 : base) - base;
+    const int64_t hi = ((u1 < base + nr) ? u1 : base + nr) - base;
+    const uint4* src = reinterpret_cast<const uint4*>(pf.p[r]);
+    int64_t u = lo + threadIdx.x;
+    for (; u + 7 * (int64_t)blockDim.x < hi; u += 8 * (int64_t)blockDim.x) {
+      uint4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = src[u + i * (int64_t)blockDim.x];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+    }
+    for (; u < hi; u += blockDim.x) {
+      const uint4 v = src[u];
+      acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    base += nr;
   }
+  asm volatile("" ::"v"(acc));   // the loads must happen; the value is unused
 }
 
 // Per-wave tasks (each wave one row group x K range). Used for Q8_0.
@@ -381,9 +408,14 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_group_kernel(GemvGroup g
   __shared__ __attribute__((aligned(16))) uint8_t slots[kGemvWaves][kSlots * kChunk];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int compute_blocks = (int)gridDim.x - grp.pf.blocks;
+  if ((int)blockIdx.x >= compute_blocks) {
+    prefetch_block(grp.pf, (int)blockIdx.x - compute_blocks);
+    return;
+  }
   const int64_t T = grp.d[grp.n - 1].task_end;
   for (int64_t t = (int64_t)blockIdx.x * kGemvWaves + wave; t < T;
-       t += (int64_t)gridDim.x * kGemvWaves) {
+       t += (int64_t)compute_blocks * kGemvWaves) {
     int g = 0;
     while (g + 1 < grp.n && t >= grp.d[g].task_end) ++g;
     const GemvDesc& D = grp.d[g];
@@ -405,52 +437,49 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_group_kernel(GemvGroup g
   }
 }
 
-// Block tasks for Q4_K: a block of kBlockWaves waves owns one row group and
-// a range of up to kBlockWaves super-blocks along K, one per wave. The waves'
-// 64 partial sums are added in LDS in wave order; a row group whose K is cut
-// into P > 1 ranges (K > kBlockWaves super-blocks) finishes through the
-// split-K hand-off between blocks. The prefetch share is issued first so it
-// overlaps this block's own loads and multiply-adds.
+// Block tasks for Q4_K: block t (one per task) has kBlockWaves waves and owns
+// one row group and a range of up to kBlockWaves super-blocks along K, one per
+// wave. The waves' 64 partial sums are added in LDS in wave order; a row group
+// whose K is cut into P > 1 ranges (K > kBlockWaves super-blocks) finishes
+// through the split-K hand-off between blocks. Blocks past the last task are
+// prefetch blocks.
 __global__ __launch_bounds__(kBlockWaves * 64) void gemv_q4k_block_kernel(GemvGroup grp,
                                                                           float* partials,
                                                                           int* counters) {
   __shared__ __attribute__((aligned(16))) uint8_t slots[kBlockWaves][kQ4KChunk];
-  __shared__ __attribute__((aligned(16))) uint8_t junk[1024];
   __shared__ float red[kBlockWaves][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (grp.pf.n)
-    prefetch_share(grp.pf, (int64_t)blockIdx.x * kBlockWaves + wave,
-                   (int64_t)gridDim.x * kBlockWaves, lane, junk);
   const int64_t T = grp.d[grp.n - 1].task_end;
-  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
-    int g = 0;
-    while (g + 1 < grp.n && t >= grp.d[g].task_end) ++g;
-    const GemvDesc& D = grp.d[g];
-    const int64_t lt = t - (g ? grp.d[g - 1].task_end : 0);
-    const int P = D.P;
-    const int rg = (int)(lt / P), part = (int)(lt % P);
-    const int n = D.nchunks;
-    const int c0 = (int)((int64_t)part * n / P), c1 = (int)((int64_t)(part + 1) * n / P);
-    const int64_t row0 = (int64_t)rg * 64;
-    const int valid = (int)((D.rows - row0) < 64 ? (D.rows - row0) : 64);
-    const uint32_t row_bytes = (uint32_t)n * kQ4KBlockBytes;
-    // wave w takes super-blocks c0 + w, c0 + w + kBlockWaves, ...
-    float acc = 0.f;
-    for (int c = c0 + wave; c < c1; c += kBlockWaves)
-      acc += q4k_wave_task<1>(D.W, D.x, row_bytes, row0, valid, c, c + 1, &slots[wave][0], lane);
-    red[wave][lane] = acc;
-    __syncthreads();
-    if (wave == 0) {
-      float s = 0.f;
-#pragma unroll
-      for (int w = 0; w < kBlockWaves; ++w) s += red[w][lane];
-      const SplitK sk{partials + D.part_off, counters + (int64_t)D.cnt_off * kCounterStride};
-      splitk_finish(s, D.y, D.rows, row0, valid, rg, part, P, sk, lane);
-    }
-    __syncthreads();
+  const int64_t t = blockIdx.x;
+  if (t >= T) {
+    prefetch_block(grp.pf, (int)(t - T));
+    return;
   }
-  GQK_WAIT_VMCNT(0);   // prefetch loads of waves without a task
+  int g = 0;
+  while (g + 1 < grp.n && t >= grp.d[g].task_end) ++g;
+  const GemvDesc& D = grp.d[g];
+  const int64_t lt = t - (g ? grp.d[g - 1].task_end : 0);
+  const int P = D.P;
+  const int rg = (int)(lt / P), part = (int)(lt % P);
+  const int n = D.nchunks;
+  const int c0 = (int)((int64_t)part * n / P), c1 = (int)((int64_t)(part + 1) * n / P);
+  const int64_t row0 = (int64_t)rg * 64;
+  const int valid = (int)((D.rows - row0) < 64 ? (D.rows - row0) : 64);
+  const uint32_t row_bytes = (uint32_t)n * kQ4KBlockBytes;
+  // wave w takes super-blocks c0 + w, c0 + w + kBlockWaves, ...
+  float acc = 0.f;
+  for (int c = c0 + wave; c < c1; c += kBlockWaves)
+    acc += q4k_wave_task<1>(D.W, D.x, row_bytes, row0, valid, c, c + 1, &slots[wave][0], lane);
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kBlockWaves; ++w) s += red[w][lane];
+    const SplitK sk{partials + D.part_off, counters + (int64_t)D.cnt_off * kCounterStride};
+    splitk_finish(s, D.y, D.rows, row0, valid, rg, part, P, sk, lane);
+  }
 }
 
 // Q8_0 rows whose length is not a multiple of 256 weights (row bytes not a

@@ -39,7 +39,10 @@ struct Tuning {
   int target_tasks = 2048;   // wave tasks a split-K GEMV aims for
   int q4k_slots = 1;         // LDS chunks in flight per wave, Q4_K
   int q80_slots = 1;         // LDS chunks in flight per wave, Q8_0
-  int prefetch = 0;          // decode batches pull the next step's weights on chip (measured slower)
+  int prefetch = 1;          // batch steps pull the next step's bytes on chip
+  int pf_kb = 32;            // prefetch bytes per prefetch block, KiB
+  int pf_w = 100;            // weight bytes prefetched, % of this step's own weight bytes
+  int pf_x = 1;              // prefetch the next step's inputs
 };
 
 static const Tuning& tuning() {
@@ -57,6 +60,9 @@ static const Tuning& tuning() {
       if (key == "q4k_slots" && (v == 1 || v == 2)) r.q4k_slots = v;
       if (key == "q80_slots" && (v == 1 || v == 2)) r.q80_slots = v;
       if (key == "prefetch") r.prefetch = v != 0;
+      if (key == "pf_kb" && v > 0) r.pf_kb = v;
+      if (key == "pf_w" && v >= 0) r.pf_w = v;
+      if (key == "pf_x") r.pf_x = v != 0;
       const char* comma = std::strchr(eq, ',');
       if (!comma) break;
       p = comma + 1;
@@ -69,12 +75,13 @@ static const Tuning& tuning() {
 struct DeviceState {
   std::atomic<int> checked{0};   // 0 unknown, 1 gfx950, -1 unsupported
   ScratchArea* scratch = nullptr;
+  int cus = 0;
   std::mutex mu;
 };
 static DeviceState g_dev[kMaxDevices];
 
 // Returns GGUF_QK_OK and the scratch of the current device, or an error.
-static int current_device(ScratchArea** scratch) {
+static int current_device(ScratchArea** scratch, int* cus = nullptr) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
     (void)hipGetLastError();
@@ -93,12 +100,14 @@ static int current_device(ScratchArea** scratch) {
       if (ok) ok = hipGetSymbolAddress(&p, HIP_SYMBOL(g_scratch)) == hipSuccess && p != nullptr;
       (void)hipGetLastError();
       st.scratch = static_cast<ScratchArea*>(p);
+      st.cus = ok ? prop.multiProcessorCount : 0;
       c = ok ? 1 : -1;
       st.checked.store(c, std::memory_order_release);
     }
   }
   if (c != 1) return GGUF_QK_ERR_DEVICE;
   if (scratch) *scratch = st.scratch;
+  if (cus) *cus = st.cus;
   return GGUF_QK_OK;
 }
 
@@ -229,13 +238,12 @@ static int check_gemv(int type, const void* W, const float* x, const float* y, i
 // Q8_0 GEMVs with cols % 256 != 0 are not grouped (see launch_step).
 // Q4_K runs as block tasks (8 waves per row group and up to 8 super-blocks,
 // partials added in LDS); Q8_0 as per-wave tasks with split-K sized to the
-// task target. `pf` (may be null) lists weight ranges to pull into the
-// Infinity Cache while this launch runs.
+// task target. `pf` (may be null) lists byte ranges to pull into the
+// Infinity Cache while this launch runs; `cus` is the device's CU count.
 static int launch_group(int type, const gguf_qk_gemv* const* v, int n, const ScratchArea* scratch,
-                        hipStream_t stream, const Prefetch* pf) {
+                        hipStream_t stream, const Prefetch* pf, int cus) {
   GemvGroup grp{};
   grp.n = n;
-  if (pf) grp.pf = *pf;
   int64_t total_bytes = 0;
   for (int i = 0; i < n; ++i) total_bytes += v[i]->rows * row_bytes_of(type, v[i]->cols);
   int64_t tasks = 0, part_off = 0, cnt_off = 0;
@@ -275,14 +283,28 @@ static int launch_group(int type, const gguf_qk_gemv* const* v, int n, const Scr
   }
   float* partials = const_cast<float*>(scratch->partials);
   int* counters = const_cast<int*>(scratch->counters);
+  const int64_t compute_blocks =
+      type == GGUF_QK_TYPE_Q4_K ? tasks : (tasks + kGemvWaves - 1) / kGemvWaves;
+  if (pf && pf->n > 0) {
+    // Prefetch blocks: about pf_kb KiB each, but no more than fit on the
+    // device beside the compute blocks (two blocks per CU: both kernels hold
+    // 70-80 KB of LDS per block), and at least 32.
+    int64_t bytes = 0;
+    for (int r = 0; r < pf->n; ++r) bytes += pf->bytes[r];
+    int64_t want = (bytes + (int64_t)tuning().pf_kb * 1024 - 1) / ((int64_t)tuning().pf_kb * 1024);
+    const int64_t room = 2 * (int64_t)cus - compute_blocks;
+    if (want > room) want = room;
+    if (want < 32) want = 32;
+    grp.pf = *pf;
+    grp.pf.blocks = (int)want;
+  }
+  const int64_t blocks = compute_blocks + grp.pf.blocks;
+  if (blocks > INT32_MAX) return GGUF_QK_ERR_LIMIT;
   if (type == GGUF_QK_TYPE_Q4_K) {
-    if (tasks > INT32_MAX) return GGUF_QK_ERR_LIMIT;
-    hipLaunchKernelGGL(gemv_q4k_block_kernel, dim3((unsigned)tasks), dim3(kBlockWaves * 64), 0,
+    hipLaunchKernelGGL(gemv_q4k_block_kernel, dim3((unsigned)blocks), dim3(kBlockWaves * 64), 0,
                        stream, grp, partials, counters);
     return launch_status();
   }
-  const int64_t blocks = (tasks + kGemvWaves - 1) / kGemvWaves;
-  if (blocks > INT32_MAX) return GGUF_QK_ERR_LIMIT;
   const dim3 grid((unsigned)blocks), block(kGemvWaves * 64);
   if (tuning().q80_slots == 2)
     hipLaunchKernelGGL((gemv_group_kernel<2, false>), grid, block, 0, stream, grp, partials, counters);
@@ -301,9 +323,10 @@ static int launch_rowwise_q8_0(const gguf_qk_gemv& g, hipStream_t stream) {
 }
 
 // Launches the GEMVs of one step: same-format GEMVs go together, kMaxGroup at
-// a time; each launch follows the previous one on the stream.
+// a time; each launch follows the previous one on the stream. The prefetch
+// `pf` (may be null) rides on the first group launch of the step.
 static int launch_step(const gguf_qk_gemv* list, int n, const ScratchArea* scratch,
-                       hipStream_t stream, const Prefetch* pf) {
+                       hipStream_t stream, const Prefetch* pf, int cus) {
   for (int type : {GGUF_QK_TYPE_Q4_K, GGUF_QK_TYPE_Q8_0}) {
     const gguf_qk_gemv* grp[kMaxGroup];
     int k = 0;
@@ -317,14 +340,16 @@ static int launch_step(const gguf_qk_gemv* list, int n, const ScratchArea* scrat
       }
       grp[k++] = &g;
       if (k == kMaxGroup) {
-        const int st = launch_group(type, grp, k, scratch, stream, pf);
+        const int st = launch_group(type, grp, k, scratch, stream, pf, cus);
         if (st) return st;
+        pf = nullptr;
         k = 0;
       }
     }
     if (k) {
-      const int st = launch_group(type, grp, k, scratch, stream, pf);
+      const int st = launch_group(type, grp, k, scratch, stream, pf, cus);
       if (st) return st;
+      pf = nullptr;
     }
   }
   return GGUF_QK_OK;
@@ -340,7 +365,7 @@ static int matvec_common(int type, const void* W, const float* x, float* y, int6
   st = current_device(&scratch);
   if (st) return st;
   const gguf_qk_gemv g{W, x, y, rows, cols, type, 0, {0}};
-  return launch_step(&g, 1, scratch, stream, nullptr);
+  return launch_step(&g, 1, scratch, stream, nullptr, 0);
 }
 
 int gguf_qmatvec_batch(const gguf_qk_gemv* list, int32_t n, hipStream_t stream) {
@@ -371,23 +396,43 @@ int gguf_qmatvec_batch(const gguf_qk_gemv* list, int32_t n, hipStream_t stream) 
     i = j;
   }
   ScratchArea* scratch = nullptr;
-  int st = current_device(&scratch);
+  int cus = 0;
+  int st = current_device(&scratch, &cus);
   if (st) return st;
   for (int32_t i = 0; i < n;) {
     int32_t j = i;
     while (j < n && list[j].stage == list[i].stage) ++j;
-    // the next step's weights, pulled on chip while this step runs
+    // The next step's weights, and its inputs when no entry of the batch
+    // writes them, pulled on chip while this step runs.
     Prefetch pf{};
     if (tuning().prefetch && j < n) {
       int32_t k = j;
-      while (k < n && list[k].stage == list[j].stage && pf.n < kMaxPrefetch) {
-        pf.p[pf.n] = static_cast<const uint8_t*>(list[k].W);
-        pf.bytes[pf.n] = list[k].rows * row_bytes_of(list[k].type, list[k].cols);
+      while (k < n && list[k].stage == list[j].stage) ++k;
+      int64_t own = 0;
+      for (int32_t e = i; e < j; ++e) own += list[e].rows * row_bytes_of(list[e].type, list[e].cols);
+      int64_t budget = own / 100 * tuning().pf_w;
+      for (int32_t e = j; e < k && pf.n < kMaxPrefetch && budget >= 16; ++e) {
+        int64_t wb = list[e].rows * row_bytes_of(list[e].type, list[e].cols);
+        if (wb > budget) wb = budget;
+        pf.p[pf.n] = static_cast<const uint8_t*>(list[e].W);
+        pf.bytes[pf.n] = wb & ~int64_t(15);
+        budget -= pf.bytes[pf.n];
+        if (pf.bytes[pf.n] > 0) ++pf.n;
+      }
+      for (int32_t e = j; e < k && pf.n < kMaxPrefetch && tuning().pf_x; ++e) {
+        const void* x = list[e].x;
+        const int64_t xb = list[e].cols * 4;
+        bool seen = false, written = false;
+        for (int32_t f = j; f < e; ++f) seen = seen || list[f].x == x;
+        for (int32_t f = 0; f < n && !written; ++f)
+          written = overlap(list[f].y, list[f].rows * 4, x, xb);
+        if (seen || written) continue;
+        pf.p[pf.n] = static_cast<const uint8_t*>(x);
+        pf.bytes[pf.n] = xb;
         ++pf.n;
-        ++k;
       }
     }
-    st = launch_step(list + i, j - i, scratch, stream, pf.n ? &pf : nullptr);
+    st = launch_step(list + i, j - i, scratch, stream, pf.n ? &pf : nullptr, cus);
     if (st) return st;
     i = j;
   }
