@@ -12,16 +12,25 @@ are resident in HBM before timing starts.
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 
 Prints one JSON line: weight-stream GB/s (whole pass), % of the 8 TB/s HBM
-peak, tokens/s-equivalent (1 / pass time), a roofline record for the dominant
-kernel (the Q4_K GEMV group kernel) and the CPU oracle timed on a bounded
-sample of the same workload.
+peak, tokens/s-equivalent (1 / pass time), a roofline record for the
+dominant kernel (the Q4_K block-task GEMV), the CPU oracle timed on a bounded
+sample of the same workload, and labelled extras: the pass time distribution,
+an unordered upper bound (all GEMVs of the pass as one step), and the bf16
+MFMA prefill pass over the same 36-layer weights (N = 512 tokens).
+
+    python bench.py --copy-calibration
+
+only copies 1 GiB device to device three times (the plain copy whose HBM
+counter readings scale the GEMV kernel's counter readings).
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -29,6 +38,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+BF16_DENSE_PEAK_TFLOPS = 2500.0
+DOMINANT_KERNEL = "gemv_q4k_block_kernel"
+KERNEL_SOURCES = ["gguf_block_quant_dequant_amd/csrc/gemv.hpp",
+                  "gguf_block_quant_dequant_amd/csrc/device_common.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_q4k_block_kernel_decode_stream_traffic.md")
 
 
 def log(*a):
@@ -43,11 +57,41 @@ def parse():
     ap.add_argument("--layers", type=int, default=36, help="layers in the stream (36 = the workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="eager launches instead of a HIP graph")
+    ap.add_argument("--quick", action="store_true",
+                    help="only the stage-ordered pass (for counter runs): no extras, no CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="copy 1 GiB device to device three times and exit")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the prefill pass over the 36-layer weights (for counter runs)")
     return ap.parse_args()
 
 
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, if it was taken on the current kernel sources; else None."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    kv = dict(re.findall(r"^([a-z_0-9]+):\s*(\S+)\s*$", text, flags=re.M))
+    if kv.get("source_sha256") != kernel_source_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def build_stream(torch, g, synth, n_layers):
-    """Upload the seeded stream; returns (batch, steps meta, total bytes, q4k bytes)."""
+    """Upload the seeded stream; returns (batch, entries, meta, total bytes, q4k bytes)."""
     dev = "cuda:0"
     t0 = time.time()
     stages = synth.decode_stream(n_layers=n_layers, head=True, threads=16)
@@ -73,27 +117,37 @@ def build_stream(torch, g, synth, n_layers):
     return g.GemvBatch(entries), entries, meta, total, q4k
 
 
-def per_step_times(torch, g, entries, meta, reps=5):
-    """Event-timed durations of each step of the pass (eager launches, one
-    event pair per step on the launch stream), averaged over `reps` passes."""
-    s = torch.cuda.current_stream()
-    steps = []
-    i = 0
-    for layer, names, nbytes in meta:
-        n = len(names)
-        steps.append(g.GemvBatch(entries[i:i + n]))
-        i += n
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in steps]
-    acc = [0.0] * len(steps)
-    for _ in range(reps):
-        for b, (e0, e1) in zip(steps, evs):
-            e0.record(s)
-            g.gguf_qmatvec_batch(b, s)
-            e1.record(s)
-        torch.cuda.synchronize()
-        for k, (e0, e1) in enumerate(evs):
-            acc[k] += e0.elapsed_time(e1) / reps
-    return acc   # ms per step
+def capture(torch, fn, stream):
+    """One untimed eager call, then a HIP graph of `fn` on `stream`."""
+    with torch.cuda.stream(stream):
+        fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        fn()
+    return graph
+
+
+def time_replays(torch, graph, stream, reps, warm=2):
+    """Per-replay durations (ms) from events on the replay stream."""
+    with torch.cuda.stream(stream):
+        for _ in range(warm):
+            graph.replay()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    with torch.cuda.stream(stream):
+        evs[0].record(stream)
+        for i in range(reps):
+            graph.replay()
+            evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
+
+
+def pct(v, q):
+    s = sorted(v)
+    k = min(len(s) - 1, max(0, int(round(q * (len(s) - 1)))))
+    return s[k]
 
 
 def probe_ceiling(torch, g):
@@ -110,18 +164,47 @@ def probe_ceiling(torch, g):
     torch.cuda.synchronize()
     t = e0.elapsed_time(e1) / 10 / 1e3
     del buf
-    return buf_bytes_gbps(2 << 30, t)
+    return (2 << 30) / t / 1e9
 
 
-def buf_bytes_gbps(nbytes, seconds):
-    return nbytes / seconds / 1e9
+def prefill_pass(torch, g, synth, entries, meta, stream, n_tokens=512, reps=3):
+    """36 layers x 7 Q4_K GEMMs (Y = X W^T, X bf16 [n_tokens x K]) over the
+    resident decode weights, as one HIP graph; returns the labelled record."""
+    dev = "cuda:0"
+    gen = torch.Generator().manual_seed(synth.ROOT_SEED * 1000 + synth.PREFILL_CFG_ID)
+    xs, ys, calls = {}, {}, []
+    flops = 0.0
+    for tid, W, x, y, si in entries:
+        if tid != g.TYPE_Q4_K:
+            continue
+        cols, rows = x.numel(), y.numel()
+        if cols not in xs:
+            xs[cols] = torch.randn(n_tokens, cols, generator=gen).to(torch.bfloat16).to(dev)
+        if rows not in ys:
+            ys[rows] = torch.empty(n_tokens, rows, dtype=torch.bfloat16, device=dev)
+        calls.append((W, xs[cols], ys[rows]))
+        flops += 2.0 * n_tokens * rows * cols
+
+    def run():
+        for W, X, Y in calls:
+            g.gguf_qmatmul_q4_k(W, X, Y, stream=stream)
+
+    graph = capture(torch, run, stream)
+    t = time_replays(torch, graph, stream, reps)
+    ms = sorted(t)[len(t) // 2]
+    tflops = flops / (ms / 1e3) / 1e12
+    return {"label": "prefill: 36 layers x 7 Q4_K GEMMs, X bf16 [512 x K], Y bf16, bf16 MFMA, "
+                     "fp32 accumulate (HIP graph)",
+            "gemms": len(calls), "flop": flops, "ms_per_pass": round(ms, 4),
+            "roofline": {"bound": "mfma", "kernel": "gemm_q4_k_kernel", "achieved": round(tflops, 1),
+                         "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / BF16_DENSE_PEAK_TFLOPS, 4), "traffic": None}}
 
 
 def cpu_baseline():
     """The oracle as it stands, on a bounded sample of the same workload:
     layer 0's seven Q4_K GEMVs and the first 8192 rows of the Q8_0 head,
     decoded to fp32 and multiplied in fp64 with NumPy, one BLAS thread."""
-    import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
@@ -147,12 +230,26 @@ def cpu_baseline():
                       f"{gbps * 1e9 / synth.decode_stream_bytes():.4f}"}
 
 
+def copy_calibration():
+    import torch
+    torch.cuda.set_device(0)
+    a = torch.ones(1 << 30, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": 1 << 30, "copies": 3}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the workload fits one MI355X); --gpus {args.gpus} "
               "is not supported", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
 
     import gguf_block_quant_dequant_amd as g
@@ -163,16 +260,14 @@ def main():
 
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
+    if args.prefill_only:
+        print(json.dumps(prefill_pass(torch, g, synth, entries, meta, stream)), flush=True)
+        return
     if args.no_graph:
         def step():
             g.gguf_qmatvec_batch(batch, stream)
     else:
-        with torch.cuda.stream(stream):
-            g.gguf_qmatvec_batch(batch, stream)          # untimed first pass outside the graph
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            g.gguf_qmatvec_batch(batch, stream)
+        graph = capture(torch, lambda: g.gguf_qmatvec_batch(batch, stream), stream)
 
         def step():
             graph.replay()
@@ -181,26 +276,18 @@ def main():
         for _ in range(args.warmup):
             step()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t_wall = time.perf_counter()
     with torch.cuda.stream(stream):
-        e0.record(stream)
-        for _ in range(args.steps):
+        evs[0].record(stream)
+        for i in range(args.steps):
             step()
-        e1.record(stream)
+            evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1) / args.steps
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
     gbps = total_bytes / (ms / 1e3) / 1e9
-
-    # per-step durations (eager, event-timed) for the roofline record
-    with torch.cuda.stream(stream):
-        step_ms = per_step_times(torch, g, entries, meta)
-    q4k_ms = sum(t for (layer, names, b), t in zip(meta, step_ms) if layer >= 0)
-    q4k_launches = sum(1 for (layer, names, b) in meta if layer >= 0)
-    head_ms = sum(t for (layer, names, b), t in zip(meta, step_ms) if layer < 0)
-    achieved = q4k_bytes / (q4k_ms / 1e3) / 1e9
-    ceiling = probe_ceiling(torch, g)
 
     rec = {
         "metric": "weight-stream GB/s + % of HBM peak; decode tokens/s-equiv (36-layer Q4_K)",
@@ -222,16 +309,60 @@ def main():
                    "launch": "eager" if args.no_graph else "hip-graph"},
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "tokens_per_s_equiv": round(1e3 / ms, 2),
-        "read_probe_GBps": round(ceiling, 1),
-        "pct_of_read_probe": round(100 * gbps / ceiling, 2),
-        "head_ms": round(head_ms, 4),
-        "roofline": {"bound": "hbm", "kernel": "gemv_group_kernel<1, Q4_K>",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "launches": q4k_launches, "bytes_per_launch_avg": q4k_bytes / q4k_launches,
-                     "avg_launch_us": round(1e3 * q4k_ms / q4k_launches, 3)},
+        "ms_per_step_p10_p50_p90": [round(pct(per, 0.1), 5), round(pct(per, 0.5), 5),
+                                    round(pct(per, 0.9), 5)],
         "wall_s_timed": round(wall, 3),
     }
+    if args.quick:
+        print(json.dumps(rec), flush=True)
+        return
+
+    # Roofline of the dominant kernel: the Q4_K block-task GEMV launches of the
+    # pass (all stages but the head) replayed alone as a graph, so that the
+    # average launch duration is the kernel's own, back to back as in the pass.
+    q4k_entries = [e for e in entries if e[0] == g.TYPE_Q4_K]
+    q4k_launches = sum(1 for (layer, names, b) in meta if layer >= 0)
+    q4k_batch = g.GemvBatch(q4k_entries)
+    gq = capture(torch, lambda: g.gguf_qmatvec_batch(q4k_batch, stream), stream)
+    tq = time_replays(torch, gq, stream, 10)
+    q4k_ms = sorted(tq)[len(tq) // 2]
+    avg_launch_s = q4k_ms / 1e3 / q4k_launches
+    bytes_per_launch = q4k_bytes / q4k_launches
+    achieved = bytes_per_launch / avg_launch_s / 1e9
+    traffic = recorded_traffic()
+    rec["roofline"] = {"bound": "hbm", "kernel": DOMINANT_KERNEL, "achieved": round(achieved, 1),
+                       "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                       "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                       "traffic": round(traffic) if traffic is not None else None,
+                       "launches": q4k_launches, "bytes_per_launch_avg": bytes_per_launch,
+                       "avg_launch_us": round(avg_launch_s * 1e6, 3)}
+    del gq
+
+    head_entries = [e for e in entries if e[0] == g.TYPE_Q8_0]
+    hb = g.GemvBatch(head_entries)
+    gh = capture(torch, lambda: g.gguf_qmatvec_batch(hb, stream), stream)
+    th = time_replays(torch, gh, stream, 10)
+    head_ms = sorted(th)[len(th) // 2]
+    head_bytes = sum(e[1].numel() for e in head_entries)
+    rec["head"] = {"ms": round(head_ms, 4), "GBps": round(head_bytes / (head_ms / 1e3) / 1e9, 1)}
+    del gh
+
+    # Labelled upper bound: every GEMV of the pass in one step (no stage order),
+    # grouped four to a launch.
+    ub = g.GemvBatch([(tid, W, x, y, 0) for tid, W, x, y, si in entries])
+    gu = capture(torch, lambda: g.gguf_qmatvec_batch(ub, stream), stream)
+    tu = time_replays(torch, gu, stream, 10)
+    ums = sorted(tu)[len(tu) // 2]
+    rec["unordered_upper_bound"] = {
+        "label": "all 253 GEMVs of the pass as one unordered step (not the headline)",
+        "ms": round(ums, 4), "GBps": round(total_bytes / (ums / 1e3) / 1e9, 1),
+        "pct_hbm_peak": round(100 * total_bytes / (ums / 1e3) / 1e9 / HBM_PEAK_GBPS, 2)}
+    del gu
+
+    ceiling = probe_ceiling(torch, g)
+    rec["read_probe_GBps"] = round(ceiling, 1)
+    rec["pct_of_read_probe"] = round(100 * gbps / ceiling, 2)
+    rec["prefill"] = prefill_pass(torch, g, synth, entries, meta, stream)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline()
     print(json.dumps(rec), flush=True)

@@ -332,7 +332,6 @@ __device__ __forceinline__ void splitk_finish(float acc, float* __restrict__ y, 
 constexpr int kGemvWaves = 4;      // per-wave task kernel (Q8_0)
 constexpr int kBlockWaves = 8;     // block task kernel (Q4_K)
 constexpr int kMaxGroup = 4;
-constexpr int kMaxPrefetch = 4;
 
 struct GemvDesc {
   const uint8_t* W;
@@ -347,56 +346,57 @@ struct GemvDesc {
   int pad;
 };
 
-// Byte ranges to pull into the memory-side Infinity Cache while a launch
-// runs: the weights (and inputs) of the next step of a decode pass, so that
-// its first loads find them on chip instead of paying the HBM round trip.
-// The reads are made by `blocks` extra blocks at the end of the grid; each
-// takes an equal share of the ranges, reads it with 16-byte loads and drops
-// the data. Every range is a multiple of 16 bytes and 16-byte aligned.
-struct Prefetch {
-  const uint8_t* p[kMaxPrefetch];
-  int64_t bytes[kMaxPrefetch];
-  int n;
-  int blocks;
-};
-
 struct GemvGroup {
   GemvDesc d[kMaxGroup];
   int n;
-  Prefetch pf;
 };
 
-// Prefetch block `b` of pf.blocks: read its share of the ranges. Eight
-// 16-byte loads per thread are in flight before the first is consumed.
-__device__ __forceinline__ void prefetch_block(const Prefetch& pf, int b) {
-  if (pf.blocks <= 0 || b >= pf.blocks) return;
-  int64_t units = 0;
-  for (int r = 0; r < pf.n; ++r) units += pf.bytes[r] >> 4;
-  const int64_t per = (units + pf.blocks - 1) / pf.blocks;
-  const int64_t u0 = (int64_t)b * per;
-  const int64_t u1 = (u0 + per) < units ? (u0 + per) : units;
-  uint32_t acc = 0;
-  int64_t base = 0;
-  for (int r = 0; r < pf.n; ++r) {
-    const int64_t nr = pf.bytes[r] >> 4;
-    const int64_t lo = (u0 > base ? u0 : base) - base;
-    const int64_t hi = ((u1 < base + nr) ? u1 : base + nr) - base;
-    const uint4* src = reinterpret_cast<const uint4*>(pf.p[r]);
-    int64_t u = lo + threadIdx.x;
-    for (; u + 7 * (int64_t)blockDim.x < hi; u += 8 * (int64_t)blockDim.x) {
-      uint4 v[8];
+// Task t of a group: which GEMV (g) and its descriptor. Kernel arguments live
+// in a buffer that is new, hence cold, at every launch; indexing d[] with a
+// computed g would make the descriptor loads wait for the task_end loads. All
+// kMaxGroup descriptors are therefore read at fixed offsets (one batch of
+// scalar loads) and g picks among them with selects.
+template <class T>
+__device__ __forceinline__ T pick4(int g, T a0, T a1, T a2, T a3) {
+  return g == 0 ? a0 : g == 1 ? a1 : g == 2 ? a2 : a3;
+}
+
+__device__ __forceinline__ int64_t group_tasks(const GemvDesc (&d)[kMaxGroup], int n) {
+  return pick4(n - 1, d[0].task_end, d[1].task_end, d[2].task_end, d[3].task_end);
+}
+
+__device__ __forceinline__ void pick_desc(const GemvDesc (&d)[kMaxGroup], int n, int64_t t,
+                                          int* g_out, int64_t* lt_out, GemvDesc* out) {
+  const int g = (n > 1 && t >= d[0].task_end) + (n > 2 && t >= d[1].task_end) +
+                (n > 3 && t >= d[2].task_end);
+  const int64_t before = pick4<int64_t>(g, 0, d[0].task_end, d[1].task_end, d[2].task_end);
+  out->W = pick4(g, d[0].W, d[1].W, d[2].W, d[3].W);
+  out->x = pick4(g, d[0].x, d[1].x, d[2].x, d[3].x);
+  out->y = pick4(g, d[0].y, d[1].y, d[2].y, d[3].y);
+  out->rows = pick4(g, d[0].rows, d[1].rows, d[2].rows, d[3].rows);
+  out->task_end = pick4(g, d[0].task_end, d[1].task_end, d[2].task_end, d[3].task_end);
+  out->part_off = pick4(g, d[0].part_off, d[1].part_off, d[2].part_off, d[3].part_off);
+  out->nchunks = pick4(g, d[0].nchunks, d[1].nchunks, d[2].nchunks, d[3].nchunks);
+  out->P = pick4(g, d[0].P, d[1].P, d[2].P, d[3].P);
+  out->cnt_off = pick4(g, d[0].cnt_off, d[1].cnt_off, d[2].cnt_off, d[3].cnt_off);
+  *g_out = g;
+  *lt_out = t - before;
+}
+
+// Copies the group's descriptors and count out of the kernel arguments in one
+// batch of scalar loads: the empty asm consumes every loaded word, so no load
+// can be sunk behind a branch that depends on another load.
+__device__ __forceinline__ void load_group(const GemvGroup& grp, GemvDesc (&dl)[kMaxGroup],
+                                           int* n) {
+  typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+  u32x16 w[kMaxGroup];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = src[u + i * (int64_t)blockDim.x];
+  for (int k = 0; k < kMaxGroup; ++k) w[k] = *reinterpret_cast<const u32x16*>(&grp.d[k]);
+  int cnt = grp.n;
+  asm volatile("" : "+s"(w[0]), "+s"(w[1]), "+s"(w[2]), "+s"(w[3]), "+s"(cnt));
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
-    }
-    for (; u < hi; u += blockDim.x) {
-      const uint4 v = src[u];
-      acc ^= v.x ^ v.y ^ v.z ^ v.w;
-    }
-    base += nr;
-  }
-  asm volatile("" ::"v"(acc));   // the loads must happen; the value is unused
+  for (int k = 0; k < kMaxGroup; ++k) dl[k] = __builtin_bit_cast(GemvDesc, w[k]);
+  *n = cnt;
 }
 
 // Per-wave tasks (each wave one row group x K range). Used for Q8_0.
@@ -408,14 +408,9 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_group_kernel(GemvGroup g
   __shared__ __attribute__((aligned(16))) uint8_t slots[kGemvWaves][kSlots * kChunk];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int compute_blocks = (int)gridDim.x - grp.pf.blocks;
-  if ((int)blockIdx.x >= compute_blocks) {
-    prefetch_block(grp.pf, (int)blockIdx.x - compute_blocks);
-    return;
-  }
   const int64_t T = grp.d[grp.n - 1].task_end;
   for (int64_t t = (int64_t)blockIdx.x * kGemvWaves + wave; t < T;
-       t += (int64_t)compute_blocks * kGemvWaves) {
+       t += (int64_t)gridDim.x * kGemvWaves) {
     int g = 0;
     while (g + 1 < grp.n && t >= grp.d[g].task_end) ++g;
     const GemvDesc& D = grp.d[g];
@@ -441,8 +436,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_group_kernel(GemvGroup g
 // one row group and a range of up to kBlockWaves super-blocks along K, one per
 // wave. The waves' 64 partial sums are added in LDS in wave order; a row group
 // whose K is cut into P > 1 ranges (K > kBlockWaves super-blocks) finishes
-// through the split-K hand-off between blocks. Blocks past the last task are
-// prefetch blocks.
+// through the split-K hand-off between blocks.
 __global__ __launch_bounds__(kBlockWaves * 64) void gemv_q4k_block_kernel(GemvGroup grp,
                                                                           float* partials,
                                                                           int* counters) {
@@ -450,16 +444,14 @@ __global__ __launch_bounds__(kBlockWaves * 64) void gemv_q4k_block_kernel(GemvGr
   __shared__ float red[kBlockWaves][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t T = grp.d[grp.n - 1].task_end;
   const int64_t t = blockIdx.x;
-  if (t >= T) {
-    prefetch_block(grp.pf, (int)(t - T));
-    return;
-  }
-  int g = 0;
-  while (g + 1 < grp.n && t >= grp.d[g].task_end) ++g;
-  const GemvDesc& D = grp.d[g];
-  const int64_t lt = t - (g ? grp.d[g - 1].task_end : 0);
+  GemvDesc dl[kMaxGroup];
+  int ng;
+  load_group(grp, dl, &ng);
+  int g;
+  int64_t lt;
+  GemvDesc D;
+  pick_desc(dl, ng, t, &g, &lt, &D);
   const int P = D.P;
   const int rg = (int)(lt / P), part = (int)(lt % P);
   const int n = D.nchunks;

@@ -39,10 +39,6 @@ struct Tuning {
   int target_tasks = 2048;   // wave tasks a split-K GEMV aims for
   int q4k_slots = 1;         // LDS chunks in flight per wave, Q4_K
   int q80_slots = 1;         // LDS chunks in flight per wave, Q8_0
-  int prefetch = 1;          // batch steps pull the next step's bytes on chip
-  int pf_kb = 32;            // prefetch bytes per prefetch block, KiB
-  int pf_w = 100;            // weight bytes prefetched, % of this step's own weight bytes
-  int pf_x = 1;              // prefetch the next step's inputs
 };
 
 static const Tuning& tuning() {
@@ -59,10 +55,6 @@ static const Tuning& tuning() {
       if (key == "tasks" && v > 0) r.target_tasks = v;
       if (key == "q4k_slots" && (v == 1 || v == 2)) r.q4k_slots = v;
       if (key == "q80_slots" && (v == 1 || v == 2)) r.q80_slots = v;
-      if (key == "prefetch") r.prefetch = v != 0;
-      if (key == "pf_kb" && v > 0) r.pf_kb = v;
-      if (key == "pf_w" && v >= 0) r.pf_w = v;
-      if (key == "pf_x") r.pf_x = v != 0;
       const char* comma = std::strchr(eq, ',');
       if (!comma) break;
       p = comma + 1;
@@ -75,13 +67,12 @@ static const Tuning& tuning() {
 struct DeviceState {
   std::atomic<int> checked{0};   // 0 unknown, 1 gfx950, -1 unsupported
   ScratchArea* scratch = nullptr;
-  int cus = 0;
   std::mutex mu;
 };
 static DeviceState g_dev[kMaxDevices];
 
 // Returns GGUF_QK_OK and the scratch of the current device, or an error.
-static int current_device(ScratchArea** scratch, int* cus = nullptr) {
+static int current_device(ScratchArea** scratch) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
     (void)hipGetLastError();
@@ -100,14 +91,12 @@ static int current_device(ScratchArea** scratch, int* cus = nullptr) {
       if (ok) ok = hipGetSymbolAddress(&p, HIP_SYMBOL(g_scratch)) == hipSuccess && p != nullptr;
       (void)hipGetLastError();
       st.scratch = static_cast<ScratchArea*>(p);
-      st.cus = ok ? prop.multiProcessorCount : 0;
       c = ok ? 1 : -1;
       st.checked.store(c, std::memory_order_release);
     }
   }
   if (c != 1) return GGUF_QK_ERR_DEVICE;
   if (scratch) *scratch = st.scratch;
-  if (cus) *cus = st.cus;
   return GGUF_QK_OK;
 }
 
@@ -234,16 +223,14 @@ static int check_gemv(int type, const void* W, const float* x, const float* y, i
   return GGUF_QK_OK;
 }
 
-// Launches one group of same-format GEMVs (already validated, rows > 0).
-// Q8_0 GEMVs with cols % 256 != 0 are not grouped (see launch_step).
-// Q4_K runs as block tasks (8 waves per row group and up to 8 super-blocks,
-// partials added in LDS); Q8_0 as per-wave tasks with split-K sized to the
-// task target. `pf` (may be null) lists byte ranges to pull into the
-// Infinity Cache while this launch runs; `cus` is the device's CU count.
-static int launch_group(int type, const gguf_qk_gemv* const* v, int n, const ScratchArea* scratch,
-                        hipStream_t stream, const Prefetch* pf, int cus) {
-  GemvGroup grp{};
-  grp.n = n;
+// Lays out one group of same-format GEMVs (already validated, rows > 0) as
+// tasks: Q4_K as block tasks (8 waves per row group and up to 8 super-blocks,
+// partials added in LDS), Q8_0 as per-wave tasks with split-K sized to the
+// task target. Returns the task count. Q8_0 GEMVs with cols % 256 != 0 are
+// never grouped (see launch_step).
+static int64_t plan_group(int type, const gguf_qk_gemv* const* v, int n, GemvGroup* grp) {
+  *grp = GemvGroup{};
+  grp->n = n;
   int64_t total_bytes = 0;
   for (int i = 0; i < n; ++i) total_bytes += v[i]->rows * row_bytes_of(type, v[i]->cols);
   int64_t tasks = 0, part_off = 0, cnt_off = 0;
@@ -265,7 +252,7 @@ static int launch_group(int type, const gguf_qk_gemv* const* v, int n, const Scr
     }
     while (P > 1 && part_off + P * g.rows > kScratchPartials) --P;
     if (P > 1 && cnt_off + RG > kScratchCounters) P = 1;
-    GemvDesc& d = grp.d[i];
+    GemvDesc& d = grp->d[i];
     d.W = static_cast<const uint8_t*>(g.W);
     d.x = g.x;
     d.y = g.y;
@@ -281,24 +268,17 @@ static int launch_group(int type, const gguf_qk_gemv* const* v, int n, const Scr
       cnt_off += RG;
     }
   }
+  return tasks;
+}
+
+// Launches one planned group.
+static int launch_group(int type, const gguf_qk_gemv* const* v, int n, const ScratchArea* scratch,
+                        hipStream_t stream) {
+  GemvGroup grp;
+  const int64_t tasks = plan_group(type, v, n, &grp);
   float* partials = const_cast<float*>(scratch->partials);
   int* counters = const_cast<int*>(scratch->counters);
-  const int64_t compute_blocks =
-      type == GGUF_QK_TYPE_Q4_K ? tasks : (tasks + kGemvWaves - 1) / kGemvWaves;
-  if (pf && pf->n > 0) {
-    // Prefetch blocks: about pf_kb KiB each, but no more than fit on the
-    // device beside the compute blocks (two blocks per CU: both kernels hold
-    // 70-80 KB of LDS per block), and at least 32.
-    int64_t bytes = 0;
-    for (int r = 0; r < pf->n; ++r) bytes += pf->bytes[r];
-    int64_t want = (bytes + (int64_t)tuning().pf_kb * 1024 - 1) / ((int64_t)tuning().pf_kb * 1024);
-    const int64_t room = 2 * (int64_t)cus - compute_blocks;
-    if (want > room) want = room;
-    if (want < 32) want = 32;
-    grp.pf = *pf;
-    grp.pf.blocks = (int)want;
-  }
-  const int64_t blocks = compute_blocks + grp.pf.blocks;
+  const int64_t blocks = type == GGUF_QK_TYPE_Q4_K ? tasks : (tasks + kGemvWaves - 1) / kGemvWaves;
   if (blocks > INT32_MAX) return GGUF_QK_ERR_LIMIT;
   if (type == GGUF_QK_TYPE_Q4_K) {
     hipLaunchKernelGGL(gemv_q4k_block_kernel, dim3((unsigned)blocks), dim3(kBlockWaves * 64), 0,
@@ -323,10 +303,9 @@ static int launch_rowwise_q8_0(const gguf_qk_gemv& g, hipStream_t stream) {
 }
 
 // Launches the GEMVs of one step: same-format GEMVs go together, kMaxGroup at
-// a time; each launch follows the previous one on the stream. The prefetch
-// `pf` (may be null) rides on the first group launch of the step.
+// a time; each launch follows the previous one on the stream.
 static int launch_step(const gguf_qk_gemv* list, int n, const ScratchArea* scratch,
-                       hipStream_t stream, const Prefetch* pf, int cus) {
+                       hipStream_t stream) {
   for (int type : {GGUF_QK_TYPE_Q4_K, GGUF_QK_TYPE_Q8_0}) {
     const gguf_qk_gemv* grp[kMaxGroup];
     int k = 0;
@@ -340,16 +319,14 @@ static int launch_step(const gguf_qk_gemv* list, int n, const ScratchArea* scrat
       }
       grp[k++] = &g;
       if (k == kMaxGroup) {
-        const int st = launch_group(type, grp, k, scratch, stream, pf, cus);
+        const int st = launch_group(type, grp, k, scratch, stream);
         if (st) return st;
-        pf = nullptr;
         k = 0;
       }
     }
     if (k) {
-      const int st = launch_group(type, grp, k, scratch, stream, pf, cus);
+      const int st = launch_group(type, grp, k, scratch, stream);
       if (st) return st;
-      pf = nullptr;
     }
   }
   return GGUF_QK_OK;
@@ -365,7 +342,7 @@ static int matvec_common(int type, const void* W, const float* x, float* y, int6
   st = current_device(&scratch);
   if (st) return st;
   const gguf_qk_gemv g{W, x, y, rows, cols, type, 0, {0}};
-  return launch_step(&g, 1, scratch, stream, nullptr, 0);
+  return launch_step(&g, 1, scratch, stream);
 }
 
 int gguf_qmatvec_batch(const gguf_qk_gemv* list, int32_t n, hipStream_t stream) {
@@ -396,43 +373,12 @@ int gguf_qmatvec_batch(const gguf_qk_gemv* list, int32_t n, hipStream_t stream) 
     i = j;
   }
   ScratchArea* scratch = nullptr;
-  int cus = 0;
-  int st = current_device(&scratch, &cus);
+  int st = current_device(&scratch);
   if (st) return st;
   for (int32_t i = 0; i < n;) {
     int32_t j = i;
     while (j < n && list[j].stage == list[i].stage) ++j;
-    // The next step's weights, and its inputs when no entry of the batch
-    // writes them, pulled on chip while this step runs.
-    Prefetch pf{};
-    if (tuning().prefetch && j < n) {
-      int32_t k = j;
-      while (k < n && list[k].stage == list[j].stage) ++k;
-      int64_t own = 0;
-      for (int32_t e = i; e < j; ++e) own += list[e].rows * row_bytes_of(list[e].type, list[e].cols);
-      int64_t budget = own / 100 * tuning().pf_w;
-      for (int32_t e = j; e < k && pf.n < kMaxPrefetch && budget >= 16; ++e) {
-        int64_t wb = list[e].rows * row_bytes_of(list[e].type, list[e].cols);
-        if (wb > budget) wb = budget;
-        pf.p[pf.n] = static_cast<const uint8_t*>(list[e].W);
-        pf.bytes[pf.n] = wb & ~int64_t(15);
-        budget -= pf.bytes[pf.n];
-        if (pf.bytes[pf.n] > 0) ++pf.n;
-      }
-      for (int32_t e = j; e < k && pf.n < kMaxPrefetch && tuning().pf_x; ++e) {
-        const void* x = list[e].x;
-        const int64_t xb = list[e].cols * 4;
-        bool seen = false, written = false;
-        for (int32_t f = j; f < e; ++f) seen = seen || list[f].x == x;
-        for (int32_t f = 0; f < n && !written; ++f)
-          written = overlap(list[f].y, list[f].rows * 4, x, xb);
-        if (seen || written) continue;
-        pf.p[pf.n] = static_cast<const uint8_t*>(x);
-        pf.bytes[pf.n] = xb;
-        ++pf.n;
-      }
-    }
-    st = launch_step(list + i, j - i, scratch, stream, pf.n ? &pf : nullptr, cus);
+    st = launch_step(list + i, j - i, scratch, stream);
     if (st) return st;
     i = j;
   }
