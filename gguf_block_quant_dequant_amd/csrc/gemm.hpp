@@ -1,16 +1,28 @@
 // Prefill: Y[n, r] = sum_k X[n, k] W[r, k], X and Y bf16, W Q4_K, on the
 // gfx950 matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
 //
-// Block tile: 128 tokens x 128 weight rows, K consumed 64 at a time (one
-// sub-block pair of a super-block). Per step every thread stages 32 bf16 of X
-// and decodes 32 weights of W (fp32 dequant rounded to nearest-even bf16) into
-// LDS; the four waves then each multiply a 64x64 sub-tile as 2x2 MFMA tiles.
-// LDS rows are padded to 144 bytes (36 dwords, 4 modulo 32 banks) so the
-// 16-byte operand reads of 32 consecutive rows are conflict-free.
+// Block tile: 128 tokens x 128 weight rows, 4 waves, each wave a 64 x 64
+// sub-tile held as 2 x 2 MFMA accumulators. K is consumed 128 at a time (half
+// a super-block). Each thread stages, in registers, the next step's 64 bf16
+// of X and 32 bytes of nibbles (+ the 16-byte super-block header) of one
+// weight row, loaded while the current step's MFMAs run; at its step the
+// thread decodes the 64 weights (fp32 dequant rounded to nearest-even bf16, as
+// the bf16 dequant entry point) and stores both operands to LDS. (A second
+// staged step does not fit the register file beside the accumulators and
+// the unrolled operand reads without spilling.)
+//
+// Split K: a launch may cut K into S ranges of whole super-blocks (grid z).
+// With S > 1 each block stores its fp32 tile to scratch with agent-scope
+// stores, waits for them, and bumps the tile's counter; the block that
+// arrives last adds the S partial tiles in range order 0..S-1 (the result
+// does not depend on arrival order), writes Y in bf16 and resets the counter.
+//
+// LDS rows are 272 bytes (68 dwords, 4 modulo 32 banks): the 16-byte operand
+// reads of 8 consecutive rows by 8 lanes cover all 32 banks once.
 //
 // MFMA operand layout used (32x32x16): lane l supplies A[i = l % 32][8 k] and
-// B[8 k][j = l % 32] from k-group l / 32; because A and B are fed with the
-// same (k-group, element) labels the product is independent of how the
+// B[8 k][j = l % 32] from k-group l / 32; A and B are fed with the same
+// (k-group, element) labels, so the product does not depend on how the
 // hardware orders k inside a group. Accumulator element e of lane l is
 // D[8 (e / 4) + 4 (l / 32) + e % 4][l % 32].
 #pragma once
@@ -22,99 +34,196 @@ namespace gqk {
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
-constexpr int kGemmBM = 128;
-constexpr int kGemmBN = 128;
-constexpr int kGemmBK = 64;
-constexpr int kGemmLdsRow = kGemmBK * 2 + 16;   // 144 bytes
+constexpr int kGemmBM = 128;                     // tokens per block
+constexpr int kGemmBN = 128;                     // weight rows per block
+constexpr int kGemmBK = 128;                     // k per step (half a super-block)
+constexpr int kGemmLdsRow = kGemmBK * 2 + 16;    // 272 bytes
+constexpr int kGemmTileFloats = kGemmBM * kGemmBN;
+constexpr int kGemmCounterStride = 32;           // ints: one 128-byte line per tile counter
+
+// Loads step `step` (global, relative to this thread's rows) into stage set S.
+#define GQK_GEMM_LOAD(S, step)                                                                 \
+  do {                                                                                         \
+    const uint4* xp_ = xrow + (int64_t)(step) * (kGemmBK / 8);                                 \
+    x##S##0 = xp_[0]; x##S##1 = xp_[1]; x##S##2 = xp_[2]; x##S##3 = xp_[3];                    \
+    x##S##4 = xp_[4]; x##S##5 = xp_[5]; x##S##6 = xp_[6]; x##S##7 = xp_[7];                    \
+    const uint8_t* sb_ = wrow + (int64_t)((step) >> 1) * kQ4KBlockBytes;                       \
+    h##S = *reinterpret_cast<const uint4*>(sb_);                                               \
+    const uint4* q_ = reinterpret_cast<const uint4*>(sb_ + 16 + 32 * (2 * ((step) & 1) + half)); \
+    qa##S = q_[0];                                                                             \
+    qb##S = q_[1];                                                                             \
+  } while (0)
+
+// Decodes stage set S (step `step`), stores it to LDS, refills S with step
+// `next` (if inside this block's range) and runs the step's MFMAs.
+#define GQK_GEMM_STEP(S, step, next)                                                           \
+  do {                                                                                         \
+    const int hs_ = (step) & 1;                                                                \
+    const float d_ = half_lo(h##S.x), dmin_ = half_hi(h##S.x);                                 \
+    const uint32_t scw_ = hs_ ? ((h##S.w & 0x0F0F0F0Fu) | ((h##S.y >> 2) & 0x30303030u))       \
+                              : (h##S.y & 0x3F3F3F3Fu);                                        \
+    const uint32_t mw_ = hs_ ? (((h##S.w >> 4) & 0x0F0F0F0Fu) | ((h##S.z >> 2) & 0x30303030u)) \
+                             : (h##S.z & 0x3F3F3F3Fu);                                         \
+    const uint32_t scp_ = opaque(scw_ >> (16 * half)), mp_ = opaque(mw_ >> (16 * half));      \
+    const float dl_ = d_ * ubyte0(scp_), dh_ = d_ * ubyte1(scp_);                              \
+    const float ml_ = dmin_ * ubyte0(mp_), mh_ = dmin_ * ubyte1(mp_);                          \
+    const uint32_t qw_[8] = {qa##S.x, qa##S.y, qa##S.z, qa##S.w,                               \
+                             qb##S.x, qb##S.y, qb##S.z, qb##S.w};                              \
+    uint32_t lo_[16], hi_[16];                                                                 \
+    _Pragma("unroll") for (int t_ = 0; t_ < 8; ++t_) {                                         \
+      const uint32_t l4_ = opaque(qw_[t_] & 0x0F0F0F0Fu);                                      \
+      const uint32_t h4_ = opaque((qw_[t_] >> 4) & 0x0F0F0F0Fu);                               \
+      lo_[2 * t_] = pack_bf16x2(fmaf(dl_, ubyte0(l4_), -ml_), fmaf(dl_, ubyte1(l4_), -ml_));    \
+      lo_[2 * t_ + 1] = pack_bf16x2(fmaf(dl_, ubyte2(l4_), -ml_), fmaf(dl_, ubyte3(l4_), -ml_)); \
+      hi_[2 * t_] = pack_bf16x2(fmaf(dh_, ubyte0(h4_), -mh_), fmaf(dh_, ubyte1(h4_), -mh_));    \
+      hi_[2 * t_ + 1] = pack_bf16x2(fmaf(dh_, ubyte2(h4_), -mh_), fmaf(dh_, ubyte3(h4_), -mh_)); \
+    }                                                                                          \
+    __syncthreads(); /* the previous step's operand reads are done */                          \
+    uint4* xd_ = reinterpret_cast<uint4*>(xs + ld_row * kGemmLdsRow + 128 * half);             \
+    xd_[0] = x##S##0; xd_[1] = x##S##1; xd_[2] = x##S##2; xd_[3] = x##S##3;                    \
+    xd_[4] = x##S##4; xd_[5] = x##S##5; xd_[6] = x##S##6; xd_[7] = x##S##7;                    \
+    uint4* wd_ = reinterpret_cast<uint4*>(ws + ld_row * kGemmLdsRow + 128 * half);             \
+    wd_[0] = make_uint4(lo_[0], lo_[1], lo_[2], lo_[3]);                                       \
+    wd_[1] = make_uint4(lo_[4], lo_[5], lo_[6], lo_[7]);                                       \
+    wd_[2] = make_uint4(lo_[8], lo_[9], lo_[10], lo_[11]);                                     \
+    wd_[3] = make_uint4(lo_[12], lo_[13], lo_[14], lo_[15]);                                   \
+    wd_[4] = make_uint4(hi_[0], hi_[1], hi_[2], hi_[3]);                                       \
+    wd_[5] = make_uint4(hi_[4], hi_[5], hi_[6], hi_[7]);                                       \
+    wd_[6] = make_uint4(hi_[8], hi_[9], hi_[10], hi_[11]);                                     \
+    wd_[7] = make_uint4(hi_[12], hi_[13], hi_[14], hi_[15]);                                   \
+    __syncthreads();                                                                           \
+    if ((next) < step_end) GQK_GEMM_LOAD(S, (next));                                           \
+    _Pragma("unroll") for (int kk_ = 0; kk_ < kGemmBK; kk_ += 16) {                            \
+      const int kb_ = (kk_ + 8 * (lane >> 5)) * 2;                                             \
+      const bf16x8 a0_ = *reinterpret_cast<const bf16x8*>(                                     \
+          xs + (wi * 64 + (lane & 31)) * kGemmLdsRow + kb_);                                   \
+      const bf16x8 a1_ = *reinterpret_cast<const bf16x8*>(                                     \
+          xs + (wi * 64 + 32 + (lane & 31)) * kGemmLdsRow + kb_);                              \
+      const bf16x8 b0_ = *reinterpret_cast<const bf16x8*>(                                     \
+          ws + (wj * 64 + (lane & 31)) * kGemmLdsRow + kb_);                                   \
+      const bf16x8 b1_ = *reinterpret_cast<const bf16x8*>(                                     \
+          ws + (wj * 64 + 32 + (lane & 31)) * kGemmLdsRow + kb_);                              \
+      acc00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0_, b0_, acc00, 0, 0, 0);               \
+      acc01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0_, b1_, acc01, 0, 0, 0);               \
+      acc10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1_, b0_, acc10, 0, 0, 0);               \
+      acc11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1_, b1_, acc11, 0, 0, 0);               \
+    }                                                                                          \
+  } while (0)
+
+// Writes accumulator `acc` (sub-tile it, jt of this wave) to Y as bf16.
+__device__ __forceinline__ void gemm_store_bf16(const f32x16& acc, uint16_t* __restrict__ Y,
+                                                int64_t n_tokens, int64_t rows, int64_t n0,
+                                                int64_t r0, int wi, int wj, int it, int jt,
+                                                int lane) {
+  const int64_t r = r0 + wj * 64 + jt * 32 + (lane & 31);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int64_t n = n0 + wi * 64 + it * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+    if (n < n_tokens && r < rows) Y[n * rows + r] = to_bf16(acc[e]);
+  }
+}
+
+// Partial tile layout in scratch: [wave][it][jt][e][lane] floats, so each
+// (wave, it, jt, e) is 64 consecutive floats written and read by one wave.
+__device__ __forceinline__ float* gemm_partial_slot(float* tile, int wave, int it, int jt, int e,
+                                                    int lane) {
+  return tile + ((((wave * 2 + it) * 2 + jt) * 16 + e) * 64 + lane);
+}
 
 __global__ __launch_bounds__(256) void gemm_q4_k_kernel(const uint8_t* __restrict__ W,
                                                         const uint16_t* __restrict__ X,
                                                         uint16_t* __restrict__ Y, int64_t n_tokens,
-                                                        int64_t rows, int nsb) {
+                                                        int64_t rows, int nsb, float* partials,
+                                                        int* counters) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[kGemmBM * kGemmLdsRow];
   __shared__ __attribute__((aligned(16))) uint8_t ws[kGemmBN * kGemmLdsRow];
+  __shared__ int last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wi = wave >> 1, wj = wave & 1;
   const int64_t n0 = (int64_t)blockIdx.y * kGemmBM;
   const int64_t r0 = (int64_t)blockIdx.x * kGemmBN;
+  const int S = (int)gridDim.z, split = (int)blockIdx.z;
   const int64_t K = (int64_t)nsb * kQ4KBlockWeights;
   const int64_t row_bytes = (int64_t)nsb * kQ4KBlockBytes;
+  // this block's steps: super-blocks [nsb * split / S, nsb * (split + 1) / S)
+  const int step_begin = 2 * (int)((int64_t)nsb * split / S);
+  const int step_end = 2 * (int)((int64_t)nsb * (split + 1) / S);
 
-  const int ld_row = tid >> 1, ld_half = tid & 1;
+  // Staging role: thread = (row, half). X: k [64 half, 64 half + 64) of the
+  // step. W: nibble group g = 2 h + half of the step's half super-block h,
+  // i.e. Qb[32 g .. 32 g + 31]: low nibbles are local k 64 half + 0..31,
+  // high nibbles local k 64 half + 32..63. Rows past the end are clamped
+  // (read, never stored).
+  const int ld_row = tid >> 1, half = tid & 1;
   const int64_t xr = (n0 + ld_row) < n_tokens ? (n0 + ld_row) : (n_tokens - 1);
   const int64_t wr = (r0 + ld_row) < rows ? (r0 + ld_row) : (rows - 1);
-  const uint16_t* xrow = X + xr * K + 32 * ld_half;
+  const uint4* xrow = reinterpret_cast<const uint4*>(X + xr * K + 64 * half);
   const uint8_t* wrow = W + wr * row_bytes;
 
-  f32x16 acc[2][2];
+  uint4 xA0, xA1, xA2, xA3, xA4, xA5, xA6, xA7, hA, qaA, qbA;
+  f32x16 acc00, acc01, acc10, acc11;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+  for (int e = 0; e < 16; ++e) acc00[e] = acc01[e] = acc10[e] = acc11[e] = 0.f;
 
-  for (int64_t k0 = 0; k0 < K; k0 += kGemmBK) {
-    const int64_t s = k0 >> 8;
-    const int g = (int)((k0 >> 6) & 3);
-    const uint4* xp = reinterpret_cast<const uint4*>(xrow + k0);
-    const uint4 xv0 = xp[0], xv1 = xp[1], xv2 = xp[2], xv3 = xp[3];
-    const uint8_t* sb = wrow + s * kQ4KBlockBytes;
-    const uint4 hdr = *reinterpret_cast<const uint4*>(sb);
-    const uint4 qv = *reinterpret_cast<const uint4*>(sb + 16 + 32 * g + 16 * ld_half);
-    float dsc[8], dmm[8];
-    q4k_scales(hdr.x, hdr.y, hdr.z, hdr.w, dsc, dmm);
-    const float dl = dsc[2 * g], ml = dmm[2 * g], dh = dsc[2 * g + 1], mh = dmm[2 * g + 1];
-    const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-    uint32_t lo_bf[8], hi_bf[8];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint32_t lo = opaque(qw[t] & 0x0F0F0F0Fu);
-      const uint32_t hi = opaque((qw[t] >> 4) & 0x0F0F0F0Fu);
-      lo_bf[2 * t] = pack_bf16x2(fmaf(dl, ubyte0(lo), -ml), fmaf(dl, ubyte1(lo), -ml));
-      lo_bf[2 * t + 1] = pack_bf16x2(fmaf(dl, ubyte2(lo), -ml), fmaf(dl, ubyte3(lo), -ml));
-      hi_bf[2 * t] = pack_bf16x2(fmaf(dh, ubyte0(hi), -mh), fmaf(dh, ubyte1(hi), -mh));
-      hi_bf[2 * t + 1] = pack_bf16x2(fmaf(dh, ubyte2(hi), -mh), fmaf(dh, ubyte3(hi), -mh));
-    }
-    __syncthreads();   // the previous step's operand reads are done
-    uint4* xd = reinterpret_cast<uint4*>(xs + ld_row * kGemmLdsRow + 64 * ld_half);
-    xd[0] = xv0; xd[1] = xv1; xd[2] = xv2; xd[3] = xv3;
-    // low nibbles: k = 16 ld_half + 0..15 of this 64-k step; high: 32 + 16 ld_half + 0..15
-    uint4* wl = reinterpret_cast<uint4*>(ws + ld_row * kGemmLdsRow + 32 * ld_half);
-    uint4* wh = reinterpret_cast<uint4*>(ws + ld_row * kGemmLdsRow + 64 + 32 * ld_half);
-    wl[0] = make_uint4(lo_bf[0], lo_bf[1], lo_bf[2], lo_bf[3]);
-    wl[1] = make_uint4(lo_bf[4], lo_bf[5], lo_bf[6], lo_bf[7]);
-    wh[0] = make_uint4(hi_bf[0], hi_bf[1], hi_bf[2], hi_bf[3]);
-    wh[1] = make_uint4(hi_bf[4], hi_bf[5], hi_bf[6], hi_bf[7]);
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < kGemmBK; kk += 16) {
-      const int kb = (kk + 8 * (lane >> 5)) * 2;
-      bf16x8 a[2], b[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        a[t] = *reinterpret_cast<const bf16x8*>(xs + (wi * 64 + t * 32 + (lane & 31)) * kGemmLdsRow + kb);
-        b[t] = *reinterpret_cast<const bf16x8*>(ws + (wj * 64 + t * 32 + (lane & 31)) * kGemmLdsRow + kb);
-      }
-#pragma unroll
-      for (int it = 0; it < 2; ++it)
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
-          acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[it], b[jt], acc[it][jt], 0, 0, 0);
-    }
+  GQK_GEMM_LOAD(A, step_begin);
+  for (int step = step_begin; step < step_end; ++step) GQK_GEMM_STEP(A, step, step + 1);
+
+  if (S == 1) {
+    gemm_store_bf16(acc00, Y, n_tokens, rows, n0, r0, wi, wj, 0, 0, lane);
+    gemm_store_bf16(acc01, Y, n_tokens, rows, n0, r0, wi, wj, 0, 1, lane);
+    gemm_store_bf16(acc10, Y, n_tokens, rows, n0, r0, wi, wj, 1, 0, lane);
+    gemm_store_bf16(acc11, Y, n_tokens, rows, n0, r0, wi, wj, 1, 1, lane);
+    return;
   }
 
+  const int64_t tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const int64_t ntiles = (int64_t)gridDim.x * gridDim.y;
+  float* mine = partials + ((int64_t)split * ntiles + tile) * kGemmTileFloats;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    __hip_atomic_store(gemm_partial_slot(mine, wave, 0, 0, e, lane), acc00[e], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gemm_partial_slot(mine, wave, 0, 1, e, lane), acc01[e], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gemm_partial_slot(mine, wave, 1, 0, e, lane), acc10[e], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gemm_partial_slot(mine, wave, 1, 1, e, lane), acc11[e], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // every wave's partial stores have completed before thread 0 signals
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  GQK_WAIT_VMCNT(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(&counters[tile * kGemmCounterStride], 1,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = old == S - 1;
+  }
+  __syncthreads();
+  if (!last) return;
 #pragma unroll
   for (int it = 0; it < 2; ++it)
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
-      const int64_t r = r0 + wj * 64 + jt * 32 + (lane & 31);
+      f32x16 sum;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t n = n0 + wi * 64 + it * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (n < n_tokens && r < rows) Y[n * rows + r] = to_bf16(acc[it][jt][e]);
+      for (int e = 0; e < 16; ++e) sum[e] = 0.f;
+      for (int s = 0; s < S; ++s) {
+        float* p = partials + ((int64_t)s * ntiles + tile) * kGemmTileFloats;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          sum[e] += __hip_atomic_load(gemm_partial_slot(p, wave, it, jt, e, lane),
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+      gemm_store_bf16(sum, Y, n_tokens, rows, n0, r0, wi, wj, it, jt, lane);
     }
+  if (tid == 0)
+    __hip_atomic_store(&counters[tile * kGemmCounterStride], 0, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
+
+#undef GQK_GEMM_LOAD
+#undef GQK_GEMM_STEP
 
 }  // namespace gqk

@@ -25,9 +25,15 @@ namespace gqk {
 constexpr int64_t kScratchPartials = int64_t(2) << 20;   // floats (8 MiB)
 constexpr int64_t kScratchCounters = int64_t(1) << 14;   // row-group counters
 constexpr int kMaxSplits = 16;                            // K ranges per row group
+// Prefill split K: fp32 partial tiles (32 MiB) and one counter per tile.
+constexpr int64_t kGemmScratchFloats = int64_t(8) << 20;
+constexpr int64_t kGemmMaxTiles = int64_t(1) << 12;
+constexpr int kGemmMaxSplits = 8;
 struct ScratchArea {
   float partials[kScratchPartials];
   int counters[kScratchCounters * kCounterStride];
+  float gemm_partials[kGemmScratchFloats];
+  int gemm_counters[kGemmMaxTiles * kGemmCounterStride];
 };
 static __device__ __attribute__((aligned(256))) ScratchArea g_scratch;
 
@@ -37,6 +43,8 @@ constexpr int kMaxDevices = 64;
 // sweeps, e.g. "tasks=2048,q4k_slots=1,q80_slots=1") overrides them.
 struct Tuning {
   int target_tasks = 2048;   // wave tasks a split-K GEMV aims for
+  int gemm_blocks = 0;       // blocks a prefill GEMM aims for (0: by K, see gguf_qmatmul_q4_k)
+  int gemm_max_split = 0;    // largest K split of a prefill GEMM (0: by K)
   int q4k_slots = 1;         // LDS chunks in flight per wave, Q4_K
   int q80_slots = 1;         // LDS chunks in flight per wave, Q8_0
 };
@@ -53,6 +61,8 @@ static const Tuning& tuning() {
       const std::string key(p, eq - p);
       const int v = std::atoi(eq + 1);
       if (key == "tasks" && v > 0) r.target_tasks = v;
+      if (key == "gemm_blocks" && v >= 0) r.gemm_blocks = v;
+      if (key == "gemm_max_split" && v >= 0 && v <= kGemmMaxSplits) r.gemm_max_split = v;
       if (key == "q4k_slots" && (v == 1 || v == 2)) r.q4k_slots = v;
       if (key == "q80_slots" && (v == 1 || v == 2)) r.q80_slots = v;
       const char* comma = std::strchr(eq, ',');
@@ -408,13 +418,29 @@ int gguf_qmatmul_q4_k(const void* W, const uint16_t* X, uint16_t* Y, int64_t n_t
   const int64_t xb = n_tokens * cols * 2, yb = n_tokens * rows * 2;
   if (overlap(Y, yb, W, wb) || overlap(Y, yb, X, xb)) return GGUF_QK_ERR_ALIAS;
   if (rows == 0 || n_tokens == 0) return GGUF_QK_OK;
-  st = current_device(nullptr);
+  ScratchArea* scratch = nullptr;
+  st = current_device(&scratch);
   if (st) return st;
   const int64_t gx = (rows + kGemmBN - 1) / kGemmBN, gy = (n_tokens + kGemmBM - 1) / kGemmBM;
   if (gx > INT32_MAX || gy > 65535) return GGUF_QK_ERR_LIMIT;
-  hipLaunchKernelGGL(gemm_q4_k_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream,
-                     static_cast<const uint8_t*>(W), X, Y, n_tokens, rows,
-                     (int)(cols / kQ4KBlockWeights));
+  // Split K over whole super-blocks when there are too few tiles to fill the
+  // device, as far as the scratch for the fp32 partial tiles allows.
+  // Measured on the 2048-hidden shapes: long K (down, 43 super-blocks) gains
+  // from up to 8 ranges and two blocks per CU; short K (8 super-blocks) from
+  // at most 4 ranges and one block per CU, past which the last block's sum
+  // over the partial tiles costs more than the extra blocks save.
+  const int64_t tiles = gx * gy, nsb = cols / kQ4KBlockWeights;
+  const bool long_k = nsb >= 32;
+  const int64_t target = tuning().gemm_blocks ? tuning().gemm_blocks : (long_k ? 512 : 256);
+  const int64_t max_split = tuning().gemm_max_split ? tuning().gemm_max_split : (long_k ? 8 : 4);
+  int64_t S = target / tiles;
+  if (S > max_split) S = max_split;
+  if (S > nsb) S = nsb;
+  while (S > 1 && S * tiles * kGemmTileFloats > kGemmScratchFloats) --S;
+  if (S < 1 || tiles > kGemmMaxTiles) S = 1;
+  hipLaunchKernelGGL(gemm_q4_k_kernel, dim3((unsigned)gx, (unsigned)gy, (unsigned)S), dim3(256), 0,
+                     stream, static_cast<const uint8_t*>(W), X, Y, n_tokens, rows, (int)nsb,
+                     scratch->gemm_partials, scratch->gemm_counters);
   return launch_status();
 }
 

@@ -290,8 +290,11 @@ def _matmul_case(n, rows, cols, seed):
 
 @pytest.mark.parametrize("n,rows,cols", [(512, 256, 512), (1, 200, 256), (100, 129, 768),
                                          (129, 300, 2048), (512, 2048, 2048), (512, 512, 2048),
-                                         (512, 2048, 11008)])
+                                         (512, 2048, 11008), (512, 11008, 2048),
+                                         (64, 128, 7 * 256)])
 def test_matmul_q4_k(n, rows, cols):
+    """Includes the prefill shapes at N = 512 and a K of 7 super-blocks, which
+    the K split cuts into unequal ranges."""
     Y, ref = _matmul_case(n, rows, cols, 12)
     e, ok = oracle.floored_rel_err(Y, ref)
     say("err", e)
@@ -316,6 +319,23 @@ def test_matmul_q4_k_integer_exact():
     Y = bf16_bits(g.gguf_qmatmul_q4_k(dev(w), bf16_tensor(xb)))
     exact = X.astype(np.int64) @ q.T
     assert np.array_equal(oracle.bf16_bits_to_f64(Y), exact.astype(np.float64))
+
+
+def test_matmul_deterministic_across_calls():
+    """Split-K tiles are summed in range order by whichever block arrives last:
+    repeated calls give identical bits, also after a call of another shape
+    (tile counters return to zero)."""
+    rng = synth.rng_for(15, 0, 0)
+    W1 = dev(synth.q4_k_weights(rng, 2048, 11008))
+    X1 = bf16_tensor(synth.activations_bf16_bits(rng, 512, 11008))
+    W2 = dev(synth.q4_k_weights(rng, 300, 2048))
+    X2 = bf16_tensor(synth.activations_bf16_bits(rng, 129, 2048))
+    a = bf16_bits(g.gguf_qmatmul_q4_k(W1, X1))
+    b2 = bf16_bits(g.gguf_qmatmul_q4_k(W2, X2))
+    b = bf16_bits(g.gguf_qmatmul_q4_k(W1, X1))
+    c2 = bf16_bits(g.gguf_qmatmul_q4_k(W2, X2))
+    assert np.array_equal(a, b)
+    assert np.array_equal(b2, c2)
 
 
 def test_matmul_single_token_agrees_with_matvec():
