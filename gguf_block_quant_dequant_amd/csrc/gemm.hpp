@@ -4,10 +4,11 @@
 // Block tile: 128 tokens x 128 weight rows, 4 waves, each wave a 64 x 64
 // sub-tile held as 2 x 2 MFMA accumulators. K is consumed 128 at a time (half
 // a super-block). Each thread stages, in registers, the next step's 64 bf16
-// of X and 32 bytes of nibbles (+ the 16-byte super-block header) of one
-// weight row, loaded while the current step's MFMAs run; at its step the
-// thread decodes the 64 weights (fp32 dequant rounded to nearest-even bf16, as
-// the bf16 dequant entry point) and stores both operands to LDS. (A second
+// of X (16 bytes from each of 8 token rows) and 32 bytes of nibbles (+ the
+// 16-byte super-block header) of one weight row, loaded while the current
+// step's MFMAs run; at its step the thread decodes the 64 weights (fp32
+// dequant rounded to nearest-even bf16, as the bf16 dequant entry point) and
+// stores both operands to LDS. (A second
 // staged step does not fit the register file beside the accumulators and
 // the unrolled operand reads without spilling.)
 //
@@ -41,12 +42,21 @@ constexpr int kGemmLdsRow = kGemmBK * 2 + 16;    // 272 bytes
 constexpr int kGemmTileFloats = kGemmBM * kGemmBN;
 constexpr int kGemmCounterStride = 32;           // ints: one 128-byte line per tile counter
 
-// Loads step `step` (global, relative to this thread's rows) into stage set S.
+// Loads step `step` into stage set S: 16 bytes of X from each of this
+// thread's 8 token rows (16 consecutive lanes read one row's 256 bytes, so a
+// wave's load touches 8 cache lines) and the header and 32 nibble bytes of
+// its weight row.
 #define GQK_GEMM_LOAD(S, step)                                                                 \
   do {                                                                                         \
-    const uint4* xp_ = xrow + (int64_t)(step) * (kGemmBK / 8);                                 \
-    x##S##0 = xp_[0]; x##S##1 = xp_[1]; x##S##2 = xp_[2]; x##S##3 = xp_[3];                    \
-    x##S##4 = xp_[4]; x##S##5 = xp_[5]; x##S##6 = xp_[6]; x##S##7 = xp_[7];                    \
+    const int64_t ko_ = (int64_t)(step) * kGemmBK + 8 * xc;                                    \
+    x##S##0 = *reinterpret_cast<const uint4*>(X + xoff0 + ko_);                                \
+    x##S##1 = *reinterpret_cast<const uint4*>(X + xoff1 + ko_);                                \
+    x##S##2 = *reinterpret_cast<const uint4*>(X + xoff2 + ko_);                                \
+    x##S##3 = *reinterpret_cast<const uint4*>(X + xoff3 + ko_);                                \
+    x##S##4 = *reinterpret_cast<const uint4*>(X + xoff4 + ko_);                                \
+    x##S##5 = *reinterpret_cast<const uint4*>(X + xoff5 + ko_);                                \
+    x##S##6 = *reinterpret_cast<const uint4*>(X + xoff6 + ko_);                                \
+    x##S##7 = *reinterpret_cast<const uint4*>(X + xoff7 + ko_);                                \
     const uint8_t* sb_ = wrow + (int64_t)((step) >> 1) * kQ4KBlockBytes;                       \
     h##S = *reinterpret_cast<const uint4*>(sb_);                                               \
     const uint4* q_ = reinterpret_cast<const uint4*>(sb_ + 16 + 32 * (2 * ((step) & 1) + half)); \
@@ -79,9 +89,15 @@ constexpr int kGemmCounterStride = 32;           // ints: one 128-byte line per 
       hi_[2 * t_ + 1] = pack_bf16x2(fmaf(dh_, ubyte2(h4_), -mh_), fmaf(dh_, ubyte3(h4_), -mh_)); \
     }                                                                                          \
     __syncthreads(); /* the previous step's operand reads are done */                          \
-    uint4* xd_ = reinterpret_cast<uint4*>(xs + ld_row * kGemmLdsRow + 128 * half);             \
-    xd_[0] = x##S##0; xd_[1] = x##S##1; xd_[2] = x##S##2; xd_[3] = x##S##3;                    \
-    xd_[4] = x##S##4; xd_[5] = x##S##5; xd_[6] = x##S##6; xd_[7] = x##S##7;                    \
+    uint8_t* xd_ = xs + xr0 * kGemmLdsRow + 16 * xc;                                           \
+    *reinterpret_cast<uint4*>(xd_ + 0 * 16 * kGemmLdsRow) = x##S##0;                           \
+    *reinterpret_cast<uint4*>(xd_ + 1 * 16 * kGemmLdsRow) = x##S##1;                           \
+    *reinterpret_cast<uint4*>(xd_ + 2 * 16 * kGemmLdsRow) = x##S##2;                           \
+    *reinterpret_cast<uint4*>(xd_ + 3 * 16 * kGemmLdsRow) = x##S##3;                           \
+    *reinterpret_cast<uint4*>(xd_ + 4 * 16 * kGemmLdsRow) = x##S##4;                           \
+    *reinterpret_cast<uint4*>(xd_ + 5 * 16 * kGemmLdsRow) = x##S##5;                           \
+    *reinterpret_cast<uint4*>(xd_ + 6 * 16 * kGemmLdsRow) = x##S##6;                           \
+    *reinterpret_cast<uint4*>(xd_ + 7 * 16 * kGemmLdsRow) = x##S##7;                           \
     uint4* wd_ = reinterpret_cast<uint4*>(ws + ld_row * kGemmLdsRow + 128 * half);             \
     wd_[0] = make_uint4(lo_[0], lo_[1], lo_[2], lo_[3]);                                       \
     wd_[1] = make_uint4(lo_[4], lo_[5], lo_[6], lo_[7]);                                       \
@@ -149,15 +165,21 @@ __global__ __launch_bounds__(256) void gemm_q4_k_kernel(const uint8_t* __restric
   const int step_begin = 2 * (int)((int64_t)nsb * split / S);
   const int step_end = 2 * (int)((int64_t)nsb * (split + 1) / S);
 
-  // Staging role: thread = (row, half). X: k [64 half, 64 half + 64) of the
-  // step. W: nibble group g = 2 h + half of the step's half super-block h,
-  // i.e. Qb[32 g .. 32 g + 31]: low nibbles are local k 64 half + 0..31,
-  // high nibbles local k 64 half + 32..63. Rows past the end are clamped
-  // (read, never stored).
+  // Staging roles. X: thread t stages 16 bytes (k 8 xc .. 8 xc + 7 of the
+  // step, xc = t % 16) of token rows xr0 + 16 j, j = 0..7 (xr0 = t / 16).
+  // W: thread = (row, half) decodes nibble group g = 2 h + half of the step's
+  // half super-block h, i.e. Qb[32 g .. 32 g + 31]: low nibbles are local k
+  // 64 half + 0..31, high nibbles local k 64 half + 32..63. Rows past the end
+  // are clamped (read, never stored).
+  const int xc = tid & 15, xr0 = tid >> 4;
+  auto xrow_off = [&](int j) -> int64_t {
+    const int64_t n = n0 + xr0 + 16 * j;
+    return (n < n_tokens ? n : n_tokens - 1) * K;
+  };
+  const int64_t xoff0 = xrow_off(0), xoff1 = xrow_off(1), xoff2 = xrow_off(2), xoff3 = xrow_off(3);
+  const int64_t xoff4 = xrow_off(4), xoff5 = xrow_off(5), xoff6 = xrow_off(6), xoff7 = xrow_off(7);
   const int ld_row = tid >> 1, half = tid & 1;
-  const int64_t xr = (n0 + ld_row) < n_tokens ? (n0 + ld_row) : (n_tokens - 1);
   const int64_t wr = (r0 + ld_row) < rows ? (r0 + ld_row) : (rows - 1);
-  const uint4* xrow = reinterpret_cast<const uint4*>(X + xr * K + 64 * half);
   const uint8_t* wrow = W + wr * row_bytes;
 
   uint4 xA0, xA1, xA2, xA3, xA4, xA5, xA6, xA7, hA, qaA, qbA;
