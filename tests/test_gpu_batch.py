@@ -1,0 +1,139 @@
+"""gguf_qmatvec_batch against the oracle: the full 36-layer decode pass in the
+launch configuration the benchmark times (sampled rows of every GEMV, two calls
+bit-identical, HIP-graph replays identical to the eager call), a pass whose
+steps read the previous step's outputs, and ragged shapes over many steps."""
+
+import numpy as np
+import pytest
+import torch
+
+import gguf_block_quant_dequant_amd as g
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL_F32 = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def _ref_rows(fmt, w, rows, cols, x):
+    if fmt == synth.Q8_0:
+        deq = oracle.dequant_q8_0_f32(w[rows], len(rows), cols)
+    else:
+        deq = oracle.dequant_q4_k_f32(w[rows], len(rows), cols)
+    return oracle.matvec_f64(deq, x)
+
+
+def test_batch_full_decode_pass_sampled_rows():
+    """36 layers x {q,k,v}, {o}, {gate,up}, {down} + the Q8_0 head, as the
+    benchmark builds it; 33 sampled rows of every GEMV against the oracle,
+    two calls bit-identical, HIP-graph replays identical to the eager call."""
+    stages = synth.decode_stream(n_layers=36, head=True, threads=8)
+    entries, checks = [], []
+    for si, st in enumerate(stages):
+        X = dev(st.x)
+        for gm, w in zip(st.gemvs, st.weights):
+            y = torch.empty(gm.rows, dtype=torch.float32, device=DEV)
+            tid = g.TYPE_Q8_0 if gm.fmt == synth.Q8_0 else g.TYPE_Q4_K
+            entries.append((tid, dev(w), X, y, si))
+            rows = np.unique(np.concatenate([np.linspace(0, gm.rows - 1, 32).astype(np.int64),
+                                             [gm.rows - 1]]))
+            checks.append((y, rows, _ref_rows(gm.fmt, w, rows, gm.cols, st.x)))
+    del stages
+    say("full pass:", len(entries), "GEMVs")
+    b = g.GemvBatch(entries)
+    g.gguf_qmatvec_batch(b)
+    first = [host(y).copy() for y, _, _ in checks]
+    worst = 0.0
+    for (y, rows, ref), got in zip(checks, first):
+        e, ok = oracle.floored_rel_err(got[rows], ref)
+        worst = max(worst, e)
+        assert ok and e <= TOL_F32, e
+    say("worst sampled error", worst)
+    g.gguf_qmatvec_batch(b)
+    for (y, _, _), a in zip(checks, first):
+        assert np.array_equal(host(y).view(np.uint32), a.view(np.uint32))
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        g.gguf_qmatvec_batch(b, s)
+    for _ in range(2):
+        for y, _, _ in checks:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for (y, _, _), a in zip(checks, first):
+            assert np.array_equal(host(y).view(np.uint32), a.view(np.uint32))
+
+
+def test_batch_chained_layers_read_previous_outputs():
+    """Two layers where every step reads the previous step's output as its
+    input (q -> o -> gate/up -> down -> next q/k/v): each step against the
+    oracle on the input the GPU actually read."""
+    stages = synth.decode_stream(n_layers=2, head=False, threads=8)
+    x0 = dev(stages[0].x)
+    entries, steps = [], []
+    prev = {"x": x0}
+    for si, st in enumerate(stages):
+        ys = []
+        for gm, w in zip(st.gemvs, st.weights):
+            y = torch.empty(gm.rows, dtype=torch.float32, device=DEV)
+            ys.append((gm, w, y))
+        steps.append((prev["x"], ys))
+        for gm, w, y in ys:
+            entries.append((g.TYPE_Q4_K, dev(w), prev["x"], y, si))
+        # the next step reads the first GEMV's output of this one (q, o, gate, down)
+        prev = {"x": ys[0][2]}
+    b = g.GemvBatch(entries)
+    for _ in range(2):
+        for _, ys in steps:
+            for _, _, y in ys:
+                y.fill_(float("nan"))
+        g.gguf_qmatvec_batch(b)
+        for x_t, ys in steps:
+            x = host(x_t).astype(np.float32)
+            for gm, w, y in ys:
+                ref = oracle.matvec_f64(oracle.dequant_q4_k_f32(w, gm.rows, gm.cols), x)
+                e, ok = oracle.floored_rel_err(host(y), ref)
+                assert ok and e <= TOL_F32, (gm.name, e)
+
+
+def test_batch_ragged_shapes_many_steps():
+    """33 steps of 1 to 4 Q4_K GEMVs with ragged row counts and several K,
+    every row against the oracle."""
+    rng = np.random.default_rng(31)
+    entries, refs = [], []
+    row_choices = [1, 63, 64, 65, 200, 777]
+    k_choices = [256, 768, 2048]
+    for si in range(33):
+        m = int(rng.integers(1, 5))
+        cols = int(rng.choice(k_choices))
+        x = synth.activations_f32(rng, cols)
+        X = dev(x)
+        for _ in range(m):
+            rows = int(rng.choice(row_choices))
+            w = synth.q4_k_weights(rng, rows, cols)
+            y = torch.empty(rows, dtype=torch.float32, device=DEV)
+            entries.append((g.TYPE_Q4_K, dev(w), X, y, si))
+            refs.append((y, oracle.matvec_f64(oracle.dequant_q4_k_f32(w, rows, cols), x)))
+    say("ragged:", len(entries), "GEMVs in 33 steps")
+    g.gguf_qmatvec_batch(g.GemvBatch(entries))
+    for y, ref in refs:
+        e, ok = oracle.floored_rel_err(host(y), ref)
+        assert ok and e <= TOL_F32, e
