@@ -46,6 +46,19 @@ __device__ __forceinline__ float ubyte0(uint32_t v) { return (float)(v & 0xFFu);
 __device__ __forceinline__ float ubyte1(uint32_t v) { return (float)((v >> 8) & 0xFFu); }
 __device__ __forceinline__ float ubyte2(uint32_t v) { return (float)((v >> 16) & 0xFFu); }
 __device__ __forceinline__ float ubyte3(uint32_t v) { return (float)(v >> 24); }
+
+// Four bytes holding values 0..15 converted to fp32 as value / 512, two per
+// instruction: read as OCP E4M3 fp8, a byte b < 16 is b x 2^-9 exactly
+// (b < 8: subnormal m x 2^-9; 8 <= b < 16: exponent 1, (8 + m) x 2^-9).
+typedef float gqk_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void nibbles_div512(uint32_t v, float (&q)[4]) {
+  const gqk_f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v, false);
+  const gqk_f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v, true);
+  q[0] = lo.x;
+  q[1] = lo.y;
+  q[2] = hi.x;
+  q[3] = hi.y;
+}
 __device__ __forceinline__ float sbyte0(uint32_t v) { return (float)(int)(int8_t)(v & 0xFFu); }
 __device__ __forceinline__ float sbyte1(uint32_t v) { return (float)(int)(int8_t)((v >> 8) & 0xFFu); }
 __device__ __forceinline__ float sbyte2(uint32_t v) { return (float)(int)(int8_t)((v >> 16) & 0xFFu); }

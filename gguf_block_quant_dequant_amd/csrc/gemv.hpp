@@ -114,7 +114,9 @@ __device__ __forceinline__ void sload_first_with_touch(xreg16& xa, const float* 
 // low nibbles are weights 64g + 4t + 0..3 (sub-block 2g) and high nibbles
 // weights 64g + 32 + 4t + 0..3 (sub-block 2g + 1).
 //   sum_i w_i x_i = sum_j (d sc_j) (sum_{i in j} q_i x_i) - sum_j (dmin m_j) xsum_j
-// High nibbles are converted in place (16 q), the 1/16 folded into d sc_j.
+// Nibbles are masked into byte positions (high nibbles shifted down first)
+// and converted two per instruction as q / 512 (nibbles_div512); the 512 is
+// folded into d sc_j, an exact power-of-two scaling.
 // 16 steps of 16 weights. On entry xa holds xs[0..15]; on exit, if `more`,
 // it holds xs[256..271] (the next super-block's first step).
 // ---------------------------------------------------------------------------
@@ -134,19 +136,21 @@ __device__ __forceinline__ float q4k_superblock_dot(const uint32_t (&c)[36], con
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const uint32_t v = c[4 + 8 * (u >> 1) + 4 * (h & 1) + t];
-      const uint32_t nib = opaque((u & 1) ? (v & 0xF0F0F0F0u) : (v & 0x0F0F0F0Fu));
+      const uint32_t nib = opaque((u & 1) ? ((v >> 4) & 0x0F0F0F0Fu) : (v & 0x0F0F0F0Fu));
+      float q[4];
+      nibbles_div512(nib, q);
       float& a = (t & 1) ? a1 : a0;
-      a = fmaf(ubyte0(nib), xa[4 * t + 0], a);
-      a = fmaf(ubyte1(nib), xa[4 * t + 1], a);
-      a = fmaf(ubyte2(nib), xa[4 * t + 2], a);
-      a = fmaf(ubyte3(nib), xa[4 * t + 3], a);
+      a = fmaf(q[0], xa[4 * t + 0], a);
+      a = fmaf(q[1], xa[4 * t + 1], a);
+      a = fmaf(q[2], xa[4 * t + 2], a);
+      a = fmaf(q[3], xa[4 * t + 3], a);
     }
     if (h < 15 || more) {
       GQK_SWAIT_AFTER(xb, a0, a1);
       xa = xb;
     }
     if (h & 1) {
-      acc = fmaf((u & 1) ? dsc[u] * 0.0625f : dsc[u], a0 + a1, acc);
+      acc = fmaf(dsc[u] * 512.0f, a0 + a1, acc);
       a0 = 0.f;
       a1 = 0.f;
     }
@@ -470,10 +474,25 @@ __global__ __launch_bounds__(kBlockWaves * 64) void gemv_q4k_block_kernel(GemvGr
   const int64_t row0 = (int64_t)rg * 64;
   const int valid = (int)((D.rows - row0) < 64 ? (D.rows - row0) : 64);
   const uint32_t row_bytes = (uint32_t)n * kQ4KBlockBytes;
-  // wave w takes super-blocks c0 + w, c0 + w + kBlockWaves, ...
+  // wave w takes super-block c0 + w (a range holds at most kBlockWaves)
   float acc = 0.f;
-  for (int c = c0 + wave; c < c1; c += kBlockWaves)
-    acc += q4k_wave_task<1>(D.W, D.x, row_bytes, row0, valid, c, c + 1, &slots[wave][0], lane);
+  const int c = c0 + wave;
+  if (c < c1) {
+    uint8_t* slot = &slots[wave][0];
+    uint32_t off[9];
+    dma_offsets<9, kQ4KBlockBytes>(lane, row_bytes, valid, off);
+    const float* xs = D.x + (int64_t)c * kQ4KBlockWeights;
+    const float4 xq = reinterpret_cast<const float4*>(xs)[lane];
+    dma_chunk<9>(D.W + row0 * (int64_t)row_bytes + (int64_t)c * kQ4KBlockBytes, off, slot);
+    xreg16 xa;
+    sload_first_with_touch(xa, xs);
+    GQK_WAIT_VMCNT(0);
+    uint32_t cw[36];
+    lds_read_9x16(lds_addr(slot + lane * kQ4KBlockBytes), cw);
+    float xsum[8];
+    q4k_xsums(xq, xsum);
+    acc = q4k_superblock_dot(cw, xs, false, xa, xsum);
+  }
   red[wave][lane] = acc;
   __syncthreads();
   if (wave == 0) {
