@@ -21,6 +21,7 @@ What it computes, and from which passage:
   files (none available); pinned for self-consistency by hand-packed bytes.
 * matvec y = W x ("culpeo.ws", naive-implementation post, the matvec op), in
   fp64 from the fp32 dequantized weights.
+* small batch Y = X W^T with fp32 X (the matvec of each token row), in fp64.
 * prefill Y = X W^T with bf16 X ("GGUF Inferencer in R", section 1 and section
   4: prefill is the same math on the whole prompt as one matrix), in fp64.
 """
@@ -49,6 +50,7 @@ from .formats import (  # noqa: F401
 from .linalg import (  # noqa: F401
     floored_rel_err,
     matmul_bf16_x_f64,
+    matmul_f32_x_f64,
     matvec_exact,
     matvec_f64,
 )

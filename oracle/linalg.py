@@ -27,6 +27,16 @@ def matmul_bf16_x_f64(x_bf16_bits: np.ndarray, w32: np.ndarray) -> np.ndarray:
     return X @ np.asarray(w32, dtype=np.float64).T
 
 
+def matmul_f32_x_f64(x32: np.ndarray, w32: np.ndarray) -> np.ndarray:
+    """Y[n, r] = sum_k X[n, k] W[r, k] in fp64, X fp32 [n_tokens, K] and W the
+    fp32 dequant [rows, K]: the decode matvec applied to several activation
+    vectors at once (culpeo.ws naive-implementation post, matvec of w [r, c]
+    by x [c]; "GGUF Inferencer in R", section 1: prefill runs the same math
+    on a matrix of tokens). Row n of Y is the matvec of token n."""
+    X = np.asarray(x32, dtype=np.float32).astype(np.float64)
+    return X @ np.asarray(w32, dtype=np.float64).T
+
+
 def matvec_exact(w, x) -> list:
     """Exact y = W x with Fractions, for tiny shapes (brute force)."""
     w = np.asarray(w)
