@@ -37,6 +37,8 @@ _SIGS = {
     "gguf_qmatvec_q8_0": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "gguf_qmatvec_q4_k": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "gguf_qmatmul_q4_k": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P]),
+    "gguf_qmatmul_f32_q8_0": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P]),
+    "gguf_qmatmul_f32_q4_k": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P]),
     "gguf_qk_probe_read": (ctypes.c_int, [_P, _I64, _P, _P]),
     "gguf_qmatvec_batch": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
 }
@@ -195,6 +197,30 @@ def gguf_qmatmul_q4_k(W, X, Y=None, rows=None, stream=None):
                                    _dev(Y, "Y", torch.bfloat16), n, rows, cols, _stream(stream)),
            "gguf_qmatmul_q4_k")
     return Y
+
+
+def _matmul_f32(name, fmt, W, X, Y, rows, stream):
+    if X.dim() != 2:
+        raise ValueError("X must be [n_tokens, cols]")
+    n, cols = X.shape
+    rows, cols = _rows_cols(W, fmt, rows, cols)
+    if Y is None:
+        Y = torch.empty((n, rows), dtype=torch.float32, device=W.device)
+    if Y.numel() != n * rows:
+        raise ValueError("Y must have n_tokens x rows elements")
+    _check(getattr(lib(), name)(_dev(W, "W", torch.uint8), _dev(X, "X", torch.float32),
+                                _dev(Y, "Y", torch.float32), n, rows, cols, _stream(stream)), name)
+    return Y
+
+
+def gguf_qmatmul_f32_q8_0(W, X, Y=None, rows=None, stream=None):
+    """Y = X @ dequant(W)^T for a Q8_0 W, X fp32 [n_tokens, cols], Y fp32 [n_tokens, rows]."""
+    return _matmul_f32("gguf_qmatmul_f32_q8_0", TYPE_Q8_0, W, X, Y, rows, stream)
+
+
+def gguf_qmatmul_f32_q4_k(W, X, Y=None, rows=None, stream=None):
+    """Y = X @ dequant(W)^T for a Q4_K W, X fp32 [n_tokens, cols], Y fp32 [n_tokens, rows]."""
+    return _matmul_f32("gguf_qmatmul_f32_q4_k", TYPE_Q4_K, W, X, Y, rows, stream)
 
 
 def gguf_qk_probe_read(buf, sink=None, stream=None):

@@ -29,11 +29,9 @@
 #pragma once
 
 #include "device_common.hpp"
+#include "mfma_types.hpp"
 
 namespace gqk {
-
-typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 constexpr int kGemmBM = 128;                     // tokens per block
 constexpr int kGemmBN = 128;                     // weight rows per block

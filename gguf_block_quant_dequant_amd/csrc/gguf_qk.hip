@@ -14,6 +14,7 @@
 #include "dequant.hpp"
 #include "gemm.hpp"
 #include "gemv.hpp"
+#include "gemv_small_batch.hpp"
 #include "probe.hpp"
 
 namespace gqk {
@@ -45,6 +46,7 @@ struct Tuning {
   int target_tasks = 2048;   // wave tasks a split-K GEMV aims for
   int gemm_blocks = 0;       // blocks a prefill GEMM aims for (0: by K, see gguf_qmatmul_q4_k)
   int gemm_max_split = 0;    // largest K split of a prefill GEMM (0: by K)
+  int sb_blocks = 512;       // blocks a small-batch product aims for
   int q4k_slots = 1;         // LDS chunks in flight per wave, Q4_K
   int q80_slots = 1;         // LDS chunks in flight per wave, Q8_0
 };
@@ -63,6 +65,7 @@ static const Tuning& tuning() {
       if (key == "tasks" && v > 0) r.target_tasks = v;
       if (key == "gemm_blocks" && v >= 0) r.gemm_blocks = v;
       if (key == "gemm_max_split" && v >= 0 && v <= kGemmMaxSplits) r.gemm_max_split = v;
+      if (key == "sb_blocks" && v > 0) r.sb_blocks = v;
       if (key == "q4k_slots" && (v == 1 || v == 2)) r.q4k_slots = v;
       if (key == "q80_slots" && (v == 1 || v == 2)) r.q80_slots = v;
       const char* comma = std::strchr(eq, ',');
@@ -446,6 +449,63 @@ int gguf_qmatmul_q4_k(const void* W, const uint16_t* X, uint16_t* Y, int64_t n_t
                      stream, static_cast<const uint8_t*>(W), X, Y, n_tokens, rows, (int)nsb,
                      scratch->gemm_partials, scratch->gemm_counters);
   return launch_status();
+}
+
+// Small batch (fp32 X and Y, 32 tokens x 128 rows per block, K in steps of
+// 256). Shares the prefill GEMM's partial-tile scratch and tile counters.
+static_assert(kSbCounterStride == kGemmCounterStride, "shared tile counters");
+constexpr int kSbMaxSplits = 8;
+
+static int small_batch_common(int type, const void* W, const float* X, float* Y, int64_t n_tokens,
+                              int64_t rows, int64_t cols, hipStream_t stream) {
+  int64_t wb = 0;
+  int st = check_matrix(type, W, rows, cols, &wb);
+  if (st) return st;
+  if (!X || !Y) return GGUF_QK_ERR_NULL;
+  if (n_tokens < 0 || cols % kSbK) return GGUF_QK_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(Y)) return GGUF_QK_ERR_ALIGN;
+  if (n_tokens > 0 && (cols > INT64_MAX / 4 / n_tokens || rows > INT64_MAX / 4 / n_tokens))
+    return GGUF_QK_ERR_SHAPE;
+  const int64_t xb = n_tokens * cols * 4, yb = n_tokens * rows * 4;
+  if (overlap(Y, yb, W, wb) || overlap(Y, yb, X, xb)) return GGUF_QK_ERR_ALIAS;
+  if (rows == 0 || n_tokens == 0) return GGUF_QK_OK;
+  const int64_t steps = cols / kSbK;
+  if (row_bytes_of(type, cols) * kSbRows > INT32_MAX || n_tokens > INT32_MAX || steps > INT32_MAX)
+    return GGUF_QK_ERR_LIMIT;   // 32-bit offsets inside a block's rows
+  ScratchArea* scratch = nullptr;
+  st = current_device(&scratch);
+  if (st) return st;
+  const int64_t gx = (rows + kSbRows - 1) / kSbRows, gy = (n_tokens + kSbTokens - 1) / kSbTokens;
+  if (gx > INT32_MAX || gy > 65535) return GGUF_QK_ERR_LIMIT;
+  // Split K over whole steps when the tiles alone do not fill the device, as
+  // far as the partial-tile scratch allows.
+  const int64_t tiles = gx * gy;
+  int64_t S = tuning().sb_blocks / tiles;
+  if (S > kSbMaxSplits) S = kSbMaxSplits;
+  if (S > steps) S = steps;
+  while (S > 1 && S * tiles * kSbTileFloats > kGemmScratchFloats) --S;
+  if (S < 1 || tiles > kGemmMaxTiles) S = 1;
+  const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)S), block(256);
+  const uint8_t* w = static_cast<const uint8_t*>(W);
+  if (type == GGUF_QK_TYPE_Q4_K)
+    hipLaunchKernelGGL(gemv_small_batch_kernel<true>, grid, block, 0, stream, w, X, Y,
+                       (int)n_tokens, rows, (int)steps, scratch->gemm_partials,
+                       scratch->gemm_counters);
+  else
+    hipLaunchKernelGGL(gemv_small_batch_kernel<false>, grid, block, 0, stream, w, X, Y,
+                       (int)n_tokens, rows, (int)steps, scratch->gemm_partials,
+                       scratch->gemm_counters);
+  return launch_status();
+}
+
+int gguf_qmatmul_f32_q8_0(const void* W, const float* X, float* Y, int64_t n_tokens, int64_t rows,
+                          int64_t cols, hipStream_t stream) {
+  return small_batch_common(GGUF_QK_TYPE_Q8_0, W, X, Y, n_tokens, rows, cols, stream);
+}
+
+int gguf_qmatmul_f32_q4_k(const void* W, const float* X, float* Y, int64_t n_tokens, int64_t rows,
+                          int64_t cols, hipStream_t stream) {
+  return small_batch_common(GGUF_QK_TYPE_Q4_K, W, X, Y, n_tokens, rows, cols, stream);
 }
 
 int gguf_qk_probe_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream) {

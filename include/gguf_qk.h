@@ -148,6 +148,23 @@ int gguf_qmatvec_batch(const gguf_qk_gemv* list, int32_t n, hipStream_t stream);
 int gguf_qmatmul_q4_k(const void* W, const uint16_t* X, uint16_t* Y, int64_t n_tokens,
                       int64_t rows, int64_t cols, hipStream_t stream);
 
+/* --- small batch: fused dequant x a few fp32 vectors (MFMA) --------------- */
+
+/* Y[n, r] = sum_k X[n, k] * w[r, k] for n < n_tokens: the fp32 matvec above
+ * applied to each token row of X at once (culpeo.ws naive-implementation
+ * post, the matvec op; "GGUF Inferencer in R", section 1: several tokens make
+ * the activation a matrix). X fp32 row-major [n_tokens x cols], Y fp32
+ * row-major [n_tokens x rows]. Same accuracy bar as the matvec (fp32
+ * accumulation): the integer quants enter the matrix cores exactly, each x
+ * as a pair of bf16 whose sum is x within 2^-16 |x|, and every block scale is
+ * applied in fp32. Deterministic. Built for a few tokens (1 to 64; blocks of
+ * 32 tokens x 128 rows, weights re-read per 32 tokens); cols must be a
+ * multiple of 256 for both formats (GGUF_QK_ERR_SHAPE otherwise). */
+int gguf_qmatmul_f32_q8_0(const void* W, const float* X, float* Y, int64_t n_tokens,
+                          int64_t rows, int64_t cols, hipStream_t stream);
+int gguf_qmatmul_f32_q4_k(const void* W, const float* X, float* Y, int64_t n_tokens,
+                          int64_t rows, int64_t cols, hipStream_t stream);
+
 /* --- measurement ---------------------------------------------------------- */
 
 /* Streaming-read probe: reads `bytes` (a multiple of 16) from device buffer

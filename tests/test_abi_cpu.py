@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ["gguf_qmatvec_q8_0", "gguf_qmatvec_q4_k", "gguf_qmatmul_q4_k", "dequant_q8_0",
               "dequant_q4_k", "dequant_q4_k_bf16", "gguf_row_bytes", "gguf_qk_strerror",
-              "gguf_qk_abi_version", "gguf_qmatvec_batch"]:
+              "gguf_qk_abi_version", "gguf_qmatvec_batch", "gguf_qmatmul_f32_q8_0",
+              "gguf_qmatmul_f32_q4_k"]:
         assert n in names
 
 
@@ -121,6 +122,26 @@ def test_matmul_validation():
     assert f(A, B, C, 8, 4, 128, None) == g.ERR_SHAPE
     assert f(A, B + 2, C, 8, 4, 256, None) == g.ERR_ALIGN
     assert f(A, B, B + 16, 8, 4, 256, None) == g.ERR_ALIAS          # Y overlaps X
+    assert f(A, B, C, 0, 4, 256, None) == g.OK
+    assert f(A, B, C, 8, 0, 256, None) == g.OK
+
+
+@pytest.mark.parametrize("name", ["gguf_qmatmul_f32_q8_0", "gguf_qmatmul_f32_q4_k"])
+def test_small_batch_validation(name):
+    f = getattr(g.lib(), name)
+    assert f(None, B, C, 8, 4, 256, None) == g.ERR_NULL
+    assert f(A, None, C, 8, 4, 256, None) == g.ERR_NULL
+    assert f(A, B, None, 8, 4, 256, None) == g.ERR_NULL
+    assert f(A, B, C, -1, 4, 256, None) == g.ERR_SHAPE
+    assert f(A, B, C, 8, -4, 256, None) == g.ERR_SHAPE
+    assert f(A, B, C, 8, 4, 0, None) == g.ERR_SHAPE
+    assert f(A, B, C, 8, 4, 224, None) == g.ERR_SHAPE              # K steps are 256 wide
+    assert f(A, B, C, 1 << 40, 4, 1 << 30, None) == g.ERR_SHAPE    # X bytes overflow
+    assert f(A + 8, B, C, 8, 4, 256, None) == g.ERR_ALIGN
+    assert f(A, B + 4, C, 8, 4, 256, None) == g.ERR_ALIGN
+    assert f(A, B, C + 4, 8, 4, 256, None) == g.ERR_ALIGN
+    assert f(A, B, B + 16, 8, 4, 256, None) == g.ERR_ALIAS          # Y overlaps X
+    assert f(A, B, A + 16, 8, 4, 256, None) == g.ERR_ALIAS          # Y overlaps W
     assert f(A, B, C, 0, 4, 256, None) == g.OK
     assert f(A, B, C, 8, 0, 256, None) == g.OK
 
