@@ -15,8 +15,10 @@ Prints one JSON line: weight-stream GB/s (whole pass), % of the 8 TB/s HBM
 peak, tokens/s-equivalent (1 / pass time), a roofline record for the
 dominant kernel (the Q4_K block-task GEMV), the CPU oracle timed on a bounded
 sample of the same workload, and labelled extras: the pass time distribution,
-an unordered upper bound (all GEMVs of the pass as one step), and the bf16
-MFMA prefill pass over the same 36-layer weights (N = 512 tokens).
+an unordered upper bound (all GEMVs of the pass as one step), the bf16
+MFMA prefill pass over the same 36-layer weights (N = 512 tokens), and the
+fp32 small-batch passes (the same 253 matrices times 8, 32 and 64 activation
+vectors).
 
     python bench.py --copy-calibration
 
@@ -42,6 +44,7 @@ BF16_DENSE_PEAK_TFLOPS = 2500.0
 DOMINANT_KERNEL = "gemv_q4k_block_kernel"
 KERNEL_SOURCES = ["gguf_block_quant_dequant_amd/csrc/gemv.hpp",
                   "gguf_block_quant_dequant_amd/csrc/device_common.hpp"]
+SMALL_BATCH_TOKENS = (8, 32, 64)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_q4k_block_kernel_decode_stream_traffic.md")
 
 
@@ -61,6 +64,8 @@ def parse():
                     help="only the stage-ordered pass (for counter runs): no extras, no CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="copy 1 GiB device to device three times and exit")
+    ap.add_argument("--small-batch-only", action="store_true",
+                    help="only the small-batch passes (8, 32, 64 tokens) over the weight stream")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the prefill pass over the 36-layer weights (for counter runs)")
     return ap.parse_args()
@@ -201,6 +206,43 @@ def prefill_pass(torch, g, synth, entries, meta, stream, n_tokens=512, reps=3):
                          "frac": round(tflops / BF16_DENSE_PEAK_TFLOPS, 4), "traffic": None}}
 
 
+def small_batch_pass(torch, g, synth, entries, stream, n_tokens, reps=5):
+    """The whole weight stream (36 x 7 Q4_K + the Q8_0 head) multiplied by
+    n_tokens fp32 activation vectors each (Y = X W^T, fp32), one launch per
+    matrix in pass order, as one HIP graph; returns the labelled record."""
+    dev = "cuda:0"
+    gen = torch.Generator().manual_seed(synth.ROOT_SEED * 1000 + 60 + n_tokens)
+    xs, ys, calls = {}, {}, []
+    wbytes = 0
+    for tid, W, x, y, si in entries:
+        cols, rows = x.numel(), y.numel()
+        if cols not in xs:
+            xs[cols] = torch.randn(n_tokens, cols, generator=gen).to(dev)
+        if rows not in ys:
+            ys[rows] = torch.empty(n_tokens, rows, dtype=torch.float32, device=dev)
+        f = g.gguf_qmatmul_f32_q4_k if tid == g.TYPE_Q4_K else g.gguf_qmatmul_f32_q8_0
+        calls.append((f, W, xs[cols], ys[rows]))
+        wbytes += W.numel()
+
+    def run():
+        for f, W, X, Y in calls:
+            f(W, X, Y, stream=stream)
+
+    graph = capture(torch, run, stream)
+    t = time_replays(torch, graph, stream, reps)
+    ms = sorted(t)[len(t) // 2]
+    gbps = wbytes / (ms / 1e3) / 1e9
+    del graph
+    return {"label": f"small batch: the {len(calls)} matrices of the pass x {n_tokens} fp32 "
+                     "activation vectors, fp32 Y, bf16 hi/lo MFMA (HIP graph, one launch per matrix)",
+            "tokens": n_tokens, "ms_per_pass": round(ms, 4), "weight_GBps": round(gbps, 1),
+            "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+            "tokens_per_s": round(n_tokens * 1e3 / ms, 1),
+            "roofline": {"bound": "hbm", "kernel": "gemv_small_batch_kernel",
+                         "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}}
+
+
 def cpu_baseline():
     """The oracle as it stands, on a bounded sample of the same workload:
     layer 0's seven Q4_K GEMVs and the first 8192 rows of the Q8_0 head,
@@ -262,6 +304,10 @@ def main():
     torch.cuda.synchronize()
     if args.prefill_only:
         print(json.dumps(prefill_pass(torch, g, synth, entries, meta, stream)), flush=True)
+        return
+    if args.small_batch_only:
+        print(json.dumps([small_batch_pass(torch, g, synth, entries, stream, n)
+                          for n in SMALL_BATCH_TOKENS]), flush=True)
         return
     if args.no_graph:
         def step():
@@ -363,6 +409,8 @@ def main():
     rec["read_probe_GBps"] = round(ceiling, 1)
     rec["pct_of_read_probe"] = round(100 * gbps / ceiling, 2)
     rec["prefill"] = prefill_pass(torch, g, synth, entries, meta, stream)
+    rec["small_batch"] = [small_batch_pass(torch, g, synth, entries, stream, n)
+                          for n in SMALL_BATCH_TOKENS]
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline()
     print(json.dumps(rec), flush=True)

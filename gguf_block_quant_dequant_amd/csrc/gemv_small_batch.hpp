@@ -347,15 +347,28 @@ __global__ __launch_bounds__(256, 2) void gemv_small_batch_kernel(
   }
   __syncthreads();
   if (!last) return;
+  // The partial tiles are read four ranges at a time (one round trip per four,
+  // indexes past the last range clamped and not added) and added in range order.
   f32x16 sum;
 #pragma unroll
   for (int e = 0; e < 16; ++e) sum[e] = 0.f;
-  for (int s = 0; s < S; ++s) {
-    float* p = partials + ((int64_t)s * ntiles + tile) * kSbTileFloats;
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    float v[4][16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      sum[e] += __hip_atomic_load(sb_partial_slot(p, wave, e, lane), __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < 4; ++i) {
+      const int s = s0 + i < S ? s0 + i : S - 1;
+      float* p = partials + ((int64_t)s * ntiles + tile) * kSbTileFloats;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        v[i][e] = __hip_atomic_load(sb_partial_slot(p, wave, e, lane), __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (s0 + i < S) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sum[e] += v[i][e];
+      }
   }
   sb_store(sum, Y, n_tokens, rows, n0, r0, wave, lane);
   if (tid == 0)

@@ -47,6 +47,7 @@ struct Tuning {
   int gemm_blocks = 0;       // blocks a prefill GEMM aims for (0: by K, see gguf_qmatmul_q4_k)
   int gemm_max_split = 0;    // largest K split of a prefill GEMM (0: by K)
   int sb_blocks = 512;       // blocks a small-batch product aims for
+  int sb_max_split = 8;      // largest K split of a small-batch product
   int q4k_slots = 1;         // LDS chunks in flight per wave, Q4_K
   int q80_slots = 1;         // LDS chunks in flight per wave, Q8_0
 };
@@ -66,6 +67,7 @@ static const Tuning& tuning() {
       if (key == "gemm_blocks" && v >= 0) r.gemm_blocks = v;
       if (key == "gemm_max_split" && v >= 0 && v <= kGemmMaxSplits) r.gemm_max_split = v;
       if (key == "sb_blocks" && v > 0) r.sb_blocks = v;
+      if (key == "sb_max_split" && v > 0 && v <= 8) r.sb_max_split = v;
       if (key == "q4k_slots" && (v == 1 || v == 2)) r.q4k_slots = v;
       if (key == "q80_slots" && (v == 1 || v == 2)) r.q80_slots = v;
       const char* comma = std::strchr(eq, ',');
@@ -454,7 +456,6 @@ int gguf_qmatmul_q4_k(const void* W, const uint16_t* X, uint16_t* Y, int64_t n_t
 // Small batch (fp32 X and Y, 32 tokens x 128 rows per block, K in steps of
 // 256). Shares the prefill GEMM's partial-tile scratch and tile counters.
 static_assert(kSbCounterStride == kGemmCounterStride, "shared tile counters");
-constexpr int kSbMaxSplits = 8;
 
 static int small_batch_common(int type, const void* W, const float* X, float* Y, int64_t n_tokens,
                               int64_t rows, int64_t cols, hipStream_t stream) {
@@ -481,7 +482,7 @@ static int small_batch_common(int type, const void* W, const float* X, float* Y,
   // far as the partial-tile scratch allows.
   const int64_t tiles = gx * gy;
   int64_t S = tuning().sb_blocks / tiles;
-  if (S > kSbMaxSplits) S = kSbMaxSplits;
+  if (S > tuning().sb_max_split) S = tuning().sb_max_split;
   if (S > steps) S = steps;
   while (S > 1 && S * tiles * kSbTileFloats > kGemmScratchFloats) --S;
   if (S < 1 || tiles > kGemmMaxTiles) S = 1;
