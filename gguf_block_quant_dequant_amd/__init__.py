@@ -12,6 +12,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import struct
 
 import torch
 
@@ -22,6 +23,15 @@ TYPE_Q4_K = 12
 
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS, ERR_DEVICE, ERR_LAUNCH, ERR_LIMIT = -1, -2, -3, -4, -5, -6, -7
+ERR_FORMAT, ERR_IO, ERR_NOT_FOUND = -8, -9, -10
+
+# GGUF tensor and metadata value type ids (include/gguf_file.h)
+TENSOR_F32, TENSOR_F16, TENSOR_Q4_0, TENSOR_Q8_0, TENSOR_Q4_K, TENSOR_Q6_K, TENSOR_BF16 = 0, 1, 2, 8, 12, 14, 30
+(VALUE_U8, VALUE_I8, VALUE_U16, VALUE_I16, VALUE_U32, VALUE_I32, VALUE_F32, VALUE_BOOL, VALUE_STRING,
+ VALUE_ARRAY, VALUE_U64, VALUE_I64, VALUE_F64) = range(13)
+_SCALAR_FMT = {VALUE_U8: "<B", VALUE_I8: "<b", VALUE_U16: "<H", VALUE_I16: "<h", VALUE_U32: "<I",
+               VALUE_I32: "<i", VALUE_F32: "<f", VALUE_BOOL: "<?", VALUE_U64: "<Q", VALUE_I64: "<q",
+               VALUE_F64: "<d"}
 
 _lib = None
 
@@ -41,7 +51,36 @@ _SIGS = {
     "gguf_qmatmul_f32_q4_k": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P]),
     "gguf_qk_probe_read": (ctypes.c_int, [_P, _I64, _P, _P]),
     "gguf_qmatvec_batch": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
+    "gguf_tensor_nbytes": (_I64, [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]),
+    "gguf_file_open": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_void_p)]),
+    "gguf_file_close": (None, [_P]),
+    "gguf_file_version": (ctypes.c_int32, [_P]),
+    "gguf_file_tensor_count": (_I64, [_P]),
+    "gguf_file_kv_count": (_I64, [_P]),
+    "gguf_file_alignment": (_I64, [_P]),
+    "gguf_file_data_offset": (_I64, [_P]),
+    "gguf_file_size": (_I64, [_P]),
+    "gguf_file_tensor": (ctypes.c_int, [_P, _I64, _P]),
+    "gguf_file_kv": (ctypes.c_int, [_P, _I64, _P]),
+    "gguf_file_find_tensor": (_I64, [_P, ctypes.c_char_p]),
+    "gguf_file_find_kv": (_I64, [_P, ctypes.c_char_p]),
+    "gguf_file_kv_array_string": (ctypes.c_int, [_P, _I64, _I64, ctypes.POINTER(ctypes.c_void_p),
+                                                 ctypes.POINTER(ctypes.c_int64)]),
+    "gguf_file_upload_tensor": (ctypes.c_int, [_P, _I64, _P, _P]),
 }
+
+
+class GgufTensorInfo(ctypes.Structure):
+    """struct gguf_tensor_info of the C ABI."""
+    _fields_ = [("name", ctypes.c_char_p), ("type", ctypes.c_int32), ("n_dims", ctypes.c_int32),
+                ("dims", ctypes.c_int64 * 4), ("offset", ctypes.c_int64), ("nbytes", ctypes.c_int64),
+                ("data", ctypes.c_void_p)]
+
+
+class GgufKvInfo(ctypes.Structure):
+    """struct gguf_kv_info of the C ABI."""
+    _fields_ = [("key", ctypes.c_char_p), ("type", ctypes.c_int32), ("elem_type", ctypes.c_int32),
+                ("count", ctypes.c_int64), ("data", ctypes.c_void_p), ("nbytes", ctypes.c_int64)]
 
 
 class GemvEntry(ctypes.Structure):
@@ -255,3 +294,190 @@ def gguf_qmatvec_batch(batch: GemvBatch, stream=None):
     """Run a prepared GemvBatch (steps in order on the stream)."""
     _check(lib().gguf_qmatvec_batch(ctypes.cast(batch.array, ctypes.c_void_p), batch.n,
                                     _stream(stream)), "gguf_qmatvec_batch")
+
+
+# ------------------------------------------------------------------ GGUF files
+
+def gguf_tensor_nbytes(type_id: int, dims) -> int:
+    """Bytes of a tensor of this type and dims (fastest first), or a negative status."""
+    d = (ctypes.c_int64 * 4)(*([int(v) for v in dims] + [1] * (4 - len(dims))))
+    return lib().gguf_tensor_nbytes(type_id, len(dims), d)
+
+
+def gguf_file_open(path):
+    """Maps and parses a GGUF file; returns the library handle (ctypes.c_void_p)."""
+    h = ctypes.c_void_p()
+    _check(lib().gguf_file_open(os.fsencode(os.fspath(path)), ctypes.byref(h)), "gguf_file_open")
+    return h
+
+
+def gguf_file_close(h) -> None:
+    lib().gguf_file_close(h)
+
+
+def gguf_file_version(h) -> int:
+    return lib().gguf_file_version(h)
+
+
+def gguf_file_tensor_count(h) -> int:
+    return lib().gguf_file_tensor_count(h)
+
+
+def gguf_file_kv_count(h) -> int:
+    return lib().gguf_file_kv_count(h)
+
+
+def gguf_file_alignment(h) -> int:
+    return lib().gguf_file_alignment(h)
+
+
+def gguf_file_data_offset(h) -> int:
+    return lib().gguf_file_data_offset(h)
+
+
+def gguf_file_size(h) -> int:
+    return lib().gguf_file_size(h)
+
+
+def gguf_file_tensor(h, i: int) -> GgufTensorInfo:
+    info = GgufTensorInfo()
+    _check(lib().gguf_file_tensor(h, i, ctypes.byref(info)), "gguf_file_tensor")
+    return info
+
+
+def gguf_file_kv(h, i: int) -> GgufKvInfo:
+    info = GgufKvInfo()
+    _check(lib().gguf_file_kv(h, i, ctypes.byref(info)), "gguf_file_kv")
+    return info
+
+
+def gguf_file_find_tensor(h, name: str) -> int:
+    """Index of the tensor, or ERR_NOT_FOUND."""
+    return lib().gguf_file_find_tensor(h, name.encode())
+
+
+def gguf_file_find_kv(h, key: str) -> int:
+    """Index of the metadata entry, or ERR_NOT_FOUND."""
+    return lib().gguf_file_find_kv(h, key.encode())
+
+
+def gguf_file_kv_array_string(h, i: int, j: int) -> bytes:
+    p, n = ctypes.c_void_p(), ctypes.c_int64()
+    _check(lib().gguf_file_kv_array_string(h, i, j, ctypes.byref(p), ctypes.byref(n)),
+           "gguf_file_kv_array_string")
+    return ctypes.string_at(p, n.value) if n.value else b""
+
+
+def gguf_file_upload_tensor(h, i: int, dst: torch.Tensor, stream=None) -> torch.Tensor:
+    """Copies tensor i's raw bytes into the uint8 device tensor dst."""
+    _check(lib().gguf_file_upload_tensor(h, i, _dev(dst, "dst", torch.uint8), _stream(stream)),
+           "gguf_file_upload_tensor")
+    return dst
+
+
+class GgufFile:
+    """A GGUF file mapped and parsed by the library (include/gguf_file.h).
+
+    `tensors` lists the tensor records (name, type, dims fastest first, absolute
+    offset, nbytes); `metadata` decodes every entry (scalars, strings, arrays of
+    scalars or strings; nested arrays are returned as their raw payload bytes);
+    `upload` copies a tensor's raw bytes to a new device tensor through the
+    library. Use as a context manager or call close()."""
+
+    def __init__(self, path):
+        self._h = gguf_file_open(path)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            gguf_file_close(self._h)
+            self._h = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        self.close()
+
+    def _handle(self):
+        if not self._h:
+            raise ValueError("the file is closed")
+        return self._h
+
+    @property
+    def version(self) -> int:
+        return gguf_file_version(self._handle())
+
+    @property
+    def alignment(self) -> int:
+        return gguf_file_alignment(self._handle())
+
+    @property
+    def data_offset(self) -> int:
+        return gguf_file_data_offset(self._handle())
+
+    @property
+    def size(self) -> int:
+        return gguf_file_size(self._handle())
+
+    def _index(self, name_or_index) -> int:
+        if isinstance(name_or_index, int):
+            return name_or_index
+        i = gguf_file_find_tensor(self._handle(), name_or_index)
+        if i < 0:
+            raise KeyError(name_or_index)
+        return i
+
+    def tensor(self, name_or_index) -> dict:
+        info = gguf_file_tensor(self._handle(), self._index(name_or_index))
+        return {"name": info.name.decode("utf-8", "replace"), "type": info.type,
+                "dims": tuple(info.dims[: info.n_dims]), "offset": info.offset,
+                "nbytes": info.nbytes, "host_ptr": info.data}
+
+    @property
+    def tensors(self) -> list:
+        return [self.tensor(i) for i in range(gguf_file_tensor_count(self._handle()))]
+
+    def _kv_value(self, i: int, info: GgufKvInfo):
+        raw = ctypes.string_at(info.data, info.nbytes) if info.nbytes else b""
+        if info.type in _SCALAR_FMT:
+            return struct.unpack(_SCALAR_FMT[info.type], raw)[0]
+        if info.type == VALUE_STRING:
+            return raw.decode("utf-8", "replace")
+        if info.type == VALUE_ARRAY:
+            if info.elem_type in _SCALAR_FMT:
+                fmt = _SCALAR_FMT[info.elem_type]
+                return list(struct.unpack("<%d%s" % (info.count, fmt[1]), raw))
+            if info.elem_type == VALUE_STRING:
+                return [gguf_file_kv_array_string(self._handle(), i, j).decode("utf-8", "replace")
+                        for j in range(info.count)]
+            return raw
+        raise GgufQkArgumentError(ERR_FORMAT, "metadata value")
+
+    @property
+    def metadata(self) -> dict:
+        out = {}
+        for i in range(gguf_file_kv_count(self._handle())):
+            info = gguf_file_kv(self._handle(), i)
+            out[info.key.decode("utf-8", "replace")] = self._kv_value(i, info)
+        return out
+
+    def kv_type(self, key: str):
+        """(value type, element type) of a metadata entry."""
+        i = gguf_file_find_kv(self._handle(), key)
+        if i < 0:
+            raise KeyError(key)
+        info = gguf_file_kv(self._handle(), i)
+        return info.type, info.elem_type
+
+    def upload(self, name_or_index, device="cuda:0", stream=None):
+        """A new uint8 device tensor [nbytes] holding the tensor's raw bytes."""
+        i = self._index(name_or_index)
+        t = self.tensor(i)
+        if t["nbytes"] < 0:
+            raise GgufQkArgumentError(ERR_FORMAT, f"tensor {t['name']} has a type of unknown size")
+        out = torch.empty(max(t["nbytes"], 16), dtype=torch.uint8, device=device)
+        gguf_file_upload_tensor(self._handle(), i, out, stream)
+        return out[: t["nbytes"]]

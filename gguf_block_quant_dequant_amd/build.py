@@ -30,7 +30,7 @@ HIP_FLAGS = [
 
 
 def sources() -> list[str]:
-    return [os.path.join(CSRC, "gguf_qk.hip")]
+    return [os.path.join(CSRC, "gguf_qk.hip"), os.path.join(CSRC, "gguf_file.cpp")]
 
 
 def build_library(verbose: bool = False) -> str:

@@ -10,6 +10,7 @@
 #include <mutex>
 #include <string>
 
+#include "../../include/gguf_file.h"
 #include "../../include/gguf_qk.h"
 #include "dequant.hpp"
 #include "gemm.hpp"
@@ -181,6 +182,9 @@ const char* gguf_qk_strerror(int status) {
     case GGUF_QK_ERR_DEVICE: return "no HIP device, or the current device is not gfx950";
     case GGUF_QK_ERR_LAUNCH: return "kernel launch failed";
     case GGUF_QK_ERR_LIMIT: return "request exceeds a library limit";
+    case GGUF_QK_ERR_FORMAT: return "the file does not follow the GGUF layout";
+    case GGUF_QK_ERR_IO: return "the file cannot be opened or mapped";
+    case GGUF_QK_ERR_NOT_FOUND: return "no tensor or key of that name, or index out of range";
     default: return "unknown status";
   }
 }

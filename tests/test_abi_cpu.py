@@ -11,20 +11,23 @@ import pytest
 import gguf_block_quant_dequant_amd as g
 from gguf_block_quant_dequant_amd.build import LIB_PATH
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
-                      "gguf_qk.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADERS = [os.path.join(INCLUDE, h) for h in sorted(os.listdir(INCLUDE)) if h.endswith(".h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB_PATH),
                                 reason="libgguf_qk.so not built (run the build step first)")
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    body = text.split('extern "C" {', 1)[1]
-    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
-                       body, flags=re.M)
-    return sorted(set(names))
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        body = text.split('extern "C" {', 1)[1]
+        names |= set(re.findall(
+            r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+            body, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
@@ -32,7 +35,8 @@ def test_header_declares_the_entry_points():
     for n in ["gguf_qmatvec_q8_0", "gguf_qmatvec_q4_k", "gguf_qmatmul_q4_k", "dequant_q8_0",
               "dequant_q4_k", "dequant_q4_k_bf16", "gguf_row_bytes", "gguf_qk_strerror",
               "gguf_qk_abi_version", "gguf_qmatvec_batch", "gguf_qmatmul_f32_q8_0",
-              "gguf_qmatmul_f32_q4_k"]:
+              "gguf_qmatmul_f32_q4_k", "gguf_file_open", "gguf_file_close", "gguf_tensor_nbytes",
+              "gguf_file_tensor", "gguf_file_kv", "gguf_file_upload_tensor"]:
         assert n in names
 
 
@@ -49,7 +53,7 @@ def test_binding_names_match_header():
 
 def test_version_and_strerror():
     assert g.gguf_qk_abi_version() == 1
-    for s in range(-7, 1):
+    for s in range(-10, 1):
         assert g.gguf_qk_strerror(s)
     assert g.gguf_qk_strerror(-99) == "unknown status"
 

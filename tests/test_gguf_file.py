@@ -1,0 +1,251 @@
+"""The library's GGUF reader (include/gguf_file.h) on the CPU: the pages'
+worked example, the SmolLM3 tensor table's offsets, every metadata value type,
+the alignment entry, and rejection of malformed files (every truncation of a
+valid file, seeded corruptions) without reading past the file."""
+
+import json
+import os
+import struct
+
+import numpy as np
+import pytest
+
+import gguf_block_quant_dequant_amd as g
+from gguf_block_quant_dequant_amd.build import LIB_PATH
+from tests.gguf_writer import ARRAY, STRING, gguf_bytes, gstr
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB_PATH),
+                                reason="libgguf_qk.so not built (run the build step first)")
+
+
+def write(tmp_path, data, name="t.gguf"):
+    p = tmp_path / name
+    p.write_bytes(data)
+    return str(p)
+
+
+def open_status(path):
+    import ctypes
+    h = ctypes.c_void_p()
+    st = g.lib().gguf_file_open(path.encode(), ctypes.byref(h))
+    if st == 0:
+        g.lib().gguf_file_close(h)
+    return st
+
+
+def tiny_file():
+    doc = json.load(open(os.path.join(GOLDEN, "p2_tiny_gguf.json")))
+    t = doc["tensor"]
+    data = np.array(t["values"], dtype=np.float32).tobytes()
+    kvs = [(k, vt, v) for k, vt, v in doc["metadata"]]
+    blob, start, _ = gguf_bytes(kvs, [(t["name"], t["dims_fastest_first"], t["type"], data)])
+    return doc, blob, start
+
+
+def test_worked_example_byte_count(tmp_path):
+    """The tiny file of the pages: 205 bytes of header, metadata and tensor
+    record, padded to 224, 32 bytes of data, 256 in all."""
+    doc, blob, start = tiny_file()
+    parts = doc["part_bytes"]
+    assert sum(parts.values()) == doc["bytes_before_padding"]
+    assert start == doc["data_start"] and len(blob) == doc["file_bytes"]
+    with g.GgufFile(write(tmp_path, blob)) as f:
+        assert f.version == 3 and f.alignment == 32
+        assert f.data_offset == 224 and f.size == 256
+        md = f.metadata
+        assert md == {"general.architecture": "llama", "general.name": "tiny-demo",
+                      "llama.context_length": 4096}
+        assert f.kv_type("llama.context_length") == (4, -1)
+        (t,) = f.tensors
+        assert t["name"] == "blk.0.ffn_up.weight" and t["dims"] == (4, 2)
+        assert t["type"] == g.TENSOR_F32 and t["offset"] == 224 and t["nbytes"] == 32
+        import ctypes
+        vals = np.frombuffer(ctypes.string_at(t["host_ptr"], 32), np.float32).reshape(2, 4)
+        assert np.array_equal(vals, np.arange(8, dtype=np.float32).reshape(2, 4))
+
+
+def test_smollm3_table_offsets_follow_sizes():
+    """Each tensor of the page's 326-entry table starts where the previous one
+    ends, rounded up to 32 bytes, with sizes from gguf_tensor_nbytes."""
+    rows = []
+    with open(os.path.join(GOLDEN, "p1_tensor_table.tsv")) as fh:
+        for line in fh:
+            if line.startswith("#") or not line.strip():
+                continue
+            name, cols, nrows, typ, off = line.split("\t")
+            rows.append((name, int(cols), int(nrows), typ.strip(), int(off)))
+    assert len(rows) == 326
+    ids = {"F32": g.TENSOR_F32, "Q8_0": g.TENSOR_Q8_0}
+    for (n0, c0, r0, t0, o0), (_, _, _, _, o1) in zip(rows, rows[1:]):
+        nb = g.gguf_tensor_nbytes(ids[t0], (c0, r0))
+        assert nb > 0
+        assert (o0 + nb + 31) // 32 * 32 == o1, n0
+
+
+def test_bytes_per_block_of_the_listed_types():
+    doc = json.load(open(os.path.join(GOLDEN, "p2_bits_per_weight.json")))
+    ids = {"Q8_0": g.TENSOR_Q8_0, "Q4_0": g.TENSOR_Q4_0, "Q4_K": g.TENSOR_Q4_K, "Q6_K": g.TENSOR_Q6_K}
+    for name, nbytes, nweights, _ in doc["rows"]:
+        assert g.gguf_tensor_nbytes(ids[name], (nweights,)) == nbytes
+        assert g.gguf_tensor_nbytes(ids[name], (nweights * 3, 5)) == nbytes * 15
+        assert g.gguf_tensor_nbytes(ids[name], (nweights + 1,)) == g.ERR_SHAPE
+    assert g.gguf_tensor_nbytes(g.TENSOR_F16, (7, 3)) == 42
+    assert g.gguf_tensor_nbytes(g.TENSOR_BF16, (7,)) == 14
+    assert g.gguf_tensor_nbytes(99, (32,)) == g.ERR_FORMAT
+    assert g.gguf_tensor_nbytes(g.TENSOR_F32, (1 << 62, 4)) == g.ERR_SHAPE
+
+
+def test_every_value_type(tmp_path):
+    kvs = [("u8", 0, 250), ("i8", 1, -5), ("u16", 2, 65000), ("i16", 3, -30000),
+           ("u32", 4, 4000000000), ("i32", 5, -2000000000), ("f32", 6, 1.5), ("bool", 7, True),
+           ("str", STRING, "héllo"), ("empty", STRING, ""), ("u64", 10, 1 << 60), ("i64", 11, -(1 << 60)),
+           ("f64", 12, 2.0 ** -30), ("arr_i32", ARRAY, (5, [1, -2, 3])), ("arr_f32", ARRAY, (6, [0.5, 2.0])),
+           ("arr_str", ARRAY, (STRING, ["en", "fr", "", "zh"])), ("arr_empty", ARRAY, (4, [])),
+           ("arr_nested", ARRAY, (ARRAY, [(4, [1, 2]), (STRING, ["x"])]))]
+    blob, start, _ = gguf_bytes(kvs, [])
+    with g.GgufFile(write(tmp_path, blob)) as f:
+        md = f.metadata
+        assert f.tensors == []
+        for key, vt, v in kvs:
+            if key == "arr_nested":
+                continue
+            got = md[key]
+            if vt == ARRAY:
+                assert got == list(v[1]), key
+            elif vt == 6:
+                assert got == pytest.approx(v)
+            else:
+                assert got == v, key
+        assert f.kv_type("arr_str") == (ARRAY, STRING)
+        assert f.kv_type("arr_nested") == (ARRAY, ARRAY)
+        nested = struct.pack("<IQ", 4, 2) + struct.pack("<II", 1, 2) + struct.pack("<IQ", STRING, 1) + gstr("x")
+        assert md["arr_nested"] == nested
+
+
+def test_alignment_entry_moves_the_data(tmp_path):
+    data = [np.arange(5, dtype=np.float32).tobytes(), np.arange(32, dtype=np.float32).tobytes()]
+    tensors = [("a", [5], 0, data[0]), ("b", [8, 4], 0, data[1])]
+    blob, start, offs = gguf_bytes([("general.alignment", 4, 64)], tensors, alignment=64)
+    assert start % 64 == 0 and offs == [0, 64]
+    with g.GgufFile(write(tmp_path, blob)) as f:
+        assert f.alignment == 64 and f.data_offset == start
+        ts = f.tensors
+        assert [t["offset"] for t in ts] == [start, start + 64]
+        assert [t["nbytes"] for t in ts] == [20, 128]
+        assert f.tensor("b")["dims"] == (8, 4)
+
+
+def test_unknown_tensor_type_is_listed_without_size(tmp_path):
+    blob, start, _ = gguf_bytes([], [("odd", [10], 99, b"\1" * 10)])
+    with g.GgufFile(write(tmp_path, blob)) as f:
+        t = f.tensor("odd")
+        assert t["type"] == 99 and t["nbytes"] == -1 and t["offset"] == start
+
+
+def test_lookups(tmp_path):
+    _, blob, _ = tiny_file()
+    with g.GgufFile(write(tmp_path, blob)) as f:
+        h = f._handle()
+        assert g.lib().gguf_file_find_tensor(h, b"blk.0.ffn_up.weight") == 0
+        assert g.lib().gguf_file_find_tensor(h, b"nope") == g.ERR_NOT_FOUND
+        assert g.lib().gguf_file_find_kv(h, b"general.name") == 1
+        assert g.lib().gguf_file_find_kv(h, b"general") == g.ERR_NOT_FOUND
+        info = g.GgufTensorInfo()
+        import ctypes
+        assert g.lib().gguf_file_tensor(h, 1, ctypes.byref(info)) == g.ERR_NOT_FOUND
+        assert g.lib().gguf_file_tensor(h, -1, ctypes.byref(info)) == g.ERR_NOT_FOUND
+        with pytest.raises(KeyError):
+            f.tensor("nope")
+
+
+def test_open_errors(tmp_path):
+    assert open_status(str(tmp_path / "missing.gguf")) == g.ERR_IO
+    assert open_status(str(tmp_path)) == g.ERR_IO
+    import ctypes
+    assert g.lib().gguf_file_open(None, ctypes.byref(ctypes.c_void_p())) == g.ERR_NULL
+
+
+def test_every_truncation_is_rejected(tmp_path):
+    _, blob, _ = tiny_file()
+    for n in range(len(blob)):
+        assert open_status(write(tmp_path, blob[:n])) == g.ERR_FORMAT, n
+    assert open_status(write(tmp_path, blob)) == g.OK
+
+
+def _patched(blob, pos, fmt, v):
+    b = bytearray(blob)
+    struct.pack_into(fmt, b, pos, v)
+    return bytes(b)
+
+
+def test_corrupted_fields_are_rejected(tmp_path):
+    _, blob, _ = tiny_file()
+    cases = {
+        "magic": _patched(blob, 0, "<4s", b"GGUG"),
+        "version 1": _patched(blob, 4, "<I", 1),
+        "version 4": _patched(blob, 4, "<I", 4),
+        "tensor count huge": _patched(blob, 8, "<Q", 1 << 40),
+        "kv count huge": _patched(blob, 16, "<Q", 1 << 62),
+        "key length huge": _patched(blob, 24, "<Q", 1 << 63),
+        "value type unknown": _patched(blob, 24 + 8 + 20, "<I", 13),
+    }
+    # tensor record fields: name at 24 + 45 + 41 + 36 = 146
+    rec = 146 + 8 + 19
+    cases["n_dims 0"] = _patched(blob, rec, "<I", 0)
+    cases["n_dims 5"] = _patched(blob, rec, "<I", 5)
+    cases["rows beyond the file"] = _patched(blob, rec + 4 + 8, "<Q", 3)
+    cases["offset unaligned"] = _patched(blob, rec + 4 + 16 + 4, "<Q", 4)
+    cases["offset beyond the file"] = _patched(blob, rec + 4 + 16 + 4, "<Q", 64)
+    cases["row not whole blocks"] = _patched(blob, rec + 4 + 16, "<I", g.TENSOR_Q8_0)
+    for what, b in cases.items():
+        assert open_status(write(tmp_path, b)) == g.ERR_FORMAT, what
+
+
+def test_bad_alignment_entries(tmp_path):
+    for vt, v in ((4, 0), (4, 48), (5, 32)):
+        blob, _, _ = gguf_bytes([("general.alignment", vt, v)], [])
+        assert open_status(write(tmp_path, blob)) == g.ERR_FORMAT, (vt, v)
+
+
+def test_deep_nesting_is_rejected(tmp_path):
+    v = (4, [1])
+    for _ in range(4):
+        v = (ARRAY, [v])
+    blob, _, _ = gguf_bytes([("deep", ARRAY, v)], [])
+    assert open_status(write(tmp_path, blob)) == g.ERR_FORMAT
+    v = (4, [1])
+    for _ in range(3):
+        v = (ARRAY, [v])
+    blob, _, _ = gguf_bytes([("ok", ARRAY, v)], [])
+    assert open_status(write(tmp_path, blob)) == g.OK
+
+
+def test_random_corruptions_never_escape_the_file(tmp_path):
+    """Seeded byte flips of a file with metadata of several types and three
+    tensors: every open either fails with ERR_FORMAT or yields records whose
+    data lies inside the file."""
+    kvs = [("general.name", STRING, "fuzz"), ("n", 5, 7), ("arr", ARRAY, (STRING, ["a", "bc"])),
+           ("f", ARRAY, (6, [1.0, 2.0, 3.0]))]
+    tensors = [("w8", [64, 3], g.TENSOR_Q8_0, bytes(range(204))), ("w4", [256, 2], g.TENSOR_Q4_K, b"\7" * 288),
+               ("n", [16], g.TENSOR_F32, b"\0" * 64)]
+    blob, _, _ = gguf_bytes(kvs, tensors)
+    rng = np.random.default_rng(5)
+    path = str(tmp_path / "f.gguf")
+    ok = 0
+    for _ in range(400):
+        b = bytearray(blob)
+        for _ in range(int(rng.integers(1, 4))):
+            b[int(rng.integers(0, len(b)))] = int(rng.integers(0, 256))
+        open(path, "wb").write(bytes(b))
+        st = open_status(path)
+        assert st in (g.OK, g.ERR_FORMAT)
+        if st == g.OK:
+            ok += 1
+            with g.GgufFile(path) as f:
+                for t in f.tensors:
+                    if t["nbytes"] >= 0:
+                        assert t["offset"] + t["nbytes"] <= f.size
+                f.metadata
+    assert ok > 0
