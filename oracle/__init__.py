@@ -19,6 +19,13 @@ What it computes, and from which passage:
   6-bit fields and nibbles is not on the pages; the reading taken is GGUF's
   on-disk layout, stated in formats.py. PARITY UNPINNED against real GGUF
   files (none available); pinned for self-consistency by hand-packed bytes.
+* Q4_0: 18-byte block = fp16 scale + 16 bytes of 4-bit codes, the Q8_0
+  recipe with 4-bit integers ("GGUF: The File Format...", "How a Q8_0 block
+  is stored", step 4). Nibble order and code offset: GGUF's layout (not on
+  the pages). PARITY UNPINNED against real files.
+* Q6_K: 210-byte super-block of 256 weights ("GGUF: The File Format...",
+  bits-per-weight listing). Field map: GGUF's layout (not on the pages).
+  PARITY UNPINNED against real files; pinned for self-consistency.
 * matvec y = W x ("culpeo.ws", naive-implementation post, the matvec op), in
   fp64 from the fp32 dequantized weights.
 * small batch Y = X W^T with fp32 X (the matvec of each token row), in fp64.
@@ -27,25 +34,39 @@ What it computes, and from which passage:
 """
 
 from .formats import (  # noqa: F401
+    Q4_0_BLOCK_BYTES,
+    Q4_0_BLOCK_WEIGHTS,
     Q4_K_BLOCK_BYTES,
     Q4_K_BLOCK_WEIGHTS,
     Q8_0_BLOCK_BYTES,
+    Q6_K_BLOCK_BYTES,
+    Q6_K_BLOCK_WEIGHTS,
     Q8_0_BLOCK_WEIGHTS,
     bf16_bits_to_f64,
+    dequant_q4_0_f32,
+    dequant_q4_0_f64,
     dequant_q4_k_bf16_bits,
     dequant_q4_k_f32,
     dequant_q4_k_f64,
+    dequant_q6_k_f32,
+    dequant_q6_k_f64,
     dequant_q8_0_f32,
     dequant_q8_0_f64,
     f32_to_bf16_bits,
     fp16_bits_to_f64,
+    pack_q4_0_block,
     pack_q4_k_block,
+    pack_q6_k_block,
+    q4_0_block_scalar,
     q4_k_block_scalar,
+    q6_k_block_scalar,
     q8_0_block_scalar,
     quantize_q4_k_row,
     quantize_q8_0_row,
     row_bytes,
+    unpack_q4_0_block,
     unpack_q4_k_block,
+    unpack_q6_k_block,
 )
 from .linalg import (  # noqa: F401
     floored_rel_err,

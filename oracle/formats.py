@@ -20,6 +20,11 @@ Q4_K_BLOCK_BYTES = 144
 Q4_K_BLOCK_WEIGHTS = 256
 Q4_K_SUBBLOCKS = 8
 Q4_K_SUBBLOCK_WEIGHTS = 32
+# Same table: Q4_0 18 bytes per 32 weights, Q6_K 210 bytes per 256 weights.
+Q4_0_BLOCK_BYTES = 18
+Q4_0_BLOCK_WEIGHTS = 32
+Q6_K_BLOCK_BYTES = 210
+Q6_K_BLOCK_WEIGHTS = 256
 
 
 def row_bytes(fmt: str, cols: int) -> int:
@@ -35,6 +40,14 @@ def row_bytes(fmt: str, cols: int) -> int:
         if cols % Q4_K_BLOCK_WEIGHTS:
             raise ValueError("Q4_K needs cols % 256 == 0")
         return cols // Q4_K_BLOCK_WEIGHTS * Q4_K_BLOCK_BYTES
+    if fmt == "q4_0":
+        if cols % Q4_0_BLOCK_WEIGHTS:
+            raise ValueError("Q4_0 needs cols % 32 == 0")
+        return cols // Q4_0_BLOCK_WEIGHTS * Q4_0_BLOCK_BYTES
+    if fmt == "q6_k":
+        if cols % Q6_K_BLOCK_WEIGHTS:
+            raise ValueError("Q6_K needs cols % 256 == 0")
+        return cols // Q6_K_BLOCK_WEIGHTS * Q6_K_BLOCK_BYTES
     raise ValueError(fmt)
 
 
@@ -323,3 +336,141 @@ def quantize_q4_k_row(w32: np.ndarray) -> bytes:
         dmin_bits = int(np.array([dmin16], dtype="<f2").view("<u2")[0])
         out += pack_q4_k_block(d_bits, dmin_bits, list(sc), list(m), list(q))
     return bytes(out)
+
+
+# ---------------------------------------------------------------------------
+# Q4_0: 18-byte block of 32 weights. "GGUF: The File Format...", "How a Q8_0
+# block is stored", step 4: the Q8_0 recipe with 4-bit integers, a 2-byte
+# fp16 scale d and 16 bytes of 4-bit values. Reading (GGUF's on-disk layout;
+# the pages print neither the nibble order nor the offset of the 4-bit code):
+#   byte j of the 16 (j = 0..15): low nibble = code of weight j,
+#                                 high nibble = code of weight j + 16
+#   w = (code - 8) * d          (codes 0..15 stand for -8..7)
+# (code - 8) * d has at most 4 + 11 significant bits: exact in fp32.
+# Agreement with real files is unpinned.
+# ---------------------------------------------------------------------------
+
+def unpack_q4_0_block(block: bytes):
+    """(d_bits, codes[32]) of one 18-byte block, in pure Python."""
+    assert len(block) == Q4_0_BLOCK_BYTES
+    d_bits = block[0] | (block[1] << 8)
+    q = [0] * 32
+    for j in range(16):
+        q[j] = block[2 + j] & 15
+        q[j + 16] = block[2 + j] >> 4
+    return d_bits, q
+
+
+def pack_q4_0_block(d_bits: int, q) -> bytes:
+    """Inverse of unpack_q4_0_block."""
+    assert len(q) == 32 and all(0 <= v < 16 for v in q)
+    return bytes([d_bits & 255, d_bits >> 8] + [q[j] | (q[j + 16] << 4) for j in range(16)])
+
+
+def q4_0_block_scalar(block: bytes) -> list:
+    """One Q4_0 block in pure Python: 32 exact weights as Fractions."""
+    d_bits, q = unpack_q4_0_block(block)
+    d = fp16_bits_to_fraction(d_bits)
+    return [(v - 8) * d for v in q]
+
+
+def dequant_q4_0_f64(w_bytes, rows: int, cols: int) -> np.ndarray:
+    """Q4_0 matrix -> exact weights [rows, cols] in fp64."""
+    nb = cols // Q4_0_BLOCK_WEIGHTS
+    blk = np.asarray(w_bytes, dtype=np.uint8).reshape(rows, nb, Q4_0_BLOCK_BYTES)
+    d = fp16_bits_to_f64(_le_u16(blk[..., 0], blk[..., 1]))
+    qb = blk[..., 2:18].astype(np.int64)
+    code = np.concatenate([qb & 15, qb >> 4], axis=-1)        # weights 0..15, then 16..31
+    with np.errstate(invalid="ignore"):
+        return ((code - 8).astype(np.float64) * d[..., None]).reshape(rows, cols)
+
+
+def dequant_q4_0_f32(w_bytes, rows: int, cols: int) -> np.ndarray:
+    """fp32 dequant (the exact value; no rounding is needed)."""
+    return dequant_q4_0_f64(w_bytes, rows, cols).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Q6_K: 210-byte super-block of 256 weights (size: "GGUF: The File Format...",
+# bits-per-weight listing; a k-quant, so sub-blocks with their own scales under
+# one fp16 super-scale, k-quant paragraph). Reading (GGUF's on-disk layout, not
+# printed on the pages): 16 sub-blocks of 16 weights, each with a signed 8-bit
+# scale; 6-bit codes split into a low nibble and a high 2-bit part:
+#   bytes   0..127  ql   low 4 bits of the codes
+#   bytes 128..191  qh   high 2 bits of the codes
+#   bytes 192..207  sc   16 int8 sub-block scales
+#   bytes 208..209  d    fp16 super-scale
+# For half n = 0, 1 and l = 0..31, with L = ql[64 n:] and H = qh[32 n:]:
+#   code[128 n + l]      = (L[l] & 15)      | ((H[l] >> 0) & 3) << 4
+#   code[128 n + l + 32] = (L[l + 32] & 15) | ((H[l] >> 2) & 3) << 4
+#   code[128 n + l + 64] = (L[l] >> 4)      | ((H[l] >> 4) & 3) << 4
+#   code[128 n + l + 96] = (L[l + 32] >> 4) | ((H[l] >> 6) & 3) << 4
+#   weight i:  w_i = d * sc[i // 16] * (code_i - 32)
+# The product is exact in fp32: d has 11 significant bits, abs(sc) <= 128 at
+# most 7 (128 is a power of two) and abs(code - 32) <= 32 at most 5, so at most
+# 23. Agreement with real files is unpinned.
+# ---------------------------------------------------------------------------
+
+def unpack_q6_k_block(block: bytes):
+    """(d_bits, sc[16] as signed ints, codes[256]) of one 210-byte super-block."""
+    assert len(block) == Q6_K_BLOCK_BYTES
+    ql, qh = block[0:128], block[128:192]
+    sc = [v - 256 if v >= 128 else v for v in block[192:208]]
+    d_bits = block[208] | (block[209] << 8)
+    code = [0] * 256
+    for n in range(2):
+        L, H = ql[64 * n:64 * n + 64], qh[32 * n:32 * n + 32]
+        for l in range(32):
+            code[128 * n + l] = (L[l] & 15) | (((H[l] >> 0) & 3) << 4)
+            code[128 * n + l + 32] = (L[l + 32] & 15) | (((H[l] >> 2) & 3) << 4)
+            code[128 * n + l + 64] = (L[l] >> 4) | (((H[l] >> 4) & 3) << 4)
+            code[128 * n + l + 96] = (L[l + 32] >> 4) | (((H[l] >> 6) & 3) << 4)
+    return d_bits, sc, code
+
+
+def pack_q6_k_block(d_bits: int, sc, code) -> bytes:
+    """Inverse of unpack_q6_k_block (sc in -128..127, codes in 0..63)."""
+    assert len(sc) == 16 and all(-128 <= v < 128 for v in sc)
+    assert len(code) == 256 and all(0 <= v < 64 for v in code)
+    ql, qh = [0] * 128, [0] * 64
+    for n in range(2):
+        for l in range(32):
+            c0, c1, c2, c3 = (code[128 * n + l + 32 * k] for k in range(4))
+            ql[64 * n + l] = (c0 & 15) | ((c2 & 15) << 4)
+            ql[64 * n + l + 32] = (c1 & 15) | ((c3 & 15) << 4)
+            qh[32 * n + l] = (c0 >> 4) | ((c1 >> 4) << 2) | ((c2 >> 4) << 4) | ((c3 >> 4) << 6)
+    return bytes(ql + qh + [v & 255 for v in sc] + [d_bits & 255, d_bits >> 8])
+
+
+def q6_k_block_scalar(block: bytes) -> list:
+    """One super-block in pure Python: 256 exact weights as Fractions."""
+    d_bits, sc, code = unpack_q6_k_block(block)
+    d = fp16_bits_to_fraction(d_bits)
+    return [d * sc[i // 16] * (code[i] - 32) for i in range(256)]
+
+
+def dequant_q6_k_f64(w_bytes, rows: int, cols: int) -> np.ndarray:
+    """Q6_K matrix -> exact weights [rows, cols] in fp64 (same map as
+    unpack_q6_k_block, vectorised)."""
+    nsb = cols // Q6_K_BLOCK_WEIGHTS
+    blk = np.asarray(w_bytes, dtype=np.uint8).reshape(rows, nsb, Q6_K_BLOCK_BYTES).astype(np.int64)
+    ql, qh = blk[..., 0:128], blk[..., 128:192]
+    sc = _twos_complement_i8(blk[..., 192:208].astype(np.uint8)).astype(np.float64)
+    d = fp16_bits_to_f64(_le_u16(blk[..., 208], blk[..., 209]))
+    code = np.empty(blk.shape[:2] + (256,), dtype=np.int64)
+    for n in range(2):
+        L, H = ql[..., 64 * n:64 * n + 64], qh[..., 32 * n:32 * n + 32]
+        b = 128 * n
+        code[..., b:b + 32] = (L[..., 0:32] & 15) | (((H >> 0) & 3) << 4)
+        code[..., b + 32:b + 64] = (L[..., 32:64] & 15) | (((H >> 2) & 3) << 4)
+        code[..., b + 64:b + 96] = (L[..., 0:32] >> 4) | (((H >> 4) & 3) << 4)
+        code[..., b + 96:b + 128] = (L[..., 32:64] >> 4) | (((H >> 6) & 3) << 4)
+    j_of_i = np.arange(256) // 16
+    with np.errstate(invalid="ignore"):
+        w = d[..., None] * sc[..., j_of_i] * (code - 32).astype(np.float64)
+    return w.reshape(rows, nsb * 256)
+
+
+def dequant_q6_k_f32(w_bytes, rows: int, cols: int) -> np.ndarray:
+    """fp32 dequant (the exact value; no rounding is needed)."""
+    return dequant_q6_k_f64(w_bytes, rows, cols).astype(np.float32)

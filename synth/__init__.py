@@ -82,6 +82,34 @@ def q4_k_weights(rng: np.random.Generator, rows: int, cols: int,
     return out.reshape(rows, -1)
 
 
+def q4_0_weights(rng: np.random.Generator, rows: int, cols: int,
+                 scale_lo: float = 1e-3, scale_hi: float = 1e-2) -> np.ndarray:
+    """Q4_0 matrix bytes, shape [rows, cols/32*18] uint8: fp16 scale ~
+    U[scale_lo, scale_hi] in bytes 0-1, then 16 uniform bytes (every 4-bit code
+    uniform on 0..15 whatever the nibble order)."""
+    if cols % 32:
+        raise ValueError("cols must be a multiple of 32")
+    nb = rows * (cols // 32)
+    out = np.empty((nb, 18), dtype=np.uint8)
+    out[:, 0:2] = _fp16_uniform(rng, scale_lo, scale_hi, nb).view(np.uint8).reshape(nb, 2)
+    out[:, 2:] = rng.integers(0, 256, size=(nb, 16), dtype=np.uint8)
+    return out.reshape(rows, -1)
+
+
+def q6_k_weights(rng: np.random.Generator, rows: int, cols: int,
+                 d_lo: float = 1e-4, d_hi: float = 1e-3) -> np.ndarray:
+    """Q6_K matrix bytes, shape [rows, cols/256*210] uint8: 208 uniform bytes
+    (the 6-bit codes and the 16 int8 scales uniform whatever the bit map), then
+    the fp16 super-scale ~ U[d_lo, d_hi] in bytes 208-209."""
+    if cols % 256:
+        raise ValueError("cols must be a multiple of 256")
+    nb = rows * (cols // 256)
+    out = np.empty((nb, 210), dtype=np.uint8)
+    out[:, :208] = rng.integers(0, 256, size=(nb, 208), dtype=np.uint8)
+    out[:, 208:210] = _fp16_uniform(rng, d_lo, d_hi, nb).view(np.uint8).reshape(nb, 2)
+    return out.reshape(rows, -1)
+
+
 def activations_f32(rng: np.random.Generator, n: int) -> np.ndarray:
     """fp32 vector ~ N(0, 1) (drawn in fp64, rounded to fp32)."""
     return rng.standard_normal(n).astype(np.float32)

@@ -106,3 +106,66 @@ def check_one_hot_columns(matvec_f64, w32) -> bool:
         if not np.array_equal(np.asarray(matvec_f64(w32, e)), w32[:, k].astype(np.float64)):
             return False
     return True
+
+
+# ------------------------------------------------------------ Q4_0 and Q6_K
+
+def _q4_0_bytes(d_bits, qbytes):
+    return np.frombuffer(bytes([d_bits & 255, d_bits >> 8] + list(qbytes)), np.uint8)
+
+
+def check_q4_0_byte_map(dequant_f64) -> bool:
+    """d = 1: byte j's low nibble is weight j, its high nibble weight j + 16,
+    and a code c stands for c - 8 (one byte set by hand per probe)."""
+    for j in (0, 5, 15):
+        for lo, hi in ((3, 0), (0, 12), (15, 9)):
+            qb = [0x88] * 16
+            qb[j] = lo | (hi << 4)
+            w = dequant_f64(_q4_0_bytes(0x3C00, qb), 1, 32)[0]
+            want = np.zeros(32)
+            want[j] = lo - 8
+            want[j + 16] = hi - 8
+            if not np.array_equal(w, want):
+                return False
+    return True
+
+
+def _q6_k_bytes(ql, qh, sc, d_bits):
+    return np.frombuffer(bytes(list(ql) + list(qh) + [v & 255 for v in sc] +
+                               [d_bits & 255, d_bits >> 8]), np.uint8)
+
+
+def check_q6_k_bit_map(dequant_f64) -> bool:
+    """d = 1, every scale 1, so w = code - 32. One low nibble or one high 2-bit
+    field set by hand must move exactly the weight the stated map names."""
+    probes = []
+    for n in (0, 1):
+        for l in (0, 7, 31):
+            probes.append(("ql", 64 * n + l, 0x05, 128 * n + l, 5))
+            probes.append(("ql", 64 * n + l, 0x90, 128 * n + l + 64, 9))
+            probes.append(("ql", 64 * n + l + 32, 0x0B, 128 * n + l + 32, 11))
+            probes.append(("ql", 64 * n + l + 32, 0xE0, 128 * n + l + 96, 14))
+            for k in range(4):
+                probes.append(("qh", 32 * n + l, 3 << (2 * k), 128 * n + l + 32 * k, 48))
+    base = dequant_f64(_q6_k_bytes([0] * 128, [0] * 64, [1] * 16, 0x3C00), 1, 256)[0]
+    if not np.array_equal(base, np.full(256, -32.0)):
+        return False
+    for field, pos, byte, weight, code in probes:
+        ql, qh = [0] * 128, [0] * 64
+        (ql if field == "ql" else qh)[pos] = byte
+        w = dequant_f64(_q6_k_bytes(ql, qh, [1] * 16, 0x3C00), 1, 256)[0]
+        want = np.full(256, -32.0)
+        want[weight] = code - 32
+        if not np.array_equal(w, want):
+            return False
+    return True
+
+
+def check_q6_k_signed_scales(dequant_f64) -> bool:
+    """d = 0.5, every code 33 (value 1): the weights are 0.5 x the signed scale
+    of their 16-weight sub-block (scale bytes set by hand)."""
+    sc = [1, -1, 2, -2, 127, -128, 0, 5, -7, 64, -64, 3, 9, -9, 100, -100]
+    ql = [0x11] * 128                       # low nibbles 1
+    qh = [0xAA] * 64                        # high bits 2 -> code 33
+    w = dequant_f64(_q6_k_bytes(ql, qh, sc, 0x3800), 1, 256)[0]
+    return bool(np.array_equal(w, np.repeat(0.5 * np.array(sc, dtype=np.float64), 16)))
