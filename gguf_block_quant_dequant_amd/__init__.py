@@ -20,6 +20,8 @@ from .build import LIB_PATH
 
 TYPE_Q8_0 = 8
 TYPE_Q4_K = 12
+TYPE_Q4_0 = 2
+TYPE_Q6_K = 14
 
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS, ERR_DEVICE, ERR_LAUNCH, ERR_LIMIT = -1, -2, -3, -4, -5, -6, -7
@@ -46,6 +48,10 @@ _SIGS = {
     "dequant_q4_k_bf16": (ctypes.c_int, [_P, _P, _I64, _I64, _P]),
     "gguf_qmatvec_q8_0": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "gguf_qmatvec_q4_k": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
+    "dequant_q4_0": (ctypes.c_int, [_P, _P, _I64, _I64, _P]),
+    "dequant_q6_k": (ctypes.c_int, [_P, _P, _I64, _I64, _P]),
+    "gguf_qmatvec_q4_0": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
+    "gguf_qmatvec_q6_k": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "gguf_qmatmul_q4_k": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P]),
     "gguf_qmatmul_f32_q8_0": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P]),
     "gguf_qmatmul_f32_q4_k": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P]),
@@ -148,7 +154,8 @@ def _rows_cols(W: torch.Tensor, fmt: int, rows, cols):
             raise ValueError("pass rows and cols, or W as a [rows, row_bytes] uint8 tensor")
         r = W.shape[0]
         rb = W.shape[1]
-        blk_b, blk_w = (34, 32) if fmt == TYPE_Q8_0 else (144, 256)
+        blk_b, blk_w = {TYPE_Q8_0: (34, 32), TYPE_Q4_K: (144, 256), TYPE_Q4_0: (18, 32),
+                        TYPE_Q6_K: (210, 256)}[fmt]
         if rb % blk_b:
             raise ValueError("W row bytes are not a whole number of blocks")
         rows = r if rows is None else rows
@@ -194,6 +201,16 @@ def dequant_q4_k(W, out=None, rows=None, cols=None, stream=None):
     return _dequant("dequant_q4_k", TYPE_Q4_K, W, out, rows, cols, torch.float32, stream)
 
 
+def dequant_q4_0(W, out=None, rows=None, cols=None, stream=None):
+    """fp32 [rows, cols] dequant of a Q4_0 matrix (bit-exact)."""
+    return _dequant("dequant_q4_0", TYPE_Q4_0, W, out, rows, cols, torch.float32, stream)
+
+
+def dequant_q6_k(W, out=None, rows=None, cols=None, stream=None):
+    """fp32 [rows, cols] dequant of a Q6_K matrix (bit-exact)."""
+    return _dequant("dequant_q6_k", TYPE_Q6_K, W, out, rows, cols, torch.float32, stream)
+
+
 def dequant_q4_k_bf16(W, out=None, rows=None, cols=None, stream=None):
     """bf16 [rows, cols]: the fp32 dequant rounded to nearest-even."""
     return _dequant("dequant_q4_k_bf16", TYPE_Q4_K, W, out, rows, cols, torch.bfloat16, stream)
@@ -220,6 +237,16 @@ def gguf_qmatvec_q8_0(W, x, y=None, rows=None, cols=None, stream=None):
 def gguf_qmatvec_q4_k(W, x, y=None, rows=None, cols=None, stream=None):
     """y = dequant(W) @ x for a Q4_K W (fp32 x and y)."""
     return _matvec("gguf_qmatvec_q4_k", TYPE_Q4_K, W, x, y, rows, cols, stream)
+
+
+def gguf_qmatvec_q4_0(W, x, y=None, rows=None, cols=None, stream=None):
+    """y = dequant(W) @ x for a Q4_0 W (fp32 x and y)."""
+    return _matvec("gguf_qmatvec_q4_0", TYPE_Q4_0, W, x, y, rows, cols, stream)
+
+
+def gguf_qmatvec_q6_k(W, x, y=None, rows=None, cols=None, stream=None):
+    """y = dequant(W) @ x for a Q6_K W (fp32 x and y)."""
+    return _matvec("gguf_qmatvec_q6_k", TYPE_Q6_K, W, x, y, rows, cols, stream)
 
 
 def gguf_qmatmul_q4_k(W, X, Y=None, rows=None, stream=None):

@@ -15,6 +15,7 @@
 #include "dequant.hpp"
 #include "gemm.hpp"
 #include "gemv.hpp"
+#include "gemv_other.hpp"
 #include "gemv_small_batch.hpp"
 #include "probe.hpp"
 
@@ -145,6 +146,16 @@ static int64_t row_bytes_of(int type, int64_t cols) {
     if (cols % kQ4KBlockWeights) return GGUF_QK_ERR_SHAPE;
     if (cols / kQ4KBlockWeights > INT64_MAX / kQ4KBlockBytes) return GGUF_QK_ERR_SHAPE;
     return cols / kQ4KBlockWeights * kQ4KBlockBytes;
+  }
+  if (type == GGUF_QK_TYPE_Q4_0) {
+    if (cols % kQ40BlockWeights) return GGUF_QK_ERR_SHAPE;
+    if (cols / kQ40BlockWeights > INT64_MAX / kQ40BlockBytes) return GGUF_QK_ERR_SHAPE;
+    return cols / kQ40BlockWeights * kQ40BlockBytes;
+  }
+  if (type == GGUF_QK_TYPE_Q6_K) {
+    if (cols % kQ6KBlockWeights) return GGUF_QK_ERR_SHAPE;
+    if (cols / kQ6KBlockWeights > INT64_MAX / kQ6KBlockBytes) return GGUF_QK_ERR_SHAPE;
+    return cols / kQ6KBlockWeights * kQ6KBlockBytes;
   }
   return GGUF_QK_ERR_SHAPE;
 }
@@ -416,6 +427,74 @@ int gguf_qmatvec_q8_0(const void* W, const float* x, float* y, int64_t rows, int
 int gguf_qmatvec_q4_k(const void* W, const float* x, float* y, int64_t rows, int64_t cols,
                       hipStream_t stream) {
   return matvec_common(GGUF_QK_TYPE_Q4_K, W, x, y, rows, cols, stream);
+}
+
+// Q4_0 / Q6_K: dequant (one thread per Q4_0 block or Q6_K quad of 16
+// weights) and the batch-1 GEMV (kOtherRows rows per wave).
+static int dequant_other(int type, const void* W, float* out, int64_t rows, int64_t cols,
+                         hipStream_t stream) {
+  int64_t wb = 0;
+  int st = check_matrix(type, W, rows, cols, &wb);
+  if (st) return st;
+  if (!out) return GGUF_QK_ERR_NULL;
+  if (!aligned16(out)) return GGUF_QK_ERR_ALIGN;
+  if (rows > 0 && cols > INT64_MAX / 4 / rows) return GGUF_QK_ERR_SHAPE;
+  if (overlap(W, wb, out, rows * cols * 4)) return GGUF_QK_ERR_ALIAS;
+  if (rows == 0) return GGUF_QK_OK;
+  st = current_device(nullptr);
+  if (st) return st;
+  const uint8_t* w = static_cast<const uint8_t*>(W);
+  if (type == GGUF_QK_TYPE_Q4_0) {
+    const int64_t units = rows * (cols / kQ40BlockWeights);
+    if (units / 256 >= INT32_MAX) return GGUF_QK_ERR_LIMIT;
+    hipLaunchKernelGGL(dequant_q4_0_kernel, dim3(grid_1d(units, 256)), dim3(256), 0, stream, w, out,
+                       units);
+  } else {
+    const int64_t units = rows * (cols / kQ6KBlockWeights) * 16;
+    if (units / 256 >= INT32_MAX) return GGUF_QK_ERR_LIMIT;
+    hipLaunchKernelGGL(dequant_q6_k_kernel, dim3(grid_1d(units, 256)), dim3(256), 0, stream, w, out,
+                       units);
+  }
+  return launch_status();
+}
+
+static int matvec_other(int type, const void* W, const float* x, float* y, int64_t rows,
+                        int64_t cols, hipStream_t stream) {
+  int64_t wb = 0;
+  int st = check_gemv(type, W, x, y, rows, cols, &wb);
+  if (st) return st;
+  if (rows == 0) return GGUF_QK_OK;
+  st = current_device(nullptr);
+  if (st) return st;
+  const int64_t per_block = (int64_t)kOtherRows * kOtherWaves;
+  const int64_t blocks = (rows + per_block - 1) / per_block;
+  if (blocks > INT32_MAX) return GGUF_QK_ERR_LIMIT;
+  const uint8_t* w = static_cast<const uint8_t*>(W);
+  if (type == GGUF_QK_TYPE_Q4_0)
+    hipLaunchKernelGGL(gemv_q4_0_kernel, dim3((unsigned)blocks), dim3(kOtherWaves * 64), 0, stream,
+                       w, x, y, rows, cols / kQ40BlockWeights);
+  else
+    hipLaunchKernelGGL(gemv_q6_k_kernel, dim3((unsigned)blocks), dim3(kOtherWaves * 64), 0, stream,
+                       w, x, y, rows, cols / kQ6KBlockWeights);
+  return launch_status();
+}
+
+int dequant_q4_0(const void* W, float* out, int64_t rows, int64_t cols, hipStream_t stream) {
+  return dequant_other(GGUF_QK_TYPE_Q4_0, W, out, rows, cols, stream);
+}
+
+int dequant_q6_k(const void* W, float* out, int64_t rows, int64_t cols, hipStream_t stream) {
+  return dequant_other(GGUF_QK_TYPE_Q6_K, W, out, rows, cols, stream);
+}
+
+int gguf_qmatvec_q4_0(const void* W, const float* x, float* y, int64_t rows, int64_t cols,
+                      hipStream_t stream) {
+  return matvec_other(GGUF_QK_TYPE_Q4_0, W, x, y, rows, cols, stream);
+}
+
+int gguf_qmatvec_q6_k(const void* W, const float* x, float* y, int64_t rows, int64_t cols,
+                      hipStream_t stream) {
+  return matvec_other(GGUF_QK_TYPE_Q6_K, W, x, y, rows, cols, stream);
 }
 
 int gguf_qmatmul_q4_k(const void* W, const uint16_t* X, uint16_t* Y, int64_t n_tokens,

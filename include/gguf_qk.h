@@ -76,6 +76,10 @@ extern "C" {
  * not printed on those pages). */
 #define GGUF_QK_TYPE_Q8_0 8
 #define GGUF_QK_TYPE_Q4_K 12
+/* GGUF's ids of two more block types ("GGUF: The File Format...", their block
+ * sizes: Q4_0 18 bytes per 32 weights, Q6_K 210 per 256). */
+#define GGUF_QK_TYPE_Q4_0 2
+#define GGUF_QK_TYPE_Q6_K 14
 
 /* ABI version of the loaded library (GGUF_QK_ABI_VERSION it was built with). */
 int gguf_qk_abi_version(void);
@@ -108,6 +112,32 @@ int dequant_q4_k_bf16(const void* W, uint16_t* out, int64_t rows, int64_t cols,
 int gguf_qmatvec_q8_0(const void* W, const float* x, float* y, int64_t rows, int64_t cols,
                       hipStream_t stream);
 int gguf_qmatvec_q4_k(const void* W, const float* x, float* y, int64_t rows, int64_t cols,
+                      hipStream_t stream);
+
+/* --- the other block types of GGUF files: Q4_0 and Q6_K ------------------- */
+
+/* Q4_0 ("GGUF: The File Format...", "How a Q8_0 block is stored": the same
+ * recipe with 4-bit integers; 18-byte blocks of 32 weights). Field placement
+ * (GGUF's layout, not on the pages): fp16 d in bytes 0-1, then 16 bytes; byte
+ * j holds the code of weight j in its low nibble and of weight j + 16 in its
+ * high nibble; w = (code - 8) * d. cols % 32 == 0.
+ *
+ * Q6_K (210-byte super-blocks of 256 weights, same listing). Field placement
+ * (GGUF's layout): bytes 0-127 ql (low 4 bits of the 6-bit codes), 128-191 qh
+ * (high 2 bits), 192-207 sixteen int8 scales of 16 weights each, 208-209 fp16
+ * d. Weight 128 n + 32 k + l (n = 0..1, k = 0..3, l = 0..31) has low bits
+ * ql[64 n + l + 32 (k & 1)] >> (k >= 2 ? 4 : 0) & 15 and high bits
+ * qh[32 n + l] >> 2 k & 3; w = d * scale[i / 16] * (code - 32).
+ * cols % 256 == 0.
+ *
+ * Dequant: fp32 [rows x cols], bit-exact (both products are exact in fp32).
+ * GEMV: y = W x in fp32 as gguf_qmatvec_q8_0 (any summation order,
+ * deterministic). These two types are not accepted by gguf_qmatvec_batch. */
+int dequant_q4_0(const void* W, float* out, int64_t rows, int64_t cols, hipStream_t stream);
+int dequant_q6_k(const void* W, float* out, int64_t rows, int64_t cols, hipStream_t stream);
+int gguf_qmatvec_q4_0(const void* W, const float* x, float* y, int64_t rows, int64_t cols,
+                      hipStream_t stream);
+int gguf_qmatvec_q6_k(const void* W, const float* x, float* y, int64_t rows, int64_t cols,
                       hipStream_t stream);
 
 /* --- decode step: an ordered list of GEMVs -------------------------------- */

@@ -58,6 +58,19 @@ def test_version_and_strerror():
     assert g.gguf_qk_strerror(-99) == "unknown status"
 
 
+def test_row_bytes_other_types():
+    assert g.gguf_row_bytes(g.TYPE_Q4_0, 2048) == 1152
+    assert g.gguf_row_bytes(g.TYPE_Q4_0, 96) == 54
+    assert g.gguf_row_bytes(g.TYPE_Q6_K, 11008) == 9030
+    assert g.gguf_row_bytes(g.TYPE_Q4_0, 48) == g.ERR_SHAPE
+    assert g.gguf_row_bytes(g.TYPE_Q6_K, 128) == g.ERR_SHAPE
+
+
+def test_batch_rejects_other_types():
+    e = g.GemvEntry(0x10000, 0x20000, 0x30000, 4, 256, g.TYPE_Q6_K, 0)
+    assert g.lib().gguf_qmatvec_batch(ctypes.byref(e), 1, None) == g.ERR_SHAPE
+
+
 def test_row_bytes():
     assert g.gguf_row_bytes(g.TYPE_Q8_0, 2048) == 2176
     assert g.gguf_row_bytes(g.TYPE_Q8_0, 512) == 544
@@ -79,7 +92,8 @@ def _mv(name, W, x, y, rows, cols):
     return getattr(g.lib(), name)(W, x, y, rows, cols, None)
 
 
-@pytest.mark.parametrize("name", ["gguf_qmatvec_q8_0", "gguf_qmatvec_q4_k"])
+@pytest.mark.parametrize("name", ["gguf_qmatvec_q8_0", "gguf_qmatvec_q4_k", "gguf_qmatvec_q4_0",
+                                  "gguf_qmatvec_q6_k"])
 def test_matvec_validation(name):
     assert _mv(name, None, B, C, 4, 256) == g.ERR_NULL
     assert _mv(name, A, None, C, 4, 256) == g.ERR_NULL
@@ -103,7 +117,8 @@ def test_q4_k_matvec_rejects_q8_0_only_widths():
 
 
 @pytest.mark.parametrize("name,cols", [("dequant_q8_0", 64), ("dequant_q4_k", 256),
-                                       ("dequant_q4_k_bf16", 256)])
+                                       ("dequant_q4_k_bf16", 256), ("dequant_q4_0", 64),
+                                       ("dequant_q6_k", 256)])
 def test_dequant_validation(name, cols):
     f = getattr(g.lib(), name)
     assert f(None, B, 4, cols, None) == g.ERR_NULL

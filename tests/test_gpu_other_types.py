@@ -1,0 +1,119 @@
+"""Q4_0 and Q6_K through the C ABI against the oracle: dequantization
+bit-exact, GEMV within the fp32 bar (1e-3 floored), exact where every partial
+sum is an integer, repeat calls bit-identical. Row lengths with an odd number
+of blocks put every other row (and, for Q4_0, every other block) at a 2-byte
+offset from a 4-byte boundary, the realignment case."""
+
+import numpy as np
+import pytest
+import torch
+
+import gguf_block_quant_dequant_amd as g
+import oracle
+import synth
+from oracle.formats import pack_q4_0_block, pack_q6_k_block
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL_F32 = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def same_bits(a, b):
+    a = np.asarray(a, np.float32).ravel()
+    b = np.asarray(b, np.float32).ravel()
+    nan = np.isnan(a) & np.isnan(b)
+    return bool(np.all(nan | (a.view(np.uint32) == b.view(np.uint32))))
+
+
+FMTS = {"q4_0": (synth.q4_0_weights, oracle.dequant_q4_0_f32, g.dequant_q4_0, g.gguf_qmatvec_q4_0),
+        "q6_k": (synth.q6_k_weights, oracle.dequant_q6_k_f32, g.dequant_q6_k, g.gguf_qmatvec_q6_k)}
+
+
+@pytest.mark.parametrize("fmt,rows,cols", [("q4_0", 1, 32), ("q4_0", 7, 96), ("q4_0", 33, 160),
+                                           ("q4_0", 300, 2048), ("q4_0", 64, 11008),
+                                           ("q6_k", 1, 256), ("q6_k", 5, 768), ("q6_k", 9, 2816),
+                                           ("q6_k", 40, 11008), ("q6_k", 200, 2048)])
+def test_dequant_bit_exact(fmt, rows, cols):
+    gen, ref, fn, _ = FMTS[fmt]
+    w = gen(np.random.default_rng([rows, cols, 1]), rows, cols)
+    say("dequant", fmt, rows, cols)
+    got = host(fn(dev(w), rows=rows, cols=cols))
+    assert same_bits(got, ref(w, rows, cols))
+
+
+def test_dequant_q4_0_every_scale_and_code():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    q = [(i * 7) % 16 for i in range(32)]
+    proto = np.frombuffer(pack_q4_0_block(0, q), np.uint8)
+    blk = np.tile(proto, (65536, 1))
+    blk[:, 0] = bits & 255
+    blk[:, 1] = bits >> 8
+    raw = blk.reshape(65536 // 2, 36)        # two blocks per row: rows 36 bytes, odd blocks at +2 mod 4
+    got = host(g.dequant_q4_0(dev(raw), rows=65536 // 2, cols=64))
+    assert same_bits(got, oracle.dequant_q4_0_f32(raw, 65536 // 2, 64))
+
+
+def test_dequant_q6_k_extreme_fields():
+    rng = np.random.default_rng(9)
+    blocks = []
+    for d_bits in (0x0001, 0x03FF, 0x3C00, 0x7BFF, 0xFBFF, 0x8000):
+        sc = [int(v) for v in rng.integers(-128, 128, 16)]
+        sc[0], sc[1] = -128, 127
+        code = [int(v) for v in rng.integers(0, 64, 256)]
+        code[0], code[1] = 0, 63
+        blocks.append(pack_q6_k_block(d_bits, sc, code))
+    raw = np.frombuffer(b"".join(blocks), np.uint8)
+    got = host(g.dequant_q6_k(dev(raw), rows=3, cols=512))
+    assert same_bits(got, oracle.dequant_q6_k_f32(raw, 3, 512))
+
+
+@pytest.mark.parametrize("fmt,rows,cols", [("q4_0", 1, 32), ("q4_0", 5, 96), ("q4_0", 300, 2048),
+                                           ("q4_0", 2048, 11008), ("q4_0", 11008, 2048),
+                                           ("q6_k", 1, 256), ("q6_k", 7, 768), ("q6_k", 333, 2816),
+                                           ("q6_k", 2048, 11008), ("q6_k", 11008, 2048)])
+def test_gemv_matches_oracle(fmt, rows, cols):
+    gen, ref, _, fn = FMTS[fmt]
+    rng = np.random.default_rng([rows, cols, 2])
+    w = gen(rng, rows, cols)
+    x = synth.activations_f32(rng, cols)
+    say("gemv", fmt, rows, cols)
+    Wd, xd = dev(w), dev(x)
+    y = host(fn(Wd, xd, rows=rows, cols=cols))
+    yref = oracle.matvec_f64(ref(w, rows, cols), x)
+    e, ok = oracle.floored_rel_err(y, yref)
+    assert ok and e <= TOL_F32, e
+    y2 = host(fn(Wd, xd, rows=rows, cols=cols))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
+def test_gemv_integer_cases_are_exact():
+    rng = np.random.default_rng(12)
+    rows, cols = 70, 96 * 32
+    q4 = b"".join(pack_q4_0_block(0x3C00, [int(v) for v in rng.integers(0, 16, 32)])
+                  for _ in range(rows * cols // 32))
+    w4 = np.frombuffer(q4, np.uint8)
+    x = rng.integers(-8, 9, cols).astype(np.float32)
+    y = host(g.gguf_qmatvec_q4_0(dev(w4), dev(x), rows=rows, cols=cols))
+    assert np.array_equal(y.astype(np.float64), oracle.dequant_q4_0_f64(w4, rows, cols) @ x.astype(np.float64))
+    rows, cols = 50, 2816
+    q6 = b"".join(pack_q6_k_block(0x3C00, [int(v) for v in rng.integers(-4, 5, 16)],
+                                  [int(v) for v in rng.integers(0, 64, 256)])
+                  for _ in range(rows * cols // 256))
+    w6 = np.frombuffer(q6, np.uint8)
+    x = rng.integers(-8, 9, cols).astype(np.float32)
+    y = host(g.gguf_qmatvec_q6_k(dev(w6), dev(x), rows=rows, cols=cols))
+    assert np.array_equal(y.astype(np.float64), oracle.dequant_q6_k_f64(w6, rows, cols) @ x.astype(np.float64))
