@@ -18,7 +18,7 @@ sample of the same workload, and labelled extras: the pass time distribution,
 an unordered upper bound (all GEMVs of the pass as one step), the bf16
 MFMA prefill pass over the same 36-layer weights (N = 512 tokens), and the
 fp32 small-batch passes (the same 253 matrices times 8, 32 and 64 activation
-vectors).
+vectors), and batch-1 GEMV passes over the same shapes stored as Q4_0 and Q6_K.
 
     python bench.py --copy-calibration
 
@@ -66,6 +66,8 @@ def parse():
                     help="copy 1 GiB device to device three times and exit")
     ap.add_argument("--small-batch-only", action="store_true",
                     help="only the small-batch passes (8, 32, 64 tokens) over the weight stream")
+    ap.add_argument("--other-types-only", action="store_true",
+                    help="only the Q4_0 and Q6_K GEMV passes")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the prefill pass over the 36-layer weights (for counter runs)")
     return ap.parse_args()
@@ -243,6 +245,51 @@ def small_batch_pass(torch, g, synth, entries, stream, n_tokens, reps=5):
                          "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}}
 
 
+def other_types_pass(torch, g, synth, reps=5):
+    """Batch-1 GEMV passes over the 36-layer shapes stored as Q4_0 and as Q6_K:
+    one layer's seven tensors generated per type, cloned to 36 distinct device
+    copies (so each pass streams every byte from HBM), one launch per GEMV in
+    layer order, as a HIP graph. Returns one labelled record per type."""
+    dev = "cuda:0"
+    out = []
+    for name, gen, fn in (("q4_0", synth.q4_0_weights, g.gguf_qmatvec_q4_0),
+                          ("q6_k", synth.q6_k_weights, g.gguf_qmatvec_q6_k)):
+        layer = []
+        for gm in [gm for st in synth.LAYER_STAGES for gm in st]:
+            w = gen(synth.rng_for(70, 0, synth.TENSOR_IDS[gm.name]), gm.rows, gm.cols)
+            layer.append((gm, torch.from_numpy(w).to(dev)))
+        xs = {c: torch.randn(c, generator=torch.Generator().manual_seed(c)).to(dev)
+              for c in {gm.cols for gm, _ in layer}}
+        ys = {r: torch.empty(r, dtype=torch.float32, device=dev) for r in {gm.rows for gm, _ in layer}}
+        calls, wbytes = [], 0
+        for li in range(synth.N_LAYERS):
+            for gm, W in layer:
+                Wc = W if li == 0 else W.clone()
+                calls.append((Wc, xs[gm.cols], ys[gm.rows], gm.rows, gm.cols))
+                wbytes += Wc.numel()
+        stream = torch.cuda.Stream()
+
+        def run():
+            for W, x, y, r, c in calls:
+                fn(W, x, y, rows=r, cols=c, stream=stream)
+
+        graph = capture(torch, run, stream)
+        t = time_replays(torch, graph, stream, reps)
+        ms = sorted(t)[len(t) // 2]
+        gbps = wbytes / (ms / 1e3) / 1e9
+        out.append({"label": f"batch-1 GEMV pass, 36 layers x 7 {name.upper()} tensors "
+                             "(SmolLM3-3B shapes), one launch per GEMV (HIP graph)",
+                    "type": name, "weight_bytes": wbytes, "ms_per_pass": round(ms, 4),
+                    "GBps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+                    "roofline": {"bound": "hbm", "kernel": f"gemv_{name}_kernel", "achieved": round(gbps, 1),
+                                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}})
+        del graph, calls, layer
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline():
     """The oracle as it stands, on a bounded sample of the same workload:
     layer 0's seven Q4_K GEMVs and the first 8192 rows of the Q8_0 head,
@@ -304,6 +351,9 @@ def main():
     torch.cuda.synchronize()
     if args.prefill_only:
         print(json.dumps(prefill_pass(torch, g, synth, entries, meta, stream)), flush=True)
+        return
+    if args.other_types_only:
+        print(json.dumps(other_types_pass(torch, g, synth)), flush=True)
         return
     if args.small_batch_only:
         print(json.dumps([small_batch_pass(torch, g, synth, entries, stream, n)
@@ -411,6 +461,7 @@ def main():
     rec["prefill"] = prefill_pass(torch, g, synth, entries, meta, stream)
     rec["small_batch"] = [small_batch_pass(torch, g, synth, entries, stream, n)
                           for n in SMALL_BATCH_TOKENS]
+    rec["other_types"] = other_types_pass(torch, g, synth)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline()
     print(json.dumps(rec), flush=True)

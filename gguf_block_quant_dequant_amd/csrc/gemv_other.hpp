@@ -148,11 +148,95 @@ __global__ __launch_bounds__(256) void dequant_q6_k_kernel(const uint8_t* __rest
 }
 
 // --------------------------------------------------------------------- GEMV
+//
+// Each step's loads (x and the raw words of every row) are issued one step
+// ahead, so that they are in flight while the previous step computes; the
+// words are re-aligned and decoded when their step computes.
+
+typedef float gqk_f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
   return v;
+}
+
+// Raw words of one Q4_0 block (see q40_block): w[0..3] at p & ~3, then the two
+// 2-byte loads; s = p & 2.
+struct Q40Raw {
+  uint32_t w[6];
+  uint32_t s;
+};
+
+__device__ __forceinline__ void q40_fetch(const uint8_t* p, Q40Raw& r) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const uint8_t* q = reinterpret_cast<const uint8_t*>(a & ~uintptr_t(3));
+  r.s = (uint32_t)(a & 2u);
+  r.w[0] = ld_u32(q);
+  r.w[1] = ld_u32(q + 4);
+  r.w[2] = ld_u32(q + 8);
+  r.w[3] = ld_u32(q + 12);
+  r.w[4] = ld_u16(q + 16);
+  r.w[5] = ld_u16(p + 16);
+}
+
+__device__ __forceinline__ void q40_assemble(const Q40Raw& r, uint32_t& dbits, uint32_t (&qb)[4]) {
+  const uint32_t w4 = r.w[4] | (r.w[5] << 16);
+  dbits = (r.s ? (r.w[0] >> 16) : r.w[0]) & 0xFFFFu;
+  qb[0] = r.s ? r.w[1] : __builtin_amdgcn_alignbyte(r.w[1], r.w[0], 2);
+  qb[1] = r.s ? r.w[2] : __builtin_amdgcn_alignbyte(r.w[2], r.w[1], 2);
+  qb[2] = r.s ? r.w[3] : __builtin_amdgcn_alignbyte(r.w[3], r.w[2], 2);
+  qb[3] = r.s ? w4 : __builtin_amdgcn_alignbyte(w4, r.w[3], 2);
+}
+
+struct Q40Step {
+  gqk_f32x4 x[8];
+  Q40Raw w[kOtherRows];
+};
+
+__device__ __forceinline__ void q40_step_fetch(Q40Step& f, const uint8_t* W, const float* x,
+                                               int64_t row0, int64_t rows, int64_t row_bytes,
+                                               int64_t b, int64_t nb) {
+  if (b >= nb) return;
+  const gqk_f32x4* xv = reinterpret_cast<const gqk_f32x4*>(x + b * kQ40BlockWeights);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f.x[i] = xv[i];
+#pragma unroll
+  for (int r = 0; r < kOtherRows; ++r) {
+    const int64_t row = (row0 + r) < rows ? (row0 + r) : (rows - 1);
+    q40_fetch(W + row * row_bytes + b * kQ40BlockBytes, f.w[r]);
+  }
+}
+
+__device__ __forceinline__ void q40_step_compute(const Q40Step& f, float (&acc)[kOtherRows]) {
+  float xsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xsum += (f.x[i].x + f.x[i].y) + (f.x[i].z + f.x[i].w);
+#pragma unroll
+  for (int r = 0; r < kOtherRows; ++r) {
+    uint32_t dbits, qb[4];
+    q40_assemble(f.w[r], dbits, qb);
+    // sum (code - 8) d x = 512 d sum (code / 512) x - 8 d sum x
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float lo[4], hi[4];
+      nibbles_div512(qb[i] & 0x0F0F0F0Fu, lo);
+      nibbles_div512((qb[i] >> 4) & 0x0F0F0F0Fu, hi);
+      const gqk_f32x4 xl = f.x[i], xh = f.x[4 + i];
+      a0 = fmaf(lo[0], xl.x, a0);
+      a0 = fmaf(lo[1], xl.y, a0);
+      a0 = fmaf(lo[2], xl.z, a0);
+      a0 = fmaf(lo[3], xl.w, a0);
+      a1 = fmaf(hi[0], xh.x, a1);
+      a1 = fmaf(hi[1], xh.y, a1);
+      a1 = fmaf(hi[2], xh.z, a1);
+      a1 = fmaf(hi[3], xh.w, a1);
+    }
+    const float d = half_lo(dbits);
+    acc[r] = fmaf(d * 512.f, a0 + a1, acc[r]);
+    acc[r] = fmaf(-8.f * d, xsum, acc[r]);
+  }
 }
 
 // grid: ceil(rows / (kOtherRows * kOtherWaves)) blocks of kOtherWaves waves.
@@ -167,48 +251,112 @@ __global__ __launch_bounds__(kOtherWaves * 64) void gemv_q4_0_kernel(
   float acc[kOtherRows];
 #pragma unroll
   for (int r = 0; r < kOtherRows; ++r) acc[r] = 0.f;
+  Q40Step cur, nxt;
+  q40_step_fetch(cur, W, x, row0, rows, row_bytes, lane, nb);
   for (int64_t b0 = 0; b0 < nb; b0 += 64) {
-    const int64_t b = b0 + lane;
-    if (b < nb) {
-      // x of this block: lo[j] = x[32 b + j], hi[j] = x[32 b + 16 + j]
-      const float4* xv = reinterpret_cast<const float4*>(x + b * kQ40BlockWeights);
-      float xs[32];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float4 v = xv[i];
-        xs[4 * i] = v.x; xs[4 * i + 1] = v.y; xs[4 * i + 2] = v.z; xs[4 * i + 3] = v.w;
-      }
-      float xsum = 0.f;
-#pragma unroll
-      for (int j = 0; j < 32; ++j) xsum += xs[j];
-#pragma unroll
-      for (int r = 0; r < kOtherRows; ++r) {
-        const int64_t row = (row0 + r) < rows ? (row0 + r) : (rows - 1);
-        uint32_t dbits, qb[4];
-        q40_block(W + row * row_bytes + b * kQ40BlockBytes, dbits, qb);
-        // sum (code - 8) d x = 512 d sum (code / 512) x - 8 d sum x
-        float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float lo[4], hi[4];
-          nibbles_div512(qb[i] & 0x0F0F0F0Fu, lo);
-          nibbles_div512((qb[i] >> 4) & 0x0F0F0F0Fu, hi);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            a0 = fmaf(lo[e], xs[4 * i + e], a0);
-            a1 = fmaf(hi[e], xs[16 + 4 * i + e], a1);
-          }
-        }
-        const float d = half_lo(dbits);
-        acc[r] = fmaf(d * 512.f, a0 + a1, acc[r]);
-        acc[r] = fmaf(-8.f * d, xsum, acc[r]);
-      }
-    }
+    if (b0 + 64 < nb) q40_step_fetch(nxt, W, x, row0, rows, row_bytes, b0 + 64 + lane, nb);
+    if (b0 + lane < nb) q40_step_compute(cur, acc);
+    cur = nxt;
   }
 #pragma unroll
   for (int r = 0; r < kOtherRows; ++r) {
-    const float s = wave_sum(acc[r]);
-    if (lane == 0 && row0 + r < rows) y[row0 + r] = s;
+    const float v = wave_sum(acc[r]);
+    if (lane == 0 && row0 + r < rows) y[row0 + r] = v;
+  }
+}
+
+// Raw words of one Q6_K quad (see q6k_quad): three aligned pairs, the 4
+// scale 2-byte loads and d.
+struct Q6KRaw {
+  uint32_t lo0[2], lo1[2], hi[2], sc[4], d;
+  uint32_t s;   // p & 2 (the super-block's offset from a 4-byte boundary)
+};
+
+__device__ __forceinline__ void q6k_fetch(const uint8_t* p, int u, Q6KRaw& r) {
+  const int n = u >> 3, l0 = 4 * (u & 7);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  r.s = (uint32_t)(a & 2u);
+  const uint8_t* q0 = reinterpret_cast<const uint8_t*>((a + 64 * n + l0) & ~uintptr_t(3));
+  const uint8_t* q1 = reinterpret_cast<const uint8_t*>((a + 64 * n + 32 + l0) & ~uintptr_t(3));
+  const uint8_t* q2 = reinterpret_cast<const uint8_t*>((a + 128 + 32 * n + l0) & ~uintptr_t(3));
+  r.lo0[0] = ld_u32(q0);
+  r.lo0[1] = ld_u32(q0 + 4);
+  r.lo1[0] = ld_u32(q1);
+  r.lo1[1] = ld_u32(q1 + 4);
+  r.hi[0] = ld_u32(q2);
+  r.hi[1] = ld_u32(q2 + 4);
+  const uint8_t* sp = p + 192 + 8 * n;
+  r.sc[0] = ld_u16(sp);
+  r.sc[1] = ld_u16(sp + 2);
+  r.sc[2] = ld_u16(sp + 4);
+  r.sc[3] = ld_u16(sp + 6);
+  r.d = ld_u16(p + 208);
+}
+
+__device__ __forceinline__ void q6k_assemble(const Q6KRaw& r, int u, uint32_t (&code)[4],
+                                             float (&sc)[4], float& d) {
+  // the three 4-byte fields sit at offsets that are multiples of 4 from p
+  const uint32_t lo0 = __builtin_amdgcn_alignbyte(r.lo0[1], r.lo0[0], r.s);
+  const uint32_t lo1 = __builtin_amdgcn_alignbyte(r.lo1[1], r.lo1[0], r.s);
+  const uint32_t hi = __builtin_amdgcn_alignbyte(r.hi[1], r.hi[0], r.s);
+  code[0] = (lo0 & 0x0F0F0F0Fu) | ((hi << 4) & 0x30303030u);
+  code[1] = (lo1 & 0x0F0F0F0Fu) | ((hi << 2) & 0x30303030u);
+  code[2] = ((lo0 >> 4) & 0x0F0F0F0Fu) | (hi & 0x30303030u);
+  code[3] = ((lo1 >> 4) & 0x0F0F0F0Fu) | ((hi >> 2) & 0x30303030u);
+  const uint32_t s0 = r.sc[0] | (r.sc[1] << 16), s1 = r.sc[2] | (r.sc[3] << 16);
+  const int h = (u & 7) >> 2;   // l0 >= 16
+  const uint32_t ev = h ? ((s0 >> 8) & 0xFFu) | ((s0 >> 16) & 0xFF00u) | ((s1 << 8) & 0xFF0000u) |
+                              (s1 & 0xFF000000u)
+                        : (s0 & 0xFFu) | ((s0 >> 8) & 0xFF00u) | ((s1 << 16) & 0xFF0000u) |
+                              ((s1 << 8) & 0xFF000000u);
+  sc[0] = sbyte0(ev);
+  sc[1] = sbyte1(ev);
+  sc[2] = sbyte2(ev);
+  sc[3] = sbyte3(ev);
+  d = half_lo(r.d);
+}
+
+struct Q6KStep {
+  gqk_f32x4 x[4];
+  Q6KRaw w[kOtherRows];
+};
+
+__device__ __forceinline__ void q6k_step_fetch(Q6KStep& f, const uint8_t* W, const float* x,
+                                               int64_t row0, int64_t rows, int64_t row_bytes,
+                                               int64_t sb, int64_t nsb, int u) {
+  if (sb >= nsb) return;
+  const int n = u >> 3, l0 = 4 * (u & 7);
+  const float* xb = x + sb * kQ6KBlockWeights + 128 * n + l0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) f.x[k] = *reinterpret_cast<const gqk_f32x4*>(xb + 32 * k);
+#pragma unroll
+  for (int r = 0; r < kOtherRows; ++r) {
+    const int64_t row = (row0 + r) < rows ? (row0 + r) : (rows - 1);
+    q6k_fetch(W + row * row_bytes + sb * kQ6KBlockBytes, u, f.w[r]);
+  }
+}
+
+__device__ __forceinline__ void q6k_step_compute(const Q6KStep& f, int u, float (&acc)[kOtherRows]) {
+  float xsum[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) xsum[k] = (f.x[k].x + f.x[k].y) + (f.x[k].z + f.x[k].w);
+#pragma unroll
+  for (int r = 0; r < kOtherRows; ++r) {
+    uint32_t code[4];
+    float sc[4], d;
+    q6k_assemble(f.w[r], u, code, sc, d);
+    // sum_k d sc_k (sum_i code_i x_i - 32 sum_i x_i)
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float a = ubyte0(code[k]) * f.x[k].x;
+      a = fmaf(ubyte1(code[k]), f.x[k].y, a);
+      a = fmaf(ubyte2(code[k]), f.x[k].z, a);
+      a = fmaf(ubyte3(code[k]), f.x[k].w, a);
+      a = fmaf(-32.f, xsum[k], a);
+      t = fmaf(sc[k], a, t);
+    }
+    acc[r] = fmaf(d, t, acc[r]);
   }
 }
 
@@ -221,47 +369,21 @@ __global__ __launch_bounds__(kOtherWaves * 64) void gemv_q6_k_kernel(
   if (row0 >= rows) return;
   const int64_t row_bytes = nsb * kQ6KBlockBytes;
   const int u = lane & 15;
-  const int n = u >> 3, l0 = 4 * (u & 7);
+  const int sl = lane >> 4;   // this lane's super-block within a step of 4
   float acc[kOtherRows];
 #pragma unroll
   for (int r = 0; r < kOtherRows; ++r) acc[r] = 0.f;
+  Q6KStep cur, nxt;
+  q6k_step_fetch(cur, W, x, row0, rows, row_bytes, sl, nsb, u);
   for (int64_t s0 = 0; s0 < nsb; s0 += 4) {
-    const int64_t sb = s0 + (lane >> 4);
-    if (sb < nsb) {
-      // x of this quad: xs[k][i] = x[256 sb + 128 n + 32 k + l0 + i]
-      const float* xb = x + sb * kQ6KBlockWeights + 128 * n + l0;
-      float xs[4][4], xsum[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 v = *reinterpret_cast<const float4*>(xb + 32 * k);
-        xs[k][0] = v.x; xs[k][1] = v.y; xs[k][2] = v.z; xs[k][3] = v.w;
-        xsum[k] = (v.x + v.y) + (v.z + v.w);
-      }
-#pragma unroll
-      for (int r = 0; r < kOtherRows; ++r) {
-        const int64_t row = (row0 + r) < rows ? (row0 + r) : (rows - 1);
-        uint32_t code[4];
-        float sc[4], d;
-        q6k_quad(W + row * row_bytes + sb * kQ6KBlockBytes, u, code, sc, d);
-        // sum_k d sc_k (sum_i code_i x_i - 32 sum_i x_i)
-        float t = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          float a = ubyte0(code[k]) * xs[k][0];
-          a = fmaf(ubyte1(code[k]), xs[k][1], a);
-          a = fmaf(ubyte2(code[k]), xs[k][2], a);
-          a = fmaf(ubyte3(code[k]), xs[k][3], a);
-          a = fmaf(-32.f, xsum[k], a);
-          t = fmaf(sc[k], a, t);
-        }
-        acc[r] = fmaf(d, t, acc[r]);
-      }
-    }
+    if (s0 + 4 < nsb) q6k_step_fetch(nxt, W, x, row0, rows, row_bytes, s0 + 4 + sl, nsb, u);
+    if (s0 + sl < nsb) q6k_step_compute(cur, u, acc);
+    cur = nxt;
   }
 #pragma unroll
   for (int r = 0; r < kOtherRows; ++r) {
-    const float s = wave_sum(acc[r]);
-    if (lane == 0 && row0 + r < rows) y[row0 + r] = s;
+    const float v = wave_sum(acc[r]);
+    if (lane == 0 && row0 + r < rows) y[row0 + r] = v;
   }
 }
 
