@@ -29,6 +29,9 @@ What it computes, and from which passage:
 * matvec y = W x ("culpeo.ws", naive-implementation post, the matvec op), in
   fp64 from the fp32 dequantized weights.
 * small batch Y = X W^T with fp32 X (the matvec of each token row), in fp64.
+* the steps either side of the GEMVs ("GGUF Inferencer in R", section 5.2):
+  RMSN(v) = norm * v / sqrt(mean(v^2) + eps), SiLU(x) = x / (1 + exp(-x)),
+  the gated activation SiLU(G) * U, in fp64.
 * prefill Y = X W^T with bf16 X ("GGUF Inferencer in R", section 1 and section
   4: prefill is the same math on the whole prompt as one matrix), in fp64.
 """
@@ -68,6 +71,7 @@ from .formats import (  # noqa: F401
     unpack_q4_k_block,
     unpack_q6_k_block,
 )
+from .layer import rmsnorm_f64, silu_f64, swiglu_f64  # noqa: F401
 from .linalg import (  # noqa: F401
     floored_rel_err,
     matmul_bf16_x_f64,
