@@ -57,6 +57,11 @@ _SIGS = {
     "gguf_qmatmul_f32_q4_k": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P]),
     "gguf_qk_probe_read": (ctypes.c_int, [_P, _I64, _P, _P]),
     "gguf_qmatvec_batch": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
+    "gguf_qmatvec_batch_ep": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P]),
+    "gguf_rmsnorm_prep_f32": (ctypes.c_int, [_P, _P, _P, _P, _I64, _P]),
+    "gguf_rmsnorm_f32": (ctypes.c_int, [_P, _P, ctypes.c_float, _P, _I64, _P]),
+    "gguf_swiglu_f32": (ctypes.c_int, [_P, _P, _P, _I64, _P]),
+    "gguf_add_f32": (ctypes.c_int, [_P, _P, _P, _I64, _P]),
     "gguf_tensor_nbytes": (_I64, [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]),
     "gguf_file_open": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_void_p)]),
     "gguf_file_close": (None, [_P]),
@@ -300,11 +305,27 @@ def gguf_qk_probe_read(buf, sink=None, stream=None):
     return sink
 
 
+class GemvEpEntry(ctypes.Structure):
+    """struct gguf_qk_gemv_ep of the C ABI."""
+    _fields_ = [("scale_ss", ctypes.c_void_p), ("scale_n", ctypes.c_int64), ("eps", ctypes.c_float),
+                ("pair", ctypes.c_int32), ("residual", ctypes.c_void_p), ("norm_w", ctypes.c_void_p),
+                ("norm_out", ctypes.c_void_p), ("ss_out", ctypes.c_void_p), ("act", ctypes.c_void_p)]
+
+
+def _opt(t, name):
+    return None if t is None else _dev(t, name, torch.float32)
+
+
 class GemvBatch:
     """A prepared gguf_qmatvec_batch list: entries (type, W, x, y, stage) with
-    device tensors; keeps the tensors alive and the C array built once."""
+    device tensors; keeps the tensors alive and the C array built once.
 
-    def __init__(self, entries):
+    `epilogues` (optional, one per entry, None for none) are dicts with the
+    gguf_qk_gemv_ep fields as keys (scale_ss, eps, pair, residual, norm_w,
+    norm_out, ss_out, act; tensors for the vectors); the batch then runs through
+    gguf_qmatvec_batch_ep."""
+
+    def __init__(self, entries, epilogues=None):
         self._keep = []
         arr = (GemvEntry * len(entries))()
         for i, (type_id, W, x, y, stage) in enumerate(entries):
@@ -315,12 +336,82 @@ class GemvBatch:
             self._keep.append((W, x, y))
         self.array = arr
         self.n = len(entries)
+        self.ep = None
+        if epilogues is not None:
+            if len(epilogues) != len(entries):
+                raise ValueError("one epilogue (or None) per entry")
+            ep = (GemvEpEntry * len(entries))()
+            for i, e in enumerate(epilogues):
+                if not e:
+                    continue
+                ss = e.get("scale_ss")
+                ep[i] = GemvEpEntry(_opt(ss, "scale_ss"), 0 if ss is None else ss.numel(),
+                                    float(e.get("eps", 0.0)), int(e.get("pair", 0)),
+                                    _opt(e.get("residual"), "residual"), _opt(e.get("norm_w"), "norm_w"),
+                                    _opt(e.get("norm_out"), "norm_out"), _opt(e.get("ss_out"), "ss_out"),
+                                    _opt(e.get("act"), "act"))
+                self._keep.append(tuple(v for v in e.values() if isinstance(v, torch.Tensor)))
+            self.ep = ep
 
 
 def gguf_qmatvec_batch(batch: GemvBatch, stream=None):
     """Run a prepared GemvBatch (steps in order on the stream)."""
+    if batch.ep is not None:
+        return gguf_qmatvec_batch_ep(batch, stream)
     _check(lib().gguf_qmatvec_batch(ctypes.cast(batch.array, ctypes.c_void_p), batch.n,
                                     _stream(stream)), "gguf_qmatvec_batch")
+
+
+def gguf_qmatvec_batch_ep(batch: GemvBatch, stream=None):
+    """Run a prepared GemvBatch with its per-entry epilogues."""
+    ep = ctypes.cast(batch.ep, ctypes.c_void_p) if batch.ep is not None else None
+    _check(lib().gguf_qmatvec_batch_ep(ctypes.cast(batch.array, ctypes.c_void_p), ep, batch.n,
+                                       _stream(stream)), "gguf_qmatvec_batch_ep")
+
+
+def _vec(t, name, n=None):
+    p = _dev(t, name, torch.float32)
+    if n is not None and t.numel() < n:
+        raise ValueError(f"{name} is too small")
+    return p
+
+
+def gguf_rmsnorm_prep_f32(v, norm_w, vw=None, ss=None, stream=None):
+    """vw = v * norm_w and ss[j] = sum of v^2 over elements 64 j .. 64 j + 63."""
+    n = v.numel()
+    vw = torch.empty_like(v) if vw is None else vw
+    ss = torch.empty((n + 63) // 64, dtype=torch.float32, device=v.device) if ss is None else ss
+    _check(lib().gguf_rmsnorm_prep_f32(_vec(v, "v"), _vec(norm_w, "norm_w", n), _vec(vw, "vw", n),
+                                       _vec(ss, "ss", (n + 63) // 64), n, _stream(stream)),
+           "gguf_rmsnorm_prep_f32")
+    return vw, ss
+
+
+def gguf_rmsnorm_f32(v, norm_w, eps, out=None, stream=None):
+    """out = norm_w * v / sqrt(mean(v^2) + eps)."""
+    n = v.numel()
+    out = torch.empty_like(v) if out is None else out
+    _check(lib().gguf_rmsnorm_f32(_vec(v, "v"), _vec(norm_w, "norm_w", n), float(eps),
+                                  _vec(out, "out", n), n, _stream(stream)), "gguf_rmsnorm_f32")
+    return out
+
+
+def gguf_swiglu_f32(g, u, out=None, stream=None):
+    """out = SiLU(g) * u."""
+    n = g.numel()
+    out = torch.empty_like(g) if out is None else out
+    _check(lib().gguf_swiglu_f32(_vec(g, "g"), _vec(u, "u", n), _vec(out, "out", n), n,
+                                 _stream(stream)), "gguf_swiglu_f32")
+    return out
+
+
+def gguf_add_f32(a, b, out=None, stream=None):
+    """out = a + b."""
+    n = a.numel()
+    out = torch.empty_like(a) if out is None else out
+    _check(lib().gguf_add_f32(_vec(a, "a"), _vec(b, "b", n), _vec(out, "out", n), n, _stream(stream)),
+           "gguf_add_f32")
+    return out
 
 
 # ------------------------------------------------------------------ GGUF files

@@ -289,8 +289,110 @@ struct SplitK {
   int* counters;     // [row groups] ints at stride kCounterStride, zero between calls
 };
 
+// What the wave that holds a row group's final sums does with them (the steps
+// either side of the decode GEMVs, "GGUF Inferencer in R", section 5.2, fused
+// into the GEMV that produces or consumes their vector). flags == 0: store y.
+//  kEpScale    y = s * (W x), s = 1 / sqrt(sum(scale_ss[0..scale_n)) * inv_k + eps):
+//              RMSN of the input when x holds v * norm and scale_ss the partial
+//              sums of v^2 (the scalar factor of RMSN moves past the product)
+//  kEpResidual y += residual (the residual add)
+//  kEpNorm     also norm_out = y * norm_w and ss_out[rg] = sum of y^2 over the
+//              row group's rows (fixed butterfly order): the next RMSN's inputs
+//  kEpPair     one of a gate/up pair: the second of the pair to finish a row
+//              group writes act = SiLU(gate) * up for it (y stores and the
+//              partner's loads are agent-scope; a counter per row group)
+constexpr int kEpScale = 1, kEpResidual = 2, kEpNorm = 4, kEpPair = 8;
+
+struct GemvEpilogue {
+  const float* scale_ss;
+  const float* residual;
+  const float* norm_w;
+  float* norm_out;
+  float* ss_out;
+  float* act;
+  const float* partner_y;
+  int* pair_cnt;       // [row groups] at stride kCounterStride, zero between calls
+  int scale_n;
+  float eps;
+  float inv_k;         // 1 / length of the normalized vector
+  int flags;
+  int role;            // pair: 0 gate, 1 up
+  int pad[3];
+};
+
+__device__ __forceinline__ float wave_sum_fixed(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// v: this lane's final sum for row row0 + lane (lanes >= valid hold garbage).
+// Called by the whole wave (wave-uniform control flow).
+__device__ __forceinline__ void finish_rows(const GemvEpilogue& ep, float v, float* __restrict__ y,
+                                            int64_t row0, int valid, int rg, int lane) {
+  const int flags = ep.flags;
+  if (flags == 0) {
+    if (lane < valid) y[row0 + lane] = v;
+    return;
+  }
+  const bool live = lane < valid;
+  const int64_t r = row0 + (live ? lane : 0);
+  if (flags & kEpScale) {
+    // the partial sums in order, eight loads in flight at a time
+    float S = 0.f;
+    const int n = ep.scale_n;
+    for (int i0 = 0; i0 < n; i0 += 8) {
+      float t[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t[i] = ep.scale_ss[(i0 + i) < n ? (i0 + i) : (n - 1)];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i0 + i < n) S += t[i];
+    }
+    v *= 1.0f / sqrtf(S * ep.inv_k + ep.eps);
+  }
+  if ((flags & kEpResidual) && live) v += ep.residual[r];
+  if (live) {
+    if (flags & kEpPair)
+      __hip_atomic_store(&y[r], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      y[r] = v;
+  }
+  if (flags & kEpNorm) {
+    if (live) ep.norm_out[r] = v * ep.norm_w[r];
+    // the square rounded on its own (kept out of the butterfly's first add,
+    // which could otherwise take it unrounded as an fma): the same bits as the
+    // standalone preparation kernel
+    float sq = live ? v * v : 0.f;
+    asm volatile("" : "+v"(sq));
+    const float ss = wave_sum_fixed(sq);
+    if (lane == 0) ep.ss_out[rg] = ss;
+  }
+  if (flags & kEpPair) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    GQK_WAIT_VMCNT(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    int old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(&ep.pair_cnt[rg * kCounterStride], 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old == 1) {
+      if (live) {
+        const float o = __hip_atomic_load(&ep.partner_y[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float gv = ep.role == 0 ? v : o, uv = ep.role == 0 ? o : v;
+        ep.act[r] = gv / (1.0f + expf(-gv)) * uv;
+      }
+      if (lane == 0)
+        __hip_atomic_store(&ep.pair_cnt[rg * kCounterStride], 0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // Store this lane's partial; the last of the P waves of the row group sums
-// them in order 0..P-1 and writes y. Wave-uniform control flow.
+// them in order 0..P-1 and hands the sums to finish_rows. Wave-uniform
+// control flow.
 //
 // Hand-off between waves on different XCDs without L2-wide write-back or
 // invalidation: partials are written and read with agent-scope atomic
@@ -299,9 +401,10 @@ struct SplitK {
 // (vmcnt(0)); the last arriver's loads are issued after its increment returned.
 __device__ __forceinline__ void splitk_finish(float acc, float* __restrict__ y, int64_t rows,
                                               int64_t row0, int valid_rows, int rg, int part,
-                                              int P, const SplitK& sk, int lane) {
+                                              int P, const SplitK& sk, int lane,
+                                              const GemvEpilogue& ep) {
   if (P == 1) {
-    if (lane < valid_rows) y[row0 + lane] = acc;
+    finish_rows(ep, acc, y, row0, valid_rows, rg, lane);
     return;
   }
   if (lane < valid_rows)
@@ -316,10 +419,10 @@ __device__ __forceinline__ void splitk_finish(float acc, float* __restrict__ y, 
                                  __HIP_MEMORY_SCOPE_AGENT);
   old = __builtin_amdgcn_readfirstlane(old);
   if (old == P - 1) {
+    float s = 0.f;
     if (lane < valid_rows) {
       // eight loads in flight at a time (indexes past P repeat the last
       // partial and are not added), added strictly in order 0..P-1
-      float s = 0.f;
       for (int p0 = 0; p0 < P; p0 += 8) {
         float v[8];
 #pragma unroll
@@ -332,8 +435,8 @@ __device__ __forceinline__ void splitk_finish(float acc, float* __restrict__ y, 
         for (int i = 0; i < 8; ++i)
           if (p0 + i < P) s += v[i];
       }
-      y[row0 + lane] = s;
     }
+    finish_rows(ep, s, y, row0, valid_rows, rg, lane);
     if (lane == 0)
       __hip_atomic_store(&sk.counters[rg * kCounterStride], 0, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
@@ -364,6 +467,7 @@ struct GemvDesc {
 struct GemvGroup {
   GemvDesc d[kMaxGroup];
   int n;
+  GemvEpilogue ep[kMaxGroup];   // read only by the wave that finishes a row group
 };
 
 // Task t of a group: which GEMV (g) and its descriptor. Kernel arguments live
@@ -443,7 +547,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_group_kernel(GemvGroup g
     else
       acc = q80_wave_task<kSlots>(D.W, D.x, row_bytes, row0, valid, c0, c1, &slots[wave][0], lane);
     const SplitK sk{partials + D.part_off, counters + (int64_t)D.cnt_off * kCounterStride};
-    splitk_finish(acc, D.y, D.rows, row0, valid, rg, part, P, sk, lane);
+    splitk_finish(acc, D.y, D.rows, row0, valid, rg, part, P, sk, lane, grp.ep[g]);
   }
 }
 
@@ -500,7 +604,7 @@ __global__ __launch_bounds__(kBlockWaves * 64) void gemv_q4k_block_kernel(GemvGr
 #pragma unroll
     for (int w = 0; w < kBlockWaves; ++w) s += red[w][lane];
     const SplitK sk{partials + D.part_off, counters + (int64_t)D.cnt_off * kCounterStride};
-    splitk_finish(s, D.y, D.rows, row0, valid, rg, part, P, sk, lane);
+    splitk_finish(s, D.y, D.rows, row0, valid, rg, part, P, sk, lane, grp.ep[g]);
   }
 }
 

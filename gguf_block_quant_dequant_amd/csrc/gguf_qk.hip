@@ -7,8 +7,10 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/gguf_file.h"
 #include "../../include/gguf_qk.h"
@@ -17,6 +19,7 @@
 #include "gemv.hpp"
 #include "gemv_other.hpp"
 #include "gemv_small_batch.hpp"
+#include "layer_ops.hpp"
 #include "probe.hpp"
 
 namespace gqk {
@@ -32,11 +35,15 @@ constexpr int kMaxSplits = 16;                            // K ranges per row gr
 constexpr int64_t kGemmScratchFloats = int64_t(8) << 20;
 constexpr int64_t kGemmMaxTiles = int64_t(1) << 12;
 constexpr int kGemmMaxSplits = 8;
+// Gate/up pair counters of the fused SiLU(gate) * up epilogue (row groups of
+// the pairs of one step).
+constexpr int64_t kPairCounters = int64_t(1) << 12;
 struct ScratchArea {
   float partials[kScratchPartials];
   int counters[kScratchCounters * kCounterStride];
   float gemm_partials[kGemmScratchFloats];
   int gemm_counters[kGemmMaxTiles * kGemmCounterStride];
+  int pair_counters[kPairCounters * kCounterStride];
 };
 static __device__ __attribute__((aligned(256))) ScratchArea g_scratch;
 
@@ -258,9 +265,12 @@ static int check_gemv(int type, const void* W, const float* x, const float* y, i
 // partials added in LDS), Q8_0 as per-wave tasks with split-K sized to the
 // task target. Returns the task count. Q8_0 GEMVs with cols % 256 != 0 are
 // never grouped (see launch_step).
-static int64_t plan_group(int type, const gguf_qk_gemv* const* v, int n, GemvGroup* grp) {
+static int64_t plan_group(int type, const gguf_qk_gemv* const* v, const GemvEpilogue* const* e,
+                          int n, GemvGroup* grp) {
   *grp = GemvGroup{};
   grp->n = n;
+  for (int i = 0; i < n; ++i)
+    if (e && e[i]) grp->ep[i] = *e[i];
   int64_t total_bytes = 0;
   for (int i = 0; i < n; ++i) total_bytes += v[i]->rows * row_bytes_of(type, v[i]->cols);
   int64_t tasks = 0, part_off = 0, cnt_off = 0;
@@ -306,10 +316,10 @@ static int64_t plan_group(int type, const gguf_qk_gemv* const* v, int n, GemvGro
 }
 
 // Launches one planned group.
-static int launch_group(int type, const gguf_qk_gemv* const* v, int n, const ScratchArea* scratch,
-                        hipStream_t stream) {
+static int launch_group(int type, const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n,
+                        const ScratchArea* scratch, hipStream_t stream) {
   GemvGroup grp;
-  const int64_t tasks = plan_group(type, v, n, &grp);
+  const int64_t tasks = plan_group(type, v, e, n, &grp);
   float* partials = const_cast<float*>(scratch->partials);
   int* counters = const_cast<int*>(scratch->counters);
   const int64_t blocks = type == GGUF_QK_TYPE_Q4_K ? tasks : (tasks + kGemvWaves - 1) / kGemvWaves;
@@ -338,10 +348,11 @@ static int launch_rowwise_q8_0(const gguf_qk_gemv& g, hipStream_t stream) {
 
 // Launches the GEMVs of one step: same-format GEMVs go together, kMaxGroup at
 // a time; each launch follows the previous one on the stream.
-static int launch_step(const gguf_qk_gemv* list, int n, const ScratchArea* scratch,
-                       hipStream_t stream) {
+static int launch_step(const gguf_qk_gemv* list, const GemvEpilogue* eps, int n,
+                       const ScratchArea* scratch, hipStream_t stream) {
   for (int type : {GGUF_QK_TYPE_Q4_K, GGUF_QK_TYPE_Q8_0}) {
     const gguf_qk_gemv* grp[kMaxGroup];
+    const GemvEpilogue* ge[kMaxGroup];
     int k = 0;
     for (int i = 0; i < n; ++i) {
       const gguf_qk_gemv& g = list[i];
@@ -351,15 +362,16 @@ static int launch_step(const gguf_qk_gemv* list, int n, const ScratchArea* scrat
         if (st) return st;
         continue;
       }
+      ge[k] = eps ? &eps[i] : nullptr;
       grp[k++] = &g;
       if (k == kMaxGroup) {
-        const int st = launch_group(type, grp, k, scratch, stream);
+        const int st = launch_group(type, grp, ge, k, scratch, stream);
         if (st) return st;
         k = 0;
       }
     }
     if (k) {
-      const int st = launch_group(type, grp, k, scratch, stream);
+      const int st = launch_group(type, grp, ge, k, scratch, stream);
       if (st) return st;
     }
   }
@@ -376,10 +388,90 @@ static int matvec_common(int type, const void* W, const float* x, float* y, int6
   st = current_device(&scratch);
   if (st) return st;
   const gguf_qk_gemv g{W, x, y, rows, cols, type, 0, {0}};
-  return launch_step(&g, 1, scratch, stream);
+  return launch_step(&g, nullptr, 1, scratch, stream);
 }
 
-int gguf_qmatvec_batch(const gguf_qk_gemv* list, int32_t n, hipStream_t stream) {
+// Validates entry i's epilogue (the whole list is in view for pairs) and
+// fills the device form; the pair counters are attached later (pair_rg: the
+// first pair counter row group of the entry's pair, else -1). pair_off: next
+// free pair counter row group of the step.
+static int make_epilogue(const gguf_qk_gemv* list, const gguf_qk_gemv_ep* ep, int32_t n, int32_t i,
+                         int64_t* pair_off, int64_t* pair_rg, GemvEpilogue* out) {
+  *pair_rg = -1;
+  *out = GemvEpilogue{};
+  const gguf_qk_gemv& g = list[i];
+  const gguf_qk_gemv_ep& e = ep[i];
+  const int64_t RG = (g.rows + 63) / 64;
+  auto al4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+  int flags = 0;
+  if (e.scale_ss) {
+    if (e.scale_n < 1 || e.scale_n > INT32_MAX || !(e.eps >= 0.f) || e.eps > 3.0e38f || !al4(e.scale_ss))
+      return GGUF_QK_ERR_SHAPE;
+    flags |= kEpScale;
+  }
+  if (e.residual) {
+    if (!al4(e.residual)) return GGUF_QK_ERR_ALIGN;
+    if (e.residual != g.y && overlap(e.residual, g.rows * 4, g.y, g.rows * 4)) return GGUF_QK_ERR_ALIAS;
+    flags |= kEpResidual;
+  }
+  if (e.norm_w || e.norm_out || e.ss_out) {
+    if (!e.norm_w || !e.norm_out || !e.ss_out) return GGUF_QK_ERR_NULL;
+    if (!al4(e.norm_w) || !al4(e.norm_out) || !al4(e.ss_out)) return GGUF_QK_ERR_ALIGN;
+    flags |= kEpNorm;
+  }
+  if (e.pair != 0) {
+    if (e.pair != 1 && e.pair != 2) return GGUF_QK_ERR_SHAPE;
+    const int32_t j = e.pair == 1 ? i + 1 : i - 1;   // the partner
+    if (j < 0 || j >= n) return GGUF_QK_ERR_SHAPE;
+    const gguf_qk_gemv& h = list[j];
+    if (ep[j].pair != 3 - e.pair || h.stage != g.stage || h.rows != g.rows || h.type != g.type ||
+        ep[j].act != e.act)
+      return GGUF_QK_ERR_SHAPE;
+    if (!e.act) return GGUF_QK_ERR_NULL;
+    if (!al4(e.act)) return GGUF_QK_ERR_ALIGN;
+    if (e.pair == 1) {                              // counters are taken once per pair
+      if (*pair_off + RG > kPairCounters) return GGUF_QK_ERR_LIMIT;
+      *pair_rg = *pair_off;
+      *pair_off += RG;
+    }
+    out->partner_y = h.y;
+    out->role = e.pair - 1;
+    out->act = e.act;
+    flags |= kEpPair;
+  }
+  // outputs written by the epilogue may not overlap what the step reads or writes
+  const void* outs[3] = {e.norm_out, e.ss_out, e.act};
+  const int64_t outn[3] = {g.rows * 4, RG * 4, g.rows * 4};
+  for (int a = 0; a < 3; ++a) {
+    if (!outs[a]) continue;
+    for (int32_t b = 0; b < n; ++b) {
+      if (list[b].stage != g.stage) continue;
+      const int64_t wb = list[b].rows * row_bytes_of(list[b].type, list[b].cols);
+      if (overlap(outs[a], outn[a], list[b].y, list[b].rows * 4) ||
+          overlap(outs[a], outn[a], list[b].x, list[b].cols * 4) ||
+          overlap(outs[a], outn[a], list[b].W, wb))
+        return GGUF_QK_ERR_ALIAS;
+    }
+    if (overlap(outs[a], outn[a], e.residual, e.residual ? g.rows * 4 : 0) ||
+        overlap(outs[a], outn[a], e.norm_w, e.norm_w ? g.rows * 4 : 0) ||
+        overlap(outs[a], outn[a], e.scale_ss, e.scale_ss ? e.scale_n * 4 : 0))
+      return GGUF_QK_ERR_ALIAS;
+  }
+  if (flags && g.type == GGUF_QK_TYPE_Q8_0 && g.cols % 256) return GGUF_QK_ERR_SHAPE;
+  out->scale_ss = e.scale_ss;
+  out->residual = e.residual;
+  out->norm_w = e.norm_w;
+  out->norm_out = e.norm_out;
+  out->ss_out = e.ss_out;
+  out->scale_n = (int)e.scale_n;
+  out->eps = e.eps;
+  out->inv_k = 1.0f / (float)g.cols;
+  out->flags = flags;
+  return GGUF_QK_OK;
+}
+
+static int batch_common(const gguf_qk_gemv* list, const gguf_qk_gemv_ep* ep, int32_t n,
+                        hipStream_t stream) {
   if (n < 0) return GGUF_QK_ERR_SHAPE;
   if (n == 0) return GGUF_QK_OK;
   if (!list) return GGUF_QK_ERR_NULL;
@@ -406,17 +498,41 @@ int gguf_qmatvec_batch(const gguf_qk_gemv* list, int32_t n, hipStream_t stream) 
       }
     i = j;
   }
+  std::vector<GemvEpilogue> eps;
+  std::vector<int64_t> pair_rg;
+  if (ep) {
+    eps.resize(n);
+    pair_rg.resize(n);
+    int64_t pair_off = 0;
+    for (int32_t i = 0; i < n; ++i) {
+      if (i > 0 && list[i].stage != list[i - 1].stage) pair_off = 0;   // a step has finished
+      const int st = make_epilogue(list, ep, n, i, &pair_off, &pair_rg[i], &eps[i]);
+      if (st) return st;
+      if (ep[i].pair == 2) pair_rg[i] = pair_rg[i - 1];   // the gate's counters
+    }
+  }
   ScratchArea* scratch = nullptr;
   int st = current_device(&scratch);
   if (st) return st;
+  for (int32_t i = 0; i < (int32_t)eps.size(); ++i)
+    if (pair_rg[i] >= 0) eps[i].pair_cnt = scratch->pair_counters + pair_rg[i] * kCounterStride;
   for (int32_t i = 0; i < n;) {
     int32_t j = i;
     while (j < n && list[j].stage == list[i].stage) ++j;
-    st = launch_step(list + i, j - i, scratch, stream);
+    st = launch_step(list + i, ep ? eps.data() + i : nullptr, j - i, scratch, stream);
     if (st) return st;
     i = j;
   }
   return GGUF_QK_OK;
+}
+
+int gguf_qmatvec_batch(const gguf_qk_gemv* list, int32_t n, hipStream_t stream) {
+  return batch_common(list, nullptr, n, stream);
+}
+
+int gguf_qmatvec_batch_ep(const gguf_qk_gemv* list, const gguf_qk_gemv_ep* ep, int32_t n,
+                          hipStream_t stream) {
+  return batch_common(list, ep, n, stream);
 }
 
 int gguf_qmatvec_q8_0(const void* W, const float* x, float* y, int64_t rows, int64_t cols,
@@ -590,6 +706,75 @@ int gguf_qmatmul_f32_q8_0(const void* W, const float* X, float* Y, int64_t n_tok
 int gguf_qmatmul_f32_q4_k(const void* W, const float* X, float* Y, int64_t n_tokens, int64_t rows,
                           int64_t cols, hipStream_t stream) {
   return small_batch_common(GGUF_QK_TYPE_Q4_K, W, X, Y, n_tokens, rows, cols, stream);
+}
+
+// Standalone layer steps (vectors of n fp32).
+static int vec_check(std::initializer_list<const void*> ptrs, int64_t n) {
+  for (const void* p : ptrs) {
+    if (!p) return GGUF_QK_ERR_NULL;
+    if (!aligned16(p)) return GGUF_QK_ERR_ALIGN;
+  }
+  if (n < 0 || n > INT64_MAX / 4) return GGUF_QK_ERR_SHAPE;
+  return GGUF_QK_OK;
+}
+
+int gguf_rmsnorm_prep_f32(const float* v, const float* norm_w, float* vw, float* ss, int64_t n,
+                          hipStream_t stream) {
+  int st = vec_check({v, norm_w, vw, ss}, n);
+  if (st) return st;
+  const int64_t groups = (n + 63) / 64;
+  if (overlap(vw, n * 4, v, n * 4) || overlap(vw, n * 4, norm_w, n * 4) ||
+      overlap(ss, groups * 4, v, n * 4) || overlap(ss, groups * 4, norm_w, n * 4) ||
+      overlap(ss, groups * 4, vw, n * 4))
+    return GGUF_QK_ERR_ALIAS;
+  if (n == 0) return GGUF_QK_OK;
+  st = current_device(nullptr);
+  if (st) return st;
+  if ((groups + 3) / 4 > INT32_MAX) return GGUF_QK_ERR_LIMIT;
+  hipLaunchKernelGGL(rmsnorm_prep_kernel, dim3((unsigned)((groups + 3) / 4)), dim3(256), 0, stream,
+                     v, norm_w, vw, ss, n);
+  return launch_status();
+}
+
+int gguf_rmsnorm_f32(const float* v, const float* norm_w, float eps, float* out, int64_t n,
+                     hipStream_t stream) {
+  int st = vec_check({v, norm_w, out}, n);
+  if (st) return st;
+  if (!(eps >= 0.f) || eps > 3.0e38f) return GGUF_QK_ERR_SHAPE;
+  if (overlap(out, n * 4, v, n * 4) || overlap(out, n * 4, norm_w, n * 4)) return GGUF_QK_ERR_ALIAS;
+  if (n == 0) return GGUF_QK_OK;
+  st = current_device(nullptr);
+  if (st) return st;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(1), dim3(256), 0, stream, v, norm_w, eps, out, n);
+  return launch_status();
+}
+
+static int elementwise2(int kind, const float* a, const float* b, float* out, int64_t n,
+                        hipStream_t stream) {
+  int st = vec_check({a, b, out}, n);
+  if (st) return st;
+  // out may be a or b exactly (each element is read before it is written by
+  // the same thread), not a partial overlap
+  if ((out != a && overlap(out, n * 4, a, n * 4)) || (out != b && overlap(out, n * 4, b, n * 4)))
+    return GGUF_QK_ERR_ALIAS;
+  if (n == 0) return GGUF_QK_OK;
+  st = current_device(nullptr);
+  if (st) return st;
+  if ((n + 255) / 256 > INT32_MAX) return GGUF_QK_ERR_LIMIT;
+  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (kind == 0)
+    hipLaunchKernelGGL(swiglu_kernel, grid, block, 0, stream, a, b, out, n);
+  else
+    hipLaunchKernelGGL(add_kernel, grid, block, 0, stream, a, b, out, n);
+  return launch_status();
+}
+
+int gguf_swiglu_f32(const float* g, const float* u, float* out, int64_t n, hipStream_t stream) {
+  return elementwise2(0, g, u, out, n, stream);
+}
+
+int gguf_add_f32(const float* a, const float* b, float* out, int64_t n, hipStream_t stream) {
+  return elementwise2(1, a, b, out, n, stream);
 }
 
 int gguf_qk_probe_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream) {

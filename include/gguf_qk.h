@@ -167,6 +167,59 @@ typedef struct gguf_qk_gemv {
  * enqueued. */
 int gguf_qmatvec_batch(const gguf_qk_gemv* list, int32_t n, hipStream_t stream);
 
+/* --- decode step with the neighbouring steps fused ------------------------ */
+
+/* What the GEMV of a list entry does with its outputs besides storing y: the
+ * steps either side of the decode GEMVs ("GGUF Inferencer in R", section 5.2:
+ * RMSN(v) = norm * v / sqrt(mean(v^2) + epsilon) before q/k/v and before
+ * gate/up; Activation = SiLU(G) * U with SiLU(x) = x / (1 + exp(-x)); the
+ * residual adds after the output and down projections), folded into the
+ * GEMV that produces or consumes the vector so that they cost no launch.
+ * A NULL pointer (or pair 0) switches a part off. */
+typedef struct gguf_qk_gemv_ep {
+  /* Input RMSN: y is scaled by 1 / sqrt(sum(scale_ss[0..scale_n)) / cols + eps).
+   * With x = v * norm (elementwise) and scale_ss the partial sums of v^2,
+   * y = W RMSN(v): RMSN's scalar factor moves past the product. */
+  const float* scale_ss;
+  int64_t scale_n;
+  float eps;
+  /* 0: none. 1: this entry is the gate of a pair whose up is the next entry;
+   * 2: the up of the previous entry. The pair (same stage, type and rows) writes
+   * act = SiLU(y_gate) * y_up (rows floats, the same pointer in both). */
+  int32_t pair;
+  /* y = residual + ... (rows floats; may be y itself, not a partial overlap). */
+  const float* residual;
+  /* Output half of the next RMSN: norm_out = y * norm_w (rows floats) and
+   * ss_out[j] = sum of y^2 over rows 64 j .. 64 j + 63 (ceil(rows / 64) floats),
+   * the scale_ss of the GEMVs that read norm_out. All three or none. */
+  const float* norm_w;
+  float* norm_out;
+  float* ss_out;
+  float* act;
+} gguf_qk_gemv_ep;
+
+/* gguf_qmatvec_batch with an epilogue per entry (ep: n entries, or NULL for
+ * none). Entries with epilogues must be Q4_K, or Q8_0 with cols % 256 == 0.
+ * Epilogue arrays need 4-byte alignment; their outputs may not overlap any
+ * input or output of the step. The fp32 sums of the scale and of ss_out run
+ * in fixed orders: results are deterministic. */
+int gguf_qmatvec_batch_ep(const gguf_qk_gemv* list, const gguf_qk_gemv_ep* ep, int32_t n,
+                          hipStream_t stream);
+
+/* The same steps standalone, on vectors of n fp32 (16-byte aligned):
+ *   gguf_rmsnorm_prep_f32: vw = v * norm_w and ss[j] = sum of v^2 over
+ *     elements 64 j .. 64 j + 63 (the input half of a fused RMSN, for a
+ *     vector no GEMV epilogue produced, such as the first layer's input);
+ *   gguf_rmsnorm_f32: out = RMSN(v) (one block; for the unfused path);
+ *   gguf_swiglu_f32: out = SiLU(g) * u;  gguf_add_f32: out = a + b
+ *     (out may be one of the inputs exactly). */
+int gguf_rmsnorm_prep_f32(const float* v, const float* norm_w, float* vw, float* ss, int64_t n,
+                          hipStream_t stream);
+int gguf_rmsnorm_f32(const float* v, const float* norm_w, float eps, float* out, int64_t n,
+                     hipStream_t stream);
+int gguf_swiglu_f32(const float* g, const float* u, float* out, int64_t n, hipStream_t stream);
+int gguf_add_f32(const float* a, const float* b, float* out, int64_t n, hipStream_t stream);
+
 /* --- prefill: fused dequant x matrix (small batch, MFMA) ------------------ */
 
 /* Y[n, r] = sum_k X[n, k] * w[r, k] for n < n_tokens. X bf16 row-major

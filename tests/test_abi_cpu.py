@@ -213,3 +213,69 @@ def test_batch_validation():
     bad = (g.GemvEntry * 2)(_entry(A, B, C, 4, 256, g.TYPE_Q4_K, 0),
                             _entry(A + 4096, B, C, 4, 256, g.TYPE_Q4_K, 0))
     assert f(ctypes.cast(bad, ctypes.c_void_p), 2, None) == g.ERR_ALIAS
+
+
+# ---------------------------------------------------- fused epilogues (batch_ep)
+
+def _pair_entries(type_id=None, cols=2048, rows=64):
+    """gate/up entries at fake, non-overlapping addresses."""
+    t = g.TYPE_Q4_K if type_id is None else type_id
+    arr = (g.GemvEntry * 2)()
+    arr[0] = g.GemvEntry(0x1000000, 0x5000000, 0x6000000, rows, cols, t, 0, (0, 0))
+    arr[1] = g.GemvEntry(0x2000000, 0x5000000, 0x7000000, rows, cols, t, 0, (0, 0))
+    return arr
+
+
+def _ep(**kw):
+    e = g.GemvEpEntry()
+    for k, v in kw.items():
+        setattr(e, k, v)
+    return e
+
+
+def _run_ep(arr, eps):
+    ep = (g.GemvEpEntry * len(eps))(*eps)
+    return g.lib().gguf_qmatvec_batch_ep(ctypes.cast(arr, ctypes.c_void_p), ctypes.cast(ep, ctypes.c_void_p),
+                                         len(eps), None)
+
+
+def test_batch_ep_validation():
+    ACT = 0x8000000
+    ok = [_ep(pair=1, act=ACT), _ep(pair=2, act=ACT)]
+    assert _run_ep(_pair_entries(), ok) == g.ERR_DEVICE          # valid: fails only at the device check
+    assert _run_ep(_pair_entries(), [_ep(pair=1, act=ACT), _ep()]) == g.ERR_SHAPE       # partner missing
+    assert _run_ep(_pair_entries(), [_ep(pair=1, act=ACT), _ep(pair=2, act=ACT + 64)]) == g.ERR_SHAPE
+    assert _run_ep(_pair_entries(), [_ep(pair=3, act=ACT), _ep()]) == g.ERR_SHAPE
+    assert _run_ep(_pair_entries(), [_ep(pair=1), _ep(pair=2)]) == g.ERR_NULL          # no act
+    assert _run_ep(_pair_entries(), [_ep(pair=1, act=ACT + 2), _ep(pair=2, act=ACT + 2)]) == g.ERR_ALIGN
+    assert _run_ep(_pair_entries(), [_ep(pair=1, act=0x6000000), _ep(pair=2, act=0x6000000)]) == g.ERR_ALIAS
+    assert _run_ep(_pair_entries(), [_ep(norm_w=0x9000000), _ep()]) == g.ERR_NULL
+    assert _run_ep(_pair_entries(), [_ep(norm_w=0x9000000, norm_out=0x7000000, ss_out=0xA000000),
+                                     _ep()]) == g.ERR_ALIAS                              # over the other y
+    assert _run_ep(_pair_entries(), [_ep(scale_ss=0xB000000, scale_n=0), _ep()]) == g.ERR_SHAPE
+    assert _run_ep(_pair_entries(), [_ep(scale_ss=0xB000000, scale_n=4, eps=-1.0), _ep()]) == g.ERR_SHAPE
+    assert _run_ep(_pair_entries(), [_ep(scale_ss=0xB000000, scale_n=4, eps=float("nan")), _ep()]) == g.ERR_SHAPE
+    assert _run_ep(_pair_entries(), [_ep(residual=0xC000001), _ep()]) == g.ERR_ALIGN
+    assert _run_ep(_pair_entries(), [_ep(residual=0x6000000 + 4), _ep()]) == g.ERR_ALIAS   # partial overlap with y
+    assert _run_ep(_pair_entries(), [_ep(residual=0x6000000), _ep()]) == g.ERR_DEVICE      # y itself: in place
+    # Q8_0 rows that are not whole 256-weight chunks take the row-wise kernel, which has no epilogue
+    assert _run_ep(_pair_entries(g.TYPE_Q8_0, cols=96), [_ep(residual=0xC000000), _ep()]) == g.ERR_SHAPE
+    assert _run_ep(_pair_entries(g.TYPE_Q8_0, cols=96), [_ep(), _ep()]) == g.ERR_DEVICE
+
+
+def test_layer_ops_validation():
+    L = g.lib()
+    assert L.gguf_rmsnorm_prep_f32(None, B, C, 0x40000, 64, None) == g.ERR_NULL
+    assert L.gguf_rmsnorm_prep_f32(A, B, C + 4, 0x40000, 64, None) == g.ERR_ALIGN
+    assert L.gguf_rmsnorm_prep_f32(A, B, A, 0x40000, 64, None) == g.ERR_ALIAS
+    assert L.gguf_rmsnorm_prep_f32(A, B, C, 0x40000, 0, None) == g.OK
+    assert L.gguf_rmsnorm_prep_f32(A, B, C, 0x40000, 64, None) == g.ERR_DEVICE
+    assert L.gguf_rmsnorm_f32(A, B, ctypes.c_float(-1.0), C, 64, None) == g.ERR_SHAPE
+    assert L.gguf_rmsnorm_f32(A, B, ctypes.c_float(1e-6), A + 16, 64, None) == g.ERR_ALIAS
+    assert L.gguf_rmsnorm_f32(A, B, ctypes.c_float(1e-6), C, 64, None) == g.ERR_DEVICE
+    for f in (L.gguf_swiglu_f32, L.gguf_add_f32):
+        assert f(A, B, None, 64, None) == g.ERR_NULL
+        assert f(A, B, A + 16, 64, None) == g.ERR_ALIAS       # partial overlap
+        assert f(A, B, A, 64, None) == g.ERR_DEVICE           # in place is allowed
+        assert f(A, B, C, -1, None) == g.ERR_SHAPE
+        assert f(A, B, C, 0, None) == g.OK
