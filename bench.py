@@ -18,7 +18,9 @@ sample of the same workload, and labelled extras: the pass time distribution,
 an unordered upper bound (all GEMVs of the pass as one step), the bf16
 MFMA prefill pass over the same 36-layer weights (N = 512 tokens), and the
 fp32 small-batch passes (the same 253 matrices times 8, 32 and 64 activation
-vectors), and batch-1 GEMV passes over the same shapes stored as Q4_0 and Q6_K.
+vectors), batch-1 GEMV passes over the same shapes stored as Q4_0 and Q6_K,
+and the 36 layers as decode layers with RMSN, SiLU(gate) * up and the
+residual adds fused into the GEMVs against the same steps as separate kernels.
 
     python bench.py --copy-calibration
 
@@ -66,6 +68,8 @@ def parse():
                     help="copy 1 GiB device to device three times and exit")
     ap.add_argument("--small-batch-only", action="store_true",
                     help="only the small-batch passes (8, 32, 64 tokens) over the weight stream")
+    ap.add_argument("--fused-only", action="store_true",
+                    help="only the fused / unfused decode-layer passes")
     ap.add_argument("--other-types-only", action="store_true",
                     help="only the Q4_0 and Q6_K GEMV passes")
     ap.add_argument("--prefill-only", action="store_true",
@@ -245,6 +249,89 @@ def small_batch_pass(torch, g, synth, entries, stream, n_tokens, reps=5):
                          "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}}
 
 
+def fused_layer_pass(torch, g, synth, entries, stream, reps=10):
+    """The 36 resident Q4_K layers as decode layers with the neighbouring steps
+    (RMSN before q/k/v and before gate/up, SiLU(gate) * up, the two residual
+    adds) fused into the GEMVs (4 launches per layer) and, for comparison, as
+    separate kernels between plain GEMV launches (9 per layer). The attention
+    result, out of scope, is stood in by the q projection's output. Both as
+    HIP graphs; returns the labelled record."""
+    dev = "cuda:0"
+    H, F, KV, EPS = synth.HIDDEN, synth.FFN, synth.KV, 1e-6
+    q4 = [e for e in entries if e[0] == g.TYPE_Q4_K]
+    layers = [dict(zip(("q", "k", "v", "o", "gate", "up", "down"), (e[1] for e in q4[7 * i:7 * i + 7])))
+              for i in range(len(q4) // 7)]
+    gen = torch.Generator().manual_seed(80)
+    norms = [(torch.rand(H, generator=gen) + 0.5).to(dev) for _ in range(2 * len(layers))]
+    e_ = lambda n: torch.empty(n, dtype=torch.float32, device=dev)
+    h0 = torch.randn(H, generator=gen).to(dev)
+    # fused
+    hw, ss = e_(H), e_(H // 64)
+    ents, eps, h = [], [], h0
+    for li, L in enumerate(layers):
+        st = 4 * li
+        q, k, v = e_(H), e_(KV), e_(KV)
+        h1, hw2, ss2, gg, uu, act = e_(H), e_(H), e_(H // 64), e_(F), e_(F), e_(F)
+        h2, hw3, ss3 = e_(H), e_(H), e_(H // 64)
+        for name, y in (("q", q), ("k", k), ("v", v)):
+            ents.append((g.TYPE_Q4_K, L[name], hw, y, st))
+            eps.append({"scale_ss": ss, "eps": EPS})
+        ents.append((g.TYPE_Q4_K, L["o"], q, h1, st + 1))
+        eps.append({"residual": h, "norm_w": norms[2 * li + 1], "norm_out": hw2, "ss_out": ss2})
+        ents.append((g.TYPE_Q4_K, L["gate"], hw2, gg, st + 2))
+        eps.append({"scale_ss": ss2, "eps": EPS, "pair": 1, "act": act})
+        ents.append((g.TYPE_Q4_K, L["up"], hw2, uu, st + 2))
+        eps.append({"scale_ss": ss2, "eps": EPS, "pair": 2, "act": act})
+        nxt = norms[2 * (li + 1)] if li + 1 < len(layers) else norms[0]
+        ents.append((g.TYPE_Q4_K, L["down"], act, h2, st + 3))
+        eps.append({"residual": h1, "norm_w": nxt, "norm_out": hw3, "ss_out": ss3})
+        h, hw, ss = h2, hw3, ss3
+    fb = g.GemvBatch(ents, eps)
+    hw0, ss0 = ents[0][2], eps[0]["scale_ss"]
+
+    def fused():
+        g.gguf_rmsnorm_prep_f32(h0, norms[0], hw0, ss0, stream=stream)
+        g.gguf_qmatvec_batch(fb, stream)
+
+    # unfused: plain grouped GEMV steps with standalone steps between them
+    plan, h = [], h0
+    for li, L in enumerate(layers):
+        x1, q, k, v, o, h1 = e_(H), e_(H), e_(KV), e_(KV), e_(H), e_(H)
+        x2, gg, uu, act, d, h2 = e_(H), e_(F), e_(F), e_(F), e_(H), e_(H)
+        qkv = g.GemvBatch([(g.TYPE_Q4_K, L["q"], x1, q, 0), (g.TYPE_Q4_K, L["k"], x1, k, 0),
+                           (g.TYPE_Q4_K, L["v"], x1, v, 0)])
+        ob = g.GemvBatch([(g.TYPE_Q4_K, L["o"], q, o, 0)])
+        gu = g.GemvBatch([(g.TYPE_Q4_K, L["gate"], x2, gg, 0), (g.TYPE_Q4_K, L["up"], x2, uu, 0)])
+        db = g.GemvBatch([(g.TYPE_Q4_K, L["down"], act, d, 0)])
+        plan.append((h, x1, norms[2 * li], qkv, ob, o, h1, x2, norms[2 * li + 1], gu, gg, uu, act, db, d, h2))
+        h = h2
+
+    def unfused():
+        for (hh, x1, n1, qkv, ob, o, h1, x2, n2, gu, gg, uu, act, db, d, h2) in plan:
+            g.gguf_rmsnorm_f32(hh, n1, EPS, x1, stream=stream)
+            g.gguf_qmatvec_batch(qkv, stream)
+            g.gguf_qmatvec_batch(ob, stream)
+            g.gguf_add_f32(hh, o, h1, stream=stream)
+            g.gguf_rmsnorm_f32(h1, n2, EPS, x2, stream=stream)
+            g.gguf_qmatvec_batch(gu, stream)
+            g.gguf_swiglu_f32(gg, uu, act, stream=stream)
+            g.gguf_qmatvec_batch(db, stream)
+            g.gguf_add_f32(h1, d, h2, stream=stream)
+
+    out = {"label": f"{len(layers)} decode layers (Q4_K, SmolLM3-3B shapes) with RMSN, SiLU(gate)*up "
+                    "and the residual adds; attention stood in by q (not measured); HIP graphs",
+           "layers": len(layers)}
+    wbytes = sum(e[1].numel() for e in q4)
+    for name, fn, launches in (("fused", fused, 4 * len(layers) + 1), ("unfused", unfused, 9 * len(layers))):
+        graph = capture(torch, fn, stream)
+        t = time_replays(torch, graph, stream, reps)
+        ms = sorted(t)[len(t) // 2]
+        out[name] = {"ms_per_pass": round(ms, 4), "launches": launches,
+                     "weight_GBps": round(wbytes / (ms / 1e3) / 1e9, 1)}
+        del graph
+    return out
+
+
 def other_types_pass(torch, g, synth, reps=5):
     """Batch-1 GEMV passes over the 36-layer shapes stored as Q4_0 and as Q6_K:
     one layer's seven tensors generated per type, cloned to 36 distinct device
@@ -351,6 +438,9 @@ def main():
     torch.cuda.synchronize()
     if args.prefill_only:
         print(json.dumps(prefill_pass(torch, g, synth, entries, meta, stream)), flush=True)
+        return
+    if args.fused_only:
+        print(json.dumps(fused_layer_pass(torch, g, synth, entries, stream)), flush=True)
         return
     if args.other_types_only:
         print(json.dumps(other_types_pass(torch, g, synth)), flush=True)
@@ -461,6 +551,7 @@ def main():
     rec["prefill"] = prefill_pass(torch, g, synth, entries, meta, stream)
     rec["small_batch"] = [small_batch_pass(torch, g, synth, entries, stream, n)
                           for n in SMALL_BATCH_TOKENS]
+    rec["fused_layers"] = fused_layer_pass(torch, g, synth, entries, stream)
     rec["other_types"] = other_types_pass(torch, g, synth)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline()

@@ -327,10 +327,12 @@ __device__ __forceinline__ float wave_sum_fixed(float v) {
 }
 
 // v: this lane's final sum for row row0 + lane (lanes >= valid hold garbage).
-// Called by the whole wave (wave-uniform control flow).
+// Called by the whole wave (wave-uniform control flow). kEp false: plain store
+// (the launch has no epilogue; nothing of it is compiled in).
+template <bool kEp>
 __device__ __forceinline__ void finish_rows(const GemvEpilogue& ep, float v, float* __restrict__ y,
                                             int64_t row0, int valid, int rg, int lane) {
-  const int flags = ep.flags;
+  const int flags = kEp ? ep.flags : 0;
   if (flags == 0) {
     if (lane < valid) y[row0 + lane] = v;
     return;
@@ -399,12 +401,13 @@ __device__ __forceinline__ void finish_rows(const GemvEpilogue& ep, float v, flo
 // accesses, which bypass the per-XCD L2's non-coherent lines, and the
 // counter increment is issued only after the partial stores have completed
 // (vmcnt(0)); the last arriver's loads are issued after its increment returned.
+template <bool kEp>
 __device__ __forceinline__ void splitk_finish(float acc, float* __restrict__ y, int64_t rows,
                                               int64_t row0, int valid_rows, int rg, int part,
                                               int P, const SplitK& sk, int lane,
                                               const GemvEpilogue& ep) {
   if (P == 1) {
-    finish_rows(ep, acc, y, row0, valid_rows, rg, lane);
+    finish_rows<kEp>(ep, acc, y, row0, valid_rows, rg, lane);
     return;
   }
   if (lane < valid_rows)
@@ -436,7 +439,7 @@ __device__ __forceinline__ void splitk_finish(float acc, float* __restrict__ y, 
           if (p0 + i < P) s += v[i];
       }
     }
-    finish_rows(ep, s, y, row0, valid_rows, rg, lane);
+    finish_rows<kEp>(ep, s, y, row0, valid_rows, rg, lane);
     if (lane == 0)
       __hip_atomic_store(&sk.counters[rg * kCounterStride], 0, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
@@ -519,7 +522,7 @@ __device__ __forceinline__ void load_group(const GemvGroup& grp, GemvDesc (&dl)[
 }
 
 // Per-wave tasks (each wave one row group x K range). Used for Q8_0.
-template <int kSlots, bool kQ4K>
+template <int kSlots, bool kQ4K, bool kEp>
 __global__ __launch_bounds__(kGemvWaves * 64) void gemv_group_kernel(GemvGroup grp, float* partials,
                                                                     int* counters) {
   constexpr int kChunk = kQ4K ? kQ4KChunk : kQ80Chunk;
@@ -547,7 +550,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_group_kernel(GemvGroup g
     else
       acc = q80_wave_task<kSlots>(D.W, D.x, row_bytes, row0, valid, c0, c1, &slots[wave][0], lane);
     const SplitK sk{partials + D.part_off, counters + (int64_t)D.cnt_off * kCounterStride};
-    splitk_finish(acc, D.y, D.rows, row0, valid, rg, part, P, sk, lane, grp.ep[g]);
+    splitk_finish<kEp>(acc, D.y, D.rows, row0, valid, rg, part, P, sk, lane, grp.ep[g]);
   }
 }
 
@@ -556,6 +559,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_group_kernel(GemvGroup g
 // wave. The waves' 64 partial sums are added in LDS in wave order; a row group
 // whose K is cut into P > 1 ranges (K > kBlockWaves super-blocks) finishes
 // through the split-K hand-off between blocks.
+template <bool kEp>
 __global__ __launch_bounds__(kBlockWaves * 64) void gemv_q4k_block_kernel(GemvGroup grp,
                                                                           float* partials,
                                                                           int* counters) {
@@ -604,7 +608,7 @@ __global__ __launch_bounds__(kBlockWaves * 64) void gemv_q4k_block_kernel(GemvGr
 #pragma unroll
     for (int w = 0; w < kBlockWaves; ++w) s += red[w][lane];
     const SplitK sk{partials + D.part_off, counters + (int64_t)D.cnt_off * kCounterStride};
-    splitk_finish(s, D.y, D.rows, row0, valid, rg, part, P, sk, lane, grp.ep[g]);
+    splitk_finish<kEp>(s, D.y, D.rows, row0, valid, rg, part, P, sk, lane, grp.ep[g]);
   }
 }
 

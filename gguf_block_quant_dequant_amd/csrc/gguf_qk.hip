@@ -324,16 +324,27 @@ static int launch_group(int type, const gguf_qk_gemv* const* v, const GemvEpilog
   int* counters = const_cast<int*>(scratch->counters);
   const int64_t blocks = type == GGUF_QK_TYPE_Q4_K ? tasks : (tasks + kGemvWaves - 1) / kGemvWaves;
   if (blocks > INT32_MAX) return GGUF_QK_ERR_LIMIT;
+  bool ep = false;   // any epilogue in this launch: the kernel variant that has them
+  for (int i = 0; i < n; ++i) ep = ep || grp.ep[i].flags != 0;
   if (type == GGUF_QK_TYPE_Q4_K) {
-    hipLaunchKernelGGL(gemv_q4k_block_kernel, dim3((unsigned)blocks), dim3(kBlockWaves * 64), 0,
-                       stream, grp, partials, counters);
+    if (ep)
+      hipLaunchKernelGGL(gemv_q4k_block_kernel<true>, dim3((unsigned)blocks), dim3(kBlockWaves * 64), 0,
+                         stream, grp, partials, counters);
+    else
+      hipLaunchKernelGGL(gemv_q4k_block_kernel<false>, dim3((unsigned)blocks), dim3(kBlockWaves * 64),
+                         0, stream, grp, partials, counters);
     return launch_status();
   }
   const dim3 grid((unsigned)blocks), block(kGemvWaves * 64);
-  if (tuning().q80_slots == 2)
-    hipLaunchKernelGGL((gemv_group_kernel<2, false>), grid, block, 0, stream, grp, partials, counters);
+  if (ep)
+    hipLaunchKernelGGL((gemv_group_kernel<1, false, true>), grid, block, 0, stream, grp, partials,
+                       counters);
+  else if (tuning().q80_slots == 2)
+    hipLaunchKernelGGL((gemv_group_kernel<2, false, false>), grid, block, 0, stream, grp, partials,
+                       counters);
   else
-    hipLaunchKernelGGL((gemv_group_kernel<1, false>), grid, block, 0, stream, grp, partials, counters);
+    hipLaunchKernelGGL((gemv_group_kernel<1, false, false>), grid, block, 0, stream, grp, partials,
+                       counters);
   return launch_status();
 }
 
