@@ -756,7 +756,7 @@ int gguf_rmsnorm_f32(const float* v, const float* norm_w, float eps, float* out,
   if (n == 0) return GGUF_QK_OK;
   st = current_device(nullptr);
   if (st) return st;
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(1), dim3(256), 0, stream, v, norm_w, eps, out, n);
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(1), dim3(1024), 0, stream, v, norm_w, eps, out, n);
   return launch_status();
 }
 

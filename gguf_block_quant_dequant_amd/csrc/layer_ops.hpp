@@ -42,30 +42,34 @@ __global__ __launch_bounds__(256) void rmsnorm_prep_kernel(const float* __restri
   if (lane == 0) ss[j] = s;
 }
 
-// out = norm_w * v / sqrt(mean(v^2) + eps) for one vector, one block of 256
-// threads: partial sums per 64 elements (as above), added in order.
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ v,
-                                                      const float* __restrict__ w, float eps,
-                                                      float* __restrict__ out, int64_t n) {
-  __shared__ float part[4];
+// out = norm_w * v / sqrt(mean(v^2) + eps) for one vector, one block of 16
+// waves: each wave sums the squares of its 64-element groups (as above) into
+// LDS, thread 0 adds the group sums in order (up to kNormGroups per pass).
+constexpr int kNormGroups = 1024;
+__global__ __launch_bounds__(1024) void rmsnorm_kernel(const float* __restrict__ v,
+                                                       const float* __restrict__ w, float eps,
+                                                       float* __restrict__ out, int64_t n) {
+  __shared__ float part[kNormGroups];
   __shared__ float scale;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t ngroups = (n + 63) / 64;
-  float total = 0.f;   // wave 0 / lane 0 accumulates the group sums in order
-  for (int64_t j0 = 0; j0 < ngroups; j0 += 4) {
-    const int64_t j = j0 + wave, i = j * 64 + lane;
-    const float x = (j < ngroups && i < n) ? v[i] : 0.f;
-    const float s = wave_sum64(square_rounded(x));
-    if (lane == 0) part[wave] = s;
+  float total = 0.f;   // thread 0's running sum
+  for (int64_t g0 = 0; g0 < ngroups; g0 += kNormGroups) {
+    const int gn = (int)((ngroups - g0) < kNormGroups ? (ngroups - g0) : kNormGroups);
+    for (int j = wave; j < gn; j += 16) {
+      const int64_t i = (g0 + j) * 64 + lane;
+      const float s = wave_sum64(square_rounded(i < n ? v[i] : 0.f));
+      if (lane == 0) part[j] = s;
+    }
     __syncthreads();
     if (threadIdx.x == 0)
-      for (int k = 0; k < 4 && j0 + k < ngroups; ++k) total += part[k];
+      for (int j = 0; j < gn; ++j) total += part[j];
     __syncthreads();
   }
   if (threadIdx.x == 0) scale = 1.0f / sqrtf(total * (1.0f / (float)n) + eps);
   __syncthreads();
   const float sc = scale;
-  for (int64_t i = threadIdx.x; i < n; i += 256) out[i] = v[i] * w[i] * sc;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) out[i] = v[i] * w[i] * sc;
 }
 
 __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ g,
