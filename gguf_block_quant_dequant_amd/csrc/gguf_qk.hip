@@ -359,8 +359,18 @@ static int launch_rowwise_q8_0(const gguf_qk_gemv& g, hipStream_t stream) {
 
 // Launches the GEMVs of one step: same-format GEMVs go together, kMaxGroup at
 // a time; each launch follows the previous one on the stream.
+static int launch_other(int type, const void* W, const float* x, float* y, int64_t rows,
+                        int64_t cols, hipStream_t stream);
+
 static int launch_step(const gguf_qk_gemv* list, const GemvEpilogue* eps, int n,
                        const ScratchArea* scratch, hipStream_t stream) {
+  // Q4_0 and Q6_K GEMVs: one launch each (no grouping, no epilogue)
+  for (int i = 0; i < n; ++i) {
+    const gguf_qk_gemv& g = list[i];
+    if ((g.type != GGUF_QK_TYPE_Q4_0 && g.type != GGUF_QK_TYPE_Q6_K) || g.rows == 0) continue;
+    const int st = launch_other(g.type, g.W, g.x, g.y, g.rows, g.cols, stream);
+    if (st) return st;
+  }
   for (int type : {GGUF_QK_TYPE_Q4_K, GGUF_QK_TYPE_Q8_0}) {
     const gguf_qk_gemv* grp[kMaxGroup];
     const GemvEpilogue* ge[kMaxGroup];
@@ -468,7 +478,9 @@ static int make_epilogue(const gguf_qk_gemv* list, const gguf_qk_gemv_ep* ep, in
         overlap(outs[a], outn[a], e.scale_ss, e.scale_ss ? e.scale_n * 4 : 0))
       return GGUF_QK_ERR_ALIAS;
   }
-  if (flags && g.type == GGUF_QK_TYPE_Q8_0 && g.cols % 256) return GGUF_QK_ERR_SHAPE;
+  if (flags && ((g.type == GGUF_QK_TYPE_Q8_0 && g.cols % 256) || g.type == GGUF_QK_TYPE_Q4_0 ||
+                g.type == GGUF_QK_TYPE_Q6_K))
+    return GGUF_QK_ERR_SHAPE;
   out->scale_ss = e.scale_ss;
   out->residual = e.residual;
   out->norm_w = e.norm_w;
@@ -490,7 +502,9 @@ static int batch_common(const gguf_qk_gemv* list, const gguf_qk_gemv_ep* ep, int
   for (int32_t i = 0; i < n; ++i) {
     int64_t wb = 0;
     const gguf_qk_gemv& g = list[i];
-    if (g.type != GGUF_QK_TYPE_Q8_0 && g.type != GGUF_QK_TYPE_Q4_K) return GGUF_QK_ERR_SHAPE;
+    if (g.type != GGUF_QK_TYPE_Q8_0 && g.type != GGUF_QK_TYPE_Q4_K && g.type != GGUF_QK_TYPE_Q4_0 &&
+        g.type != GGUF_QK_TYPE_Q6_K)
+      return GGUF_QK_ERR_SHAPE;
     const int st = check_gemv(g.type, g.W, g.x, g.y, g.rows, g.cols, &wb);
     if (st) return st;
   }
@@ -585,6 +599,9 @@ static int dequant_other(int type, const void* W, float* out, int64_t rows, int6
   return launch_status();
 }
 
+static int launch_other(int type, const void* W, const float* x, float* y, int64_t rows,
+                        int64_t cols, hipStream_t stream);
+
 static int matvec_other(int type, const void* W, const float* x, float* y, int64_t rows,
                         int64_t cols, hipStream_t stream) {
   int64_t wb = 0;
@@ -593,6 +610,11 @@ static int matvec_other(int type, const void* W, const float* x, float* y, int64
   if (rows == 0) return GGUF_QK_OK;
   st = current_device(nullptr);
   if (st) return st;
+  return launch_other(type, W, x, y, rows, cols, stream);
+}
+
+static int launch_other(int type, const void* W, const float* x, float* y, int64_t rows,
+                        int64_t cols, hipStream_t stream) {
   const int64_t per_block = (int64_t)kOtherRows * kOtherWaves;
   const int64_t blocks = (rows + per_block - 1) / per_block;
   if (blocks > INT32_MAX) return GGUF_QK_ERR_LIMIT;

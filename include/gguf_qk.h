@@ -132,7 +132,9 @@ int gguf_qmatvec_q4_k(const void* W, const float* x, float* y, int64_t rows, int
  *
  * Dequant: fp32 [rows x cols], bit-exact (both products are exact in fp32).
  * GEMV: y = W x in fp32 as gguf_qmatvec_q8_0 (any summation order,
- * deterministic). These two types are not accepted by gguf_qmatvec_batch. */
+ * deterministic). In gguf_qmatvec_batch these two types run one launch per
+ * GEMV (a Q4_K_M file keeps some tensors in Q6_K); gguf_qmatvec_batch_ep has
+ * no epilogue for them. */
 int dequant_q4_0(const void* W, float* out, int64_t rows, int64_t cols, hipStream_t stream);
 int dequant_q6_k(const void* W, float* out, int64_t rows, int64_t cols, hipStream_t stream);
 int gguf_qmatvec_q4_0(const void* W, const float* x, float* y, int64_t rows, int64_t cols,
@@ -199,7 +201,8 @@ typedef struct gguf_qk_gemv_ep {
 } gguf_qk_gemv_ep;
 
 /* gguf_qmatvec_batch with an epilogue per entry (ep: n entries, or NULL for
- * none). Entries with epilogues must be Q4_K, or Q8_0 with cols % 256 == 0.
+ * none). Entries with epilogues must be Q4_K, or Q8_0 with cols % 256 == 0
+ * (GGUF_QK_ERR_SHAPE otherwise).
  * Epilogue arrays need 4-byte alignment; their outputs may not overlap any
  * input or output of the step. The fp32 sums of the scale and of ss_out run
  * in fixed orders: results are deterministic. */

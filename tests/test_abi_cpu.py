@@ -66,9 +66,14 @@ def test_row_bytes_other_types():
     assert g.gguf_row_bytes(g.TYPE_Q6_K, 128) == g.ERR_SHAPE
 
 
-def test_batch_rejects_other_types():
+def test_batch_type_checks():
     e = g.GemvEntry(0x10000, 0x20000, 0x30000, 4, 256, g.TYPE_Q6_K, 0)
+    assert g.lib().gguf_qmatvec_batch(ctypes.byref(e), 1, None) == g.ERR_DEVICE   # accepted
+    e = g.GemvEntry(0x10000, 0x20000, 0x30000, 4, 256, 99, 0)
     assert g.lib().gguf_qmatvec_batch(ctypes.byref(e), 1, None) == g.ERR_SHAPE
+    # no fused epilogue for Q4_0 / Q6_K
+    arr = (g.GemvEntry * 1)(g.GemvEntry(0x1000000, 0x5000000, 0x6000000, 64, 2048, g.TYPE_Q6_K, 0, (0, 0)))
+    assert _run_ep(arr, [_ep(residual=0xC000000)]) == g.ERR_SHAPE
 
 
 def test_row_bytes():

@@ -117,3 +117,40 @@ def test_gemv_integer_cases_are_exact():
     x = rng.integers(-8, 9, cols).astype(np.float32)
     y = host(g.gguf_qmatvec_q6_k(dev(w6), dev(x), rows=rows, cols=cols))
     assert np.array_equal(y.astype(np.float64), oracle.dequant_q6_k_f64(w6, rows, cols) @ x.astype(np.float64))
+
+
+def test_mixed_types_in_one_decode_batch():
+    """A Q4_K_M-like step list: q/k/o/gate/up Q4_K, v and down Q6_K, an extra
+    Q4_0 projection, the head Q8_0; stages in order, each GEMV against the
+    oracle, a later stage reading an earlier stage's output."""
+    rng = np.random.default_rng(44)
+    H, F, KV = 2048, 2816, 512
+    mats = {"q": ("q4_k", H, H), "k": ("q4_k", KV, H), "v": ("q6_k", KV, H), "o": ("q4_k", H, H),
+            "gate": ("q4_k", F, H), "up": ("q4_k", F, H), "down": ("q6_k", H, F), "extra": ("q4_0", 300, H),
+            "head": ("q8_0", 4000, H)}
+    gen = {"q4_k": (synth.q4_k_weights, oracle.dequant_q4_k_f32, g.TYPE_Q4_K),
+           "q6_k": (synth.q6_k_weights, oracle.dequant_q6_k_f32, g.TYPE_Q6_K),
+           "q4_0": (synth.q4_0_weights, oracle.dequant_q4_0_f32, g.TYPE_Q4_0),
+           "q8_0": (synth.q8_0_weights, oracle.dequant_q8_0_f32, g.TYPE_Q8_0)}
+    W, W32, Y = {}, {}, {}
+    for name, (fmt, r, c) in mats.items():
+        fn, ref, _ = gen[fmt]
+        w = fn(rng, r, c)
+        W[name], W32[name] = dev(w), ref(w, r, c)
+        Y[name] = torch.empty(r, dtype=torch.float32, device=DEV)
+    x = dev(synth.activations_f32(rng, H))
+    t = lambda n: gen[mats[n][0]][2]
+    ents = [(t("q"), W["q"], x, Y["q"], 0), (t("k"), W["k"], x, Y["k"], 0), (t("v"), W["v"], x, Y["v"], 0),
+            (t("extra"), W["extra"], x, Y["extra"], 0),
+            (t("o"), W["o"], Y["q"], Y["o"], 1),
+            (t("gate"), W["gate"], Y["o"], Y["gate"], 2), (t("up"), W["up"], Y["o"], Y["up"], 2),
+            (t("down"), W["down"], Y["gate"], Y["down"], 3),
+            (t("head"), W["head"], Y["down"], Y["head"], 4)]
+    say("mixed batch", len(ents))
+    g.gguf_qmatvec_batch(g.GemvBatch(ents))
+    inputs = {"q": x, "k": x, "v": x, "extra": x, "o": Y["q"], "gate": Y["o"], "up": Y["o"],
+              "down": Y["gate"], "head": Y["down"]}
+    for name in mats:
+        xin = host(inputs[name])
+        e, ok = oracle.floored_rel_err(host(Y[name]), oracle.matvec_f64(W32[name], xin))
+        assert ok and e <= TOL_F32, (name, e)
