@@ -13,7 +13,7 @@ are resident in HBM before timing starts.
 
 Prints one JSON line: weight-stream GB/s (whole pass), % of the 8 TB/s HBM
 peak, tokens/s-equivalent (1 / pass time), a roofline record for the
-dominant kernel (the Q4_K block-task GEMV), the CPU oracle timed on a bounded
+dominant kernel (the Q4_K lanes-along-K GEMV), the CPU oracle timed on a bounded
 sample of the same workload, and labelled extras: the pass time distribution,
 an unordered upper bound (all GEMVs of the pass as one step), the bf16
 MFMA prefill pass over the same 36-layer weights (N = 512 tokens), and the
@@ -43,11 +43,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 BF16_DENSE_PEAK_TFLOPS = 2500.0
-DOMINANT_KERNEL = "gemv_q4k_block_kernel"
-KERNEL_SOURCES = ["gguf_block_quant_dequant_amd/csrc/gemv.hpp",
+DOMINANT_KERNEL = "gemv_q4k_lk_kernel"
+KERNEL_SOURCES = ["gguf_block_quant_dequant_amd/csrc/gemv_lk.hpp",
                   "gguf_block_quant_dequant_amd/csrc/device_common.hpp"]
 SMALL_BATCH_TOKENS = (8, 32, 64)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_q4k_block_kernel_decode_stream_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_q4k_lk_kernel_decode_stream_traffic.md")
 
 
 def log(*a):
@@ -503,9 +503,11 @@ def main():
         print(json.dumps(rec), flush=True)
         return
 
-    # Roofline of the dominant kernel: the Q4_K block-task GEMV launches of the
-    # pass (all stages but the head) replayed alone as a graph, so that the
-    # average launch duration is the kernel's own, back to back as in the pass.
+    # Roofline of the dominant kernel: the Q4_K lanes-along-K GEMV launches of
+    # the pass (all stages but the head; the down stage's long rows run the
+    # same kernel family's long-row variant) replayed alone as a graph, so that
+    # the average launch duration is the kernels' own, back to back as in the
+    # pass.
     q4k_entries = [e for e in entries if e[0] == g.TYPE_Q4_K]
     q4k_launches = sum(1 for (layer, names, b) in meta if layer >= 0)
     q4k_batch = g.GemvBatch(q4k_entries)

@@ -15,6 +15,7 @@ constexpr int kWave = 64;
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 
 #define GQK_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define GQK_GLOBAL __attribute__((address_space(1)))
 
 // fp16 bit pattern (low 16 bits) -> fp32. v_cvt_f32_f16 is exact for every
 // finite half, subnormals included (fp16 denormals are enabled in the kernel

@@ -1,0 +1,471 @@
+// Batch-1 Q4_K GEMV with lanes along K, for rows of at most 16 super-blocks
+// (K = 256, 512, 1024, 2048 or 4096): the decode stages whose rows are short.
+//
+// Work mapping: a row is cut into U = K / 64 "quarters" (a quarter is 64
+// weights: sub-blocks 2g and 2g + 1 of a super-block, whose quants share the
+// 32-byte nibble group g). Lane l takes quarter l mod U of row l / U, so a wave
+// covers 64 / U whole rows per step ("row step") and walks a contiguous range
+// of row steps. A lane's quarter is the same in every step, so its 64
+// activations and their two sub-block sums are formed once, held in VGPRs,
+// and reused for every row the wave visits; the block stages x in LDS once
+// (padded so that the lanes' 256-byte slices start on different banks), so x
+// crosses the L1 once per block instead of once per lane. Weight bytes go straight
+// from HBM to registers: per step a lane loads the super-block header (16 B)
+// and its 32 bytes of quants with three 16-byte loads, and the loads of the
+// next kLkDepth - 1 steps are in flight while a step computes. Consecutive
+// lanes read consecutive bytes of a row, and a wave's rows are consecutive, so
+// a wave streams one contiguous byte range. Each row's U lane sums are added
+// by a fixed butterfly (DPP within 16 lanes, then lane shuffles), so results
+// do not depend on timing, and no partial sum leaves the wave: there is no
+// split-K hand-off and no scratch.
+//
+// Every block of the launch belongs to one GEMV of the group (its four waves
+// share the GEMV's x); the host gives each GEMV blocks in proportion to its
+// rows, each block an equal share of that GEMV's row steps, and each wave a
+// quarter of its block's.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace gqk {
+
+constexpr int kLkWaves = 4;   // waves per block
+constexpr int kLkMaxGroup = 4;
+
+// One GEMV of a launch (64 bytes, read as one 16-dword scalar load). Its row
+// steps are cut among its blocks by the host: block lb (counted from
+// block_begin) takes q + (lb < r) consecutive steps starting at
+// lb q + min(lb, r).
+struct LkDesc {
+  const uint8_t* W;
+  const float* x;
+  float* y;
+  int rows;
+  int block_begin;   // first block of this GEMV in the launch
+  int q;             // row steps per block
+  int r;             // blocks that take one step more
+  int nsb;           // super-blocks per row
+  int pad[5];
+};
+static_assert(sizeof(LkDesc) == 64, "one 16-dword load per descriptor");
+
+struct LkGroup {
+  LkDesc d[kLkMaxGroup];
+  int n;
+  int total_blocks;
+};
+
+// The block's share of a launch: its GEMV (pointers, rows, super-blocks per
+// row) and the wave's row steps [st0, st0 + n).
+struct LkBlock {
+  const GQK_GLOBAL uint8_t* W;
+  const GQK_GLOBAL float* x;
+  GQK_GLOBAL float* y;
+  int64_t rows;
+  int64_t st0;
+  int n;
+  int nsb;
+};
+
+// The kernel arguments sit in memory that is cold at every launch: all four
+// descriptors and the count are read in one batch of scalar loads (the empty
+// asm consumes every word, so no load can be deferred behind a branch on
+// another), and the block's own descriptor is picked with selects. The
+// pointers come through the asm, which hides that they are global ones: they
+// are cast back, or every access would become a flat access (counted against
+// the LDS counter too, so each LDS wait would also wait for the weight loads).
+__device__ __forceinline__ LkBlock lk_block(const LkGroup& grp, int b, int wave) {
+  typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+  u32x16 dw[kLkMaxGroup];
+#pragma unroll
+  for (int k = 0; k < kLkMaxGroup; ++k) dw[k] = *reinterpret_cast<const u32x16*>(&grp.d[k]);
+  int ng = grp.n;
+  asm volatile("" : "+s"(dw[0]), "+s"(dw[1]), "+s"(dw[2]), "+s"(dw[3]), "+s"(ng));
+  LkDesc dd[kLkMaxGroup];
+#pragma unroll
+  for (int k = 0; k < kLkMaxGroup; ++k) dd[k] = __builtin_bit_cast(LkDesc, dw[k]);
+  const int g = (ng > 1 && b >= dd[1].block_begin) + (ng > 2 && b >= dd[2].block_begin) +
+                (ng > 3 && b >= dd[3].block_begin);
+  auto pick = [g](auto a0, auto a1, auto a2, auto a3) {
+    return g == 0 ? a0 : g == 1 ? a1 : g == 2 ? a2 : a3;
+  };
+  LkBlock o;
+  o.W = (const GQK_GLOBAL uint8_t*)pick(dd[0].W, dd[1].W, dd[2].W, dd[3].W);
+  o.x = (const GQK_GLOBAL float*)pick(dd[0].x, dd[1].x, dd[2].x, dd[3].x);
+  o.y = (GQK_GLOBAL float*)pick(dd[0].y, dd[1].y, dd[2].y, dd[3].y);
+  o.rows = pick(dd[0].rows, dd[1].rows, dd[2].rows, dd[3].rows);
+  o.nsb = pick(dd[0].nsb, dd[1].nsb, dd[2].nsb, dd[3].nsb);
+  const int lb = b - pick(dd[0].block_begin, dd[1].block_begin, dd[2].block_begin, dd[3].block_begin);
+  const int q = pick(dd[0].q, dd[1].q, dd[2].q, dd[3].q);
+  const int r = pick(dd[0].r, dd[1].r, dd[2].r, dd[3].r);
+  const int bn = q + (lb < r ? 1 : 0);
+  const int bs0 = lb * q + (lb < r ? lb : r);
+  o.st0 = bs0 + ((wave * bn) >> 2);
+  o.n = (((wave + 1) * bn) >> 2) - ((wave * bn) >> 2);
+  return o;
+}
+
+// d * sc and dmin * m of the two sub-blocks 2 gq and 2 gq + 1 of a Q4_K
+// super-block header (h0 = d | dmin << 16, h1..h3 = scale bytes S[0..11]);
+// d * sc comes out multiplied by 512 to undo the q / 512 of the nibble
+// conversion (exact: a power of two).
+//   j < 4 : sc = S[j] & 63,  m = S[j+4] & 63
+//   j >= 4: sc = (S[j+4] & 15) | ((S[j-4] >> 6) << 4)
+//           m  = (S[j+4] >> 4) | ((S[j]   >> 6) << 4)
+// Both sub-blocks of the pair have the same j / 4 and their bytes sit in the
+// same half of each scale word (t0 = 2 (gq & 1)): sh = 16 (gq & 1), and
+// hi_mask is all ones for gq >= 2 (j >= 4), else zero; both are per lane and
+// the two forms are blended without a branch.
+__device__ __forceinline__ void q4k_pair_scales(uint32_t h0, uint32_t h1, uint32_t h2, uint32_t h3,
+                                                uint32_t sh, uint32_t hi_mask, float& dsc0,
+                                                float& dsc1, float& dmm0, float& dmm1) {
+  const float d512 = half_lo(h0) * 512.0f;
+  const float dmin = half_hi(h0);
+  const uint32_t a = (h1 >> sh) & 0xFFFFu;   // S[t0], S[t0 + 1]
+  const uint32_t b = (h2 >> sh) & 0xFFFFu;   // S[t0 + 4], S[t0 + 5]
+  const uint32_t c = (h3 >> sh) & 0xFFFFu;   // S[t0 + 8], S[t0 + 9]
+  const uint32_t sc_hi = (c & 0x0F0Fu) | ((a >> 2) & 0x3030u);
+  const uint32_t m_hi = ((c >> 4) & 0x0F0Fu) | ((b >> 2) & 0x3030u);
+  const uint32_t sc = (sc_hi & hi_mask) | (a & 0x3F3Fu & ~hi_mask);
+  const uint32_t m = (m_hi & hi_mask) | (b & 0x3F3Fu & ~hi_mask);
+  dsc0 = d512 * ubyte0(sc);
+  dsc1 = d512 * ubyte1(sc);
+  dmm0 = dmin * ubyte0(m);
+  dmm1 = dmin * ubyte1(m);
+}
+
+// A DPP move of a float (bound_ctrl set: lanes without a source read 0).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float s) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), kCtrl, 0xF, 0xF, true));
+}
+
+// Sum over each aligned segment of kU lanes (kU = 4 .. 64) in a fixed order.
+// Lane kU - 1 of each segment ends with the segment's sum (for kU <= 16 every
+// lane of the segment does). For kU >= 32 the 16-lane row sums are joined
+// with row broadcasts: row_bcast:15 adds row 2k's sum into row 2k + 1, and
+// row_bcast:31 adds lane 31 (rows 0 + 1) into rows 2 and 3.
+template <int kU>
+__device__ __forceinline__ float lk_segment_sum(float v) {
+  v += dpp_f32<0xB1>(v);                 // quad_perm 1,0,3,2
+  v += dpp_f32<0x4E>(v);                 // quad_perm 2,3,0,1
+  if constexpr (kU == 8) v += dpp_f32<0x141>(v);   // row_half_mirror
+  if constexpr (kU >= 16) {
+    v += dpp_f32<0x124>(v);              // row_ror:4
+    v += dpp_f32<0x128>(v);              // row_ror:8
+  }
+  if constexpr (kU >= 32)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
+  if constexpr (kU >= 64)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
+  return v;
+}
+
+typedef uint32_t lk_u32x4 __attribute__((ext_vector_type(4)));
+typedef float lk_f32x4 __attribute__((ext_vector_type(4)));
+
+struct LkLoad {
+  lk_u32x4 h, qa, qb;
+};
+
+template <int kNsb, int kDepth>
+__global__ __launch_bounds__(kLkWaves * 64) void gemv_q4k_lk_kernel(LkGroup grp) {
+  constexpr int kU = 4 * kNsb;                 // lanes per row
+  constexpr int kRps = 64 / kU;                // rows per step
+  constexpr int kK = 256 * kNsb;
+  constexpr uint32_t kRowBytes = (uint32_t)kNsb * kQ4KBlockBytes;
+  constexpr int kXF4 = kK / 4;                 // float4 of x
+  static_assert(kU >= 4 && kU <= 64 && 64 % kU == 0, "rows of 1 to 16 super-blocks");
+  // x in LDS with 4 floats of padding after every 64: the slice of lane u
+  // starts at float 68 u, i.e. on bank 4 u mod 32 (16-byte reads conflict-free)
+  __shared__ __attribute__((aligned(16))) float xl[kK + kK / 16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = (int)blockIdx.x;
+  const LkBlock B = lk_block(grp, b, wave);
+  const GQK_GLOBAL uint8_t* const W = B.W;
+  const GQK_GLOBAL float* const x = B.x;
+  GQK_GLOBAL float* const y = B.y;
+  const int64_t rows = B.rows;
+  const int64_t st0 = B.st0;
+  const int n = B.n;
+
+  const int u = lane % kU;
+  const int rsub = lane / kU;
+  const int s = u >> 2, gq = u & 3;
+  const uint32_t hoff = (uint32_t)s * kQ4KBlockBytes;
+  const uint32_t qoff = 16u + 32u * (uint32_t)gq;
+  const uint32_t sh = 16u * (uint32_t)(gq & 1);
+  const uint32_t hi_mask = gq >= 2 ? 0xFFFFFFFFu : 0u;
+
+  // x: every thread loads its float4s first ...
+  constexpr int kXIt = (kXF4 + kLkWaves * 64 - 1) / (kLkWaves * 64);
+  lk_f32x4 xg[kXIt];
+#pragma unroll
+  for (int j = 0; j < kXIt; ++j) {
+    const int i = tid + j * kLkWaves * 64;
+    if (kXF4 % (kLkWaves * 64) == 0 || i < kXF4) xg[j] = reinterpret_cast<const GQK_GLOBAL lk_f32x4*>(x)[i];
+  }
+
+  // ... then the weight loads of the first kDepth steps. A wave's steps are
+  // consecutive rows: step st reads rows [st kRps, st kRps + kRps) at base
+  // W + st kRps kRowBytes plus a 32-bit lane offset. Loads for steps past the
+  // wave's last re-read that step's bytes (every step issues the same loads,
+  // so the in-order load counter stays exact), and rows past the matrix
+  // re-read its last row; neither is ever stored. A wave without steps
+  // (n = 0) re-reads step max(st0 - 1, 0), which exists.
+  const int64_t last = st0 + n - 1 > 0 ? st0 + n - 1 : 0;
+  auto issue = [&](int64_t st, LkLoad& L) {
+    st = st < last ? st : last;
+    const int64_t r0 = st * kRps;
+    const int64_t lim = rows - 1 - r0;
+    const uint32_t rr = lim < kRps - 1 ? (uint32_t)((int64_t)rsub < lim ? rsub : lim) : (uint32_t)rsub;
+    const uint32_t off = rr * kRowBytes + hoff;
+    const GQK_GLOBAL uint8_t* base = W + r0 * (int64_t)kRowBytes;
+    L.h = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + off);
+    L.qa = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + (off + qoff));
+    L.qb = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + (off + qoff + 16));
+  };
+  LkLoad ring[kDepth];
+#pragma unroll
+  for (int p = 0; p < kDepth; ++p) issue(st0 + p, ring[p]);
+
+#pragma unroll
+  for (int j = 0; j < kXIt; ++j) {
+    const int i = tid + j * kLkWaves * 64;
+    if (kXF4 % (kLkWaves * 64) == 0 || i < kXF4)
+      *reinterpret_cast<lk_f32x4*>(&xl[4 * i + (i >> 4) * 4]) = xg[j];
+  }
+  __syncthreads();
+  if (n <= 0) return;
+
+  float xv[64];
+  {
+    const float4* xp = reinterpret_cast<const float4*>(&xl[68 * u]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float4 t = xp[i];
+      xv[4 * i + 0] = t.x;
+      xv[4 * i + 1] = t.y;
+      xv[4 * i + 2] = t.z;
+      xv[4 * i + 3] = t.w;
+    }
+  }
+  float xs0 = 0.f, xs1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    xs0 += xv[i];
+    xs1 += xv[32 + i];
+  }
+
+  // Step i: the dot products of the lane's 64 weights of rows
+  // (st0 + i) kRps .. + kRps - 1, summed per row and stored.
+  auto step = [&](const LkLoad& L) {
+    float dsc0, dsc1, dmm0, dmm1;
+    q4k_pair_scales(L.h.x, L.h.y, L.h.z, L.h.w, sh, hi_mask, dsc0, dsc1, dmm0, dmm1);
+    const uint32_t qw[8] = {L.qa.x, L.qa.y, L.qa.z, L.qa.w, L.qb.x, L.qb.y, L.qb.z, L.qb.w};
+    float la0 = 0.f, la1 = 0.f, ha0 = 0.f, ha1 = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      // byte 4t + e: low nibble = weight 4t + e of sub-block 2 gq,
+      // high nibble = weight 4t + e of sub-block 2 gq + 1
+      float ql[4], qh[4];
+      nibbles_div512(opaque(qw[t] & 0x0F0F0F0Fu), ql);
+      nibbles_div512(opaque((qw[t] >> 4) & 0x0F0F0F0Fu), qh);
+      float& la = (t & 1) ? la1 : la0;
+      float& ha = (t & 1) ? ha1 : ha0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        la = fmaf(ql[e], xv[4 * t + e], la);
+        ha = fmaf(qh[e], xv[32 + 4 * t + e], ha);
+      }
+    }
+    float r = dsc0 * (la0 + la1);
+    r = fmaf(dsc1, ha0 + ha1, r);
+    r = fmaf(-dmm0, xs0, r);
+    r = fmaf(-dmm1, xs1, r);
+    return r;
+  };
+  auto finish = [&](float r, int i) {
+    r = lk_segment_sum<kU>(r);
+    const int64_t row = (st0 + i) * kRps + rsub;
+    if (u == kU - 1 && row < rows) y[row] = r;
+  };
+
+  // Whole groups of kDepth steps: step i consumes ring slot i mod kDepth and
+  // refills it with step i + kDepth, so kDepth - 1 later steps stay in flight
+  // while it computes. Every pass of this loop issues the same loads in the
+  // same order, so the wait before each step is exact.
+  int i0 = 0;
+  for (; i0 + kDepth <= n; i0 += kDepth) {
+#pragma unroll
+    for (int p = 0; p < kDepth; ++p) {
+      const float r = step(ring[p]);
+      issue(st0 + i0 + p + kDepth, ring[p]);
+      finish(r, i0 + p);
+    }
+  }
+  // The last n - i0 < kDepth steps, already in flight: no more loads.
+#pragma unroll
+  for (int p = 0; p < kDepth - 1; ++p)
+    if (i0 + p < n) finish(step(ring[p]), i0 + p);
+}
+
+// ---------------------------------------------------------------------------
+// Long rows (K = 256 nsb > 4096, up to 12288): one row per step; lane l takes
+// quarters l, l + 64, ... (kQ rounds, the last one partial), so a step reads
+// a whole row. Too many activations per lane to keep in VGPRs: the block
+// stages x in LDS (the same padded layout) together with the sums of x over
+// each 32-weight sub-block, and every step reads each quarter's 64 values
+// from LDS.
+// ---------------------------------------------------------------------------
+constexpr int kLkxMaxK = 12288;
+
+struct LkxLoad {
+  lk_u32x4 h, qa, qb;
+};
+
+template <int kQ, int kDepth>
+__global__ __launch_bounds__(kLkWaves * 64) void gemv_q4k_lkx_kernel(LkGroup grp) {
+  // [K + K/16] padded x, then [K/32] sub-block sums
+  extern __shared__ __attribute__((aligned(16))) float xl[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const LkBlock B = lk_block(grp, (int)blockIdx.x, wave);
+  const int nsb = B.nsb;
+  const int U = 4 * nsb;                    // quarters per row
+  const int K = 256 * nsb;
+  const int nxf4 = K / 4;
+  const uint32_t row_bytes = (uint32_t)nsb * kQ4KBlockBytes;
+  float* const xsum = xl + K + K / 16;
+
+  // x: the block's threads load it all first (at most 4 kQ float4 each) ...
+  lk_f32x4 xg[4 * kQ];
+#pragma unroll
+  for (int j = 0; j < 4 * kQ; ++j) {
+    const int i = tid + j * kLkWaves * 64;
+    if (i < nxf4) xg[j] = reinterpret_cast<const GQK_GLOBAL lk_f32x4*>(B.x)[i];
+  }
+
+  // ... then the weight loads of the first kDepth steps (rows). Quarter q of
+  // the lane is uq = lane + 64 q; in the last round lanes past the row
+  // re-read its last quarter and their sums are dropped.
+  uint32_t hoff[kQ], qoff[kQ], sh[kQ], him[kQ];
+  int uqc[kQ];
+  bool val[kQ];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    const int uq = lane + 64 * q;
+    val[q] = uq < U;
+    uqc[q] = val[q] ? uq : U - 1;
+    const int gq = uqc[q] & 3;
+    hoff[q] = (uint32_t)(uqc[q] >> 2) * kQ4KBlockBytes;
+    qoff[q] = hoff[q] + 16u + 32u * (uint32_t)gq;
+    sh[q] = 16u * (uint32_t)(gq & 1);
+    him[q] = gq >= 2 ? 0xFFFFFFFFu : 0u;
+  }
+  const int64_t st0 = B.st0;
+  const int n = B.n;
+  const int64_t last = st0 + n - 1 > 0 ? st0 + n - 1 : 0;
+  auto issue = [&](int64_t row, LkxLoad (&L)[kQ]) {
+    row = row < last ? row : last;
+    const GQK_GLOBAL uint8_t* base = B.W + row * (int64_t)row_bytes;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      L[q].h = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + hoff[q]);
+      L[q].qa = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + qoff[q]);
+      L[q].qb = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + (qoff[q] + 16));
+    }
+  };
+  LkxLoad ring[kDepth][kQ];
+#pragma unroll
+  for (int p = 0; p < kDepth; ++p) issue(st0 + p, ring[p]);
+
+#pragma unroll
+  for (int j = 0; j < 4 * kQ; ++j) {
+    const int i = tid + j * kLkWaves * 64;
+    if (i < nxf4) *reinterpret_cast<lk_f32x4*>(&xl[4 * i + (i >> 4) * 4]) = xg[j];
+  }
+  __syncthreads();
+  // sub-block sums, each added in index order by one thread
+  for (int sb = tid; sb < K / 32; sb += kLkWaves * 64) {
+    const lk_f32x4* p = reinterpret_cast<const lk_f32x4*>(&xl[32 * sb + (sb >> 1) * 4]);
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const lk_f32x4 v = p[i];
+      t += v.x;
+      t += v.y;
+      t += v.z;
+      t += v.w;
+    }
+    xsum[sb] = t;
+  }
+  __syncthreads();
+  if (n <= 0) return;
+  float xs0[kQ], xs1[kQ];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    xs0[q] = xsum[2 * uqc[q]];
+    xs1[q] = xsum[2 * uqc[q] + 1];
+  }
+
+  auto step = [&](const LkxLoad (&L)[kQ]) {
+    float r = 0.f;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      float dsc0, dsc1, dmm0, dmm1;
+      q4k_pair_scales(L[q].h.x, L[q].h.y, L[q].h.z, L[q].h.w, sh[q], him[q], dsc0, dsc1, dmm0, dmm1);
+      const uint32_t qw[8] = {L[q].qa.x, L[q].qa.y, L[q].qa.z, L[q].qa.w,
+                              L[q].qb.x, L[q].qb.y, L[q].qb.z, L[q].qb.w};
+      const lk_f32x4* xp = reinterpret_cast<const lk_f32x4*>(&xl[68 * uqc[q]]);
+      float la0 = 0.f, la1 = 0.f, ha0 = 0.f, ha1 = 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const lk_f32x4 xa = xp[t];       // x of sub-block 2 gq, weights 4t .. 4t + 3
+        const lk_f32x4 xb = xp[8 + t];   // x of sub-block 2 gq + 1
+        float ql[4], qh[4];
+        nibbles_div512(opaque(qw[t] & 0x0F0F0F0Fu), ql);
+        nibbles_div512(opaque((qw[t] >> 4) & 0x0F0F0F0Fu), qh);
+        float& la = (t & 1) ? la1 : la0;
+        float& ha = (t & 1) ? ha1 : ha0;
+        la = fmaf(ql[0], xa.x, la);
+        la = fmaf(ql[1], xa.y, la);
+        la = fmaf(ql[2], xa.z, la);
+        la = fmaf(ql[3], xa.w, la);
+        ha = fmaf(qh[0], xb.x, ha);
+        ha = fmaf(qh[1], xb.y, ha);
+        ha = fmaf(qh[2], xb.z, ha);
+        ha = fmaf(qh[3], xb.w, ha);
+      }
+      float rq = dsc0 * (la0 + la1);
+      rq = fmaf(dsc1, ha0 + ha1, rq);
+      rq = fmaf(-dmm0, xs0[q], rq);
+      rq = fmaf(-dmm1, xs1[q], rq);
+      r += val[q] ? rq : 0.f;
+    }
+    return r;
+  };
+  auto finish = [&](float r, int i) {
+    r = lk_segment_sum<64>(r);
+    if (lane == 63) B.y[st0 + i] = r;
+  };
+
+  int i0 = 0;
+  for (; i0 + kDepth <= n; i0 += kDepth) {
+#pragma unroll
+    for (int p = 0; p < kDepth; ++p) {
+      const float r = step(ring[p]);
+      issue(st0 + i0 + p + kDepth, ring[p]);
+      finish(r, i0 + p);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < kDepth - 1; ++p)
+    if (i0 + p < n) finish(step(ring[p]), i0 + p);
+}
+
+}  // namespace gqk

@@ -17,6 +17,7 @@
 #include "dequant.hpp"
 #include "gemm.hpp"
 #include "gemv.hpp"
+#include "gemv_lk.hpp"
 #include "gemv_other.hpp"
 #include "gemv_small_batch.hpp"
 #include "layer_ops.hpp"
@@ -59,6 +60,9 @@ struct Tuning {
   int sb_max_split = 8;      // largest K split of a small-batch product
   int q4k_slots = 1;         // LDS chunks in flight per wave, Q4_K
   int q80_slots = 1;         // LDS chunks in flight per wave, Q8_0
+  int q4k_lk = 1;            // Q4_K GEMVs without epilogue: lanes-along-K kernels
+  int lk_waves = 1024;       // waves a lanes-along-K launch aims for
+  int lkx_waves = 2048;      // the same for rows longer than 16 super-blocks
 };
 
 static const Tuning& tuning() {
@@ -79,6 +83,9 @@ static const Tuning& tuning() {
       if (key == "sb_max_split" && v > 0 && v <= 8) r.sb_max_split = v;
       if (key == "q4k_slots" && (v == 1 || v == 2)) r.q4k_slots = v;
       if (key == "q80_slots" && (v == 1 || v == 2)) r.q80_slots = v;
+      if (key == "q4k_lk" && (v == 0 || v == 1)) r.q4k_lk = v;
+      if (key == "lk_waves" && v > 0) r.lk_waves = v;
+      if (key == "lkx_waves" && v > 0) r.lkx_waves = v;
       const char* comma = std::strchr(eq, ',');
       if (!comma) break;
       p = comma + 1;
@@ -315,9 +322,90 @@ static int64_t plan_group(int type, const gguf_qk_gemv* const* v, const GemvEpil
   return tasks;
 }
 
+// Q4_K GEMVs whose rows hold 1, 2, 4, 8 or 16 super-blocks, all the same:
+// the lanes-along-K kernel can take them.
+static bool lk_fits(const gguf_qk_gemv* const* v, int n) {
+  const int64_t c = v[0]->cols;
+  if (c != 256 && c != 512 && c != 1024 && c != 2048 && c != 4096 && (c <= 4096 || c > kLkxMaxK))
+    return false;
+  for (int i = 0; i < n; ++i)
+    if (v[i]->cols != c || v[i]->rows > (int64_t(1) << 30)) return false;
+  return true;
+}
+
+// Lanes-along-K launch: blocks go to the GEMVs in proportion to their rows
+// (at least one, at most one per row step); a shallow load ring when a wave
+// has only a few steps.
+extern "C++" {
+template <int kNsb>
+static void launch_lk_nsb(const LkGroup& grp, int depth, hipStream_t stream) {
+  const dim3 grid((unsigned)grp.total_blocks), block(kLkWaves * 64);
+  if (depth <= 2)
+    hipLaunchKernelGGL((gemv_q4k_lk_kernel<kNsb, 2>), grid, block, 0, stream, grp);
+  else
+    hipLaunchKernelGGL((gemv_q4k_lk_kernel<kNsb, 4>), grid, block, 0, stream, grp);
+}
+}
+
+static int launch_lk(const gguf_qk_gemv* const* v, int n, hipStream_t stream) {
+  const int nsb = (int)(v[0]->cols / 256);
+  const bool longrow = nsb > 16;
+  const int rps = longrow ? 1 : 64 / (4 * nsb);
+  LkGroup grp{};
+  grp.n = n;
+  int64_t total_rows = 0;
+  for (int i = 0; i < n; ++i) total_rows += v[i]->rows;
+  const int64_t target_blocks =
+      ((longrow ? tuning().lkx_waves : tuning().lk_waves) + kLkWaves - 1) / kLkWaves;
+  int64_t bb = 0, max_wave_steps = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t steps = (v[i]->rows + rps - 1) / rps;
+    int64_t want = (int64_t)((double)target_blocks * (double)v[i]->rows / (double)total_rows + 0.5);
+    if (want < 1) want = 1;
+    if (want > steps) want = steps;
+    LkDesc& d = grp.d[i];
+    d.W = static_cast<const uint8_t*>(v[i]->W);
+    d.x = v[i]->x;
+    d.y = v[i]->y;
+    d.rows = (int)v[i]->rows;
+    d.block_begin = (int)bb;
+    d.q = (int)(steps / want);
+    d.r = (int)(steps % want);
+    d.nsb = nsb;
+    bb += want;
+    const int64_t ws = ((steps + want - 1) / want + kLkWaves - 1) / kLkWaves;
+    if (ws > max_wave_steps) max_wave_steps = ws;
+  }
+  grp.total_blocks = (int)bb;
+  const int depth = max_wave_steps <= 2 ? 2 : 4;
+  if (longrow) {
+    const int kq = (4 * nsb + 63) / 64;
+    const size_t lds = (size_t)(256 * nsb) * 4 * 35 / 32;   // x padded + sub-block sums
+    const dim3 grid((unsigned)grp.total_blocks), block(kLkWaves * 64);
+    if (kq == 2)
+      hipLaunchKernelGGL((gemv_q4k_lkx_kernel<2, 2>), grid, block, lds, stream, grp);
+    else
+      hipLaunchKernelGGL((gemv_q4k_lkx_kernel<3, 2>), grid, block, lds, stream, grp);
+    return launch_status();
+  }
+  switch (nsb) {
+    case 1: launch_lk_nsb<1>(grp, depth, stream); break;
+    case 2: launch_lk_nsb<2>(grp, depth, stream); break;
+    case 4: launch_lk_nsb<4>(grp, depth, stream); break;
+    case 8: launch_lk_nsb<8>(grp, depth, stream); break;
+    default: launch_lk_nsb<16>(grp, depth, stream); break;
+  }
+  return launch_status();
+}
+
 // Launches one planned group.
 static int launch_group(int type, const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n,
                         const ScratchArea* scratch, hipStream_t stream) {
+  if (type == GGUF_QK_TYPE_Q4_K && tuning().q4k_lk && lk_fits(v, n)) {
+    bool any_ep = false;
+    for (int i = 0; i < n; ++i) any_ep = any_ep || (e && e[i] && e[i]->flags != 0);
+    if (!any_ep) return launch_lk(v, n, stream);
+  }
   GemvGroup grp;
   const int64_t tasks = plan_group(type, v, e, n, &grp);
   float* partials = const_cast<float*>(scratch->partials);
