@@ -26,6 +26,9 @@ HIP_FLAGS = [
     "-fPIC",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the dispatcher places up to 16 leading scalar kernel arguments in SGPRs
+    # before the waves start (no argument load on the critical path)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

@@ -65,6 +65,8 @@ struct LkBlock {
   int64_t st0;
   int n;
   int nsb;
+  int bs0;           // the block's row steps [bs0, bs0 + bn)
+  int bn;
 };
 
 // The kernel arguments sit in memory that is cold at every launch: all four
@@ -102,6 +104,8 @@ __device__ __forceinline__ LkBlock lk_block(const LkGroup& grp, int b, int wave)
   const int bs0 = lb * q + (lb < r ? lb : r);
   o.st0 = bs0 + ((wave * bn) >> 2);
   o.n = (((wave + 1) * bn) >> 2) - ((wave * bn) >> 2);
+  o.bs0 = bs0;
+  o.bn = bn;
   return o;
 }
 
@@ -168,23 +172,57 @@ struct LkLoad {
   lk_u32x4 h, qa, qb;
 };
 
+// One GEMV alone, its descriptor in scalar kernel arguments (which the
+// dispatcher can place in SGPRs before the waves start).
+__device__ __forceinline__ LkBlock lk_block_single(const uint8_t* W, const float* x, float* y,
+                                                   int rows, int q, int r, int nsb, int b,
+                                                   int wave) {
+  LkBlock o;
+  o.W = (const GQK_GLOBAL uint8_t*)W;
+  o.x = (const GQK_GLOBAL float*)x;
+  o.y = (GQK_GLOBAL float*)y;
+  o.rows = rows;
+  o.nsb = nsb;
+  const int bn = q + (b < r ? 1 : 0);
+  const int bs0 = b * q + (b < r ? b : r);
+  o.st0 = bs0 + ((wave * bn) >> 2);
+  o.n = (((wave + 1) * bn) >> 2) - ((wave * bn) >> 2);
+  o.bs0 = bs0;
+  o.bn = bn;
+  return o;
+}
+
+template <int kNsb, int kDepth>
+__device__ __forceinline__ void lk_run(const LkBlock& B, float* xl);
+
 template <int kNsb, int kDepth>
 __global__ __launch_bounds__(kLkWaves * 64) void gemv_q4k_lk_kernel(LkGroup grp) {
+  // x in LDS with 4 floats of padding after every 64: the slice of lane u
+  // starts at float 68 u, i.e. on bank 4 u mod 32 (16-byte reads conflict-free)
+  __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  lk_run<kNsb, kDepth>(lk_block(grp, (int)blockIdx.x, wave), xl);
+}
+
+template <int kNsb, int kDepth>
+__global__ __launch_bounds__(kLkWaves * 64) void gemv_q4k_lk1_kernel(const uint8_t* W, const float* x,
+                                                                     float* y, int rows, int q,
+                                                                     int r) {
+  __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  lk_run<kNsb, kDepth>(lk_block_single(W, x, y, rows, q, r, kNsb, (int)blockIdx.x, wave), xl);
+}
+
+template <int kNsb, int kDepth>
+__device__ __forceinline__ void lk_run(const LkBlock& B, float* xl) {
   constexpr int kU = 4 * kNsb;                 // lanes per row
   constexpr int kRps = 64 / kU;                // rows per step
   constexpr int kK = 256 * kNsb;
   constexpr uint32_t kRowBytes = (uint32_t)kNsb * kQ4KBlockBytes;
   constexpr int kXF4 = kK / 4;                 // float4 of x
   static_assert(kU >= 4 && kU <= 64 && 64 % kU == 0, "rows of 1 to 16 super-blocks");
-  // x in LDS with 4 floats of padding after every 64: the slice of lane u
-  // starts at float 68 u, i.e. on bank 4 u mod 32 (16-byte reads conflict-free)
-  __shared__ __attribute__((aligned(16))) float xl[kK + kK / 16];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = (int)blockIdx.x;
-  const LkBlock B = lk_block(grp, b, wave);
   const GQK_GLOBAL uint8_t* const W = B.W;
   const GQK_GLOBAL float* const x = B.x;
   GQK_GLOBAL float* const y = B.y;

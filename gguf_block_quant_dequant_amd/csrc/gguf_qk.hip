@@ -63,6 +63,7 @@ struct Tuning {
   int q4k_lk = 1;            // Q4_K GEMVs without epilogue: lanes-along-K kernels
   int lk_waves = 1024;       // waves a lanes-along-K launch aims for
   int lkx_waves = 2048;      // the same for rows longer than 16 super-blocks
+  int lk_single = 1;         // one-GEMV launches take their descriptor as scalar arguments
 };
 
 static const Tuning& tuning() {
@@ -86,6 +87,7 @@ static const Tuning& tuning() {
       if (key == "q4k_lk" && (v == 0 || v == 1)) r.q4k_lk = v;
       if (key == "lk_waves" && v > 0) r.lk_waves = v;
       if (key == "lkx_waves" && v > 0) r.lkx_waves = v;
+      if (key == "lk_single" && (v == 0 || v == 1)) r.lk_single = v;
       const char* comma = std::strchr(eq, ',');
       if (!comma) break;
       p = comma + 1;
@@ -340,6 +342,16 @@ extern "C++" {
 template <int kNsb>
 static void launch_lk_nsb(const LkGroup& grp, int depth, hipStream_t stream) {
   const dim3 grid((unsigned)grp.total_blocks), block(kLkWaves * 64);
+  if (grp.n == 1 && tuning().lk_single) {
+    const LkDesc& d = grp.d[0];
+    if (depth <= 2)
+      hipLaunchKernelGGL((gemv_q4k_lk1_kernel<kNsb, 2>), grid, block, 0, stream, d.W, d.x, d.y, d.rows,
+                         d.q, d.r);
+    else
+      hipLaunchKernelGGL((gemv_q4k_lk1_kernel<kNsb, 4>), grid, block, 0, stream, d.W, d.x, d.y, d.rows,
+                         d.q, d.r);
+    return;
+  }
   if (depth <= 2)
     hipLaunchKernelGGL((gemv_q4k_lk_kernel<kNsb, 2>), grid, block, 0, stream, grp);
   else

@@ -208,6 +208,35 @@ def test_matvec_q8_0_ragged(rows, cols):
     assert ok and e <= TOL_F32, e
 
 
+# Every row length the lanes-along-K kernels take (a row of 1 to 16
+# super-blocks held by lanes, 17 to 48 read in rounds from LDS) and the first
+# past them (lane-per-row kernel), with row counts that leave a partial step.
+@pytest.mark.parametrize("cols", [256, 1024, 4096, 4352, 5120, 8192, 12288, 12544])
+@pytest.mark.parametrize("rows", [1, 3, 130])
+def test_matvec_q4_k_every_row_length(rows, cols):
+    y, ref, _, _ = _matvec_case("q4_k", rows, cols, 11)
+    e, ok = oracle.floored_rel_err(y, ref)
+    assert ok and e <= TOL_F32, e
+
+
+@pytest.mark.parametrize("cols", [1024, 4608, 11008])
+def test_matvec_q4_k_integer_exact_long_rows(cols):
+    # d = 1, dmin = 0, sc = 1: integer weights 0..15 and integer x, every
+    # partial sum exact in fp32, so the result is exact whatever the order
+    rng = np.random.default_rng(17)
+    rows = 67
+    q = rng.integers(0, 16, size=(rows, cols))
+    raw = bytearray()
+    for r in range(rows):
+        for s in range(cols // 256):
+            raw += pack_q4_k_block(0x3C00, 0x0000, [1] * 8, [int(v) for v in rng.integers(0, 64, 8)],
+                                   [int(v) for v in q[r, s * 256:(s + 1) * 256]])
+    w = np.frombuffer(bytes(raw), np.uint8).reshape(rows, -1)
+    x = rng.integers(-8, 9, size=cols).astype(np.float32)
+    y = host(g.gguf_qmatvec_q4_k(dev(w), dev(x)))
+    assert np.array_equal(y.astype(np.float64), (q @ x.astype(np.int64)).astype(np.float64))
+
+
 def test_matvec_q4_k_integer_exact():
     rng = np.random.default_rng(7)
     rows, cols = 130, 1024
