@@ -317,7 +317,9 @@ struct GemvEpilogue {
   float inv_k;         // 1 / length of the normalized vector
   int flags;
   int role;            // pair: 0 gate, 1 up
-  int pad[3];
+  int* norm_cnt;       // [row groups] at stride kCounterStride, zero between calls: the
+                       // lanes-along-K kernels count finished rows of a row group before
+                       // its ss_out sum (a block kernel owns whole row groups, no count)
 };
 
 __device__ __forceinline__ float wave_sum_fixed(float v) {

@@ -26,10 +26,11 @@
 #pragma once
 
 #include "device_common.hpp"
+#include "gemv.hpp"
 
 namespace gqk {
 
-constexpr int kLkWaves = 4;   // waves per block
+constexpr int kLkWaves = 4;   // waves per block (the default; kernels take 4 or 8)
 constexpr int kLkMaxGroup = 4;
 
 // One GEMV of a launch (64 bytes, read as one 16-dword scalar load). Its row
@@ -45,7 +46,10 @@ struct LkDesc {
   int q;             // row steps per block
   int r;             // blocks that take one step more
   int nsb;           // super-blocks per row
-  int pad[5];
+  int pad;
+  const float* scale_ss;   // the epilogue's input RMSN partial sums (kEpScale), else null
+  int scale_n;
+  int ep_flags;            // the epilogue's flags (0: none)
 };
 static_assert(sizeof(LkDesc) == 64, "one 16-dword load per descriptor");
 
@@ -53,6 +57,7 @@ struct LkGroup {
   LkDesc d[kLkMaxGroup];
   int n;
   int total_blocks;
+  GemvEpilogue ep[kLkMaxGroup];   // read by the kernel variants with epilogues only
 };
 
 // The block's share of a launch: its GEMV (pointers, rows, super-blocks per
@@ -67,6 +72,10 @@ struct LkBlock {
   int nsb;
   int bs0;           // the block's row steps [bs0, bs0 + bn)
   int bn;
+  int g;             // which GEMV of the launch
+  const GQK_GLOBAL float* scale_ss;
+  int scale_n;
+  int ep_flags;
 };
 
 // The kernel arguments sit in memory that is cold at every launch: all four
@@ -76,6 +85,7 @@ struct LkBlock {
 // pointers come through the asm, which hides that they are global ones: they
 // are cast back, or every access would become a flat access (counted against
 // the LDS counter too, so each LDS wait would also wait for the weight loads).
+template <int kW>
 __device__ __forceinline__ LkBlock lk_block(const LkGroup& grp, int b, int wave) {
   typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
   u32x16 dw[kLkMaxGroup];
@@ -97,13 +107,17 @@ __device__ __forceinline__ LkBlock lk_block(const LkGroup& grp, int b, int wave)
   o.y = (GQK_GLOBAL float*)pick(dd[0].y, dd[1].y, dd[2].y, dd[3].y);
   o.rows = pick(dd[0].rows, dd[1].rows, dd[2].rows, dd[3].rows);
   o.nsb = pick(dd[0].nsb, dd[1].nsb, dd[2].nsb, dd[3].nsb);
+  o.g = g;
+  o.scale_ss = (const GQK_GLOBAL float*)pick(dd[0].scale_ss, dd[1].scale_ss, dd[2].scale_ss, dd[3].scale_ss);
+  o.scale_n = pick(dd[0].scale_n, dd[1].scale_n, dd[2].scale_n, dd[3].scale_n);
+  o.ep_flags = pick(dd[0].ep_flags, dd[1].ep_flags, dd[2].ep_flags, dd[3].ep_flags);
   const int lb = b - pick(dd[0].block_begin, dd[1].block_begin, dd[2].block_begin, dd[3].block_begin);
   const int q = pick(dd[0].q, dd[1].q, dd[2].q, dd[3].q);
   const int r = pick(dd[0].r, dd[1].r, dd[2].r, dd[3].r);
   const int bn = q + (lb < r ? 1 : 0);
   const int bs0 = lb * q + (lb < r ? lb : r);
-  o.st0 = bs0 + ((wave * bn) >> 2);
-  o.n = (((wave + 1) * bn) >> 2) - ((wave * bn) >> 2);
+  o.st0 = bs0 + (wave * bn) / kW;
+  o.n = ((wave + 1) * bn) / kW - (wave * bn) / kW;
   o.bs0 = bs0;
   o.bn = bn;
   return o;
@@ -172,8 +186,106 @@ struct LkLoad {
   lk_u32x4 h, qa, qb;
 };
 
+// ---------------------------------------------------------------------------
+// The neighbouring steps of a decode layer fused into these GEMVs (the same
+// epilogues as the lane-per-row kernels, see GemvEpilogue): per row, in the
+// lane that holds the row's sum, the input RMSN scale, the residual add and
+// norm_out = y * norm_w; per 64-row group, once every row of the group is
+// stored (a count per group, agent-scope stores and loads), the next RMSN's
+// partial sum ss_out (the same fixed butterfly of squares as the standalone
+// preparation kernel) or, for a gate/up pair, act = SiLU(gate) * up.
+// ---------------------------------------------------------------------------
+struct LkEp {
+  GemvEpilogue e;
+  float scale;       // input RMSN factor (1 without kEpScale)
+  int gflags;        // group work: kEpNorm or kEpPair (not both), else 0
+};
+
+// The lane's share of the input RMSN's partial sums (kEpScale; at most 256
+// of them): scale_ss[lane + 64 k], k = 0..3, added in k order.
+__device__ __forceinline__ float lk_ep_ss(const LkBlock& B, int lane) {
+  float t = 0.f;
+  if (B.ep_flags & kEpScale) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = lane + 64 * k;
+      const float v = i < B.scale_n ? B.scale_ss[i] : 0.f;
+      t += v;
+    }
+  }
+  return t;
+}
+
+// The block's epilogue; the scale is 1 / sqrt(S / K + eps) with S the lanes'
+// shares added by a fixed butterfly.
+__device__ __forceinline__ LkEp lk_ep(const LkGroup& grp, const LkBlock& B, float ss_share) {
+  LkEp o;
+  o.e = grp.ep[B.g];
+  o.scale = 1.f;
+  o.gflags = o.e.flags & (kEpNorm | kEpPair);
+  if (o.e.flags & kEpScale) o.scale = 1.0f / sqrtf(wave_sum_fixed(ss_share) * o.e.inv_k + o.e.eps);
+  return o;
+}
+
+// Row `row`'s final sum v, in the lane that holds it.
+__device__ __forceinline__ void lk_ep_row(const LkEp& E, float v, int64_t row, GQK_GLOBAL float* y) {
+  if (E.e.flags & kEpScale) v *= E.scale;
+  if (E.e.flags & kEpResidual) v += E.e.residual[row];
+  if (E.gflags)
+    __hip_atomic_store((float*)&y[row], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    y[row] = v;
+  if (E.e.flags & kEpNorm) E.e.norm_out[row] = v * E.e.norm_w[row];
+}
+
+// After the block's rows [rb0, rb1) are stored: count them per 64-row group;
+// the block that completes a group does its group work. Called by the whole
+// block (wave-uniform; a barrier inside).
+__device__ __forceinline__ void lk_ep_groups(const LkEp& E, int64_t rb0, int64_t rb1, int64_t rows,
+                                             const GQK_GLOBAL float* y, int wave, int lane) {
+  if (!E.gflags) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  GQK_WAIT_VMCNT(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (wave != 0 || rb1 <= rb0) return;
+  const bool pair = (E.gflags & kEpPair) != 0;
+  int* cnt = pair ? E.e.pair_cnt : E.e.norm_cnt;
+  for (int64_t rg = rb0 / 64; rg * 64 < rb1; ++rg) {
+    const int64_t g0 = rg * 64;
+    const int grows = (int)(rows - g0 < 64 ? rows - g0 : 64);
+    const int count = (int)((rb1 < g0 + 64 ? rb1 : g0 + 64) - (rb0 > g0 ? rb0 : g0));
+    int old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(&cnt[rg * kCounterStride], count, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old + count != (pair ? 2 * grows : grows)) continue;
+    const bool live = lane < grows;
+    const int64_t r = g0 + (live ? lane : 0);
+    const float v = __hip_atomic_load((const float*)&y[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (pair) {
+      if (live) {
+        const float o = __hip_atomic_load(&E.e.partner_y[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float gv = E.e.role == 0 ? v : o, uv = E.e.role == 0 ? o : v;
+        E.e.act[r] = gv / (1.0f + expf(-gv)) * uv;
+      }
+    } else {
+      // the square rounded on its own, then the fixed butterfly: the same bits
+      // as the standalone preparation kernel
+      float sq = live ? v * v : 0.f;
+      asm volatile("" : "+v"(sq));
+      const float ss = wave_sum_fixed(sq);
+      if (lane == 0) E.e.ss_out[rg] = ss;
+    }
+    if (lane == 0)
+      __hip_atomic_store(&cnt[rg * kCounterStride], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // One GEMV alone, its descriptor in scalar kernel arguments (which the
 // dispatcher can place in SGPRs before the waves start).
+template <int kW>
 __device__ __forceinline__ LkBlock lk_block_single(const uint8_t* W, const float* x, float* y,
                                                    int rows, int q, int r, int nsb, int b,
                                                    int wave) {
@@ -183,38 +295,43 @@ __device__ __forceinline__ LkBlock lk_block_single(const uint8_t* W, const float
   o.y = (GQK_GLOBAL float*)y;
   o.rows = rows;
   o.nsb = nsb;
+  o.g = 0;
+  o.scale_ss = nullptr;
+  o.scale_n = 0;
+  o.ep_flags = 0;
   const int bn = q + (b < r ? 1 : 0);
   const int bs0 = b * q + (b < r ? b : r);
-  o.st0 = bs0 + ((wave * bn) >> 2);
-  o.n = (((wave + 1) * bn) >> 2) - ((wave * bn) >> 2);
+  o.st0 = bs0 + (wave * bn) / kW;
+  o.n = ((wave + 1) * bn) / kW - (wave * bn) / kW;
   o.bs0 = bs0;
   o.bn = bn;
   return o;
 }
 
-template <int kNsb, int kDepth>
-__device__ __forceinline__ void lk_run(const LkBlock& B, float* xl);
+template <int kNsb, int kDepth, int kW, bool kEp>
+__device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGroup* grp);
 
-template <int kNsb, int kDepth>
-__global__ __launch_bounds__(kLkWaves * 64) void gemv_q4k_lk_kernel(LkGroup grp) {
+template <int kNsb, int kDepth, int kW, bool kEp>
+__global__ __launch_bounds__(kW * 64) void gemv_q4k_lk_kernel(LkGroup grp) {
   // x in LDS with 4 floats of padding after every 64: the slice of lane u
   // starts at float 68 u, i.e. on bank 4 u mod 32 (16-byte reads conflict-free)
   __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  lk_run<kNsb, kDepth>(lk_block(grp, (int)blockIdx.x, wave), xl);
+  lk_run<kNsb, kDepth, kW, kEp>(lk_block<kW>(grp, (int)blockIdx.x, wave), xl, &grp);
 }
 
-template <int kNsb, int kDepth>
-__global__ __launch_bounds__(kLkWaves * 64) void gemv_q4k_lk1_kernel(const uint8_t* W, const float* x,
+template <int kNsb, int kDepth, int kW>
+__global__ __launch_bounds__(kW * 64) void gemv_q4k_lk1_kernel(const uint8_t* W, const float* x,
                                                                      float* y, int rows, int q,
                                                                      int r) {
   __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  lk_run<kNsb, kDepth>(lk_block_single(W, x, y, rows, q, r, kNsb, (int)blockIdx.x, wave), xl);
+  lk_run<kNsb, kDepth, kW, false>(lk_block_single<kW>(W, x, y, rows, q, r, kNsb, (int)blockIdx.x, wave),
+                                  xl, nullptr);
 }
 
-template <int kNsb, int kDepth>
-__device__ __forceinline__ void lk_run(const LkBlock& B, float* xl) {
+template <int kNsb, int kDepth, int kW, bool kEp>
+__device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGroup* grp) {
   constexpr int kU = 4 * kNsb;                 // lanes per row
   constexpr int kRps = 64 / kU;                // rows per step
   constexpr int kK = 256 * kNsb;
@@ -237,14 +354,16 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl) {
   const uint32_t qoff = 16u + 32u * (uint32_t)gq;
   const uint32_t sh = 16u * (uint32_t)(gq & 1);
   const uint32_t hi_mask = gq >= 2 ? 0xFFFFFFFFu : 0u;
+  float ss_share = 0.f;
+  if constexpr (kEp) ss_share = lk_ep_ss(B, lane);
 
   // x: every thread loads its float4s first ...
-  constexpr int kXIt = (kXF4 + kLkWaves * 64 - 1) / (kLkWaves * 64);
+  constexpr int kXIt = (kXF4 + kW * 64 - 1) / (kW * 64);
   lk_f32x4 xg[kXIt];
 #pragma unroll
   for (int j = 0; j < kXIt; ++j) {
-    const int i = tid + j * kLkWaves * 64;
-    if (kXF4 % (kLkWaves * 64) == 0 || i < kXF4) xg[j] = reinterpret_cast<const GQK_GLOBAL lk_f32x4*>(x)[i];
+    const int i = tid + j * kW * 64;
+    if (kXF4 % (kW * 64) == 0 || i < kXF4) xg[j] = reinterpret_cast<const GQK_GLOBAL lk_f32x4*>(x)[i];
   }
 
   // ... then the weight loads of the first kDepth steps. A wave's steps are
@@ -272,12 +391,14 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl) {
 
 #pragma unroll
   for (int j = 0; j < kXIt; ++j) {
-    const int i = tid + j * kLkWaves * 64;
-    if (kXF4 % (kLkWaves * 64) == 0 || i < kXF4)
+    const int i = tid + j * kW * 64;
+    if (kXF4 % (kW * 64) == 0 || i < kXF4)
       *reinterpret_cast<lk_f32x4*>(&xl[4 * i + (i >> 4) * 4]) = xg[j];
   }
   __syncthreads();
-  if (n <= 0) return;
+  LkEp E;
+  if constexpr (kEp) E = lk_ep(*grp, B, ss_share);
+  if (n > 0) {
 
   float xv[64];
   {
@@ -329,7 +450,12 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl) {
   auto finish = [&](float r, int i) {
     r = lk_segment_sum<kU>(r);
     const int64_t row = (st0 + i) * kRps + rsub;
-    if (u == kU - 1 && row < rows) y[row] = r;
+    if (u == kU - 1 && row < rows) {
+      if constexpr (kEp)
+        lk_ep_row(E, r, row, y);
+      else
+        y[row] = r;
+    }
   };
 
   // Whole groups of kDepth steps: step i consumes ring slot i mod kDepth and
@@ -349,6 +475,12 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl) {
 #pragma unroll
   for (int p = 0; p < kDepth - 1; ++p)
     if (i0 + p < n) finish(step(ring[p]), i0 + p);
+  }   // n > 0
+  if constexpr (kEp) {
+    const int64_t rb0 = (int64_t)B.bs0 * kRps;
+    const int64_t re = (int64_t)(B.bs0 + B.bn) * kRps;
+    lk_ep_groups(E, rb0, re < rows ? re : rows, rows, y, __builtin_amdgcn_readfirstlane(tid >> 6), lane);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -365,26 +497,30 @@ struct LkxLoad {
   lk_u32x4 h, qa, qb;
 };
 
-template <int kQ, int kDepth>
-__global__ __launch_bounds__(kLkWaves * 64) void gemv_q4k_lkx_kernel(LkGroup grp) {
+template <int kQ, int kDepth, int kW, bool kEp>
+__global__ __launch_bounds__(kW * 64) void gemv_q4k_lkx_kernel(LkGroup grp) {
   // [K + K/16] padded x, then [K/32] sub-block sums
   extern __shared__ __attribute__((aligned(16))) float xl[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const LkBlock B = lk_block(grp, (int)blockIdx.x, wave);
+  const LkBlock B = lk_block<kW>(grp, (int)blockIdx.x, wave);
   const int nsb = B.nsb;
   const int U = 4 * nsb;                    // quarters per row
   const int K = 256 * nsb;
   const int nxf4 = K / 4;
   const uint32_t row_bytes = (uint32_t)nsb * kQ4KBlockBytes;
   float* const xsum = xl + K + K / 16;
+  float ss_share = 0.f;
+  if constexpr (kEp) ss_share = lk_ep_ss(B, lane);
 
-  // x: the block's threads load it all first (at most 4 kQ float4 each) ...
-  lk_f32x4 xg[4 * kQ];
+  // x: the block's threads load it all first (at most 16 kQ / kW float4
+  // each) ...
+  constexpr int kXIt = 16 * kQ / kW;
+  lk_f32x4 xg[kXIt];
 #pragma unroll
-  for (int j = 0; j < 4 * kQ; ++j) {
-    const int i = tid + j * kLkWaves * 64;
+  for (int j = 0; j < kXIt; ++j) {
+    const int i = tid + j * kW * 64;
     if (i < nxf4) xg[j] = reinterpret_cast<const GQK_GLOBAL lk_f32x4*>(B.x)[i];
   }
 
@@ -422,28 +558,24 @@ __global__ __launch_bounds__(kLkWaves * 64) void gemv_q4k_lkx_kernel(LkGroup grp
 #pragma unroll
   for (int p = 0; p < kDepth; ++p) issue(st0 + p, ring[p]);
 
+  // store x; the eight threads 8m .. 8m + 7 hold the 32 values of
+  // sub-block i / 8 (i = their float4 index) and add them with a fixed
+  // butterfly, the first of them storing the sum
 #pragma unroll
-  for (int j = 0; j < 4 * kQ; ++j) {
-    const int i = tid + j * kLkWaves * 64;
-    if (i < nxf4) *reinterpret_cast<lk_f32x4*>(&xl[4 * i + (i >> 4) * 4]) = xg[j];
+  for (int j = 0; j < kXIt; ++j) {
+    const int i = tid + j * kW * 64;
+    const bool in = i < nxf4;
+    if (in) *reinterpret_cast<lk_f32x4*>(&xl[4 * i + (i >> 4) * 4]) = xg[j];
+    float t = in ? (xg[j].x + xg[j].y) + (xg[j].z + xg[j].w) : 0.f;
+    t += dpp_f32<0xB1>(t);    // quad_perm 1,0,3,2
+    t += dpp_f32<0x4E>(t);    // quad_perm 2,3,0,1
+    t += dpp_f32<0x141>(t);   // row_half_mirror
+    if (in && (tid & 7) == 0) xsum[i >> 3] = t;
   }
   __syncthreads();
-  // sub-block sums, each added in index order by one thread
-  for (int sb = tid; sb < K / 32; sb += kLkWaves * 64) {
-    const lk_f32x4* p = reinterpret_cast<const lk_f32x4*>(&xl[32 * sb + (sb >> 1) * 4]);
-    float t = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const lk_f32x4 v = p[i];
-      t += v.x;
-      t += v.y;
-      t += v.z;
-      t += v.w;
-    }
-    xsum[sb] = t;
-  }
-  __syncthreads();
-  if (n <= 0) return;
+  LkEp E;
+  if constexpr (kEp) E = lk_ep(grp, B, ss_share);
+  if (n > 0) {
   float xs0[kQ], xs1[kQ];
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
@@ -489,7 +621,12 @@ __global__ __launch_bounds__(kLkWaves * 64) void gemv_q4k_lkx_kernel(LkGroup grp
   };
   auto finish = [&](float r, int i) {
     r = lk_segment_sum<64>(r);
-    if (lane == 63) B.y[st0 + i] = r;
+    if (lane == 63) {
+      if constexpr (kEp)
+        lk_ep_row(E, r, st0 + i, B.y);
+      else
+        B.y[st0 + i] = r;
+    }
   };
 
   int i0 = 0;
@@ -504,6 +641,11 @@ __global__ __launch_bounds__(kLkWaves * 64) void gemv_q4k_lkx_kernel(LkGroup grp
 #pragma unroll
   for (int p = 0; p < kDepth - 1; ++p)
     if (i0 + p < n) finish(step(ring[p]), i0 + p);
+  }   // n > 0
+  if constexpr (kEp) {
+    const int64_t rb0 = B.bs0;
+    lk_ep_groups(E, rb0, rb0 + B.bn, B.rows, B.y, wave, lane);
+  }
 }
 
 }  // namespace gqk

@@ -64,6 +64,8 @@ struct Tuning {
   int lk_waves = 1024;       // waves a lanes-along-K launch aims for
   int lkx_waves = 2048;      // the same for rows longer than 16 super-blocks
   int lk_single = 1;         // one-GEMV launches take their descriptor as scalar arguments
+  int lk_bw = 4;             // waves per block, rows of <= 16 super-blocks (4 or 8)
+  int lkx_bw = 8;            // waves per block, longer rows (4 or 8)
 };
 
 static const Tuning& tuning() {
@@ -88,6 +90,8 @@ static const Tuning& tuning() {
       if (key == "lk_waves" && v > 0) r.lk_waves = v;
       if (key == "lkx_waves" && v > 0) r.lkx_waves = v;
       if (key == "lk_single" && (v == 0 || v == 1)) r.lk_single = v;
+      if (key == "lk_bw" && (v == 4 || v == 8)) r.lk_bw = v;
+      if (key == "lkx_bw" && (v == 4 || v == 8)) r.lkx_bw = v;
       const char* comma = std::strchr(eq, ',');
       if (!comma) break;
       p = comma + 1;
@@ -324,51 +328,82 @@ static int64_t plan_group(int type, const gguf_qk_gemv* const* v, const GemvEpil
   return tasks;
 }
 
-// Q4_K GEMVs whose rows hold 1, 2, 4, 8 or 16 super-blocks, all the same:
-// the lanes-along-K kernel can take them.
-static bool lk_fits(const gguf_qk_gemv* const* v, int n) {
+extern "C++" {
+template <int kNsb, int kW, bool kEp>
+static void launch_lk_nsb(const LkGroup& grp, int depth, hipStream_t stream) {
+  const dim3 grid((unsigned)grp.total_blocks), block(kW * 64);
+  if (!kEp && grp.n == 1 && tuning().lk_single) {
+    const LkDesc& d = grp.d[0];
+    if (depth <= 2)
+      hipLaunchKernelGGL((gemv_q4k_lk1_kernel<kNsb, 2, kW>), grid, block, 0, stream, d.W, d.x, d.y,
+                         d.rows, d.q, d.r);
+    else
+      hipLaunchKernelGGL((gemv_q4k_lk1_kernel<kNsb, 4, kW>), grid, block, 0, stream, d.W, d.x, d.y,
+                         d.rows, d.q, d.r);
+    return;
+  }
+  if (depth <= 2)
+    hipLaunchKernelGGL((gemv_q4k_lk_kernel<kNsb, 2, kW, kEp>), grid, block, 0, stream, grp);
+  else
+    hipLaunchKernelGGL((gemv_q4k_lk_kernel<kNsb, 4, kW, kEp>), grid, block, 0, stream, grp);
+}
+
+template <int kNsb>
+static void launch_lk_nsb(const LkGroup& grp, int depth, int waves, bool ep, hipStream_t stream) {
+  if (ep)
+    launch_lk_nsb<kNsb, 4, true>(grp, depth, stream);
+  else if (waves == 8)
+    launch_lk_nsb<kNsb, 8, false>(grp, depth, stream);
+  else
+    launch_lk_nsb<kNsb, 4, false>(grp, depth, stream);
+}
+
+template <int kQ, int kW>
+static void launch_lkx(const LkGroup& grp, size_t lds, bool ep, hipStream_t stream) {
+  const dim3 grid((unsigned)grp.total_blocks), block(kW * 64);
+  if (ep)
+    hipLaunchKernelGGL((gemv_q4k_lkx_kernel<kQ, 2, kW, true>), grid, block, lds, stream, grp);
+  else
+    hipLaunchKernelGGL((gemv_q4k_lkx_kernel<kQ, 2, kW, false>), grid, block, lds, stream, grp);
+}
+}
+
+// Q4_K GEMVs whose rows hold 1, 2, 4, 8 or 16 super-blocks (lanes hold x), or
+// 17 to 48 (x read from LDS), all the same: the lanes-along-K kernels take
+// them, with any epilogue except norm preparation and a gate/up pair together
+// on one GEMV, and at most 256 partial sums for an input RMSN.
+static bool lk_fits(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n) {
   const int64_t c = v[0]->cols;
   if (c != 256 && c != 512 && c != 1024 && c != 2048 && c != 4096 && (c <= 4096 || c > kLkxMaxK))
     return false;
-  for (int i = 0; i < n; ++i)
+  for (int i = 0; i < n; ++i) {
     if (v[i]->cols != c || v[i]->rows > (int64_t(1) << 30)) return false;
+    if (e && e[i]) {
+      const int f = e[i]->flags;
+      if ((f & kEpNorm) && (f & kEpPair)) return false;
+      if ((f & kEpScale) && e[i]->scale_n > 256) return false;
+      if ((f & kEpNorm) && !e[i]->norm_cnt) return false;
+    }
+  }
   return true;
 }
 
 // Lanes-along-K launch: blocks go to the GEMVs in proportion to their rows
 // (at least one, at most one per row step); a shallow load ring when a wave
 // has only a few steps.
-extern "C++" {
-template <int kNsb>
-static void launch_lk_nsb(const LkGroup& grp, int depth, hipStream_t stream) {
-  const dim3 grid((unsigned)grp.total_blocks), block(kLkWaves * 64);
-  if (grp.n == 1 && tuning().lk_single) {
-    const LkDesc& d = grp.d[0];
-    if (depth <= 2)
-      hipLaunchKernelGGL((gemv_q4k_lk1_kernel<kNsb, 2>), grid, block, 0, stream, d.W, d.x, d.y, d.rows,
-                         d.q, d.r);
-    else
-      hipLaunchKernelGGL((gemv_q4k_lk1_kernel<kNsb, 4>), grid, block, 0, stream, d.W, d.x, d.y, d.rows,
-                         d.q, d.r);
-    return;
-  }
-  if (depth <= 2)
-    hipLaunchKernelGGL((gemv_q4k_lk_kernel<kNsb, 2>), grid, block, 0, stream, grp);
-  else
-    hipLaunchKernelGGL((gemv_q4k_lk_kernel<kNsb, 4>), grid, block, 0, stream, grp);
-}
-}
-
-static int launch_lk(const gguf_qk_gemv* const* v, int n, hipStream_t stream) {
+static int launch_lk(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n,
+                     hipStream_t stream) {
   const int nsb = (int)(v[0]->cols / 256);
   const bool longrow = nsb > 16;
   const int rps = longrow ? 1 : 64 / (4 * nsb);
+  bool ep = false;
+  for (int i = 0; i < n; ++i) ep = ep || (e && e[i] && e[i]->flags != 0);
+  const int bw = longrow ? tuning().lkx_bw : ep ? 4 : tuning().lk_bw;   // waves per block
   LkGroup grp{};
   grp.n = n;
   int64_t total_rows = 0;
   for (int i = 0; i < n; ++i) total_rows += v[i]->rows;
-  const int64_t target_blocks =
-      ((longrow ? tuning().lkx_waves : tuning().lk_waves) + kLkWaves - 1) / kLkWaves;
+  const int64_t target_blocks = ((longrow ? tuning().lkx_waves : tuning().lk_waves) + bw - 1) / bw;
   int64_t bb = 0, max_wave_steps = 0;
   for (int i = 0; i < n; ++i) {
     const int64_t steps = (v[i]->rows + rps - 1) / rps;
@@ -384,8 +419,14 @@ static int launch_lk(const gguf_qk_gemv* const* v, int n, hipStream_t stream) {
     d.q = (int)(steps / want);
     d.r = (int)(steps % want);
     d.nsb = nsb;
+    if (e && e[i]) {
+      grp.ep[i] = *e[i];
+      d.ep_flags = e[i]->flags;
+      d.scale_ss = e[i]->scale_ss;
+      d.scale_n = e[i]->scale_n;
+    }
     bb += want;
-    const int64_t ws = ((steps + want - 1) / want + kLkWaves - 1) / kLkWaves;
+    const int64_t ws = ((steps + want - 1) / want + bw - 1) / bw;
     if (ws > max_wave_steps) max_wave_steps = ws;
   }
   grp.total_blocks = (int)bb;
@@ -393,19 +434,25 @@ static int launch_lk(const gguf_qk_gemv* const* v, int n, hipStream_t stream) {
   if (longrow) {
     const int kq = (4 * nsb + 63) / 64;
     const size_t lds = (size_t)(256 * nsb) * 4 * 35 / 32;   // x padded + sub-block sums
-    const dim3 grid((unsigned)grp.total_blocks), block(kLkWaves * 64);
-    if (kq == 2)
-      hipLaunchKernelGGL((gemv_q4k_lkx_kernel<2, 2>), grid, block, lds, stream, grp);
-    else
-      hipLaunchKernelGGL((gemv_q4k_lkx_kernel<3, 2>), grid, block, lds, stream, grp);
+    if (bw == 8) {
+      if (kq == 2)
+        launch_lkx<2, 8>(grp, lds, ep, stream);
+      else
+        launch_lkx<3, 8>(grp, lds, ep, stream);
+    } else {
+      if (kq == 2)
+        launch_lkx<2, 4>(grp, lds, ep, stream);
+      else
+        launch_lkx<3, 4>(grp, lds, ep, stream);
+    }
     return launch_status();
   }
   switch (nsb) {
-    case 1: launch_lk_nsb<1>(grp, depth, stream); break;
-    case 2: launch_lk_nsb<2>(grp, depth, stream); break;
-    case 4: launch_lk_nsb<4>(grp, depth, stream); break;
-    case 8: launch_lk_nsb<8>(grp, depth, stream); break;
-    default: launch_lk_nsb<16>(grp, depth, stream); break;
+    case 1: launch_lk_nsb<1>(grp, depth, bw, ep, stream); break;
+    case 2: launch_lk_nsb<2>(grp, depth, bw, ep, stream); break;
+    case 4: launch_lk_nsb<4>(grp, depth, bw, ep, stream); break;
+    case 8: launch_lk_nsb<8>(grp, depth, bw, ep, stream); break;
+    default: launch_lk_nsb<16>(grp, depth, bw, ep, stream); break;
   }
   return launch_status();
 }
@@ -413,11 +460,7 @@ static int launch_lk(const gguf_qk_gemv* const* v, int n, hipStream_t stream) {
 // Launches one planned group.
 static int launch_group(int type, const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n,
                         const ScratchArea* scratch, hipStream_t stream) {
-  if (type == GGUF_QK_TYPE_Q4_K && tuning().q4k_lk && lk_fits(v, n)) {
-    bool any_ep = false;
-    for (int i = 0; i < n; ++i) any_ep = any_ep || (e && e[i] && e[i]->flags != 0);
-    if (!any_ep) return launch_lk(v, n, stream);
-  }
+  if (type == GGUF_QK_TYPE_Q4_K && tuning().q4k_lk && lk_fits(v, e, n)) return launch_lk(v, e, n, stream);
   GemvGroup grp;
   const int64_t tasks = plan_group(type, v, e, n, &grp);
   float* partials = const_cast<float*>(scratch->partials);
@@ -483,6 +526,13 @@ static int launch_step(const gguf_qk_gemv* list, const GemvEpilogue* eps, int n,
         if (st) return st;
         continue;
       }
+      // the two GEMVs of a gate/up pair go into one launch: a gate that would
+      // take the last place of a group opens the next one
+      if (k == kMaxGroup - 1 && eps && (eps[i].flags & kEpPair) && eps[i].role == 0) {
+        const int st = launch_group(type, grp, ge, k, scratch, stream);
+        if (st) return st;
+        k = 0;
+      }
       ge[k] = eps ? &eps[i] : nullptr;
       grp[k++] = &g;
       if (k == kMaxGroup) {
@@ -517,8 +567,9 @@ static int matvec_common(int type, const void* W, const float* x, float* y, int6
 // first pair counter row group of the entry's pair, else -1). pair_off: next
 // free pair counter row group of the step.
 static int make_epilogue(const gguf_qk_gemv* list, const gguf_qk_gemv_ep* ep, int32_t n, int32_t i,
-                         int64_t* pair_off, int64_t* pair_rg, GemvEpilogue* out) {
+                         int64_t* pair_off, int64_t* pair_rg, int64_t* norm_rg, GemvEpilogue* out) {
   *pair_rg = -1;
+  *norm_rg = -1;
   *out = GemvEpilogue{};
   const gguf_qk_gemv& g = list[i];
   const gguf_qk_gemv_ep& e = ep[i];
@@ -539,6 +590,12 @@ static int make_epilogue(const gguf_qk_gemv* list, const gguf_qk_gemv_ep* ep, in
     if (!e.norm_w || !e.norm_out || !e.ss_out) return GGUF_QK_ERR_NULL;
     if (!al4(e.norm_w) || !al4(e.norm_out) || !al4(e.ss_out)) return GGUF_QK_ERR_ALIGN;
     flags |= kEpNorm;
+    // row-group counters for kernels whose blocks do not own whole row groups
+    // (taken from the step's group counters when there are enough left)
+    if (*pair_off + RG <= kPairCounters) {
+      *norm_rg = *pair_off;
+      *pair_off += RG;
+    }
   }
   if (e.pair != 0) {
     if (e.pair != 1 && e.pair != 2) return GGUF_QK_ERR_SHAPE;
@@ -624,14 +681,15 @@ static int batch_common(const gguf_qk_gemv* list, const gguf_qk_gemv_ep* ep, int
     i = j;
   }
   std::vector<GemvEpilogue> eps;
-  std::vector<int64_t> pair_rg;
+  std::vector<int64_t> pair_rg, norm_rg;
   if (ep) {
     eps.resize(n);
     pair_rg.resize(n);
+    norm_rg.resize(n);
     int64_t pair_off = 0;
     for (int32_t i = 0; i < n; ++i) {
       if (i > 0 && list[i].stage != list[i - 1].stage) pair_off = 0;   // a step has finished
-      const int st = make_epilogue(list, ep, n, i, &pair_off, &pair_rg[i], &eps[i]);
+      const int st = make_epilogue(list, ep, n, i, &pair_off, &pair_rg[i], &norm_rg[i], &eps[i]);
       if (st) return st;
       if (ep[i].pair == 2) pair_rg[i] = pair_rg[i - 1];   // the gate's counters
     }
@@ -639,8 +697,10 @@ static int batch_common(const gguf_qk_gemv* list, const gguf_qk_gemv_ep* ep, int
   ScratchArea* scratch = nullptr;
   int st = current_device(&scratch);
   if (st) return st;
-  for (int32_t i = 0; i < (int32_t)eps.size(); ++i)
+  for (int32_t i = 0; i < (int32_t)eps.size(); ++i) {
     if (pair_rg[i] >= 0) eps[i].pair_cnt = scratch->pair_counters + pair_rg[i] * kCounterStride;
+    if (norm_rg[i] >= 0) eps[i].norm_cnt = scratch->pair_counters + norm_rg[i] * kCounterStride;
+  }
   for (int32_t i = 0; i < n;) {
     int32_t j = i;
     while (j < n && list[j].stage == list[i].stage) ++j;
