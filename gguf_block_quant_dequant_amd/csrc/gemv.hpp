@@ -302,6 +302,9 @@ struct SplitK {
 //              group writes act = SiLU(gate) * up for it (y stores and the
 //              partner's loads are agent-scope; a counter per row group)
 constexpr int kEpScale = 1, kEpResidual = 2, kEpNorm = 4, kEpPair = 8;
+// A gate/up pair whose rows the lanes-along-K kernel computes in the same
+// wave (the gate's descriptor carries both; set by the host, never by users).
+constexpr int kEpPairInWave = 16;
 
 struct GemvEpilogue {
   const float* scale_ss;

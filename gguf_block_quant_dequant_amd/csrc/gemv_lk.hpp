@@ -73,6 +73,8 @@ struct LkBlock {
   int bs0;           // the block's row steps [bs0, bs0 + bn)
   int bn;
   int g;             // which GEMV of the launch
+  const GQK_GLOBAL uint8_t* W2;   // kEpPairInWave: the up matrix and its output
+  GQK_GLOBAL float* y2;
   const GQK_GLOBAL float* scale_ss;
   int scale_n;
   int ep_flags;
@@ -111,6 +113,9 @@ __device__ __forceinline__ LkBlock lk_block(const LkGroup& grp, int b, int wave)
   o.scale_ss = (const GQK_GLOBAL float*)pick(dd[0].scale_ss, dd[1].scale_ss, dd[2].scale_ss, dd[3].scale_ss);
   o.scale_n = pick(dd[0].scale_n, dd[1].scale_n, dd[2].scale_n, dd[3].scale_n);
   o.ep_flags = pick(dd[0].ep_flags, dd[1].ep_flags, dd[2].ep_flags, dd[3].ep_flags);
+  // the up half of an in-wave gate/up pair is the next descriptor
+  o.W2 = (const GQK_GLOBAL uint8_t*)(g == 0 ? dd[1].W : g == 1 ? dd[2].W : dd[3].W);
+  o.y2 = (GQK_GLOBAL float*)(g == 0 ? dd[1].y : g == 1 ? dd[2].y : dd[3].y);
   const int lb = b - pick(dd[0].block_begin, dd[1].block_begin, dd[2].block_begin, dd[3].block_begin);
   const int q = pick(dd[0].q, dd[1].q, dd[2].q, dd[3].q);
   const int r = pick(dd[0].r, dd[1].r, dd[2].r, dd[3].r);
@@ -218,11 +223,11 @@ __device__ __forceinline__ float lk_ep_ss(const LkBlock& B, int lane) {
 
 // The block's epilogue; the scale is 1 / sqrt(S / K + eps) with S the lanes'
 // shares added by a fixed butterfly.
-__device__ __forceinline__ LkEp lk_ep(const LkGroup& grp, const LkBlock& B, float ss_share) {
+__device__ __forceinline__ LkEp lk_ep(const GemvEpilogue& e, float ss_share) {
   LkEp o;
-  o.e = grp.ep[B.g];
+  o.e = e;
   o.scale = 1.f;
-  o.gflags = o.e.flags & (kEpNorm | kEpPair);
+  o.gflags = (o.e.flags & kEpPairInWave) ? 0 : o.e.flags & (kEpNorm | kEpPair);
   if (o.e.flags & kEpScale) o.scale = 1.0f / sqrtf(wave_sum_fixed(ss_share) * o.e.inv_k + o.e.eps);
   return o;
 }
@@ -296,6 +301,8 @@ __device__ __forceinline__ LkBlock lk_block_single(const uint8_t* W, const float
   o.rows = rows;
   o.nsb = nsb;
   o.g = 0;
+  o.W2 = nullptr;
+  o.y2 = nullptr;
   o.scale_ss = nullptr;
   o.scale_n = 0;
   o.ep_flags = 0;
@@ -348,14 +355,23 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
   const int n = B.n;
 
   const int u = lane % kU;
-  const int rsub = lane / kU;
   const int s = u >> 2, gq = u & 3;
   const uint32_t hoff = (uint32_t)s * kQ4KBlockBytes;
   const uint32_t qoff = 16u + 32u * (uint32_t)gq;
   const uint32_t sh = 16u * (uint32_t)(gq & 1);
   const uint32_t hi_mask = gq >= 2 ? 0xFFFFFFFFu : 0u;
+  // rows per step of each matrix: kRps, or kRps / 2 of the gate (lanes 0..31)
+  // and the same rows of the up matrix (lanes 32..63) for an in-wave pair
+  const bool paired = kEp && kRps >= 2 && (B.ep_flags & kEpPairInWave);
+  const int rpm = paired ? kRps / 2 : kRps;
+  const int rsub = (lane / kU) % rpm;
+  const GQK_GLOBAL uint8_t* const Wl = (paired && lane >= 32) ? B.W2 : W;
   float ss_share = 0.f;
-  if constexpr (kEp) ss_share = lk_ep_ss(B, lane);
+  GemvEpilogue epl;
+  if constexpr (kEp) {
+    epl = grp->ep[B.g];
+    ss_share = lk_ep_ss(B, lane);
+  }
 
   // x: every thread loads its float4s first ...
   constexpr int kXIt = (kXF4 + kW * 64 - 1) / (kW * 64);
@@ -376,11 +392,11 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
   const int64_t last = st0 + n - 1 > 0 ? st0 + n - 1 : 0;
   auto issue = [&](int64_t st, LkLoad& L) {
     st = st < last ? st : last;
-    const int64_t r0 = st * kRps;
+    const int64_t r0 = st * rpm;
     const int64_t lim = rows - 1 - r0;
-    const uint32_t rr = lim < kRps - 1 ? (uint32_t)((int64_t)rsub < lim ? rsub : lim) : (uint32_t)rsub;
+    const uint32_t rr = lim < rpm - 1 ? (uint32_t)((int64_t)rsub < lim ? rsub : lim) : (uint32_t)rsub;
     const uint32_t off = rr * kRowBytes + hoff;
-    const GQK_GLOBAL uint8_t* base = W + r0 * (int64_t)kRowBytes;
+    const GQK_GLOBAL uint8_t* base = Wl + r0 * (int64_t)kRowBytes;
     L.h = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + off);
     L.qa = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + (off + qoff));
     L.qb = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + (off + qoff + 16));
@@ -397,7 +413,7 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
   }
   __syncthreads();
   LkEp E;
-  if constexpr (kEp) E = lk_ep(*grp, B, ss_share);
+  if constexpr (kEp) E = lk_ep(epl, ss_share);
   if (n > 0) {
 
   float xv[64];
@@ -449,7 +465,23 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
   };
   auto finish = [&](float r, int i) {
     r = lk_segment_sum<kU>(r);
-    const int64_t row = (st0 + i) * kRps + rsub;
+    const int64_t row = (st0 + i) * rpm + rsub;
+    if constexpr (kEp) {
+      if (paired) {
+        // lane 32 + l holds the up row whose gate row lane l holds
+        const float gv = __shfl_xor(r, 32) * E.scale;
+        const float v = r * E.scale;
+        if (u == kU - 1 && row < rows) {
+          if (lane < 32) {
+            y[row] = v;
+          } else {
+            B.y2[row] = v;
+            E.e.act[row] = gv / (1.0f + expf(-gv)) * v;
+          }
+        }
+        return;
+      }
+    }
     if (u == kU - 1 && row < rows) {
       if constexpr (kEp)
         lk_ep_row(E, r, row, y);
@@ -477,8 +509,8 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
     if (i0 + p < n) finish(step(ring[p]), i0 + p);
   }   // n > 0
   if constexpr (kEp) {
-    const int64_t rb0 = (int64_t)B.bs0 * kRps;
-    const int64_t re = (int64_t)(B.bs0 + B.bn) * kRps;
+    const int64_t rb0 = (int64_t)B.bs0 * rpm;
+    const int64_t re = (int64_t)(B.bs0 + B.bn) * rpm;
     lk_ep_groups(E, rb0, re < rows ? re : rows, rows, y, __builtin_amdgcn_readfirstlane(tid >> 6), lane);
   }
 }
@@ -512,7 +544,11 @@ __global__ __launch_bounds__(kW * 64) void gemv_q4k_lkx_kernel(LkGroup grp) {
   const uint32_t row_bytes = (uint32_t)nsb * kQ4KBlockBytes;
   float* const xsum = xl + K + K / 16;
   float ss_share = 0.f;
-  if constexpr (kEp) ss_share = lk_ep_ss(B, lane);
+  GemvEpilogue epl;
+  if constexpr (kEp) {
+    epl = grp.ep[B.g];
+    ss_share = lk_ep_ss(B, lane);
+  }
 
   // x: the block's threads load it all first (at most 16 kQ / kW float4
   // each) ...
@@ -574,7 +610,7 @@ __global__ __launch_bounds__(kW * 64) void gemv_q4k_lkx_kernel(LkGroup grp) {
   }
   __syncthreads();
   LkEp E;
-  if constexpr (kEp) E = lk_ep(grp, B, ss_share);
+  if constexpr (kEp) E = lk_ep(epl, ss_share);
   if (n > 0) {
   float xs0[kQ], xs1[kQ];
 #pragma unroll

@@ -66,6 +66,7 @@ struct Tuning {
   int lk_single = 1;         // one-GEMV launches take their descriptor as scalar arguments
   int lk_bw = 4;             // waves per block, rows of <= 16 super-blocks (4 or 8)
   int lkx_bw = 8;            // waves per block, longer rows (4 or 8)
+  int lk_pair_in_wave = 1;   // gate/up pairs: both rows of an index in one wave
 };
 
 static const Tuning& tuning() {
@@ -92,6 +93,7 @@ static const Tuning& tuning() {
       if (key == "lk_single" && (v == 0 || v == 1)) r.lk_single = v;
       if (key == "lk_bw" && (v == 4 || v == 8)) r.lk_bw = v;
       if (key == "lkx_bw" && (v == 4 || v == 8)) r.lkx_bw = v;
+      if (key == "lk_pair_in_wave" && (v == 0 || v == 1)) r.lk_pair_in_wave = v;
       const char* comma = std::strchr(eq, ',');
       if (!comma) break;
       p = comma + 1;
@@ -404,30 +406,50 @@ static int launch_lk(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e,
   int64_t total_rows = 0;
   for (int i = 0; i < n; ++i) total_rows += v[i]->rows;
   const int64_t target_blocks = ((longrow ? tuning().lkx_waves : tuning().lk_waves) + bw - 1) / bw;
+  // gate/up pairs computed in the same wave (the gate's rows in lanes 0..31,
+  // the up's in 32..63): the gate's descriptor takes both matrices' blocks,
+  // the up's gets none
+  bool in_wave[kLkMaxGroup] = {false, false, false, false};
+  for (int i = 0; i + 1 < n; ++i)
+    if (!longrow && rps >= 2 && e && e[i] && e[i + 1] && (e[i]->flags & kEpPair) && e[i]->role == 0 &&
+        (e[i + 1]->flags & kEpPair) && e[i + 1]->role == 1 &&
+        !((e[i]->flags | e[i + 1]->flags) & (kEpNorm | kEpResidual)) &&
+        (e[i]->flags & kEpScale) == (e[i + 1]->flags & kEpScale) &&
+        e[i]->scale_ss == e[i + 1]->scale_ss && e[i]->scale_n == e[i + 1]->scale_n &&
+        e[i]->eps == e[i + 1]->eps && v[i]->x == v[i + 1]->x && v[i + 1]->rows == v[i]->rows &&
+        tuning().lk_pair_in_wave)
+      in_wave[i] = true;
   int64_t bb = 0, max_wave_steps = 0;
   for (int i = 0; i < n; ++i) {
-    const int64_t steps = (v[i]->rows + rps - 1) / rps;
-    int64_t want = (int64_t)((double)target_blocks * (double)v[i]->rows / (double)total_rows + 0.5);
+    const bool up_half = i > 0 && in_wave[i - 1];
+    const int rpm = in_wave[i] ? rps / 2 : rps;
+    const int64_t steps = (v[i]->rows + rpm - 1) / rpm;
+    const double share = (in_wave[i] ? 2.0 : 1.0) * (double)v[i]->rows / (double)total_rows;
+    int64_t want = (int64_t)((double)target_blocks * share + 0.5);
     if (want < 1) want = 1;
     if (want > steps) want = steps;
+    if (up_half) want = 0;
     LkDesc& d = grp.d[i];
     d.W = static_cast<const uint8_t*>(v[i]->W);
     d.x = v[i]->x;
     d.y = v[i]->y;
     d.rows = (int)v[i]->rows;
     d.block_begin = (int)bb;
-    d.q = (int)(steps / want);
-    d.r = (int)(steps % want);
+    d.q = want ? (int)(steps / want) : 0;
+    d.r = want ? (int)(steps % want) : 0;
     d.nsb = nsb;
     if (e && e[i]) {
       grp.ep[i] = *e[i];
-      d.ep_flags = e[i]->flags;
+      if (in_wave[i]) grp.ep[i].flags |= kEpPairInWave;
+      d.ep_flags = grp.ep[i].flags;
       d.scale_ss = e[i]->scale_ss;
       d.scale_n = e[i]->scale_n;
     }
     bb += want;
-    const int64_t ws = ((steps + want - 1) / want + bw - 1) / bw;
-    if (ws > max_wave_steps) max_wave_steps = ws;
+    if (want) {
+      const int64_t ws = ((steps + want - 1) / want + bw - 1) / bw;
+      if (ws > max_wave_steps) max_wave_steps = ws;
+    }
   }
   grp.total_blocks = (int)bb;
   const int depth = max_wave_steps <= 2 ? 2 : 4;
