@@ -315,7 +315,7 @@ __device__ __forceinline__ LkBlock lk_block_single(const uint8_t* W, const float
   return o;
 }
 
-template <int kNsb, int kDepth, int kW, bool kEp>
+template <int kNsb, int kDepth, int kW, bool kEp, bool kQ40 = false>
 __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGroup* grp);
 
 template <int kNsb, int kDepth, int kW, bool kEp>
@@ -325,6 +325,14 @@ __global__ __launch_bounds__(kW * 64) void gemv_q4k_lk_kernel(LkGroup grp) {
   __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   lk_run<kNsb, kDepth, kW, kEp>(lk_block<kW>(grp, (int)blockIdx.x, wave), xl, &grp);
+}
+
+// The same for a launch of Q4_0 GEMVs (no epilogues).
+template <int kNsb, int kDepth, int kW>
+__global__ __launch_bounds__(kW * 64) void gemv_q4_0_lk_kernel(LkGroup grp) {
+  __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  lk_run<kNsb, kDepth, kW, false, true>(lk_block<kW>(grp, (int)blockIdx.x, wave), xl, &grp);
 }
 
 template <int kNsb, int kDepth, int kW>
@@ -337,7 +345,19 @@ __global__ __launch_bounds__(kW * 64) void gemv_q4k_lk1_kernel(const uint8_t* W,
                                   xl, nullptr);
 }
 
-template <int kNsb, int kDepth, int kW, bool kEp>
+// Q4_0 rows of 256 kNsb weights (the same 0.5625 bytes per weight as Q4_K):
+// a lane's quarter is two 18-byte blocks, read as nine aligned words (36 u is
+// a multiple of 4; the first block's codes are re-aligned with v_alignbyte).
+template <int kNsb, int kDepth, int kW>
+__global__ __launch_bounds__(kW * 64) void gemv_q4_0_lk1_kernel(const uint8_t* W, const float* x,
+                                                                float* y, int rows, int q, int r) {
+  __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  lk_run<kNsb, kDepth, kW, false, true>(
+      lk_block_single<kW>(W, x, y, rows, q, r, kNsb, (int)blockIdx.x, wave), xl, nullptr);
+}
+
+template <int kNsb, int kDepth, int kW, bool kEp, bool kQ40>
 __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGroup* grp) {
   constexpr int kU = 4 * kNsb;                 // lanes per row
   constexpr int kRps = 64 / kU;                // rows per step
@@ -397,9 +417,18 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
     const uint32_t rr = lim < rpm - 1 ? (uint32_t)((int64_t)rsub < lim ? rsub : lim) : (uint32_t)rsub;
     const uint32_t off = rr * kRowBytes + hoff;
     const GQK_GLOBAL uint8_t* base = Wl + r0 * (int64_t)kRowBytes;
-    L.h = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + off);
-    L.qa = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + (off + qoff));
-    L.qb = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + (off + qoff + 16));
+    if constexpr (kQ40) {
+      // blocks 2 u, 2 u + 1 of the row: bytes [36 u, 36 u + 36) as 9 words
+      const GQK_GLOBAL uint32_t* w =
+          reinterpret_cast<const GQK_GLOBAL uint32_t*>(base + (rr * kRowBytes + 36u * (uint32_t)u));
+      L.h = lk_u32x4{w[0], w[1], w[2], w[3]};
+      L.qa = lk_u32x4{w[4], w[5], w[6], w[7]};
+      L.qb = lk_u32x4{w[8], 0u, 0u, 0u};
+    } else {
+      L.h = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + off);
+      L.qa = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + (off + qoff));
+      L.qb = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + (off + qoff + 16));
+    }
   };
   LkLoad ring[kDepth];
 #pragma unroll
@@ -438,6 +467,41 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
   // Step i: the dot products of the lane's 64 weights of rows
   // (st0 + i) kRps .. + kRps - 1, summed per row and stored.
   auto step = [&](const LkLoad& L) {
+    if constexpr (kQ40) {
+      // words: d0 | codes 0..1, codes 2..5, 6..9, 10..13, codes 14..15 | d1,
+      // then block 1's 16 codes; w = (code - 8) d, so each block adds
+      // 512 d sum(code / 512 x) - 8 d sum(x)
+      const uint32_t w[9] = {L.h.x, L.h.y, L.h.z, L.h.w, L.qa.x, L.qa.y, L.qa.z, L.qa.w, L.qb.x};
+      const float d0 = half_lo(w[0]), d1 = half_hi(w[4]);
+      uint32_t c[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        c[k] = __builtin_amdgcn_alignbyte(w[k + 1], w[k], 2);   // block 0, codes 4k .. 4k + 3
+        c[4 + k] = w[5 + k];                                     // block 1
+      }
+      float s0a = 0.f, s0b = 0.f, s1a = 0.f, s1b = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        // byte j of a block: low nibble = weight j, high nibble = weight j + 16
+        float l0[4], h0[4], l1[4], h1[4];
+        nibbles_div512(opaque(c[k] & 0x0F0F0F0Fu), l0);
+        nibbles_div512(opaque((c[k] >> 4) & 0x0F0F0F0Fu), h0);
+        nibbles_div512(opaque(c[4 + k] & 0x0F0F0F0Fu), l1);
+        nibbles_div512(opaque((c[4 + k] >> 4) & 0x0F0F0F0Fu), h1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s0a = fmaf(l0[e], xv[4 * k + e], s0a);
+          s0b = fmaf(h0[e], xv[16 + 4 * k + e], s0b);
+          s1a = fmaf(l1[e], xv[32 + 4 * k + e], s1a);
+          s1b = fmaf(h1[e], xv[48 + 4 * k + e], s1b);
+        }
+      }
+      float r = (d0 * 512.0f) * (s0a + s0b);
+      r = fmaf(d1 * 512.0f, s1a + s1b, r);
+      r = fmaf(-8.0f * d0, xs0, r);
+      r = fmaf(-8.0f * d1, xs1, r);
+      return r;
+    }
     float dsc0, dsc1, dmm0, dmm1;
     q4k_pair_scales(L.h.x, L.h.y, L.h.z, L.h.w, sh, hi_mask, dsc0, dsc1, dmm0, dmm1);
     const uint32_t qw[8] = {L.qa.x, L.qa.y, L.qa.z, L.qa.w, L.qb.x, L.qb.y, L.qb.z, L.qb.w};
@@ -529,8 +593,18 @@ struct LkxLoad {
   lk_u32x4 h, qa, qb;
 };
 
-template <int kQ, int kDepth, int kW, bool kEp>
-__global__ __launch_bounds__(kW * 64) void gemv_q4k_lkx_kernel(LkGroup grp) {
+//
+// kType is the row format: GGUF type 12 (Q4_K: a quarter is one 32-byte nibble
+// group plus its super-block's 16-byte header) or 2 (Q4_0, rows of 17 .. 48
+// x 256 weights, the same 0.5625 bytes per weight: a quarter is two 18-byte
+// blocks; no epilogues). One kernel body for both: the compiler allocated
+// about 100 more registers (and spilled) when the same body sat in an inlined
+// function behind two thin kernels.
+template <int kType, int kQ, int kDepth, int kW, bool kEp>
+__global__ __launch_bounds__(kW * 64) void gemv_lkx_kernel(LkGroup grp) {
+  static_assert(kType == 12 || kType == 2, "Q4_K or Q4_0 rows");
+  static_assert(kType == 12 || !kEp, "no epilogues on Q4_0");
+  constexpr bool kQ40 = kType == 2;
   // [K + K/16] padded x, then [K/32] sub-block sums
   extern __shared__ __attribute__((aligned(16))) float xl[];
   const int tid = threadIdx.x;
@@ -585,9 +659,17 @@ __global__ __launch_bounds__(kW * 64) void gemv_q4k_lkx_kernel(LkGroup grp) {
     const GQK_GLOBAL uint8_t* base = B.W + row * (int64_t)row_bytes;
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
-      L[q].h = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + hoff[q]);
-      L[q].qa = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + qoff[q]);
-      L[q].qb = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + (qoff[q] + 16));
+      if constexpr (kQ40) {
+        const GQK_GLOBAL uint32_t* w =
+            reinterpret_cast<const GQK_GLOBAL uint32_t*>(base + 36u * (uint32_t)uqc[q]);
+        L[q].h = lk_u32x4{w[0], w[1], w[2], w[3]};
+        L[q].qa = lk_u32x4{w[4], w[5], w[6], w[7]};
+        L[q].qb = lk_u32x4{w[8], 0u, 0u, 0u};
+      } else {
+        L[q].h = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + hoff[q]);
+        L[q].qa = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + qoff[q]);
+        L[q].qb = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + (qoff[q] + 16));
+      }
     }
   };
   LkxLoad ring[kDepth][kQ];
@@ -623,6 +705,40 @@ __global__ __launch_bounds__(kW * 64) void gemv_q4k_lkx_kernel(LkGroup grp) {
     float r = 0.f;
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
+      if constexpr (kQ40) {
+        // two 18-byte blocks: block 0's codes re-aligned, block 1's aligned;
+        // byte j of a block: low nibble weight j, high nibble weight j + 16
+        const uint32_t w[9] = {L[q].h.x, L[q].h.y, L[q].h.z, L[q].h.w, L[q].qa.x,
+                               L[q].qa.y, L[q].qa.z, L[q].qa.w, L[q].qb.x};
+        const float d0 = half_lo(w[0]), d1 = half_hi(w[4]);
+        const lk_f32x4* xp = reinterpret_cast<const lk_f32x4*>(&xl[68 * uqc[q]]);
+        float s0a = 0.f, s0b = 0.f, s1a = 0.f, s1b = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t c0 = __builtin_amdgcn_alignbyte(w[k + 1], w[k], 2);
+          const uint32_t c1 = w[5 + k];
+          float l0[4], h0[4], l1[4], h1[4];
+          nibbles_div512(opaque(c0 & 0x0F0F0F0Fu), l0);
+          nibbles_div512(opaque((c0 >> 4) & 0x0F0F0F0Fu), h0);
+          nibbles_div512(opaque(c1 & 0x0F0F0F0Fu), l1);
+          nibbles_div512(opaque((c1 >> 4) & 0x0F0F0F0Fu), h1);
+          const lk_f32x4 xa = xp[k], xb = xp[4 + k], xc = xp[8 + k], xd = xp[12 + k];
+          s0a = fmaf(l0[0], xa.x, s0a); s0a = fmaf(l0[1], xa.y, s0a);
+          s0a = fmaf(l0[2], xa.z, s0a); s0a = fmaf(l0[3], xa.w, s0a);
+          s0b = fmaf(h0[0], xb.x, s0b); s0b = fmaf(h0[1], xb.y, s0b);
+          s0b = fmaf(h0[2], xb.z, s0b); s0b = fmaf(h0[3], xb.w, s0b);
+          s1a = fmaf(l1[0], xc.x, s1a); s1a = fmaf(l1[1], xc.y, s1a);
+          s1a = fmaf(l1[2], xc.z, s1a); s1a = fmaf(l1[3], xc.w, s1a);
+          s1b = fmaf(h1[0], xd.x, s1b); s1b = fmaf(h1[1], xd.y, s1b);
+          s1b = fmaf(h1[2], xd.z, s1b); s1b = fmaf(h1[3], xd.w, s1b);
+        }
+        float rq = (d0 * 512.0f) * (s0a + s0b);
+        rq = fmaf(d1 * 512.0f, s1a + s1b, rq);
+        rq = fmaf(-8.0f * d0, xs0[q], rq);
+        rq = fmaf(-8.0f * d1, xs1[q], rq);
+        r += val[q] ? rq : 0.f;
+        continue;
+      }
       float dsc0, dsc1, dmm0, dmm1;
       q4k_pair_scales(L[q].h.x, L[q].h.y, L[q].h.z, L[q].h.w, sh[q], him[q], dsc0, dsc1, dmm0, dmm1);
       const uint32_t qw[8] = {L[q].qa.x, L[q].qa.y, L[q].qa.z, L[q].qa.w,

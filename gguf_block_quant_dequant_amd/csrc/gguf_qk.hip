@@ -67,6 +67,7 @@ struct Tuning {
   int lk_bw = 4;             // waves per block, rows of <= 16 super-blocks (4 or 8)
   int lkx_bw = 8;            // waves per block, longer rows (4 or 8)
   int lk_pair_in_wave = 1;   // gate/up pairs: both rows of an index in one wave
+  int q4_0_lk = 1;           // Q4_0 rows of <= 16 x 256 weights: lanes-along-K kernel
 };
 
 static const Tuning& tuning() {
@@ -94,6 +95,7 @@ static const Tuning& tuning() {
       if (key == "lk_bw" && (v == 4 || v == 8)) r.lk_bw = v;
       if (key == "lkx_bw" && (v == 4 || v == 8)) r.lkx_bw = v;
       if (key == "lk_pair_in_wave" && (v == 0 || v == 1)) r.lk_pair_in_wave = v;
+      if (key == "q4_0_lk" && (v == 0 || v == 1)) r.q4_0_lk = v;
       const char* comma = std::strchr(eq, ',');
       if (!comma) break;
       p = comma + 1;
@@ -350,8 +352,32 @@ static void launch_lk_nsb(const LkGroup& grp, int depth, hipStream_t stream) {
     hipLaunchKernelGGL((gemv_q4k_lk_kernel<kNsb, 4, kW, kEp>), grid, block, 0, stream, grp);
 }
 
+// One Q4_0 GEMV whose rows hold 256, 512, ..., 4096 weights (the lanes-along-K
+// mapping, the descriptor as scalar arguments).
 template <int kNsb>
-static void launch_lk_nsb(const LkGroup& grp, int depth, int waves, bool ep, hipStream_t stream) {
+static void launch_q4_0_lk(const LkDesc& d, int blocks, int depth, hipStream_t stream) {
+  const dim3 grid((unsigned)blocks), block(4 * 64);
+  if (depth <= 2)
+    hipLaunchKernelGGL((gemv_q4_0_lk1_kernel<kNsb, 2, 4>), grid, block, 0, stream, d.W, d.x, d.y, d.rows,
+                       d.q, d.r);
+  else
+    hipLaunchKernelGGL((gemv_q4_0_lk1_kernel<kNsb, 4, 4>), grid, block, 0, stream, d.W, d.x, d.y, d.rows,
+                       d.q, d.r);
+}
+
+template <int kNsb>
+static void launch_lk_nsb(const LkGroup& grp, int depth, int waves, bool ep, bool q40,
+                          hipStream_t stream) {
+  if (q40) {
+    const dim3 grid((unsigned)grp.total_blocks), block(4 * 64);
+    if (grp.n == 1 && tuning().lk_single)
+      launch_q4_0_lk<kNsb>(grp.d[0], grp.total_blocks, depth, stream);
+    else if (depth <= 2)
+      hipLaunchKernelGGL((gemv_q4_0_lk_kernel<kNsb, 2, 4>), grid, block, 0, stream, grp);
+    else
+      hipLaunchKernelGGL((gemv_q4_0_lk_kernel<kNsb, 4, 4>), grid, block, 0, stream, grp);
+    return;
+  }
   if (ep)
     launch_lk_nsb<kNsb, 4, true>(grp, depth, stream);
   else if (waves == 8)
@@ -361,12 +387,14 @@ static void launch_lk_nsb(const LkGroup& grp, int depth, int waves, bool ep, hip
 }
 
 template <int kQ, int kW>
-static void launch_lkx(const LkGroup& grp, size_t lds, bool ep, hipStream_t stream) {
+static void launch_lkx(const LkGroup& grp, size_t lds, bool ep, bool q40, hipStream_t stream) {
   const dim3 grid((unsigned)grp.total_blocks), block(kW * 64);
-  if (ep)
-    hipLaunchKernelGGL((gemv_q4k_lkx_kernel<kQ, 2, kW, true>), grid, block, lds, stream, grp);
+  if (q40)
+    hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q4_0, kQ, 2, kW, false>), grid, block, lds, stream, grp);
+  else if (ep)
+    hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q4_K, kQ, 2, kW, true>), grid, block, lds, stream, grp);
   else
-    hipLaunchKernelGGL((gemv_q4k_lkx_kernel<kQ, 2, kW, false>), grid, block, lds, stream, grp);
+    hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q4_K, kQ, 2, kW, false>), grid, block, lds, stream, grp);
 }
 }
 
@@ -376,7 +404,7 @@ static void launch_lkx(const LkGroup& grp, size_t lds, bool ep, hipStream_t stre
 // on one GEMV, and at most 256 partial sums for an input RMSN.
 static bool lk_fits(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n) {
   const int64_t c = v[0]->cols;
-  if (c != 256 && c != 512 && c != 1024 && c != 2048 && c != 4096 && (c <= 4096 || c > kLkxMaxK))
+  if (c % 256 || (c != 256 && c != 512 && c != 1024 && c != 2048 && c != 4096 && (c <= 4096 || c > kLkxMaxK)))
     return false;
   for (int i = 0; i < n; ++i) {
     if (v[i]->cols != c || v[i]->rows > (int64_t(1) << 30)) return false;
@@ -394,13 +422,13 @@ static bool lk_fits(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, 
 // (at least one, at most one per row step); a shallow load ring when a wave
 // has only a few steps.
 static int launch_lk(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n,
-                     hipStream_t stream) {
+                     hipStream_t stream, bool q40 = false) {
   const int nsb = (int)(v[0]->cols / 256);
   const bool longrow = nsb > 16;
   const int rps = longrow ? 1 : 64 / (4 * nsb);
   bool ep = false;
   for (int i = 0; i < n; ++i) ep = ep || (e && e[i] && e[i]->flags != 0);
-  const int bw = longrow ? tuning().lkx_bw : ep ? 4 : tuning().lk_bw;   // waves per block
+  const int bw = longrow ? tuning().lkx_bw : (ep || q40) ? 4 : tuning().lk_bw;   // waves per block
   LkGroup grp{};
   grp.n = n;
   int64_t total_rows = 0;
@@ -458,31 +486,44 @@ static int launch_lk(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e,
     const size_t lds = (size_t)(256 * nsb) * 4 * 35 / 32;   // x padded + sub-block sums
     if (bw == 8) {
       if (kq == 2)
-        launch_lkx<2, 8>(grp, lds, ep, stream);
+        launch_lkx<2, 8>(grp, lds, ep, q40, stream);
       else
-        launch_lkx<3, 8>(grp, lds, ep, stream);
+        launch_lkx<3, 8>(grp, lds, ep, q40, stream);
     } else {
       if (kq == 2)
-        launch_lkx<2, 4>(grp, lds, ep, stream);
+        launch_lkx<2, 4>(grp, lds, ep, q40, stream);
       else
-        launch_lkx<3, 4>(grp, lds, ep, stream);
+        launch_lkx<3, 4>(grp, lds, ep, q40, stream);
     }
     return launch_status();
   }
   switch (nsb) {
-    case 1: launch_lk_nsb<1>(grp, depth, bw, ep, stream); break;
-    case 2: launch_lk_nsb<2>(grp, depth, bw, ep, stream); break;
-    case 4: launch_lk_nsb<4>(grp, depth, bw, ep, stream); break;
-    case 8: launch_lk_nsb<8>(grp, depth, bw, ep, stream); break;
-    default: launch_lk_nsb<16>(grp, depth, bw, ep, stream); break;
+    case 1: launch_lk_nsb<1>(grp, depth, bw, ep, q40, stream); break;
+    case 2: launch_lk_nsb<2>(grp, depth, bw, ep, q40, stream); break;
+    case 4: launch_lk_nsb<4>(grp, depth, bw, ep, q40, stream); break;
+    case 8: launch_lk_nsb<8>(grp, depth, bw, ep, q40, stream); break;
+    default: launch_lk_nsb<16>(grp, depth, bw, ep, q40, stream); break;
   }
   return launch_status();
 }
+
+static int launch_other(int type, const void* W, const float* x, float* y, int64_t rows,
+                        int64_t cols, hipStream_t stream);
 
 // Launches one planned group.
 static int launch_group(int type, const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n,
                         const ScratchArea* scratch, hipStream_t stream) {
   if (type == GGUF_QK_TYPE_Q4_K && tuning().q4k_lk && lk_fits(v, e, n)) return launch_lk(v, e, n, stream);
+  if (type == GGUF_QK_TYPE_Q4_0) {
+    // rows of 256 .. 12288 weights in multiples of 256 (no epilogues on Q4_0):
+    // the lanes-along-K kernels; else the lane-quad kernel, one launch each
+    if (tuning().q4_0_lk && lk_fits(v, nullptr, n)) return launch_lk(v, nullptr, n, stream, true);
+    for (int i = 0; i < n; ++i) {
+      const int st = launch_other(type, v[i]->W, v[i]->x, v[i]->y, v[i]->rows, v[i]->cols, stream);
+      if (st) return st;
+    }
+    return GGUF_QK_OK;
+  }
   GemvGroup grp;
   const int64_t tasks = plan_group(type, v, e, n, &grp);
   float* partials = const_cast<float*>(scratch->partials);
@@ -529,14 +570,14 @@ static int launch_other(int type, const void* W, const float* x, float* y, int64
 
 static int launch_step(const gguf_qk_gemv* list, const GemvEpilogue* eps, int n,
                        const ScratchArea* scratch, hipStream_t stream) {
-  // Q4_0 and Q6_K GEMVs: one launch each (no grouping, no epilogue)
+  // Q6_K GEMVs: one launch each (no grouping, no epilogue)
   for (int i = 0; i < n; ++i) {
     const gguf_qk_gemv& g = list[i];
-    if ((g.type != GGUF_QK_TYPE_Q4_0 && g.type != GGUF_QK_TYPE_Q6_K) || g.rows == 0) continue;
+    if (g.type != GGUF_QK_TYPE_Q6_K || g.rows == 0) continue;
     const int st = launch_other(g.type, g.W, g.x, g.y, g.rows, g.cols, stream);
     if (st) return st;
   }
-  for (int type : {GGUF_QK_TYPE_Q4_K, GGUF_QK_TYPE_Q8_0}) {
+  for (int type : {GGUF_QK_TYPE_Q4_K, GGUF_QK_TYPE_Q4_0, GGUF_QK_TYPE_Q8_0}) {
     const gguf_qk_gemv* grp[kMaxGroup];
     const GemvEpilogue* ge[kMaxGroup];
     int k = 0;
@@ -792,6 +833,13 @@ static int matvec_other(int type, const void* W, const float* x, float* y, int64
   if (rows == 0) return GGUF_QK_OK;
   st = current_device(nullptr);
   if (st) return st;
+  if (type == GGUF_QK_TYPE_Q4_0) {
+    ScratchArea* scratch = nullptr;
+    st = current_device(&scratch);
+    if (st) return st;
+    const gguf_qk_gemv g{W, x, y, rows, cols, type, 0, {0}};
+    return launch_step(&g, nullptr, 1, scratch, stream);
+  }
   return launch_other(type, W, x, y, rows, cols, stream);
 }
 

@@ -82,6 +82,8 @@ def test_dequant_q6_k_extreme_fields():
 
 
 @pytest.mark.parametrize("fmt,rows,cols", [("q4_0", 1, 32), ("q4_0", 5, 96), ("q4_0", 300, 2048),
+                                           ("q4_0", 3, 4128), ("q4_0", 70, 4608), ("q4_0", 9, 12288),
+                                           ("q4_0", 9, 12544),
                                            ("q4_0", 2048, 11008), ("q4_0", 11008, 2048),
                                            ("q6_k", 1, 256), ("q6_k", 7, 768), ("q6_k", 333, 2816),
                                            ("q6_k", 2048, 11008), ("q6_k", 11008, 2048)])
@@ -98,6 +100,27 @@ def test_gemv_matches_oracle(fmt, rows, cols):
     assert ok and e <= TOL_F32, e
     y2 = host(fn(Wd, xd, rows=rows, cols=cols))
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
+# Q4_0 rows of 256 .. 4096 weights take the lanes-along-K kernel (two 18-byte
+# blocks per lane); row counts leave partial steps; integer weights and x make
+# every partial sum exact.
+@pytest.mark.parametrize("cols", [256, 512, 1024, 2048, 4096])
+@pytest.mark.parametrize("rows", [1, 5, 130])
+def test_gemv_q4_0_lanes_along_k(rows, cols):
+    gen, ref, _, fn = FMTS["q4_0"]
+    rng = np.random.default_rng([rows, cols, 9])
+    w = gen(rng, rows, cols)
+    x = synth.activations_f32(rng, cols)
+    y = host(fn(dev(w), dev(x), rows=rows, cols=cols))
+    e, ok = oracle.floored_rel_err(y, oracle.matvec_f64(ref(w, rows, cols), x))
+    assert ok and e <= TOL_F32, e
+    q4 = b"".join(pack_q4_0_block(0x3C00, [int(v) for v in rng.integers(0, 16, 32)])
+                  for _ in range(rows * cols // 32))
+    w4 = np.frombuffer(q4, np.uint8)
+    xi = rng.integers(-8, 9, cols).astype(np.float32)
+    yi = host(fn(dev(w4), dev(xi), rows=rows, cols=cols))
+    assert np.array_equal(yi.astype(np.float64), oracle.dequant_q4_0_f64(w4, rows, cols) @ xi.astype(np.float64))
 
 
 def test_gemv_integer_cases_are_exact():
