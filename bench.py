@@ -385,15 +385,17 @@ def other_types_pass(torch, g, synth, reps=5):
 
 def cpu_baseline():
     """The oracle as it stands, on a bounded sample of the same workload:
-    layer 0's seven Q4_K GEMVs and the first 8192 rows of the Q8_0 head,
-    decoded to fp32 and multiplied in fp64 with NumPy, one BLAS thread."""
+    layers 0..7's seven Q4_K GEMVs each and the first 32768 rows of the Q8_0
+    head (about 13 s of work on one core), decoded to fp32 and multiplied in
+    fp64 with NumPy, one BLAS thread."""
     from threadpoolctl import threadpool_limits
 
     import oracle
     import synth
 
-    stages = synth.decode_stream(n_layers=1, head=False, threads=4)
-    head_rows = 8192
+    n_layers = 8
+    stages = synth.decode_stream(n_layers=n_layers, head=False, threads=4)
+    head_rows = 32768
     hw = synth.q8_0_weights(synth.rng_for(synth.DECODE_CFG_ID, 1000, synth.TENSOR_IDS["head"]),
                             head_rows, synth.HIDDEN)
     hx = synth.activations_f32(synth.rng_for(synth.DECODE_CFG_ID, 1000, 100), synth.HIDDEN)
@@ -407,7 +409,8 @@ def cpu_baseline():
         dt = time.perf_counter() - t0
     gbps = nbytes / dt / 1e9
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"layer 0 q,k,v,o,gate,up,down (Q4_K) + head rows 0..{head_rows - 1} (Q8_0): "
+            "sample": f"layers 0..{n_layers - 1} q,k,v,o,gate,up,down (Q4_K) + head rows 0..{head_rows - 1} "
+                      f"(Q8_0): "
                       f"{nbytes} weight bytes in {dt:.2f} s; tokens/s-equiv "
                       f"{gbps * 1e9 / synth.decode_stream_bytes():.4f}"}
 

@@ -315,6 +315,25 @@ __device__ __forceinline__ LkBlock lk_block_single(const uint8_t* W, const float
   return o;
 }
 
+// Two GEMVs of one x, their descriptors in 14 dwords of scalar kernel
+// arguments (all preloaded into SGPRs: 14 is the most the dispatcher places;
+// the grid size, a hidden argument, would be a memory load): blocks [0, bb1)
+// take GEMV 0, blocks [bb1, bb1 + nb1) GEMV 1, and each GEMV's steps of kRps
+// rows are split over its blocks as the host splits them (the first r blocks
+// q + 1 steps, the others q), q and r formed here by one uniform division.
+template <int kW, int kRps>
+__device__ __forceinline__ LkBlock lk_block_two(const uint8_t* W0, const uint8_t* W1, const float* x,
+                                                float* y0, float* y1, int rows0, int rows1, int bb1,
+                                                int nb1, int nsb, int b, int wave) {
+  const bool second = b >= bb1;
+  const uint32_t rows = (uint32_t)(second ? rows1 : rows0);
+  const uint32_t nb = (uint32_t)(second ? nb1 : bb1);
+  const uint32_t steps = (rows + kRps - 1) / kRps;
+  const uint32_t q = steps / nb, r = steps - q * nb;
+  return lk_block_single<kW>(second ? W1 : W0, x, second ? y1 : y0, (int)rows, (int)q, (int)r, nsb,
+                             second ? b - bb1 : b, wave);
+}
+
 template <int kNsb, int kDepth, int kW, bool kEp, bool kQ40 = false>
 __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGroup* grp);
 
@@ -355,6 +374,20 @@ __global__ __launch_bounds__(kW * 64) void gemv_q4_0_lk1_kernel(const uint8_t* W
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   lk_run<kNsb, kDepth, kW, false, true>(
       lk_block_single<kW>(W, x, y, rows, q, r, kNsb, (int)blockIdx.x, wave), xl, nullptr);
+}
+
+// Two GEMVs of one x (stages without epilogues), the descriptors as preloaded
+// scalar arguments; kType 12 (Q4_K) or 2 (Q4_0).
+template <int kType, int kNsb, int kDepth, int kW>
+__global__ __launch_bounds__(kW * 64) void gemv_lk2_kernel(const uint8_t* W0, const uint8_t* W1,
+                                                           const float* x, float* y0, float* y1,
+                                                           int rows0, int rows1, int bb1, int nb1) {
+  static_assert(kType == 12 || kType == 2, "Q4_K or Q4_0 rows");
+  __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  lk_run<kNsb, kDepth, kW, false, kType == 2>(
+      lk_block_two<kW, 16 / kNsb>(W0, W1, x, y0, y1, rows0, rows1, bb1, nb1, kNsb, (int)blockIdx.x, wave),
+      xl, nullptr);
 }
 
 template <int kNsb, int kDepth, int kW, bool kEp, bool kQ40>
@@ -597,11 +630,15 @@ struct LkxLoad {
 // kType is the row format: GGUF type 12 (Q4_K: a quarter is one 32-byte nibble
 // group plus its super-block's 16-byte header) or 2 (Q4_0, rows of 17 .. 48
 // x 256 weights, the same 0.5625 bytes per weight: a quarter is two 18-byte
-// blocks; no epilogues). One kernel body for both: the compiler allocated
-// about 100 more registers (and spilled) when the same body sat in an inlined
-// function behind two thin kernels.
-template <int kType, int kQ, int kDepth, int kW, bool kEp>
-__global__ __launch_bounds__(kW * 64) void gemv_lkx_kernel(LkGroup grp) {
+// blocks; no epilogues). kSingle: one GEMV whose descriptor comes in the
+// leading scalar arguments (preloaded into SGPRs), else the group's. One
+// kernel body for all: the compiler allocated about 100 more registers (and
+// spilled) when the same body sat in an inlined function behind thin kernels.
+template <int kType, int kQ, int kDepth, int kW, bool kEp, bool kSingle>
+__global__ __launch_bounds__(kW * 64) void gemv_lkx_kernel(const uint8_t* W1, const float* x1, float* y1,
+                                                           int rows1, int q1, int r1, int nsb1,
+                                                           LkGroup grp) {
+  static_assert(!(kSingle && kEp), "epilogues come with the group");
   static_assert(kType == 12 || kType == 2, "Q4_K or Q4_0 rows");
   static_assert(kType == 12 || !kEp, "no epilogues on Q4_0");
   constexpr bool kQ40 = kType == 2;
@@ -610,7 +647,8 @@ __global__ __launch_bounds__(kW * 64) void gemv_lkx_kernel(LkGroup grp) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const LkBlock B = lk_block<kW>(grp, (int)blockIdx.x, wave);
+  const LkBlock B = kSingle ? lk_block_single<kW>(W1, x1, y1, rows1, q1, r1, nsb1, (int)blockIdx.x, wave)
+                            : lk_block<kW>(grp, (int)blockIdx.x, wave);
   const int nsb = B.nsb;
   const int U = 4 * nsb;                    // quarters per row
   const int K = 256 * nsb;

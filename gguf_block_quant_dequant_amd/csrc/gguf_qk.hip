@@ -67,6 +67,7 @@ struct Tuning {
   int lk_bw = 4;             // waves per block, rows of <= 16 super-blocks (4 or 8)
   int lkx_bw = 8;            // waves per block, longer rows (4 or 8)
   int lk_pair_in_wave = 1;   // gate/up pairs: both rows of an index in one wave
+  int lk_two = 1;            // two GEMVs of one x: descriptors as scalar arguments
   int q4_0_lk = 1;           // Q4_0 rows of <= 16 x 256 weights: lanes-along-K kernel
 };
 
@@ -95,6 +96,7 @@ static const Tuning& tuning() {
       if (key == "lk_bw" && (v == 4 || v == 8)) r.lk_bw = v;
       if (key == "lkx_bw" && (v == 4 || v == 8)) r.lkx_bw = v;
       if (key == "lk_pair_in_wave" && (v == 0 || v == 1)) r.lk_pair_in_wave = v;
+      if (key == "lk_two" && (v == 0 || v == 1)) r.lk_two = v;
       if (key == "q4_0_lk" && (v == 0 || v == 1)) r.q4_0_lk = v;
       const char* comma = std::strchr(eq, ',');
       if (!comma) break;
@@ -333,6 +335,26 @@ static int64_t plan_group(int type, const gguf_qk_gemv* const* v, const GemvEpil
 }
 
 extern "C++" {
+// Two GEMVs of one x without epilogues: both descriptors as scalar arguments.
+// (The kernel re-forms each GEMV's q and r from its rows and block count, so
+// both GEMVs must have blocks.)
+static bool lk_two(const LkGroup& grp) {
+  return grp.n == 2 && grp.d[0].x == grp.d[1].x && grp.d[1].block_begin > 0 &&
+         grp.d[1].block_begin < grp.total_blocks && tuning().lk_two;
+}
+
+template <int kType, int kNsb, int kW>
+static void launch_lk2(const LkGroup& grp, int depth, hipStream_t stream) {
+  const dim3 grid((unsigned)grp.total_blocks), block(kW * 64);
+  const LkDesc &a = grp.d[0], &b = grp.d[1];
+  if (depth <= 2)
+    hipLaunchKernelGGL((gemv_lk2_kernel<kType, kNsb, 2, kW>), grid, block, 0, stream, a.W, b.W, a.x, a.y, b.y,
+                       a.rows, b.rows, b.block_begin, grp.total_blocks - b.block_begin);
+  else
+    hipLaunchKernelGGL((gemv_lk2_kernel<kType, kNsb, 4, kW>), grid, block, 0, stream, a.W, b.W, a.x, a.y, b.y,
+                       a.rows, b.rows, b.block_begin, grp.total_blocks - b.block_begin);
+}
+
 template <int kNsb, int kW, bool kEp>
 static void launch_lk_nsb(const LkGroup& grp, int depth, hipStream_t stream) {
   const dim3 grid((unsigned)grp.total_blocks), block(kW * 64);
@@ -344,6 +366,10 @@ static void launch_lk_nsb(const LkGroup& grp, int depth, hipStream_t stream) {
     else
       hipLaunchKernelGGL((gemv_q4k_lk1_kernel<kNsb, 4, kW>), grid, block, 0, stream, d.W, d.x, d.y,
                          d.rows, d.q, d.r);
+    return;
+  }
+  if (!kEp && lk_two(grp)) {
+    launch_lk2<GGUF_QK_TYPE_Q4_K, kNsb, kW>(grp, depth, stream);
     return;
   }
   if (depth <= 2)
@@ -372,6 +398,8 @@ static void launch_lk_nsb(const LkGroup& grp, int depth, int waves, bool ep, boo
     const dim3 grid((unsigned)grp.total_blocks), block(4 * 64);
     if (grp.n == 1 && tuning().lk_single)
       launch_q4_0_lk<kNsb>(grp.d[0], grp.total_blocks, depth, stream);
+    else if (lk_two(grp))
+      launch_lk2<GGUF_QK_TYPE_Q4_0, kNsb, 4>(grp, depth, stream);
     else if (depth <= 2)
       hipLaunchKernelGGL((gemv_q4_0_lk_kernel<kNsb, 2, 4>), grid, block, 0, stream, grp);
     else
@@ -389,12 +417,29 @@ static void launch_lk_nsb(const LkGroup& grp, int depth, int waves, bool ep, boo
 template <int kQ, int kW>
 static void launch_lkx(const LkGroup& grp, size_t lds, bool ep, bool q40, hipStream_t stream) {
   const dim3 grid((unsigned)grp.total_blocks), block(kW * 64);
-  if (q40)
-    hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q4_0, kQ, 2, kW, false>), grid, block, lds, stream, grp);
+  // one GEMV without epilogue: its descriptor as (preloaded) scalar arguments
+  const bool single = grp.n == 1 && !ep && tuning().lk_single;
+  const LkDesc& d = grp.d[0];
+  const uint8_t* W = single ? d.W : nullptr;
+  const float* x = single ? d.x : nullptr;
+  float* y = single ? d.y : nullptr;
+  const int rows = single ? d.rows : 0, q = single ? d.q : 0, r = single ? d.r : 0;
+  const int nsb = single ? d.nsb : 0;
+  if (q40 && single)
+    hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q4_0, kQ, 2, kW, false, true>), grid, block, lds, stream,
+                       W, x, y, rows, q, r, nsb, grp);
+  else if (q40)
+    hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q4_0, kQ, 2, kW, false, false>), grid, block, lds, stream,
+                       W, x, y, rows, q, r, nsb, grp);
+  else if (single)
+    hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q4_K, kQ, 2, kW, false, true>), grid, block, lds, stream,
+                       W, x, y, rows, q, r, nsb, grp);
   else if (ep)
-    hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q4_K, kQ, 2, kW, true>), grid, block, lds, stream, grp);
+    hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q4_K, kQ, 2, kW, true, false>), grid, block, lds, stream,
+                       W, x, y, rows, q, r, nsb, grp);
   else
-    hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q4_K, kQ, 2, kW, false>), grid, block, lds, stream, grp);
+    hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q4_K, kQ, 2, kW, false, false>), grid, block, lds, stream,
+                       W, x, y, rows, q, r, nsb, grp);
 }
 }
 

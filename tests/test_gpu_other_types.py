@@ -177,3 +177,36 @@ def test_mixed_types_in_one_decode_batch():
         xin = host(inputs[name])
         e, ok = oracle.floored_rel_err(host(Y[name]), oracle.matvec_f64(W32[name], xin))
         assert ok and e <= TOL_F32, (name, e)
+
+
+def test_q4_0_decode_batch_ragged_stages():
+    """Stages of 1 to 4 Q4_0 GEMVs sharing x (grouped lanes-along-K launches,
+    two-GEMV launches with scalar descriptors, long rows), ragged row counts,
+    a later stage reading an earlier output; every row against the oracle."""
+    rng = np.random.default_rng(52)
+    row_choices = [1, 7, 64, 65, 300, 1031]
+    k_choices = [256, 2048, 4096, 5120, 11008]
+    ents, checks, prev = [], [], None
+    for si in range(14):
+        m = int(rng.integers(1, 5))
+        cols = int(rng.choice(k_choices))
+        if prev is not None and prev[1].numel() == cols:
+            xin, xh = prev[1], None   # read the previous stage's output
+        else:
+            xh = synth.activations_f32(rng, cols)
+            xin = dev(xh)
+        last = None
+        for _ in range(m):
+            rows = int(rng.choice(row_choices))
+            w = synth.q4_0_weights(rng, rows, cols)
+            y = torch.empty(rows, dtype=torch.float32, device=DEV)
+            ents.append((g.TYPE_Q4_0, dev(w), xin, y, si))
+            checks.append((si, w, rows, cols, xin, y))
+            last = (rows, y)
+        prev = last
+    say("q4_0 ragged batch:", len(ents), "GEMVs in 14 stages")
+    g.gguf_qmatvec_batch(g.GemvBatch(ents))
+    for si, w, rows, cols, xin, y in checks:
+        ref = oracle.matvec_f64(oracle.dequant_q4_0_f32(w, rows, cols), host(xin))
+        e, ok = oracle.floored_rel_err(host(y), ref)
+        assert ok and e <= TOL_F32, (si, rows, cols, e)
