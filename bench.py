@@ -43,7 +43,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 BF16_DENSE_PEAK_TFLOPS = 2500.0
-DOMINANT_KERNEL = "gemv_q4k_lk_kernel"
+DOMINANT_KERNEL = "gemv_lk_kernel"
 KERNEL_SOURCES = ["gguf_block_quant_dequant_amd/csrc/gemv_lk.hpp",
                   "gguf_block_quant_dequant_amd/csrc/device_common.hpp"]
 SMALL_BATCH_TOKENS = (8, 32, 64)
@@ -373,7 +373,7 @@ def other_types_pass(torch, g, synth, reps=5):
                     "type": name, "weight_bytes": wbytes, "ms_per_pass": round(ms, 4),
                     "GBps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
                     "roofline": {"bound": "hbm",
-                                 "kernel": "gemv_q4_0_lk_kernel" if name == "q4_0" else "gemv_q6_k_kernel",
+                                 "kernel": "gemv_lk_kernel (Q4_0)" if name == "q4_0" else "gemv_q6_k_kernel",
                                  "achieved": round(gbps, 1),
                                  "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                  "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}})

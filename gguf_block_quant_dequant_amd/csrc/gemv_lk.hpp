@@ -191,6 +191,21 @@ struct LkLoad {
   lk_u32x4 h, qa, qb;
 };
 
+// A Q8_0 quarter: two 34-byte blocks, 17 dwords.
+struct LkLoad8 {
+  lk_u32x4 a, b, c, d;
+  uint32_t e;
+};
+
+template <int kType>
+struct LkLoadOf {
+  using type = LkLoad;
+};
+template <>
+struct LkLoadOf<8> {
+  using type = LkLoad8;
+};
+
 // ---------------------------------------------------------------------------
 // The neighbouring steps of a decode layer fused into these GEMVs (the same
 // epilogues as the lane-per-row kernels, see GemvEpilogue): per row, in the
@@ -334,68 +349,57 @@ __device__ __forceinline__ LkBlock lk_block_two(const uint8_t* W0, const uint8_t
                              second ? b - bb1 : b, wave);
 }
 
-template <int kNsb, int kDepth, int kW, bool kEp, bool kQ40 = false>
+template <int kNsb, int kDepth, int kW, bool kEp, int kType = 12>
 __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGroup* grp);
 
-template <int kNsb, int kDepth, int kW, bool kEp>
-__global__ __launch_bounds__(kW * 64) void gemv_q4k_lk_kernel(LkGroup grp) {
+// kType is the row format, a GGUF type id: 12 (Q4_K), 2 (Q4_0: the same
+// 0.5625 bytes per weight, a lane's quarter two 18-byte blocks read as nine
+// aligned words, 36 u being a multiple of 4, the first block's codes
+// re-aligned with v_alignbyte) or 8 (Q8_0: a quarter two 34-byte blocks, 17
+// aligned words at 68 u). Epilogues on Q4_K only.
+template <int kType, int kNsb, int kDepth, int kW, bool kEp>
+__global__ __launch_bounds__(kW * 64) void gemv_lk_kernel(LkGroup grp) {
   // x in LDS with 4 floats of padding after every 64: the slice of lane u
   // starts at float 68 u, i.e. on bank 4 u mod 32 (16-byte reads conflict-free)
   __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  lk_run<kNsb, kDepth, kW, kEp>(lk_block<kW>(grp, (int)blockIdx.x, wave), xl, &grp);
+  lk_run<kNsb, kDepth, kW, kEp, kType>(lk_block<kW>(grp, (int)blockIdx.x, wave), xl, &grp);
 }
 
-// The same for a launch of Q4_0 GEMVs (no epilogues).
-template <int kNsb, int kDepth, int kW>
-__global__ __launch_bounds__(kW * 64) void gemv_q4_0_lk_kernel(LkGroup grp) {
+// One GEMV, its descriptor as (preloaded) scalar arguments.
+template <int kType, int kNsb, int kDepth, int kW>
+__global__ __launch_bounds__(kW * 64) void gemv_lk1_kernel(const uint8_t* W, const float* x, float* y,
+                                                           int rows, int q, int r) {
   __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  lk_run<kNsb, kDepth, kW, false, true>(lk_block<kW>(grp, (int)blockIdx.x, wave), xl, &grp);
-}
-
-template <int kNsb, int kDepth, int kW>
-__global__ __launch_bounds__(kW * 64) void gemv_q4k_lk1_kernel(const uint8_t* W, const float* x,
-                                                                     float* y, int rows, int q,
-                                                                     int r) {
-  __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  lk_run<kNsb, kDepth, kW, false>(lk_block_single<kW>(W, x, y, rows, q, r, kNsb, (int)blockIdx.x, wave),
-                                  xl, nullptr);
-}
-
-// Q4_0 rows of 256 kNsb weights (the same 0.5625 bytes per weight as Q4_K):
-// a lane's quarter is two 18-byte blocks, read as nine aligned words (36 u is
-// a multiple of 4; the first block's codes are re-aligned with v_alignbyte).
-template <int kNsb, int kDepth, int kW>
-__global__ __launch_bounds__(kW * 64) void gemv_q4_0_lk1_kernel(const uint8_t* W, const float* x,
-                                                                float* y, int rows, int q, int r) {
-  __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  lk_run<kNsb, kDepth, kW, false, true>(
-      lk_block_single<kW>(W, x, y, rows, q, r, kNsb, (int)blockIdx.x, wave), xl, nullptr);
+  lk_run<kNsb, kDepth, kW, false, kType>(lk_block_single<kW>(W, x, y, rows, q, r, kNsb, (int)blockIdx.x, wave),
+                                         xl, nullptr);
 }
 
 // Two GEMVs of one x (stages without epilogues), the descriptors as preloaded
-// scalar arguments; kType 12 (Q4_K) or 2 (Q4_0).
+// scalar arguments.
 template <int kType, int kNsb, int kDepth, int kW>
 __global__ __launch_bounds__(kW * 64) void gemv_lk2_kernel(const uint8_t* W0, const uint8_t* W1,
                                                            const float* x, float* y0, float* y1,
                                                            int rows0, int rows1, int bb1, int nb1) {
-  static_assert(kType == 12 || kType == 2, "Q4_K or Q4_0 rows");
   __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  lk_run<kNsb, kDepth, kW, false, kType == 2>(
+  lk_run<kNsb, kDepth, kW, false, kType>(
       lk_block_two<kW, 16 / kNsb>(W0, W1, x, y0, y1, rows0, rows1, bb1, nb1, kNsb, (int)blockIdx.x, wave),
       xl, nullptr);
 }
 
-template <int kNsb, int kDepth, int kW, bool kEp, bool kQ40>
+template <int kNsb, int kDepth, int kW, bool kEp, int kType>
 __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGroup* grp) {
+  static_assert(kType == 12 || kType == 2 || kType == 8, "Q4_K, Q4_0 or Q8_0 rows");
+  static_assert(kType == 12 || !kEp, "epilogues on Q4_K only");
+  constexpr bool kQ40 = kType == 2, kQ80 = kType == 8;
+  using Load = typename LkLoadOf<kType>::type;
   constexpr int kU = 4 * kNsb;                 // lanes per row
   constexpr int kRps = 64 / kU;                // rows per step
   constexpr int kK = 256 * kNsb;
-  constexpr uint32_t kRowBytes = (uint32_t)kNsb * kQ4KBlockBytes;
+  // bytes per 256 weights: 144 (Q4_K, Q4_0) or 272 (Q8_0)
+  constexpr uint32_t kRowBytes = (uint32_t)kNsb * (kQ80 ? 8u * kQ80BlockBytes : (uint32_t)kQ4KBlockBytes);
   constexpr int kXF4 = kK / 4;                 // float4 of x
   static_assert(kU >= 4 && kU <= 64 && 64 % kU == 0, "rows of 1 to 16 super-blocks");
   const int tid = threadIdx.x;
@@ -443,14 +447,23 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
   // re-read its last row; neither is ever stored. A wave without steps
   // (n = 0) re-reads step max(st0 - 1, 0), which exists.
   const int64_t last = st0 + n - 1 > 0 ? st0 + n - 1 : 0;
-  auto issue = [&](int64_t st, LkLoad& L) {
+  auto issue = [&](int64_t st, Load& L) {
     st = st < last ? st : last;
     const int64_t r0 = st * rpm;
     const int64_t lim = rows - 1 - r0;
     const uint32_t rr = lim < rpm - 1 ? (uint32_t)((int64_t)rsub < lim ? rsub : lim) : (uint32_t)rsub;
     const uint32_t off = rr * kRowBytes + hoff;
     const GQK_GLOBAL uint8_t* base = Wl + r0 * (int64_t)kRowBytes;
-    if constexpr (kQ40) {
+    if constexpr (kQ80) {
+      // blocks 2 u, 2 u + 1 of the row: bytes [68 u, 68 u + 68) as 17 words
+      const GQK_GLOBAL uint32_t* w =
+          reinterpret_cast<const GQK_GLOBAL uint32_t*>(base + (rr * kRowBytes + 68u * (uint32_t)u));
+      L.a = lk_u32x4{w[0], w[1], w[2], w[3]};
+      L.b = lk_u32x4{w[4], w[5], w[6], w[7]};
+      L.c = lk_u32x4{w[8], w[9], w[10], w[11]};
+      L.d = lk_u32x4{w[12], w[13], w[14], w[15]};
+      L.e = w[16];
+    } else if constexpr (kQ40) {
       // blocks 2 u, 2 u + 1 of the row: bytes [36 u, 36 u + 36) as 9 words
       const GQK_GLOBAL uint32_t* w =
           reinterpret_cast<const GQK_GLOBAL uint32_t*>(base + (rr * kRowBytes + 36u * (uint32_t)u));
@@ -463,7 +476,7 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
       L.qb = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + (off + qoff + 16));
     }
   };
-  LkLoad ring[kDepth];
+  Load ring[kDepth];
 #pragma unroll
   for (int p = 0; p < kDepth; ++p) issue(st0 + p, ring[p]);
 
@@ -499,8 +512,31 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
 
   // Step i: the dot products of the lane's 64 weights of rows
   // (st0 + i) kRps .. + kRps - 1, summed per row and stored.
-  auto step = [&](const LkLoad& L) {
-    if constexpr (kQ40) {
+  auto step = [&](const Load& L) {
+    if constexpr (kQ80) {
+      // words: d0 | q 0..1, q 2..29 (7 words), q 30..31 | d1, then block 1's
+      // 32 codes; w = q d, two independent sums per block
+      const uint32_t w[17] = {L.a.x, L.a.y, L.a.z, L.a.w, L.b.x, L.b.y, L.b.z, L.b.w, L.c.x,
+                              L.c.y, L.c.z, L.c.w, L.d.x, L.d.y, L.d.z, L.d.w, L.e};
+      const float d0 = half_lo(w[0]), d1 = half_hi(w[8]);
+      float s0a = 0.f, s0b = 0.f, s1a = 0.f, s1b = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t c0 = __builtin_amdgcn_alignbyte(w[k + 1], w[k], 2);   // block 0, q 4k .. 4k + 3
+        const uint32_t c1 = w[9 + k];                                         // block 1
+        float& a0 = (k & 1) ? s0b : s0a;
+        float& a1 = (k & 1) ? s1b : s1a;
+        a0 = fmaf(sbyte0(c0), xv[4 * k + 0], a0);
+        a0 = fmaf(sbyte1(c0), xv[4 * k + 1], a0);
+        a0 = fmaf(sbyte2(c0), xv[4 * k + 2], a0);
+        a0 = fmaf(sbyte3(c0), xv[4 * k + 3], a0);
+        a1 = fmaf(sbyte0(c1), xv[32 + 4 * k + 0], a1);
+        a1 = fmaf(sbyte1(c1), xv[32 + 4 * k + 1], a1);
+        a1 = fmaf(sbyte2(c1), xv[32 + 4 * k + 2], a1);
+        a1 = fmaf(sbyte3(c1), xv[32 + 4 * k + 3], a1);
+      }
+      return fmaf(d1, s1a + s1b, d0 * (s0a + s0b));
+    } else if constexpr (kQ40) {
       // words: d0 | codes 0..1, codes 2..5, 6..9, 10..13, codes 14..15 | d1,
       // then block 1's 16 codes; w = (code - 8) d, so each block adds
       // 512 d sum(code / 512 x) - 8 d sum(x)
@@ -534,31 +570,32 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
       r = fmaf(-8.0f * d0, xs0, r);
       r = fmaf(-8.0f * d1, xs1, r);
       return r;
-    }
-    float dsc0, dsc1, dmm0, dmm1;
-    q4k_pair_scales(L.h.x, L.h.y, L.h.z, L.h.w, sh, hi_mask, dsc0, dsc1, dmm0, dmm1);
-    const uint32_t qw[8] = {L.qa.x, L.qa.y, L.qa.z, L.qa.w, L.qb.x, L.qb.y, L.qb.z, L.qb.w};
-    float la0 = 0.f, la1 = 0.f, ha0 = 0.f, ha1 = 0.f;
+    } else {
+      float dsc0, dsc1, dmm0, dmm1;
+      q4k_pair_scales(L.h.x, L.h.y, L.h.z, L.h.w, sh, hi_mask, dsc0, dsc1, dmm0, dmm1);
+      const uint32_t qw[8] = {L.qa.x, L.qa.y, L.qa.z, L.qa.w, L.qb.x, L.qb.y, L.qb.z, L.qb.w};
+      float la0 = 0.f, la1 = 0.f, ha0 = 0.f, ha1 = 0.f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      // byte 4t + e: low nibble = weight 4t + e of sub-block 2 gq,
-      // high nibble = weight 4t + e of sub-block 2 gq + 1
-      float ql[4], qh[4];
-      nibbles_div512(opaque(qw[t] & 0x0F0F0F0Fu), ql);
-      nibbles_div512(opaque((qw[t] >> 4) & 0x0F0F0F0Fu), qh);
-      float& la = (t & 1) ? la1 : la0;
-      float& ha = (t & 1) ? ha1 : ha0;
+      for (int t = 0; t < 8; ++t) {
+        // byte 4t + e: low nibble = weight 4t + e of sub-block 2 gq,
+        // high nibble = weight 4t + e of sub-block 2 gq + 1
+        float ql[4], qh[4];
+        nibbles_div512(opaque(qw[t] & 0x0F0F0F0Fu), ql);
+        nibbles_div512(opaque((qw[t] >> 4) & 0x0F0F0F0Fu), qh);
+        float& la = (t & 1) ? la1 : la0;
+        float& ha = (t & 1) ? ha1 : ha0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        la = fmaf(ql[e], xv[4 * t + e], la);
-        ha = fmaf(qh[e], xv[32 + 4 * t + e], ha);
+        for (int e = 0; e < 4; ++e) {
+          la = fmaf(ql[e], xv[4 * t + e], la);
+          ha = fmaf(qh[e], xv[32 + 4 * t + e], ha);
+        }
       }
+      float r = dsc0 * (la0 + la1);
+      r = fmaf(dsc1, ha0 + ha1, r);
+      r = fmaf(-dmm0, xs0, r);
+      r = fmaf(-dmm1, xs1, r);
+      return r;
     }
-    float r = dsc0 * (la0 + la1);
-    r = fmaf(dsc1, ha0 + ha1, r);
-    r = fmaf(-dmm0, xs0, r);
-    r = fmaf(-dmm1, xs1, r);
-    return r;
   };
   auto finish = [&](float r, int i) {
     r = lk_segment_sum<kU>(r);

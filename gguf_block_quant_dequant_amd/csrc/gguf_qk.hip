@@ -68,7 +68,8 @@ struct Tuning {
   int lkx_bw = 8;            // waves per block, longer rows (4 or 8)
   int lk_pair_in_wave = 1;   // gate/up pairs: both rows of an index in one wave
   int lk_two = 1;            // two GEMVs of one x: descriptors as scalar arguments
-  int q4_0_lk = 1;           // Q4_0 rows of <= 16 x 256 weights: lanes-along-K kernel
+  int q4_0_lk = 1;           // Q4_0 rows of 256 .. 12288 weights: lanes-along-K kernels
+  int q8_0_lk = 1;           // Q8_0 rows of 256 .. 4096 weights: lanes-along-K kernels
 };
 
 static const Tuning& tuning() {
@@ -98,6 +99,7 @@ static const Tuning& tuning() {
       if (key == "lk_pair_in_wave" && (v == 0 || v == 1)) r.lk_pair_in_wave = v;
       if (key == "lk_two" && (v == 0 || v == 1)) r.lk_two = v;
       if (key == "q4_0_lk" && (v == 0 || v == 1)) r.q4_0_lk = v;
+      if (key == "q8_0_lk" && (v == 0 || v == 1)) r.q8_0_lk = v;
       const char* comma = std::strchr(eq, ',');
       if (!comma) break;
       p = comma + 1;
@@ -355,67 +357,49 @@ static void launch_lk2(const LkGroup& grp, int depth, hipStream_t stream) {
                        a.rows, b.rows, b.block_begin, grp.total_blocks - b.block_begin);
 }
 
-template <int kNsb, int kW, bool kEp>
+// One launch of the lanes-along-K kernels for rows of 256 kNsb weights of
+// type kType: one GEMV, two of one x, or a group from the descriptors.
+template <int kType, int kNsb, int kW, bool kEp>
 static void launch_lk_nsb(const LkGroup& grp, int depth, hipStream_t stream) {
   const dim3 grid((unsigned)grp.total_blocks), block(kW * 64);
   if (!kEp && grp.n == 1 && tuning().lk_single) {
     const LkDesc& d = grp.d[0];
     if (depth <= 2)
-      hipLaunchKernelGGL((gemv_q4k_lk1_kernel<kNsb, 2, kW>), grid, block, 0, stream, d.W, d.x, d.y,
+      hipLaunchKernelGGL((gemv_lk1_kernel<kType, kNsb, 2, kW>), grid, block, 0, stream, d.W, d.x, d.y,
                          d.rows, d.q, d.r);
     else
-      hipLaunchKernelGGL((gemv_q4k_lk1_kernel<kNsb, 4, kW>), grid, block, 0, stream, d.W, d.x, d.y,
+      hipLaunchKernelGGL((gemv_lk1_kernel<kType, kNsb, 4, kW>), grid, block, 0, stream, d.W, d.x, d.y,
                          d.rows, d.q, d.r);
     return;
   }
   if (!kEp && lk_two(grp)) {
-    launch_lk2<GGUF_QK_TYPE_Q4_K, kNsb, kW>(grp, depth, stream);
+    launch_lk2<kType, kNsb, kW>(grp, depth, stream);
     return;
   }
   if (depth <= 2)
-    hipLaunchKernelGGL((gemv_q4k_lk_kernel<kNsb, 2, kW, kEp>), grid, block, 0, stream, grp);
+    hipLaunchKernelGGL((gemv_lk_kernel<kType, kNsb, 2, kW, kEp>), grid, block, 0, stream, grp);
   else
-    hipLaunchKernelGGL((gemv_q4k_lk_kernel<kNsb, 4, kW, kEp>), grid, block, 0, stream, grp);
-}
-
-// One Q4_0 GEMV whose rows hold 256, 512, ..., 4096 weights (the lanes-along-K
-// mapping, the descriptor as scalar arguments).
-template <int kNsb>
-static void launch_q4_0_lk(const LkDesc& d, int blocks, int depth, hipStream_t stream) {
-  const dim3 grid((unsigned)blocks), block(4 * 64);
-  if (depth <= 2)
-    hipLaunchKernelGGL((gemv_q4_0_lk1_kernel<kNsb, 2, 4>), grid, block, 0, stream, d.W, d.x, d.y, d.rows,
-                       d.q, d.r);
-  else
-    hipLaunchKernelGGL((gemv_q4_0_lk1_kernel<kNsb, 4, 4>), grid, block, 0, stream, d.W, d.x, d.y, d.rows,
-                       d.q, d.r);
+    hipLaunchKernelGGL((gemv_lk_kernel<kType, kNsb, 4, kW, kEp>), grid, block, 0, stream, grp);
 }
 
 template <int kNsb>
-static void launch_lk_nsb(const LkGroup& grp, int depth, int waves, bool ep, bool q40,
+static void launch_lk_nsb(const LkGroup& grp, int depth, int waves, bool ep, int type,
                           hipStream_t stream) {
-  if (q40) {
-    const dim3 grid((unsigned)grp.total_blocks), block(4 * 64);
-    if (grp.n == 1 && tuning().lk_single)
-      launch_q4_0_lk<kNsb>(grp.d[0], grp.total_blocks, depth, stream);
-    else if (lk_two(grp))
-      launch_lk2<GGUF_QK_TYPE_Q4_0, kNsb, 4>(grp, depth, stream);
-    else if (depth <= 2)
-      hipLaunchKernelGGL((gemv_q4_0_lk_kernel<kNsb, 2, 4>), grid, block, 0, stream, grp);
-    else
-      hipLaunchKernelGGL((gemv_q4_0_lk_kernel<kNsb, 4, 4>), grid, block, 0, stream, grp);
-    return;
-  }
-  if (ep)
-    launch_lk_nsb<kNsb, 4, true>(grp, depth, stream);
+  if (type == GGUF_QK_TYPE_Q4_0)
+    launch_lk_nsb<GGUF_QK_TYPE_Q4_0, kNsb, 4, false>(grp, depth, stream);
+  else if (type == GGUF_QK_TYPE_Q8_0)
+    launch_lk_nsb<GGUF_QK_TYPE_Q8_0, kNsb, 4, false>(grp, depth, stream);
+  else if (ep)
+    launch_lk_nsb<GGUF_QK_TYPE_Q4_K, kNsb, 4, true>(grp, depth, stream);
   else if (waves == 8)
-    launch_lk_nsb<kNsb, 8, false>(grp, depth, stream);
+    launch_lk_nsb<GGUF_QK_TYPE_Q4_K, kNsb, 8, false>(grp, depth, stream);
   else
-    launch_lk_nsb<kNsb, 4, false>(grp, depth, stream);
+    launch_lk_nsb<GGUF_QK_TYPE_Q4_K, kNsb, 4, false>(grp, depth, stream);
 }
 
 template <int kQ, int kW>
-static void launch_lkx(const LkGroup& grp, size_t lds, bool ep, bool q40, hipStream_t stream) {
+static void launch_lkx(const LkGroup& grp, size_t lds, bool ep, int type, hipStream_t stream) {
+  const bool q40 = type == GGUF_QK_TYPE_Q4_0;
   const dim3 grid((unsigned)grp.total_blocks), block(kW * 64);
   // one GEMV without epilogue: its descriptor as (preloaded) scalar arguments
   const bool single = grp.n == 1 && !ep && tuning().lk_single;
@@ -467,13 +451,13 @@ static bool lk_fits(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, 
 // (at least one, at most one per row step); a shallow load ring when a wave
 // has only a few steps.
 static int launch_lk(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n,
-                     hipStream_t stream, bool q40 = false) {
+                     hipStream_t stream, int type = GGUF_QK_TYPE_Q4_K) {
   const int nsb = (int)(v[0]->cols / 256);
   const bool longrow = nsb > 16;
   const int rps = longrow ? 1 : 64 / (4 * nsb);
   bool ep = false;
   for (int i = 0; i < n; ++i) ep = ep || (e && e[i] && e[i]->flags != 0);
-  const int bw = longrow ? tuning().lkx_bw : (ep || q40) ? 4 : tuning().lk_bw;   // waves per block
+  const int bw = longrow ? tuning().lkx_bw : (ep || type != GGUF_QK_TYPE_Q4_K) ? 4 : tuning().lk_bw;
   LkGroup grp{};
   grp.n = n;
   int64_t total_rows = 0;
@@ -531,23 +515,23 @@ static int launch_lk(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e,
     const size_t lds = (size_t)(256 * nsb) * 4 * 35 / 32;   // x padded + sub-block sums
     if (bw == 8) {
       if (kq == 2)
-        launch_lkx<2, 8>(grp, lds, ep, q40, stream);
+        launch_lkx<2, 8>(grp, lds, ep, type, stream);
       else
-        launch_lkx<3, 8>(grp, lds, ep, q40, stream);
+        launch_lkx<3, 8>(grp, lds, ep, type, stream);
     } else {
       if (kq == 2)
-        launch_lkx<2, 4>(grp, lds, ep, q40, stream);
+        launch_lkx<2, 4>(grp, lds, ep, type, stream);
       else
-        launch_lkx<3, 4>(grp, lds, ep, q40, stream);
+        launch_lkx<3, 4>(grp, lds, ep, type, stream);
     }
     return launch_status();
   }
   switch (nsb) {
-    case 1: launch_lk_nsb<1>(grp, depth, bw, ep, q40, stream); break;
-    case 2: launch_lk_nsb<2>(grp, depth, bw, ep, q40, stream); break;
-    case 4: launch_lk_nsb<4>(grp, depth, bw, ep, q40, stream); break;
-    case 8: launch_lk_nsb<8>(grp, depth, bw, ep, q40, stream); break;
-    default: launch_lk_nsb<16>(grp, depth, bw, ep, q40, stream); break;
+    case 1: launch_lk_nsb<1>(grp, depth, bw, ep, type, stream); break;
+    case 2: launch_lk_nsb<2>(grp, depth, bw, ep, type, stream); break;
+    case 4: launch_lk_nsb<4>(grp, depth, bw, ep, type, stream); break;
+    case 8: launch_lk_nsb<8>(grp, depth, bw, ep, type, stream); break;
+    default: launch_lk_nsb<16>(grp, depth, bw, ep, type, stream); break;
   }
   return launch_status();
 }
@@ -562,12 +546,19 @@ static int launch_group(int type, const gguf_qk_gemv* const* v, const GemvEpilog
   if (type == GGUF_QK_TYPE_Q4_0) {
     // rows of 256 .. 12288 weights in multiples of 256 (no epilogues on Q4_0):
     // the lanes-along-K kernels; else the lane-quad kernel, one launch each
-    if (tuning().q4_0_lk && lk_fits(v, nullptr, n)) return launch_lk(v, nullptr, n, stream, true);
+    if (tuning().q4_0_lk && lk_fits(v, nullptr, n)) return launch_lk(v, nullptr, n, stream, type);
     for (int i = 0; i < n; ++i) {
       const int st = launch_other(type, v[i]->W, v[i]->x, v[i]->y, v[i]->rows, v[i]->cols, stream);
       if (st) return st;
     }
     return GGUF_QK_OK;
+  }
+  if (type == GGUF_QK_TYPE_Q8_0 && tuning().q8_0_lk && v[0]->cols <= 4096 && lk_fits(v, nullptr, n)) {
+    // Q8_0 rows of 256 .. 4096 weights (multiples of 256) without epilogues:
+    // the lanes-along-K kernels; else the lane-per-row kernel below
+    bool ep = false;
+    for (int i = 0; i < n; ++i) ep = ep || (e && e[i] && e[i]->flags != 0);
+    if (!ep) return launch_lk(v, nullptr, n, stream, type);
   }
   GemvGroup grp;
   const int64_t tasks = plan_group(type, v, e, n, &grp);

@@ -237,6 +237,31 @@ def test_matvec_q4_k_integer_exact_long_rows(cols):
     assert np.array_equal(y.astype(np.float64), (q @ x.astype(np.int64)).astype(np.float64))
 
 
+# Every Q8_0 row length the lanes-along-K kernels take (4 to 64 lanes per
+# row) and the first past them (lane-per-row kernel), with partial steps.
+@pytest.mark.parametrize("cols", [256, 512, 1024, 2048, 4096, 4352])
+@pytest.mark.parametrize("rows", [1, 3, 130])
+def test_matvec_q8_0_every_row_length(rows, cols):
+    y, ref, _, _ = _matvec_case("q8_0", rows, cols, 12)
+    e, ok = oracle.floored_rel_err(y, ref)
+    assert ok and e <= TOL_F32, e
+
+
+@pytest.mark.parametrize("cols", [256, 2048, 4096])
+def test_matvec_q8_0_integer_exact(cols):
+    # d = 1 (fp16 0x3C00), codes -128..127, integer x in [-8, 8]: every
+    # partial sum is an integer below 2^24, so the result is exact in any order
+    rng = np.random.default_rng(23)
+    rows = 37
+    q = rng.integers(-128, 128, size=(rows, cols))
+    blocks = q.reshape(rows, cols // 32, 32).astype(np.int8).view(np.uint8)
+    d = np.full((rows, cols // 32, 2), [0x00, 0x3C], np.uint8)
+    w = np.concatenate([d, blocks], axis=2).reshape(rows, -1)
+    x = rng.integers(-8, 9, size=cols).astype(np.float32)
+    y = host(g.gguf_qmatvec_q8_0(dev(w), dev(x)))
+    assert np.array_equal(y.astype(np.float64), (q @ x.astype(np.int64)).astype(np.float64))
+
+
 def test_matvec_q4_k_integer_exact():
     rng = np.random.default_rng(7)
     rows, cols = 130, 1024
