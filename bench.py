@@ -47,7 +47,7 @@ DOMINANT_KERNEL = "gemv_lk_kernel"
 KERNEL_SOURCES = ["gguf_block_quant_dequant_amd/csrc/gemv_lk.hpp",
                   "gguf_block_quant_dequant_amd/csrc/device_common.hpp"]
 SMALL_BATCH_TOKENS = (8, 32, 64)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_q4k_lk_kernel_decode_stream_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_lk_kernel_decode_stream_traffic.md")
 
 
 def log(*a):
