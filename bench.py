@@ -336,8 +336,8 @@ def other_types_pass(torch, g, synth, reps=5):
     """Batch-1 GEMV passes over the 36-layer shapes stored as Q4_0 and as Q6_K:
     one layer's seven tensors generated per type, cloned to 36 distinct device
     copies (so each pass streams every byte from HBM), as one decode batch in
-    the Q4_K pass's stages ({q,k,v}, {o}, {gate,up}, {down} per layer; Q4_0
-    GEMVs of a stage share a launch, Q6_K GEMVs take one each), as a HIP graph.
+    the Q4_K pass's stages ({q,k,v}, {o}, {gate,up}, {down} per layer; the
+    GEMVs of a stage share a lanes-along-K launch), as a HIP graph.
     Returns one labelled record per type."""
     dev = "cuda:0"
     out = []
@@ -373,7 +373,7 @@ def other_types_pass(torch, g, synth, reps=5):
                     "type": name, "weight_bytes": wbytes, "ms_per_pass": round(ms, 4),
                     "GBps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
                     "roofline": {"bound": "hbm",
-                                 "kernel": "gemv_lk_kernel (Q4_0)" if name == "q4_0" else "gemv_q6_k_kernel",
+                                 "kernel": f"gemv_lk_kernel ({name.upper()})",
                                  "achieved": round(gbps, 1),
                                  "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                  "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}})

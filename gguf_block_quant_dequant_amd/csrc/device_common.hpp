@@ -10,6 +10,8 @@ constexpr int kQ80BlockBytes = 34;     // fp16 scale + 32 int8
 constexpr int kQ80BlockWeights = 32;
 constexpr int kQ4KBlockBytes = 144;    // fp16 d, fp16 dmin, 12 B scales, 128 B quants
 constexpr int kQ4KBlockWeights = 256;
+constexpr int kQ6KBlockBytes = 210;    // 128 B low 4 bits, 64 B high 2 bits, 16 int8 scales, fp16 d
+constexpr int kQ6KBlockWeights = 256;
 constexpr int kWave = 64;
 
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;

@@ -197,6 +197,20 @@ struct LkLoad8 {
   uint32_t e;
 };
 
+// A Q6_K unit of 64 weights: within half n (0, 1) of a super-block, bytes
+// 16h .. 16h + 15 (h = 0, 1) of its 64 low-bit bytes, the same 16 bytes 32
+// further on, 16 bytes of its 32 high-bit bytes, its 8 scale bytes and d. The
+// 210-byte super-blocks leave every field 2 bytes off a word boundary in
+// every other super-block (mis = 2): each 16-byte field is read as the five
+// aligned words around it and re-aligned, the scales as three words (the
+// third re-reads the second when mis = 0, so no read leaves the super-block),
+// d as a 2-byte load.
+struct LkLoad6 {
+  uint32_t a[5], b[5], h[5], s[3];
+  uint32_t d;
+  uint32_t mis;
+};
+
 template <int kType>
 struct LkLoadOf {
   using type = LkLoad;
@@ -205,6 +219,85 @@ template <>
 struct LkLoadOf<8> {
   using type = LkLoad8;
 };
+template <>
+struct LkLoadOf<14> {
+  using type = LkLoad6;
+};
+
+// Unit u of the Q6_K row at rowp: super-block u / 4, half (u / 2) % 2,
+// h = u % 2. Lane slice order of its 64 weights: position 16 m + t is weight
+// 128 n + 32 m + 16 h + t of the super-block (m = 0..3, t = 0..15).
+__device__ __forceinline__ void q6k_unit_issue(const GQK_GLOBAL uint8_t* rowp, uint32_t u, LkLoad6& L) {
+  const uint32_t sb = (u >> 2) * (uint32_t)kQ6KBlockBytes;
+  const uint32_t n = (u >> 1) & 1u, h = u & 1u;
+  const uint32_t mis = ((uint32_t)(uintptr_t)rowp + sb) & 2u;
+  // (rowp + sb) - mis as pointer arithmetic: for the first super-block of a
+  // row that starts 2 bytes off a word boundary the window starts 2 bytes
+  // before the row (inside the previous row; row 0 is aligned), and sb - mis
+  // in 32-bit unsigned arithmetic would wrap
+  const GQK_GLOBAL uint32_t* w = reinterpret_cast<const GQK_GLOBAL uint32_t*>((rowp + sb) - mis);
+  const uint32_t ia = 16u * n + 4u * h, ib = ia + 8u, ih = 32u + 8u * n + 4u * h, is = 48u + 2u * n;
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    L.a[k] = w[ia + k];
+    L.b[k] = w[ib + k];
+    L.h[k] = w[ih + k];
+  }
+  L.s[0] = w[is];
+  L.s[1] = w[is + 1];
+  L.s[2] = w[is + 1 + (mis >> 1)];
+  L.d = *reinterpret_cast<const GQK_GLOBAL uint16_t*>(rowp + sb + 208u);
+  L.mis = mis;
+}
+
+// The unit's 64-weight dot product with its slice xv (xv[16 m + t], see
+// above) and the slice's sums over each m (xs[m]):
+//   d sum_m sc_m (sum_t code x - 32 sum_t x),   code = low 4 | high 2 << 4.
+// Byte l of the low-bit fields holds weights l (low nibble of the first
+// field), 32 + l (low nibble of the second), 64 + l and 96 + l (the high
+// nibbles); bits 0-1, 2-3, 4-5, 6-7 of high-bit byte l are their top bits.
+template <class XAt>
+__device__ __forceinline__ float q6k_unit_dot(const LkLoad6& L, uint32_t h, XAt xat, const float (&xs)[4]) {
+  const uint32_t mis = L.mis;
+  uint32_t qa[4], qb[4], hh[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    qa[k] = __builtin_amdgcn_alignbyte(L.a[k + 1], L.a[k], mis);
+    qb[k] = __builtin_amdgcn_alignbyte(L.b[k + 1], L.b[k], mis);
+    hh[k] = __builtin_amdgcn_alignbyte(L.h[k + 1], L.h[k], mis);
+  }
+  // one run of 16 weights (one scale) at a time
+  float S[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t c = m == 0   ? (qa[k] & 0x0F0F0F0Fu) | ((hh[k] & 0x03030303u) << 4)
+                         : m == 1 ? (qb[k] & 0x0F0F0F0Fu) | ((hh[k] & 0x0C0C0C0Cu) << 2)
+                         : m == 2 ? ((qa[k] >> 4) & 0x0F0F0F0Fu) | (hh[k] & 0x30303030u)
+                                  : ((qb[k] >> 4) & 0x0F0F0F0Fu) | ((hh[k] >> 2) & 0x30303030u);
+      acc = fmaf((float)(c & 0xFFu), xat(16 * m + 4 * k + 0), acc);
+      acc = fmaf((float)((c >> 8) & 0xFFu), xat(16 * m + 4 * k + 1), acc);
+      acc = fmaf((float)((c >> 16) & 0xFFu), xat(16 * m + 4 * k + 2), acc);
+      acc = fmaf((float)(c >> 24), xat(16 * m + 4 * k + 3), acc);
+    }
+    S[m] = acc;
+  }
+  // scale of weights 128 n + 32 m + 16 h + t: byte 2 m + h of the 8 scale
+  // bytes of half n
+  const uint32_t s0 = __builtin_amdgcn_alignbyte(L.s[1], L.s[0], mis);
+  const uint32_t s1 = __builtin_amdgcn_alignbyte(L.s[2], L.s[1], mis);
+  const uint32_t sh = 8u * h;
+  float r = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t word = m < 2 ? s0 : s1;
+    const float sc = (float)(int)(int8_t)((word >> (16u * (m & 1) + sh)) & 0xFFu);
+    r = fmaf(sc, fmaf(-32.0f, xs[m], S[m]), r);
+  }
+  return half_lo(L.d) * r;
+}
 
 // ---------------------------------------------------------------------------
 // The neighbouring steps of a decode layer fused into these GEMVs (the same
@@ -349,6 +442,22 @@ __device__ __forceinline__ LkBlock lk_block_two(const uint8_t* W0, const uint8_t
                              second ? b - bb1 : b, wave);
 }
 
+// LDS float index of x's float4 i in the staged layout: lane slice u (64
+// floats) at 68 u, four floats of padding after each. Slice u holds weights
+// 64 u .. 64 u + 63 in order, except for Q6_K, whose unit u holds weights
+// 128 n + 32 m + 16 h + t of super-block u / 4 (n = (u / 2) % 2, h = u % 2)
+// at position 16 m + t.
+template <int kType>
+__device__ __forceinline__ int lk_x_slot(int i) {
+  if constexpr (kType == 14) {
+    const int e = 4 * i, r = e & 255;
+    const int u = 4 * (e >> 8) + 2 * (r >> 7) + ((r >> 4) & 1);
+    return 68 * u + 16 * ((r >> 5) & 3) + (r & 15);
+  } else {
+    return 4 * i + (i >> 4) * 4;
+  }
+}
+
 template <int kNsb, int kDepth, int kW, bool kEp, int kType = 12>
 __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGroup* grp);
 
@@ -391,15 +500,16 @@ __global__ __launch_bounds__(kW * 64) void gemv_lk2_kernel(const uint8_t* W0, co
 
 template <int kNsb, int kDepth, int kW, bool kEp, int kType>
 __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGroup* grp) {
-  static_assert(kType == 12 || kType == 2 || kType == 8, "Q4_K, Q4_0 or Q8_0 rows");
+  static_assert(kType == 12 || kType == 2 || kType == 8 || kType == 14, "Q4_K, Q4_0, Q8_0 or Q6_K rows");
   static_assert(kType == 12 || !kEp, "epilogues on Q4_K only");
-  constexpr bool kQ40 = kType == 2, kQ80 = kType == 8;
+  constexpr bool kQ40 = kType == 2, kQ80 = kType == 8, kQ6 = kType == 14;
   using Load = typename LkLoadOf<kType>::type;
   constexpr int kU = 4 * kNsb;                 // lanes per row
   constexpr int kRps = 64 / kU;                // rows per step
   constexpr int kK = 256 * kNsb;
-  // bytes per 256 weights: 144 (Q4_K, Q4_0) or 272 (Q8_0)
-  constexpr uint32_t kRowBytes = (uint32_t)kNsb * (kQ80 ? 8u * kQ80BlockBytes : (uint32_t)kQ4KBlockBytes);
+  // bytes per 256 weights: 144 (Q4_K, Q4_0), 272 (Q8_0) or 210 (Q6_K)
+  constexpr uint32_t kRowBytes =
+      (uint32_t)kNsb * (kQ80 ? 8u * kQ80BlockBytes : kQ6 ? (uint32_t)kQ6KBlockBytes : (uint32_t)kQ4KBlockBytes);
   constexpr int kXF4 = kK / 4;                 // float4 of x
   static_assert(kU >= 4 && kU <= 64 && 64 % kU == 0, "rows of 1 to 16 super-blocks");
   const int tid = threadIdx.x;
@@ -454,7 +564,9 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
     const uint32_t rr = lim < rpm - 1 ? (uint32_t)((int64_t)rsub < lim ? rsub : lim) : (uint32_t)rsub;
     const uint32_t off = rr * kRowBytes + hoff;
     const GQK_GLOBAL uint8_t* base = Wl + r0 * (int64_t)kRowBytes;
-    if constexpr (kQ80) {
+    if constexpr (kQ6) {
+      q6k_unit_issue(base + rr * kRowBytes, (uint32_t)u, L);
+    } else if constexpr (kQ80) {
       // blocks 2 u, 2 u + 1 of the row: bytes [68 u, 68 u + 68) as 17 words
       const GQK_GLOBAL uint32_t* w =
           reinterpret_cast<const GQK_GLOBAL uint32_t*>(base + (rr * kRowBytes + 68u * (uint32_t)u));
@@ -484,7 +596,7 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
   for (int j = 0; j < kXIt; ++j) {
     const int i = tid + j * kW * 64;
     if (kXF4 % (kW * 64) == 0 || i < kXF4)
-      *reinterpret_cast<lk_f32x4*>(&xl[4 * i + (i >> 4) * 4]) = xg[j];
+      *reinterpret_cast<lk_f32x4*>(&xl[lk_x_slot<kType>(i)]) = xg[j];
   }
   __syncthreads();
   LkEp E;
@@ -509,11 +621,20 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
     xs0 += xv[i];
     xs1 += xv[32 + i];
   }
+  float xq[4] = {0.f, 0.f, 0.f, 0.f};   // Q6_K: sums over the slice's four runs of 16
+  if constexpr (kQ6) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) xq[m] += xv[16 * m + t];
+  }
 
   // Step i: the dot products of the lane's 64 weights of rows
   // (st0 + i) kRps .. + kRps - 1, summed per row and stored.
   auto step = [&](const Load& L) {
-    if constexpr (kQ80) {
+    if constexpr (kQ6) {
+      return q6k_unit_dot(L, (uint32_t)u & 1u, [&](int i) { return xv[i]; }, xq);
+    } else if constexpr (kQ80) {
       // words: d0 | q 0..1, q 2..29 (7 words), q 30..31 | d1, then block 1's
       // 32 codes; w = q d, two independent sums per block
       const uint32_t w[17] = {L.a.x, L.a.y, L.a.z, L.a.w, L.b.x, L.b.y, L.b.z, L.b.w, L.c.x,
@@ -663,6 +784,15 @@ struct LkxLoad {
   lk_u32x4 h, qa, qb;
 };
 
+template <int kType>
+struct LkxLoadOf {
+  using type = LkxLoad;
+};
+template <>
+struct LkxLoadOf<14> {
+  using type = LkLoad6;
+};
+
 //
 // kType is the row format: GGUF type 12 (Q4_K: a quarter is one 32-byte nibble
 // group plus its super-block's 16-byte header) or 2 (Q4_0, rows of 17 .. 48
@@ -676,10 +806,12 @@ __global__ __launch_bounds__(kW * 64) void gemv_lkx_kernel(const uint8_t* W1, co
                                                            int rows1, int q1, int r1, int nsb1,
                                                            LkGroup grp) {
   static_assert(!(kSingle && kEp), "epilogues come with the group");
-  static_assert(kType == 12 || kType == 2, "Q4_K or Q4_0 rows");
-  static_assert(kType == 12 || !kEp, "no epilogues on Q4_0");
-  constexpr bool kQ40 = kType == 2;
-  // [K + K/16] padded x, then [K/32] sub-block sums
+  static_assert(kType == 12 || kType == 2 || kType == 14, "Q4_K, Q4_0 or Q6_K rows");
+  static_assert(kType == 12 || !kEp, "epilogues on Q4_K only");
+  constexpr bool kQ40 = kType == 2, kQ6 = kType == 14;
+  using XLoad = typename LkxLoadOf<kType>::type;
+  // [K + K/16] padded x, then [K/32] sub-block sums ([K/16] sums of runs of
+  // 16 for Q6_K)
   extern __shared__ __attribute__((aligned(16))) float xl[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -690,7 +822,7 @@ __global__ __launch_bounds__(kW * 64) void gemv_lkx_kernel(const uint8_t* W1, co
   const int U = 4 * nsb;                    // quarters per row
   const int K = 256 * nsb;
   const int nxf4 = K / 4;
-  const uint32_t row_bytes = (uint32_t)nsb * kQ4KBlockBytes;
+  const uint32_t row_bytes = (uint32_t)nsb * (kQ6 ? (uint32_t)kQ6KBlockBytes : (uint32_t)kQ4KBlockBytes);
   float* const xsum = xl + K + K / 16;
   float ss_share = 0.f;
   GemvEpilogue epl;
@@ -729,12 +861,14 @@ __global__ __launch_bounds__(kW * 64) void gemv_lkx_kernel(const uint8_t* W1, co
   const int64_t st0 = B.st0;
   const int n = B.n;
   const int64_t last = st0 + n - 1 > 0 ? st0 + n - 1 : 0;
-  auto issue = [&](int64_t row, LkxLoad (&L)[kQ]) {
+  auto issue = [&](int64_t row, XLoad (&L)[kQ]) {
     row = row < last ? row : last;
     const GQK_GLOBAL uint8_t* base = B.W + row * (int64_t)row_bytes;
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
-      if constexpr (kQ40) {
+      if constexpr (kQ6) {
+        q6k_unit_issue(base, (uint32_t)uqc[q], L[q]);
+      } else if constexpr (kQ40) {
         const GQK_GLOBAL uint32_t* w =
             reinterpret_cast<const GQK_GLOBAL uint32_t*>(base + 36u * (uint32_t)uqc[q]);
         L[q].h = lk_u32x4{w[0], w[1], w[2], w[3]};
@@ -747,7 +881,7 @@ __global__ __launch_bounds__(kW * 64) void gemv_lkx_kernel(const uint8_t* W1, co
       }
     }
   };
-  LkxLoad ring[kDepth][kQ];
+  XLoad ring[kDepth][kQ];
 #pragma unroll
   for (int p = 0; p < kDepth; ++p) issue(st0 + p, ring[p]);
 
@@ -758,29 +892,52 @@ __global__ __launch_bounds__(kW * 64) void gemv_lkx_kernel(const uint8_t* W1, co
   for (int j = 0; j < kXIt; ++j) {
     const int i = tid + j * kW * 64;
     const bool in = i < nxf4;
-    if (in) *reinterpret_cast<lk_f32x4*>(&xl[4 * i + (i >> 4) * 4]) = xg[j];
-    float t = in ? (xg[j].x + xg[j].y) + (xg[j].z + xg[j].w) : 0.f;
-    t += dpp_f32<0xB1>(t);    // quad_perm 1,0,3,2
-    t += dpp_f32<0x4E>(t);    // quad_perm 2,3,0,1
-    t += dpp_f32<0x141>(t);   // row_half_mirror
-    if (in && (tid & 7) == 0) xsum[i >> 3] = t;
+    if constexpr (kQ6) {
+      // the four threads 4m .. 4m + 3 hold one run of 16 (a unit's positions
+      // 16 m' .. 16 m' + 15); the first stores its sum at 4 u + m'
+      if (in) *reinterpret_cast<lk_f32x4*>(&xl[lk_x_slot<14>(i)]) = xg[j];
+      float t = in ? (xg[j].x + xg[j].y) + (xg[j].z + xg[j].w) : 0.f;
+      t += dpp_f32<0xB1>(t);    // quad_perm 1,0,3,2
+      t += dpp_f32<0x4E>(t);    // quad_perm 2,3,0,1
+      if (in && (tid & 3) == 0) xsum[lk_x_slot<14>(i) / 68 * 4 + ((lk_x_slot<14>(i) % 68) >> 4)] = t;
+    } else {
+      if (in) *reinterpret_cast<lk_f32x4*>(&xl[4 * i + (i >> 4) * 4]) = xg[j];
+      float t = in ? (xg[j].x + xg[j].y) + (xg[j].z + xg[j].w) : 0.f;
+      t += dpp_f32<0xB1>(t);    // quad_perm 1,0,3,2
+      t += dpp_f32<0x4E>(t);    // quad_perm 2,3,0,1
+      t += dpp_f32<0x141>(t);   // row_half_mirror
+      if (in && (tid & 7) == 0) xsum[i >> 3] = t;
+    }
   }
   __syncthreads();
   LkEp E;
   if constexpr (kEp) E = lk_ep(epl, ss_share);
   if (n > 0) {
   float xs0[kQ], xs1[kQ];
+  float xq6[kQ][4];
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
-    xs0[q] = xsum[2 * uqc[q]];
-    xs1[q] = xsum[2 * uqc[q] + 1];
+    if constexpr (kQ6) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) xq6[q][m] = xsum[4 * uqc[q] + m];
+    } else {
+      xs0[q] = xsum[2 * uqc[q]];
+      xs1[q] = xsum[2 * uqc[q] + 1];
+    }
   }
 
-  auto step = [&](const LkxLoad (&L)[kQ]) {
+  auto step = [&](const XLoad (&L)[kQ]) {
     float r = 0.f;
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
-      if constexpr (kQ40) {
+      if constexpr (kQ6) {
+        const float* xp = &xl[68 * uqc[q]];
+        const float rq = q6k_unit_dot(L[q], (uint32_t)uqc[q] & 1u, [&](int i) { return xp[i]; }, xq6[q]);
+        r += val[q] ? rq : 0.f;
+        // one quarter at a time: left free, the scheduler hoisted the LDS
+        // reads of all of them and spilled
+        __builtin_amdgcn_sched_barrier(0);
+      } else if constexpr (kQ40) {
         // two 18-byte blocks: block 0's codes re-aligned, block 1's aligned;
         // byte j of a block: low nibble weight j, high nibble weight j + 16
         const uint32_t w[9] = {L[q].h.x, L[q].h.y, L[q].h.z, L[q].h.w, L[q].qa.x,
@@ -812,37 +969,37 @@ __global__ __launch_bounds__(kW * 64) void gemv_lkx_kernel(const uint8_t* W1, co
         rq = fmaf(-8.0f * d0, xs0[q], rq);
         rq = fmaf(-8.0f * d1, xs1[q], rq);
         r += val[q] ? rq : 0.f;
-        continue;
-      }
-      float dsc0, dsc1, dmm0, dmm1;
-      q4k_pair_scales(L[q].h.x, L[q].h.y, L[q].h.z, L[q].h.w, sh[q], him[q], dsc0, dsc1, dmm0, dmm1);
-      const uint32_t qw[8] = {L[q].qa.x, L[q].qa.y, L[q].qa.z, L[q].qa.w,
-                              L[q].qb.x, L[q].qb.y, L[q].qb.z, L[q].qb.w};
-      const lk_f32x4* xp = reinterpret_cast<const lk_f32x4*>(&xl[68 * uqc[q]]);
-      float la0 = 0.f, la1 = 0.f, ha0 = 0.f, ha1 = 0.f;
+      } else {
+        float dsc0, dsc1, dmm0, dmm1;
+        q4k_pair_scales(L[q].h.x, L[q].h.y, L[q].h.z, L[q].h.w, sh[q], him[q], dsc0, dsc1, dmm0, dmm1);
+        const uint32_t qw[8] = {L[q].qa.x, L[q].qa.y, L[q].qa.z, L[q].qa.w,
+                                L[q].qb.x, L[q].qb.y, L[q].qb.z, L[q].qb.w};
+        const lk_f32x4* xp = reinterpret_cast<const lk_f32x4*>(&xl[68 * uqc[q]]);
+        float la0 = 0.f, la1 = 0.f, ha0 = 0.f, ha1 = 0.f;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const lk_f32x4 xa = xp[t];       // x of sub-block 2 gq, weights 4t .. 4t + 3
-        const lk_f32x4 xb = xp[8 + t];   // x of sub-block 2 gq + 1
-        float ql[4], qh[4];
-        nibbles_div512(opaque(qw[t] & 0x0F0F0F0Fu), ql);
-        nibbles_div512(opaque((qw[t] >> 4) & 0x0F0F0F0Fu), qh);
-        float& la = (t & 1) ? la1 : la0;
-        float& ha = (t & 1) ? ha1 : ha0;
-        la = fmaf(ql[0], xa.x, la);
-        la = fmaf(ql[1], xa.y, la);
-        la = fmaf(ql[2], xa.z, la);
-        la = fmaf(ql[3], xa.w, la);
-        ha = fmaf(qh[0], xb.x, ha);
-        ha = fmaf(qh[1], xb.y, ha);
-        ha = fmaf(qh[2], xb.z, ha);
-        ha = fmaf(qh[3], xb.w, ha);
+        for (int t = 0; t < 8; ++t) {
+          const lk_f32x4 xa = xp[t];       // x of sub-block 2 gq, weights 4t .. 4t + 3
+          const lk_f32x4 xb = xp[8 + t];   // x of sub-block 2 gq + 1
+          float ql[4], qh[4];
+          nibbles_div512(opaque(qw[t] & 0x0F0F0F0Fu), ql);
+          nibbles_div512(opaque((qw[t] >> 4) & 0x0F0F0F0Fu), qh);
+          float& la = (t & 1) ? la1 : la0;
+          float& ha = (t & 1) ? ha1 : ha0;
+          la = fmaf(ql[0], xa.x, la);
+          la = fmaf(ql[1], xa.y, la);
+          la = fmaf(ql[2], xa.z, la);
+          la = fmaf(ql[3], xa.w, la);
+          ha = fmaf(qh[0], xb.x, ha);
+          ha = fmaf(qh[1], xb.y, ha);
+          ha = fmaf(qh[2], xb.z, ha);
+          ha = fmaf(qh[3], xb.w, ha);
+        }
+        float rq = dsc0 * (la0 + la1);
+        rq = fmaf(dsc1, ha0 + ha1, rq);
+        rq = fmaf(-dmm0, xs0[q], rq);
+        rq = fmaf(-dmm1, xs1[q], rq);
+        r += val[q] ? rq : 0.f;
       }
-      float rq = dsc0 * (la0 + la1);
-      rq = fmaf(dsc1, ha0 + ha1, rq);
-      rq = fmaf(-dmm0, xs0[q], rq);
-      rq = fmaf(-dmm1, xs1[q], rq);
-      r += val[q] ? rq : 0.f;
     }
     return r;
   };

@@ -35,8 +35,6 @@ namespace gqk {
 
 constexpr int kQ40BlockBytes = 18;
 constexpr int kQ40BlockWeights = 32;
-constexpr int kQ6KBlockBytes = 210;
-constexpr int kQ6KBlockWeights = 256;
 constexpr int kOtherRows = 4;      // rows per wave
 constexpr int kOtherWaves = 4;     // waves per block
 

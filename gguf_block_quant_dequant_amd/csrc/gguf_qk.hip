@@ -70,6 +70,7 @@ struct Tuning {
   int lk_two = 1;            // two GEMVs of one x: descriptors as scalar arguments
   int q4_0_lk = 1;           // Q4_0 rows of 256 .. 12288 weights: lanes-along-K kernels
   int q8_0_lk = 1;           // Q8_0 rows of 256 .. 4096 weights: lanes-along-K kernels
+  int q6_k_lk = 1;           // Q6_K rows of 256 .. 12288 weights: lanes-along-K kernels
 };
 
 static const Tuning& tuning() {
@@ -100,6 +101,7 @@ static const Tuning& tuning() {
       if (key == "lk_two" && (v == 0 || v == 1)) r.lk_two = v;
       if (key == "q4_0_lk" && (v == 0 || v == 1)) r.q4_0_lk = v;
       if (key == "q8_0_lk" && (v == 0 || v == 1)) r.q8_0_lk = v;
+      if (key == "q6_k_lk" && (v == 0 || v == 1)) r.q6_k_lk = v;
       const char* comma = std::strchr(eq, ',');
       if (!comma) break;
       p = comma + 1;
@@ -387,6 +389,8 @@ static void launch_lk_nsb(const LkGroup& grp, int depth, int waves, bool ep, int
                           hipStream_t stream) {
   if (type == GGUF_QK_TYPE_Q4_0)
     launch_lk_nsb<GGUF_QK_TYPE_Q4_0, kNsb, 4, false>(grp, depth, stream);
+  else if (type == GGUF_QK_TYPE_Q6_K)
+    launch_lk_nsb<GGUF_QK_TYPE_Q6_K, kNsb, 4, false>(grp, depth, stream);
   else if (type == GGUF_QK_TYPE_Q8_0)
     launch_lk_nsb<GGUF_QK_TYPE_Q8_0, kNsb, 4, false>(grp, depth, stream);
   else if (ep)
@@ -399,7 +403,7 @@ static void launch_lk_nsb(const LkGroup& grp, int depth, int waves, bool ep, int
 
 template <int kQ, int kW>
 static void launch_lkx(const LkGroup& grp, size_t lds, bool ep, int type, hipStream_t stream) {
-  const bool q40 = type == GGUF_QK_TYPE_Q4_0;
+  const bool q40 = type == GGUF_QK_TYPE_Q4_0, q6 = type == GGUF_QK_TYPE_Q6_K;
   const dim3 grid((unsigned)grp.total_blocks), block(kW * 64);
   // one GEMV without epilogue: its descriptor as (preloaded) scalar arguments
   const bool single = grp.n == 1 && !ep && tuning().lk_single;
@@ -409,6 +413,18 @@ static void launch_lkx(const LkGroup& grp, size_t lds, bool ep, int type, hipStr
   float* y = single ? d.y : nullptr;
   const int rows = single ? d.rows : 0, q = single ? d.q : 0, r = single ? d.r : 0;
   const int nsb = single ? d.nsb : 0;
+  if (q6) {
+    // (three rounds of Q6_K quarters run in 4-wave blocks only)
+    if constexpr (!(kQ == 3 && kW == 8)) {
+      if (single)
+        hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q6_K, kQ, 2, kW, false, true>), grid, block, lds,
+                           stream, W, x, y, rows, q, r, nsb, grp);
+      else
+        hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q6_K, kQ, 2, kW, false, false>), grid, block, lds,
+                           stream, W, x, y, rows, q, r, nsb, grp);
+    }
+    return;
+  }
   if (q40 && single)
     hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q4_0, kQ, 2, kW, false, true>), grid, block, lds, stream,
                        W, x, y, rows, q, r, nsb, grp);
@@ -457,7 +473,10 @@ static int launch_lk(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e,
   const int rps = longrow ? 1 : 64 / (4 * nsb);
   bool ep = false;
   for (int i = 0; i < n; ++i) ep = ep || (e && e[i] && e[i]->flags != 0);
-  const int bw = longrow ? tuning().lkx_bw : (ep || type != GGUF_QK_TYPE_Q4_K) ? 4 : tuning().lk_bw;
+  int bw = longrow ? tuning().lkx_bw : (ep || type != GGUF_QK_TYPE_Q4_K) ? 4 : tuning().lk_bw;
+  // Q6_K rows of three rounds hold 20 words per quarter in the load ring:
+  // only 4-wave blocks (512 registers a lane) fit them without scratch
+  if (longrow && type == GGUF_QK_TYPE_Q6_K && nsb > 32) bw = 4;
   LkGroup grp{};
   grp.n = n;
   int64_t total_rows = 0;
@@ -512,7 +531,8 @@ static int launch_lk(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e,
   const int depth = max_wave_steps <= 2 ? 2 : 4;
   if (longrow) {
     const int kq = (4 * nsb + 63) / 64;
-    const size_t lds = (size_t)(256 * nsb) * 4 * 35 / 32;   // x padded + sub-block sums
+    // x padded, then the sums of x per 32-weight sub-block (per run of 16 for Q6_K)
+    const size_t lds = (size_t)(256 * nsb) * 4 * (type == GGUF_QK_TYPE_Q6_K ? 36 : 35) / 32;
     if (bw == 8) {
       if (kq == 2)
         launch_lkx<2, 8>(grp, lds, ep, type, stream);
@@ -543,10 +563,12 @@ static int launch_other(int type, const void* W, const float* x, float* y, int64
 static int launch_group(int type, const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n,
                         const ScratchArea* scratch, hipStream_t stream) {
   if (type == GGUF_QK_TYPE_Q4_K && tuning().q4k_lk && lk_fits(v, e, n)) return launch_lk(v, e, n, stream);
-  if (type == GGUF_QK_TYPE_Q4_0) {
-    // rows of 256 .. 12288 weights in multiples of 256 (no epilogues on Q4_0):
-    // the lanes-along-K kernels; else the lane-quad kernel, one launch each
-    if (tuning().q4_0_lk && lk_fits(v, nullptr, n)) return launch_lk(v, nullptr, n, stream, type);
+  if (type == GGUF_QK_TYPE_Q4_0 || type == GGUF_QK_TYPE_Q6_K) {
+    // rows of 256 .. 12288 weights in multiples of 256 (no epilogues on
+    // these types): the lanes-along-K kernels; else the lane-quad kernel, one
+    // launch each
+    const bool on = type == GGUF_QK_TYPE_Q4_0 ? tuning().q4_0_lk : tuning().q6_k_lk;
+    if (on && lk_fits(v, nullptr, n)) return launch_lk(v, nullptr, n, stream, type);
     for (int i = 0; i < n; ++i) {
       const int st = launch_other(type, v[i]->W, v[i]->x, v[i]->y, v[i]->rows, v[i]->cols, stream);
       if (st) return st;
@@ -606,14 +628,7 @@ static int launch_other(int type, const void* W, const float* x, float* y, int64
 
 static int launch_step(const gguf_qk_gemv* list, const GemvEpilogue* eps, int n,
                        const ScratchArea* scratch, hipStream_t stream) {
-  // Q6_K GEMVs: one launch each (no grouping, no epilogue)
-  for (int i = 0; i < n; ++i) {
-    const gguf_qk_gemv& g = list[i];
-    if (g.type != GGUF_QK_TYPE_Q6_K || g.rows == 0) continue;
-    const int st = launch_other(g.type, g.W, g.x, g.y, g.rows, g.cols, stream);
-    if (st) return st;
-  }
-  for (int type : {GGUF_QK_TYPE_Q4_K, GGUF_QK_TYPE_Q4_0, GGUF_QK_TYPE_Q8_0}) {
+  for (int type : {GGUF_QK_TYPE_Q4_K, GGUF_QK_TYPE_Q4_0, GGUF_QK_TYPE_Q6_K, GGUF_QK_TYPE_Q8_0}) {
     const gguf_qk_gemv* grp[kMaxGroup];
     const GemvEpilogue* ge[kMaxGroup];
     int k = 0;
@@ -869,7 +884,7 @@ static int matvec_other(int type, const void* W, const float* x, float* y, int64
   if (rows == 0) return GGUF_QK_OK;
   st = current_device(nullptr);
   if (st) return st;
-  if (type == GGUF_QK_TYPE_Q4_0) {
+  if (type == GGUF_QK_TYPE_Q4_0 || type == GGUF_QK_TYPE_Q6_K) {
     ScratchArea* scratch = nullptr;
     st = current_device(&scratch);
     if (st) return st;

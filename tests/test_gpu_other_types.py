@@ -123,6 +123,32 @@ def test_gemv_q4_0_lanes_along_k(rows, cols):
     assert np.array_equal(yi.astype(np.float64), oracle.dequant_q4_0_f64(w4, rows, cols) @ xi.astype(np.float64))
 
 
+# Q6_K rows of 256 .. 12288 weights (multiples of 256) take the lanes-along-K
+# kernels: a lane's 64 weights are 16 bytes of each low-bit field and of the
+# high-bit field of one half super-block, 2 bytes off a word boundary in every
+# other super-block (odd super-block counts also shift every other row); 12544
+# is past them (lane-quad kernel). Integer weights and x make every partial
+# sum exact.
+@pytest.mark.parametrize("cols", [256, 512, 1024, 2048, 4096, 4352, 8192, 11008, 12288, 12544])
+@pytest.mark.parametrize("rows", [1, 5, 130])
+def test_gemv_q6_k_lanes_along_k(rows, cols):
+    gen, ref, _, fn = FMTS["q6_k"]
+    rng = np.random.default_rng([rows, cols, 10])
+    w = gen(rng, rows, cols)
+    x = synth.activations_f32(rng, cols)
+    say("q6_k lanes along K", rows, cols)
+    y = host(fn(dev(w), dev(x), rows=rows, cols=cols))
+    e, ok = oracle.floored_rel_err(y, oracle.matvec_f64(ref(w, rows, cols), x))
+    assert ok and e <= TOL_F32, e
+    q6 = b"".join(pack_q6_k_block(0x3C00, [int(v) for v in rng.integers(-4, 5, 16)],
+                                  [int(v) for v in rng.integers(0, 64, 256)])
+                  for _ in range(rows * cols // 256))
+    w6 = np.frombuffer(q6, np.uint8)
+    xi = rng.integers(-8, 9, cols).astype(np.float32)
+    yi = host(fn(dev(w6), dev(xi), rows=rows, cols=cols))
+    assert np.array_equal(yi.astype(np.float64), oracle.dequant_q6_k_f64(w6, rows, cols) @ xi.astype(np.float64))
+
+
 def test_gemv_integer_cases_are_exact():
     rng = np.random.default_rng(12)
     rows, cols = 70, 96 * 32
@@ -179,10 +205,14 @@ def test_mixed_types_in_one_decode_batch():
         assert ok and e <= TOL_F32, (name, e)
 
 
-def test_q4_0_decode_batch_ragged_stages():
-    """Stages of 1 to 4 Q4_0 GEMVs sharing x (grouped lanes-along-K launches,
-    two-GEMV launches with scalar descriptors, long rows), ragged row counts,
-    a later stage reading an earlier output; every row against the oracle."""
+@pytest.mark.parametrize("fmt", ["q4_0", "q6_k"])
+def test_decode_batch_ragged_stages(fmt):
+    """Stages of 1 to 4 Q4_0 or Q6_K GEMVs sharing x (grouped lanes-along-K
+    launches, two-GEMV launches with scalar descriptors, long rows), ragged
+    row counts, a later stage reading an earlier output; every row against
+    the oracle."""
+    gen, ref, _, _ = FMTS[fmt]
+    tcode = g.TYPE_Q4_0 if fmt == "q4_0" else g.TYPE_Q6_K
     rng = np.random.default_rng(52)
     row_choices = [1, 7, 64, 65, 300, 1031]
     k_choices = [256, 2048, 4096, 5120, 11008]
@@ -198,15 +228,15 @@ def test_q4_0_decode_batch_ragged_stages():
         last = None
         for _ in range(m):
             rows = int(rng.choice(row_choices))
-            w = synth.q4_0_weights(rng, rows, cols)
+            w = gen(rng, rows, cols)
             y = torch.empty(rows, dtype=torch.float32, device=DEV)
-            ents.append((g.TYPE_Q4_0, dev(w), xin, y, si))
+            ents.append((tcode, dev(w), xin, y, si))
             checks.append((si, w, rows, cols, xin, y))
             last = (rows, y)
         prev = last
-    say("q4_0 ragged batch:", len(ents), "GEMVs in 14 stages")
+    say(fmt, "ragged batch:", len(ents), "GEMVs in 14 stages")
     g.gguf_qmatvec_batch(g.GemvBatch(ents))
     for si, w, rows, cols, xin, y in checks:
-        ref = oracle.matvec_f64(oracle.dequant_q4_0_f32(w, rows, cols), host(xin))
-        e, ok = oracle.floored_rel_err(host(y), ref)
+        yref = oracle.matvec_f64(ref(w, rows, cols), host(xin))
+        e, ok = oracle.floored_rel_err(host(y), yref)
         assert ok and e <= TOL_F32, (si, rows, cols, e)
