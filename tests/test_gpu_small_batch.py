@@ -151,3 +151,47 @@ def test_zero_tokens_or_rows_launch_nothing():
         assert fn(Wp, X.data_ptr(), Y.data_ptr(), 0, 4, cols, s) == 0
         assert fn(Wp, X.data_ptr(), Y.data_ptr(), 3, 0, cols, s) == 0
     assert bool(torch.all(Y == 7.0))
+
+
+# A few tokens (1 .. 8) on every row length of 256 .. 4096 weights, row
+# counts that leave partial row blocks.
+LK_SHAPES = [(1, 256, 8), (3, 2048, 2), (64, 1024, 4), (130, 512, 6), (33, 4096, 3),
+             (257, 2048, 8), (999, 4096, 8), (2048, 2048, 5)]
+
+
+@pytest.mark.parametrize("fmt", ["q4_k", "q8_0"])
+@pytest.mark.parametrize("rows,cols,n", LK_SHAPES)
+def test_small_batch_few_tokens(fmt, rows, cols, n):
+    rng = np.random.default_rng([rows, cols, n, 7])
+    w, w32 = _weights(fmt, rng, rows, cols)
+    X = np.stack([synth.activations_f32(rng, cols) for _ in range(n)])
+    say("small batch few tokens", fmt, rows, cols, n)
+    Wd, Xd = dev(w), dev(X)
+    Y = host(_call(fmt, Wd, Xd, rows))
+    ref = oracle.matmul_f32_x_f64(X, w32)
+    e, ok = oracle.floored_rel_err(Y, ref)
+    assert ok and e <= TOL_F32, e
+    Y2 = host(_call(fmt, Wd, Xd, rows))
+    assert np.array_equal(Y.view(np.uint32), Y2.view(np.uint32))
+
+
+@pytest.mark.parametrize("n,cols", [(8, 2048), (3, 4096)])
+def test_small_batch_few_tokens_integer_cases_are_exact(n, cols):
+    rng = np.random.default_rng([n, cols, 24])
+    rows = 150
+    blocks = []
+    for _ in range(rows * cols // 256):
+        blocks.append(pack_q4_k_block(0x3C00, 0x3C00, list(rng.integers(0, 64, 8)),
+                                      list(rng.integers(0, 64, 8)), list(rng.integers(0, 16, 256))))
+    w = np.frombuffer(b"".join(blocks), np.uint8)
+    X = rng.integers(-8, 9, size=(n, cols)).astype(np.float32)
+    Y = host(g.gguf_qmatmul_f32_q4_k(dev(w), dev(X), rows=rows))
+    assert np.array_equal(Y.astype(np.float64),
+                          X.astype(np.float64) @ oracle.dequant_q4_k_f64(w, rows, cols).T)
+    blk = np.empty((rows * cols // 32, 34), np.uint8)
+    blk[:, 0], blk[:, 1] = 0x00, 0x3C                      # d = 1.0
+    blk[:, 2:] = rng.integers(0, 256, size=(blk.shape[0], 32), dtype=np.uint8)
+    w8 = blk.reshape(-1)
+    Y8 = host(g.gguf_qmatmul_f32_q8_0(dev(w8), dev(X), rows=rows))
+    assert np.array_equal(Y8.astype(np.float64),
+                          X.astype(np.float64) @ oracle.dequant_q8_0_f32(w8, rows, cols).astype(np.float64).T)
