@@ -246,4 +246,260 @@ __global__ __launch_bounds__(256) void gemm_q4_k_kernel(const uint8_t* __restric
 #undef GQK_GEMM_LOAD
 #undef GQK_GEMM_STEP
 
+// ---------------------------------------------------------------------------
+// The same product with the operand tiles double-buffered in LDS. Steps of 64
+// k (one 32-byte nibble group: sub-blocks 2 g and 2 g + 1 of a super-block);
+// each thread holds the raw bytes of the next two steps in registers (X: 16
+// bytes of 4 token rows; W: the header and the group's 32 bytes of one weight
+// row, of which it decodes one sub-block), and while a wave's MFMAs read step
+// s from one LDS buffer it decodes step s + 1 into the other: one barrier per
+// step, and the decode's VALU work and LDS stores sit between the MFMAs
+// instead of before them. The tile values are the same bits as the kernel
+// above (fma(d sc, q, -dmin m) in fp32, rounded to nearest-even bf16).
+// Block tile, wave tiles, MFMA layout, split K and the partial-tile epilogue
+// are those of the kernel above; the partial tiles and counters are indexed
+// by the grid tile, so the matrices of a group share them.
+// ---------------------------------------------------------------------------
+// Load step `step` (clamped to the block's last: every slot issues the same
+// loads, so the in-order wait counts stay exact; re-read steps are never
+// decoded): X into register set S (2 sets), W into set G = step mod 4 (4
+// sets: the weights come from HBM and get three steps of lead, X from L2 one).
+#define GQK_GDB_STEP_CLAMP(step) ((step) < step_end ? (step) : step_end - 1)
+#define GQK_GDB_LOAD_X(S, step)                                                                 \
+  do {                                                                                          \
+    const uint32_t ko_ = (uint32_t)GQK_GDB_STEP_CLAMP(step) * (kGdbBK * 2);                     \
+    x##S##0 = *reinterpret_cast<const uint4*>(xbase + (xoff[0] + ko_));                        \
+    x##S##1 = *reinterpret_cast<const uint4*>(xbase + (xoff[1] + ko_));                        \
+    x##S##2 = *reinterpret_cast<const uint4*>(xbase + (xoff[2] + ko_));                        \
+    x##S##3 = *reinterpret_cast<const uint4*>(xbase + (xoff[3] + ko_));                        \
+  } while (0)
+#define GQK_GDB_LOAD_W(G, step)                                                                 \
+  do {                                                                                          \
+    const int st_ = GQK_GDB_STEP_CLAMP(step);                                                   \
+    const uint8_t* sb_ = wrow + (int64_t)(st_ >> 2) * kQ4KBlockBytes;                           \
+    h##G = *reinterpret_cast<const uint4*>(sb_);                                                \
+    const uint4* q_ = reinterpret_cast<const uint4*>(sb_ + 16 + 32 * (st_ & 3));                \
+    qa##G = q_[0];                                                                              \
+    qb##G = q_[1];                                                                              \
+  } while (0)
+
+// Decodes X register set S and W register set G, a step of nibble group G (a
+// constant 0..3), into LDS buffer BUF. Sub-block 2 G + half: 6-bit scale and min (sub-blocks 0..3:
+// bytes j and j + 4 of the 12; 4..7: low / high nibble of byte j + 4 and the
+// top two bits of bytes j - 4 / j). G is a constant and half only moves
+// shifts, so the decode is straight-line code the scheduler can place
+// between the MFMAs.
+#define GQK_GDB_DECODE(S, G, BUF)                                                               \
+  do {                                                                                          \
+    uint8_t* xs_ = lds + (BUF) * kGdbStage;                                                     \
+    uint8_t* ws_ = xs_ + kGemmBM * kGdbRow;                                                     \
+    *reinterpret_cast<uint4*>(xs_ + (xr + 0) * kGdbRow + 16 * xc) = x##S##0;                    \
+    *reinterpret_cast<uint4*>(xs_ + (xr + 32) * kGdbRow + 16 * xc) = x##S##1;                   \
+    *reinterpret_cast<uint4*>(xs_ + (xr + 64) * kGdbRow + 16 * xc) = x##S##2;                   \
+    *reinterpret_cast<uint4*>(xs_ + (xr + 96) * kGdbRow + 16 * xc) = x##S##3;                   \
+    const uint32_t b_ = 8u * (2u * (uint32_t)((G) & 1) + (uint32_t)half);                       \
+    const uint32_t s0_ = (h##G.y >> b_) & 0xFFu, s4_ = (h##G.z >> b_) & 0xFFu;                  \
+    const uint32_t s8_ = (h##G.w >> b_) & 0xFFu;                                                \
+    const uint32_t sc_ = (G) >= 2 ? ((s8_ & 15u) | ((s0_ >> 6) << 4)) : (s0_ & 63u);            \
+    const uint32_t mm_ = (G) >= 2 ? ((s8_ >> 4) | ((s4_ >> 6) << 4)) : (s4_ & 63u);             \
+    const float dl_ = half_lo(h##G.x) * (float)sc_;                                             \
+    const float ml_ = half_hi(h##G.x) * (float)mm_;                                             \
+    const uint4 qa_ = qa##G, qb_ = qb##G;                                                         \
+    const uint32_t qw_[8] = {qa_.x, qa_.y, qa_.z, qa_.w, qb_.x, qb_.y, qb_.z, qb_.w};           \
+    uint32_t o_[16];                                                                            \
+    _Pragma("unroll") for (int t_ = 0; t_ < 8; ++t_) {                                          \
+      const uint32_t n4_ = opaque((qw_[t_] >> nsh) & 0x0F0F0F0Fu);                              \
+      o_[2 * t_] = pack_bf16x2(fmaf(dl_, ubyte0(n4_), -ml_), fmaf(dl_, ubyte1(n4_), -ml_));      \
+      o_[2 * t_ + 1] = pack_bf16x2(fmaf(dl_, ubyte2(n4_), -ml_), fmaf(dl_, ubyte3(n4_), -ml_));  \
+    }                                                                                           \
+    uint4* wd_ = reinterpret_cast<uint4*>(ws_ + ld_row * kGdbRow + 64 * half);                  \
+    wd_[0] = make_uint4(o_[0], o_[1], o_[2], o_[3]);                                            \
+    wd_[1] = make_uint4(o_[4], o_[5], o_[6], o_[7]);                                            \
+    wd_[2] = make_uint4(o_[8], o_[9], o_[10], o_[11]);                                          \
+    wd_[3] = make_uint4(o_[12], o_[13], o_[14], o_[15]);                                        \
+  } while (0)
+
+// Up to four Q4_K matrices of one X (q, k, v; gate, up) in one launch: their
+// row tiles are laid end to end along grid x.
+constexpr int kGemmMaxGroup = 4;
+struct GemmGroup {
+  const uint8_t* W[kGemmMaxGroup];
+  uint16_t* Y[kGemmMaxGroup];
+  int64_t rows[kGemmMaxGroup];
+  int tile_begin[kGemmMaxGroup];   // first grid-x index of each matrix
+  int n;
+};
+
+constexpr int kGdbBK = 64;                                   // k per step
+constexpr int kGdbRow = kGdbBK * 2 + 16;                     // 144-byte LDS rows (36 dwords)
+constexpr int kGdbStage = (kGemmBM + kGemmBN) * kGdbRow;     // one buffer: X rows, then W rows
+
+__global__ __launch_bounds__(256) void gemm_q4_k_db_kernel(GemmGroup G, const uint16_t* __restrict__ X,
+                                                           int64_t n_tokens, int nsb, float* partials,
+                                                           int* counters) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kGdbStage];
+  __shared__ int last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wi = wave >> 1, wj = wave & 1;
+  // this block's matrix and its row tile
+  const int bx = (int)blockIdx.x;
+  const int m = (G.n > 1 && bx >= G.tile_begin[1]) + (G.n > 2 && bx >= G.tile_begin[2]) +
+                (G.n > 3 && bx >= G.tile_begin[3]);
+  const uint8_t* const W = m == 0 ? G.W[0] : m == 1 ? G.W[1] : m == 2 ? G.W[2] : G.W[3];
+  uint16_t* const Y = m == 0 ? G.Y[0] : m == 1 ? G.Y[1] : m == 2 ? G.Y[2] : G.Y[3];
+  const int64_t rows = m == 0 ? G.rows[0] : m == 1 ? G.rows[1] : m == 2 ? G.rows[2] : G.rows[3];
+  const int tb = m == 0 ? G.tile_begin[0] : m == 1 ? G.tile_begin[1] : m == 2 ? G.tile_begin[2] : G.tile_begin[3];
+  const int64_t n0 = (int64_t)blockIdx.y * kGemmBM;
+  const int64_t r0 = (int64_t)(bx - tb) * kGemmBN;
+  const int S = (int)gridDim.z, split = (int)blockIdx.z;
+  const int64_t K = (int64_t)nsb * kQ4KBlockWeights;
+  const int64_t row_bytes = (int64_t)nsb * kQ4KBlockBytes;
+  // this block's steps: super-blocks [nsb * split / S, nsb * (split + 1) / S), 4 steps each
+  const int step_begin = 4 * (int)((int64_t)nsb * split / S);
+  const int step_end = 4 * (int)((int64_t)nsb * (split + 1) / S);
+
+  // X: thread t copies the 16 bytes at k 8 xc .. 8 xc + 7 of the step of
+  // token rows xr + 32 j, j = 0..3 (a wave reads 8 whole 128-byte row
+  // slices). W: thread t decodes sub-block 2 g + half of weight row ld_row.
+  // Rows past the end are clamped (read, never stored).
+  const int xc = tid & 7, xr = tid >> 3;
+  uint32_t xoff[4];   // byte offsets (the host keeps X below 4 GiB for this kernel)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = n0 + xr + 32 * j;
+    xoff[j] = (uint32_t)(((n < n_tokens ? n : n_tokens - 1) * K + 8 * xc) * 2);
+  }
+  const int ld_row = tid >> 1, half = tid & 1;
+  const int64_t wr = (r0 + ld_row) < rows ? (r0 + ld_row) : (rows - 1);
+  const uint8_t* wrow = W + wr * row_bytes;
+  const uint32_t nsh = 4u * (uint32_t)half;   // low (half 0) or high nibbles
+
+  // Register sets of raw step bytes: X (16 bytes of token rows xr + 32 j),
+  // sets A and B; W (the super-block header and the group's 32 nibble bytes),
+  // sets 0..3 by nibble group. Named variables (arrays captured by helpers
+  // stayed in scratch memory).
+  uint4 xA0, xA1, xA2, xA3, xB0, xB1, xB2, xB3;
+  uint4 h0, qa0, qb0, h1, qa1, qb1, h2, qa2, qb2, h3, qa3, qb3;
+  const uint8_t* const xbase = reinterpret_cast<const uint8_t*>(X);
+
+  f32x16 acc00, acc01, acc10, acc11;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc00[e] = acc01[e] = acc10[e] = acc11[e] = 0.f;
+  auto mfma_step = [&](int buf) {
+    const uint8_t* xs = lds + buf * kGdbStage;
+    const uint8_t* ws = xs + kGemmBM * kGdbRow;
+#pragma unroll
+    for (int kk = 0; kk < kGdbBK; kk += 16) {
+      const int kb = (kk + 8 * (lane >> 5)) * 2;
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(xs + (wi * 64 + (lane & 31)) * kGdbRow + kb);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(xs + (wi * 64 + 32 + (lane & 31)) * kGdbRow + kb);
+      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(ws + (wj * 64 + (lane & 31)) * kGdbRow + kb);
+      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(ws + (wj * 64 + 32 + (lane & 31)) * kGdbRow + kb);
+      acc00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc00, 0, 0, 0);
+      acc01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc01, 0, 0, 0);
+      acc10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc10, 0, 0, 0);
+      acc11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc11, 0, 0, 0);
+    }
+  };
+
+  // Pipeline: step s computes from buffer (s - step_begin) & 1 while the
+  // registers of step s + 1 are decoded into the other buffer and step s + 2
+  // is loaded into the registers just freed. A block has 4 steps per
+  // super-block and at least one super-block (the host never splits K finer),
+  // so the loop runs whole super-blocks; its last decode writes the re-read
+  // last step into the buffer that is not read again. The body is
+  // straight-line code, so the decode can be scheduled between the MFMAs.
+  GQK_GDB_LOAD_X(A, step_begin);
+  GQK_GDB_LOAD_W(0, step_begin);
+  GQK_GDB_LOAD_X(B, step_begin + 1);
+  GQK_GDB_LOAD_W(1, step_begin + 1);
+  GQK_GDB_LOAD_W(2, step_begin + 2);
+  GQK_GDB_LOAD_W(3, step_begin + 3);
+  GQK_GDB_DECODE(A, 0, 0);
+  __syncthreads();
+  // one super-block (4 steps, groups 0..3) per pass; step_begin is a
+  // multiple of 4, so step s + j has group j & 3
+  for (int s = step_begin; s < step_end; s += 4) {
+    GQK_GDB_LOAD_X(A, s + 2);
+    GQK_GDB_LOAD_W(0, s + 4);
+    mfma_step(0);
+    GQK_GDB_DECODE(B, 1, 1);
+    __syncthreads();
+    GQK_GDB_LOAD_X(B, s + 3);
+    GQK_GDB_LOAD_W(1, s + 5);
+    mfma_step(1);
+    GQK_GDB_DECODE(A, 2, 0);
+    __syncthreads();
+    GQK_GDB_LOAD_X(A, s + 4);
+    GQK_GDB_LOAD_W(2, s + 6);
+    mfma_step(0);
+    GQK_GDB_DECODE(B, 3, 1);
+    __syncthreads();
+    GQK_GDB_LOAD_X(B, s + 5);
+    GQK_GDB_LOAD_W(3, s + 7);
+    mfma_step(1);
+    GQK_GDB_DECODE(A, 0, 0);
+    __syncthreads();
+  }
+
+  if (S == 1) {
+    gemm_store_bf16(acc00, Y, n_tokens, rows, n0, r0, wi, wj, 0, 0, lane);
+    gemm_store_bf16(acc01, Y, n_tokens, rows, n0, r0, wi, wj, 0, 1, lane);
+    gemm_store_bf16(acc10, Y, n_tokens, rows, n0, r0, wi, wj, 1, 0, lane);
+    gemm_store_bf16(acc11, Y, n_tokens, rows, n0, r0, wi, wj, 1, 1, lane);
+    return;
+  }
+
+  const int64_t tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const int64_t ntiles = (int64_t)gridDim.x * gridDim.y;
+  float* mine = partials + ((int64_t)split * ntiles + tile) * kGemmTileFloats;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    __hip_atomic_store(gemm_partial_slot(mine, wave, 0, 0, e, lane), acc00[e], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gemm_partial_slot(mine, wave, 0, 1, e, lane), acc01[e], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gemm_partial_slot(mine, wave, 1, 0, e, lane), acc10[e], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gemm_partial_slot(mine, wave, 1, 1, e, lane), acc11[e], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // every wave's partial stores have completed before thread 0 signals
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  GQK_WAIT_VMCNT(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(&counters[tile * kGemmCounterStride], 1,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = old == S - 1;
+  }
+  __syncthreads();
+  if (!last) return;
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+      f32x16 sum;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sum[e] = 0.f;
+      for (int sp = 0; sp < S; ++sp) {
+        float* p = partials + ((int64_t)sp * ntiles + tile) * kGemmTileFloats;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          sum[e] += __hip_atomic_load(gemm_partial_slot(p, wave, it, jt, e, lane),
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      gemm_store_bf16(sum, Y, n_tokens, rows, n0, r0, wi, wj, it, jt, lane);
+    }
+  if (tid == 0)
+    __hip_atomic_store(&counters[tile * kGemmCounterStride], 0, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+#undef GQK_GDB_STEP_CLAMP
+#undef GQK_GDB_LOAD_X
+#undef GQK_GDB_LOAD_W
+#undef GQK_GDB_DECODE
+
 }  // namespace gqk

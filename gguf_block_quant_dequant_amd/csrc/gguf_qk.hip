@@ -71,6 +71,7 @@ struct Tuning {
   int q4_0_lk = 1;           // Q4_0 rows of 256 .. 12288 weights: lanes-along-K kernels
   int q8_0_lk = 1;           // Q8_0 rows of 256 .. 4096 weights: lanes-along-K kernels
   int q6_k_lk = 1;           // Q6_K rows of 256 .. 12288 weights: lanes-along-K kernels
+  int gemm_db = 1;           // prefill: the double-buffered GEMM
 };
 
 static const Tuning& tuning() {
@@ -102,6 +103,7 @@ static const Tuning& tuning() {
       if (key == "q4_0_lk" && (v == 0 || v == 1)) r.q4_0_lk = v;
       if (key == "q8_0_lk" && (v == 0 || v == 1)) r.q8_0_lk = v;
       if (key == "q6_k_lk" && (v == 0 || v == 1)) r.q6_k_lk = v;
+      if (key == "gemm_db" && (v == 0 || v == 1)) r.gemm_db = v;
       const char* comma = std::strchr(eq, ',');
       if (!comma) break;
       p = comma + 1;
@@ -927,24 +929,62 @@ int gguf_qmatvec_q6_k(const void* W, const float* x, float* y, int64_t rows, int
   return matvec_other(GGUF_QK_TYPE_Q6_K, W, x, y, rows, cols, stream);
 }
 
-int gguf_qmatmul_q4_k(const void* W, const uint16_t* X, uint16_t* Y, int64_t n_tokens,
-                      int64_t rows, int64_t cols, hipStream_t stream) {
-  int64_t wb = 0;
-  int st = check_matrix(GGUF_QK_TYPE_Q4_K, W, rows, cols, &wb);
-  if (st) return st;
-  if (!X || !Y) return GGUF_QK_ERR_NULL;
+// Prefill of n (1 .. 4) Q4_K matrices sharing X (validated as a whole before
+// any launch; one launch of the double-buffered kernel, the matrices' row
+// tiles end to end along grid x).
+static int matmul_q4_k_group(const void* const* W, uint16_t* const* Y, const int64_t* rows, int n,
+                             const uint16_t* X, int64_t n_tokens, int64_t cols, hipStream_t stream) {
+  if (!W || !Y || !rows) return GGUF_QK_ERR_NULL;
+  if (n < 1 || n > kGemmMaxGroup) return GGUF_QK_ERR_SHAPE;
+  int64_t wb[kGemmMaxGroup] = {0, 0, 0, 0};
+  for (int m = 0; m < n; ++m) {
+    if (rows[m] < 0) return GGUF_QK_ERR_SHAPE;
+    if (rows[m] == 0 && n > 1) {   // skipped: its W and Y are not touched (may be null)
+      const int64_t rb = row_bytes_of(GGUF_QK_TYPE_Q4_K, cols);
+      if (rb < 0) return (int)rb;
+      continue;
+    }
+    const int st = check_matrix(GGUF_QK_TYPE_Q4_K, W[m], rows[m], cols, &wb[m]);
+    if (st) return st;
+    if (!Y[m]) return GGUF_QK_ERR_NULL;
+    if (!aligned16(Y[m])) return GGUF_QK_ERR_ALIGN;
+  }
+  if (!X) return GGUF_QK_ERR_NULL;
   if (n_tokens < 0) return GGUF_QK_ERR_SHAPE;
-  if (!aligned16(X) || !aligned16(Y)) return GGUF_QK_ERR_ALIGN;
-  if (n_tokens > 0 && (cols > INT64_MAX / 2 / n_tokens || rows > INT64_MAX / 2 / n_tokens))
-    return GGUF_QK_ERR_SHAPE;
-  const int64_t xb = n_tokens * cols * 2, yb = n_tokens * rows * 2;
-  if (overlap(Y, yb, W, wb) || overlap(Y, yb, X, xb)) return GGUF_QK_ERR_ALIAS;
-  if (rows == 0 || n_tokens == 0) return GGUF_QK_OK;
+  if (!aligned16(X)) return GGUF_QK_ERR_ALIGN;
+  for (int m = 0; m < n; ++m)
+    if (n_tokens > 0 && (cols > INT64_MAX / 2 / n_tokens || rows[m] > INT64_MAX / 2 / n_tokens))
+      return GGUF_QK_ERR_SHAPE;
+  const int64_t xb = n_tokens * cols * 2;
+  for (int m = 0; m < n; ++m) {
+    if (rows[m] == 0) continue;
+    const int64_t yb = n_tokens * rows[m] * 2;
+    if (overlap(Y[m], yb, X, xb)) return GGUF_QK_ERR_ALIAS;
+    for (int o = 0; o < n; ++o) {
+      if (rows[o] == 0) continue;
+      if (overlap(Y[m], yb, W[o], wb[o])) return GGUF_QK_ERR_ALIAS;
+      if (o != m && overlap(Y[m], yb, Y[o], n_tokens * rows[o] * 2)) return GGUF_QK_ERR_ALIAS;
+    }
+  }
+  if (n_tokens == 0) return GGUF_QK_OK;
+  const int64_t gy = (n_tokens + kGemmBM - 1) / kGemmBM;
+  GemmGroup G{};
+  int64_t gx = 0;
+  for (int m = 0; m < n; ++m) {
+    if (rows[m] == 0) continue;   // nothing to compute, nothing written
+    G.W[G.n] = static_cast<const uint8_t*>(W[m]);
+    G.Y[G.n] = Y[m];
+    G.rows[G.n] = rows[m];
+    G.tile_begin[G.n] = (int)gx;
+    ++G.n;
+    gx += (rows[m] + kGemmBN - 1) / kGemmBN;
+    if (gx > INT32_MAX) return GGUF_QK_ERR_LIMIT;
+  }
+  if (G.n == 0) return GGUF_QK_OK;
+  if (gy > 65535) return GGUF_QK_ERR_LIMIT;
   ScratchArea* scratch = nullptr;
-  st = current_device(&scratch);
+  int st = current_device(&scratch);
   if (st) return st;
-  const int64_t gx = (rows + kGemmBN - 1) / kGemmBN, gy = (n_tokens + kGemmBM - 1) / kGemmBM;
-  if (gx > INT32_MAX || gy > 65535) return GGUF_QK_ERR_LIMIT;
   // Split K over whole super-blocks when there are too few tiles to fill the
   // device, as far as the scratch for the fp32 partial tiles allows.
   // Measured on the 2048-hidden shapes: long K (down, 43 super-blocks) gains
@@ -960,10 +1000,36 @@ int gguf_qmatmul_q4_k(const void* W, const uint16_t* X, uint16_t* Y, int64_t n_t
   if (S > nsb) S = nsb;
   while (S > 1 && S * tiles * kGemmTileFloats > kGemmScratchFloats) --S;
   if (S < 1 || tiles > kGemmMaxTiles) S = 1;
-  hipLaunchKernelGGL(gemm_q4_k_kernel, dim3((unsigned)gx, (unsigned)gy, (unsigned)S), dim3(256), 0,
-                     stream, static_cast<const uint8_t*>(W), X, Y, n_tokens, rows, (int)nsb,
-                     scratch->gemm_partials, scratch->gemm_counters);
-  return launch_status();
+  if (tuning().gemm_db && xb < (int64_t(1) << 32)) {   // 32-bit X offsets
+    hipLaunchKernelGGL(gemm_q4_k_db_kernel, dim3((unsigned)gx, (unsigned)gy, (unsigned)S), dim3(256), 0,
+                       stream, G, X, n_tokens, (int)nsb, scratch->gemm_partials, scratch->gemm_counters);
+    return launch_status();
+  }
+  // the single-buffered kernel, one launch per matrix (its own split)
+  for (int m = 0; m < G.n; ++m) {
+    const int64_t gxm = (G.rows[m] + kGemmBN - 1) / kGemmBN, tm = gxm * gy;
+    int64_t Sm = target / tm;
+    if (Sm > max_split) Sm = max_split;
+    if (Sm > nsb) Sm = nsb;
+    while (Sm > 1 && Sm * tm * kGemmTileFloats > kGemmScratchFloats) --Sm;
+    if (Sm < 1 || tm > kGemmMaxTiles) Sm = 1;
+    hipLaunchKernelGGL(gemm_q4_k_kernel, dim3((unsigned)gxm, (unsigned)gy, (unsigned)Sm), dim3(256), 0,
+                       stream, G.W[m], X, G.Y[m], n_tokens, G.rows[m], (int)nsb, scratch->gemm_partials,
+                       scratch->gemm_counters);
+    st = launch_status();
+    if (st) return st;
+  }
+  return GGUF_QK_OK;
+}
+
+int gguf_qmatmul_q4_k(const void* W, const uint16_t* X, uint16_t* Y, int64_t n_tokens,
+                      int64_t rows, int64_t cols, hipStream_t stream) {
+  return matmul_q4_k_group(&W, &Y, &rows, 1, X, n_tokens, cols, stream);
+}
+
+int gguf_qmatmul_q4_k_multi(const void* const* W, uint16_t* const* Y, const int64_t* rows, int32_t n,
+                            const uint16_t* X, int64_t n_tokens, int64_t cols, hipStream_t stream) {
+  return matmul_q4_k_group(W, Y, rows, n, X, n_tokens, cols, stream);
 }
 
 // Small batch (fp32 X and Y, 32 tokens x 128 rows per block, K in steps of

@@ -234,6 +234,21 @@ int gguf_add_f32(const float* a, const float* b, float* out, int64_t n, hipStrea
 int gguf_qmatmul_q4_k(const void* W, const uint16_t* X, uint16_t* Y, int64_t n_tokens,
                       int64_t rows, int64_t cols, hipStream_t stream);
 
+/* The same for n (1 .. 4) Q4_K matrices W[0..n-1] of rows[m] rows and the same
+ * cols that multiply one X (the query, key and value projections, or gate
+ * and up, read the same normalized input: "GGUF Inferencer in R", section 4,
+ * and the culpeo.ws naive-implementation post, the layer loop), in one
+ * launch: Y[m] bf16 [n_tokens x rows[m]]. Arrays W, Y and rows are host
+ * arrays of n entries; the matrices and outputs are device buffers with the
+ * single-matrix rules (alignment, no output overlapping any input or another
+ * output). Every matrix is validated before anything is launched; an error
+ * launches nothing. rows[m] = 0 skips matrix m (with n > 1 its W[m] and
+ * Y[m] are not looked at and may be null). Results equal the
+ * single-matrix call's within the bf16 bar (the K split, which sets the
+ * fp32 summation order, is chosen for the whole group). */
+int gguf_qmatmul_q4_k_multi(const void* const* W, uint16_t* const* Y, const int64_t* rows, int32_t n,
+                            const uint16_t* X, int64_t n_tokens, int64_t cols, hipStream_t stream);
+
 /* --- small batch: fused dequant x a few fp32 vectors (MFMA) --------------- */
 
 /* Y[n, r] = sum_k X[n, k] * w[r, k] for n < n_tokens: the fp32 matvec above

@@ -150,6 +150,27 @@ def test_matmul_validation():
     assert f(A, B, C, 8, 0, 256, None) == g.OK
 
 
+def test_matmul_multi_validation():
+    f = g.lib().gguf_qmatmul_q4_k_multi
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    W2, Y2, R2 = (P * 2)(A, A + 4096), (P * 2)(C, C + (1 << 20)), (I64 * 2)(4, 8)
+    assert f(None, Y2, R2, 2, B, 8, 256, None) == g.ERR_NULL
+    assert f(W2, None, R2, 2, B, 8, 256, None) == g.ERR_NULL
+    assert f(W2, Y2, None, 2, B, 8, 256, None) == g.ERR_NULL
+    assert f(W2, Y2, R2, 0, B, 8, 256, None) == g.ERR_SHAPE           # 1 .. 4 matrices
+    assert f(W2, Y2, R2, 5, B, 8, 256, None) == g.ERR_SHAPE
+    assert f(W2, Y2, R2, 2, None, 8, 256, None) == g.ERR_NULL
+    assert f(W2, Y2, (I64 * 2)(4, -1), 2, B, 8, 256, None) == g.ERR_SHAPE
+    assert f(W2, Y2, R2, 2, B, 8, 128, None) == g.ERR_SHAPE          # K % 256
+    assert f(W2, (P * 2)(C, None), R2, 2, B, 8, 256, None) == g.ERR_NULL
+    assert f((P * 2)(A, None), (P * 2)(C, None), (I64 * 2)(4, 0), 2, B, 0, 256, None) == g.OK
+    assert f(W2, (P * 2)(C, C + 2), R2, 2, B, 8, 256, None) == g.ERR_ALIGN
+    assert f(W2, (P * 2)(C, C + 16), R2, 2, B, 8, 256, None) == g.ERR_ALIAS   # Y1 overlaps Y0
+    assert f(W2, (P * 2)(C, A), R2, 2, B, 8, 256, None) == g.ERR_ALIAS        # Y1 overlaps W0
+    assert f(W2, Y2, R2, 2, B, 0, 256, None) == g.OK                 # no tokens: nothing to do
+    assert f(W2, Y2, (I64 * 2)(0, 0), 2, B, 8, 256, None) == g.OK    # no rows: nothing to do
+
+
 @pytest.mark.parametrize("name", ["gguf_qmatmul_f32_q8_0", "gguf_qmatmul_f32_q4_k"])
 def test_small_batch_validation(name):
     f = getattr(g.lib(), name)

@@ -475,3 +475,36 @@ def test_batch_in_hip_graph_replays_match_eager():
         torch.cuda.synchronize()
         for y, e in zip(ys, eager):
             assert np.array_equal(host(y).view(np.uint32), e.view(np.uint32))
+
+
+# (Each token's output over a matrix is one vector of the floored metric; a
+# matrix of one row would make that floor the value itself.)
+@pytest.mark.parametrize("n,rows", [(512, (2048, 512, 512)), (100, (200, 129, 1000)), (64, (11008, 11008)),
+                                    (129, (65,)), (512, (300, 0, 700, 128))])
+def test_matmul_multi_matches_oracle(n, rows):
+    """Up to four matrices of one X in one launch (q/k/v and gate/up shapes,
+    ragged row counts, a matrix of no rows): each Y against the oracle within
+    the bf16 bar."""
+    rng = synth.rng_for(19, n, len(rows))
+    cols = 2048
+    ws = [synth.q4_k_weights(rng, r, cols) if r else np.zeros((0, cols // 256 * 144), np.uint8)
+          for r in rows]
+    xb = synth.activations_bf16_bits(rng, n, cols)
+    say("matmul multi", n, rows)
+    Ys = g.gguf_qmatmul_q4_k_multi([dev(w) for w in ws], bf16_tensor(xb), rows=list(rows))
+    for w, r, Y in zip(ws, rows, Ys):
+        if r == 0:
+            continue
+        ref = oracle.matmul_bf16_x_f64(xb, oracle.dequant_q4_k_f32(w, r, cols))
+        e, ok = oracle.floored_rel_err(oracle.bf16_bits_to_f64(bf16_bits(Y)), ref)
+        assert ok and e <= TOL_BF16, (r, e)
+
+
+def test_matmul_multi_single_matrix_equals_matmul():
+    rng = synth.rng_for(20, 0, 0)
+    w = synth.q4_k_weights(rng, 777, 2048)
+    xb = synth.activations_bf16_bits(rng, 300, 2048)
+    W, X = dev(w), bf16_tensor(xb)
+    a = bf16_bits(g.gguf_qmatmul_q4_k(W, X))
+    b = bf16_bits(g.gguf_qmatmul_q4_k_multi([W], X)[0])
+    assert np.array_equal(a, b)
