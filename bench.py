@@ -224,34 +224,45 @@ def prefill_pass(torch, g, synth, entries, meta, stream, n_tokens=512, reps=3):
 
 def small_batch_pass(torch, g, synth, entries, stream, n_tokens, reps=5):
     """The whole weight stream (36 x 7 Q4_K + the Q8_0 head) multiplied by
-    n_tokens fp32 activation vectors each (Y = X W^T, fp32), one launch per
-    matrix in pass order, as one HIP graph; returns the labelled record."""
+    n_tokens fp32 activation vectors each (Y = X W^T, fp32), in pass order,
+    the matrices of a stage that share X ({q, k, v}, {gate, up}) in one
+    launch, as one HIP graph; returns the labelled record."""
     dev = "cuda:0"
     gen = torch.Generator().manual_seed(synth.ROOT_SEED * 1000 + 60 + n_tokens)
-    xs, ys, calls = {}, {}, []
+    xs, ys, stages = {}, {}, {}
     wbytes = 0
     for tid, W, x, y, si in entries:
         cols, rows = x.numel(), y.numel()
         if cols not in xs:
             xs[cols] = torch.randn(n_tokens, cols, generator=gen).to(dev)
-        if rows not in ys:
-            ys[rows] = torch.empty(n_tokens, rows, dtype=torch.float32, device=dev)
-        f = g.gguf_qmatmul_f32_q4_k if tid == g.TYPE_Q4_K else g.gguf_qmatmul_f32_q8_0
-        calls.append((f, W, xs[cols], ys[rows]))
+        stages.setdefault(si, []).append((tid, W, cols, rows))
         wbytes += W.numel()
+    calls = []
+    for si in sorted(stages):
+        mats = stages[si]
+        Ys = [ys.setdefault((r, j), torch.empty(n_tokens, r, dtype=torch.float32, device=dev))
+              for j, (_, _, _, r) in enumerate(mats)]
+        calls.append((mats[0][0], [m[1] for m in mats], xs[mats[0][2]], Ys, [m[3] for m in mats]))
 
     def run():
-        for f, W, X, Y in calls:
-            f(W, X, Y, stream=stream)
+        for tid, Ws, X, Ys, rows in calls:
+            if len(Ws) == 1:
+                f = g.gguf_qmatmul_f32_q4_k if tid == g.TYPE_Q4_K else g.gguf_qmatmul_f32_q8_0
+                f(Ws[0], X, Ys[0], rows=rows[0], stream=stream)
+            else:
+                f = g.gguf_qmatmul_f32_q4_k_multi if tid == g.TYPE_Q4_K else g.gguf_qmatmul_f32_q8_0_multi
+                f(Ws, X, Ys, rows=rows, stream=stream)
 
     graph = capture(torch, run, stream)
     t = time_replays(torch, graph, stream, reps)
     ms = sorted(t)[len(t) // 2]
     gbps = wbytes / (ms / 1e3) / 1e9
     del graph
-    return {"label": f"small batch: the {len(calls)} matrices of the pass x {n_tokens} fp32 "
-                     "activation vectors, fp32 Y, bf16 hi/lo MFMA (HIP graph, one launch per matrix)",
-            "tokens": n_tokens, "ms_per_pass": round(ms, 4), "weight_GBps": round(gbps, 1),
+    return {"label": f"small batch: the {sum(len(c[1]) for c in calls)} matrices of the pass x {n_tokens} "
+                     "fp32 activation vectors, fp32 Y, bf16 hi/lo MFMA; q/k/v and gate/up one launch "
+                     "each (HIP graph)",
+            "tokens": n_tokens, "launches": len(calls), "ms_per_pass": round(ms, 4),
+            "weight_GBps": round(gbps, 1),
             "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
             "tokens_per_s": round(n_tokens * 1e3 / ms, 1),
             "roofline": {"bound": "hbm", "kernel": "gemv_small_batch_kernel",

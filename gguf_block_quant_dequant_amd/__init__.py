@@ -56,6 +56,8 @@ _SIGS = {
     "gguf_qmatmul_q4_k_multi": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _I64, _I64, _P]),
     "gguf_qmatmul_f32_q8_0": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P]),
     "gguf_qmatmul_f32_q4_k": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P]),
+    "gguf_qmatmul_f32_q8_0_multi": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _I64, _I64, _P]),
+    "gguf_qmatmul_f32_q4_k_multi": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _I64, _I64, _P]),
     "gguf_qk_probe_read": (ctypes.c_int, [_P, _I64, _P, _P]),
     "gguf_qmatvec_batch": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
     "gguf_qmatvec_batch_ep": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P]),
@@ -295,6 +297,39 @@ def gguf_qmatmul_q4_k_multi(Ws, X, Ys=None, rows=None, stream=None):
                                          _stream(stream)),
            "gguf_qmatmul_q4_k_multi")
     return Ys
+
+
+def _matmul_f32_multi(name, fmt, Ws, X, Ys, rows, stream):
+    if X.dim() != 2:
+        raise ValueError("X must be [n_tokens, cols]")
+    if not 1 <= len(Ws) <= 4:
+        raise ValueError("one to four matrices")
+    n, cols = X.shape
+    rows = list(rows) if rows is not None else [None] * len(Ws)
+    if len(rows) != len(Ws):
+        raise ValueError("one row count per matrix")
+    rows = [_rows_cols(W, fmt, r, cols)[0] for W, r in zip(Ws, rows)]
+    if Ys is None:
+        Ys = [torch.empty((n, r), dtype=torch.float32, device=X.device) for r in rows]
+    if len(Ys) != len(Ws) or any(Y.numel() != n * r for Y, r in zip(Ys, rows)):
+        raise ValueError("one Y of n_tokens x rows[m] elements per matrix")
+    k = len(Ws)
+    warr = (ctypes.c_void_p * k)(*[_dev(W, "W", torch.uint8) for W in Ws])
+    yarr = (ctypes.c_void_p * k)(*[_dev(Y, "Y", torch.float32) for Y in Ys])
+    rarr = (ctypes.c_int64 * k)(*rows)
+    _check(getattr(lib(), name)(warr, yarr, rarr, k, _dev(X, "X", torch.float32), n, cols, _stream(stream)),
+           name)
+    return Ys
+
+
+def gguf_qmatmul_f32_q8_0_multi(Ws, X, Ys=None, rows=None, stream=None):
+    """Y[m] = X @ dequant(Ws[m])^T for up to four Q8_0 matrices of one fp32 X, one launch."""
+    return _matmul_f32_multi("gguf_qmatmul_f32_q8_0_multi", TYPE_Q8_0, Ws, X, Ys, rows, stream)
+
+
+def gguf_qmatmul_f32_q4_k_multi(Ws, X, Ys=None, rows=None, stream=None):
+    """Y[m] = X @ dequant(Ws[m])^T for up to four Q4_K matrices of one fp32 X, one launch."""
+    return _matmul_f32_multi("gguf_qmatmul_f32_q4_k_multi", TYPE_Q4_K, Ws, X, Ys, rows, stream)
 
 
 def _matmul_f32(name, fmt, W, X, Y, rows, stream):

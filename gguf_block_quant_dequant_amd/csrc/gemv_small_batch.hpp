@@ -227,11 +227,23 @@ __device__ __forceinline__ void sb_store(const f32x16& acc, float* __restrict__ 
   }
 }
 
-// grid (ceil(rows / 128), ceil(n_tokens / 32), S), block 256. `steps` = K / 256.
+// Up to four matrices of one X (q, k, v; gate, up) in one launch: their row
+// tiles are laid end to end along grid x.
+constexpr int kSbMaxGroup = 4;
+struct SbGroup {
+  const uint8_t* W[kSbMaxGroup];
+  float* Y[kSbMaxGroup];
+  int64_t rows[kSbMaxGroup];
+  int tile_begin[kSbMaxGroup];   // first grid-x index of each matrix
+  int n;
+};
+
+// grid (row tiles of all matrices, ceil(n_tokens / 32), S), block 256.
+// `steps` = K / 256. The partial tiles and counters are indexed by the grid
+// tile, so the matrices of a group share them.
 template <bool Q4K>
 __global__ __launch_bounds__(256, 2) void gemv_small_batch_kernel(
-    const uint8_t* __restrict__ W, const float* __restrict__ X, float* __restrict__ Y,
-    int n_tokens, int64_t rows, int steps, float* partials, int* counters) {
+    SbGroup G, const float* __restrict__ X, int n_tokens, int steps, float* partials, int* counters) {
   using F = SbFormat<Q4K>;
   __shared__ __attribute__((aligned(16))) uint8_t ws[F::kBlockPieces * 16];
   __shared__ __attribute__((aligned(16))) uint8_t xh[kSbTokens * kSbXRow];
@@ -239,7 +251,14 @@ __global__ __launch_bounds__(256, 2) void gemv_small_batch_kernel(
   __shared__ int last;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t r0 = (int64_t)blockIdx.x * kSbRows;
+  const int bx = (int)blockIdx.x;
+  const int m = (G.n > 1 && bx >= G.tile_begin[1]) + (G.n > 2 && bx >= G.tile_begin[2]) +
+                (G.n > 3 && bx >= G.tile_begin[3]);
+  const uint8_t* const W = m == 0 ? G.W[0] : m == 1 ? G.W[1] : m == 2 ? G.W[2] : G.W[3];
+  float* const Y = m == 0 ? G.Y[0] : m == 1 ? G.Y[1] : m == 2 ? G.Y[2] : G.Y[3];
+  const int64_t rows = m == 0 ? G.rows[0] : m == 1 ? G.rows[1] : m == 2 ? G.rows[2] : G.rows[3];
+  const int tb = m == 0 ? G.tile_begin[0] : m == 1 ? G.tile_begin[1] : m == 2 ? G.tile_begin[2] : G.tile_begin[3];
+  const int64_t r0 = (int64_t)(bx - tb) * kSbRows;
   const int n0 = (int)blockIdx.y * kSbTokens;
   const int S = (int)gridDim.z, split = (int)blockIdx.z;
   const int64_t K = (int64_t)steps * kSbK;

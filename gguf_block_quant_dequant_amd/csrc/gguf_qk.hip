@@ -1036,27 +1036,62 @@ int gguf_qmatmul_q4_k_multi(const void* const* W, uint16_t* const* Y, const int6
 // 256). Shares the prefill GEMM's partial-tile scratch and tile counters.
 static_assert(kSbCounterStride == kGemmCounterStride, "shared tile counters");
 
-static int small_batch_common(int type, const void* W, const float* X, float* Y, int64_t n_tokens,
-                              int64_t rows, int64_t cols, hipStream_t stream) {
-  int64_t wb = 0;
-  int st = check_matrix(type, W, rows, cols, &wb);
-  if (st) return st;
-  if (!X || !Y) return GGUF_QK_ERR_NULL;
+static int small_batch_group(int type, const void* const* W, float* const* Y, const int64_t* rows, int n,
+                             const float* X, int64_t n_tokens, int64_t cols, hipStream_t stream) {
+  if (!W || !Y || !rows) return GGUF_QK_ERR_NULL;
+  if (n < 1 || n > kSbMaxGroup) return GGUF_QK_ERR_SHAPE;
+  int64_t wb[kSbMaxGroup] = {0, 0, 0, 0};
+  for (int m = 0; m < n; ++m) {
+    if (rows[m] < 0) return GGUF_QK_ERR_SHAPE;
+    if (rows[m] == 0 && n > 1) {   // skipped: its W and Y are not touched (may be null)
+      const int64_t rb = row_bytes_of(type, cols);
+      if (rb < 0) return (int)rb;
+      continue;
+    }
+    const int st = check_matrix(type, W[m], rows[m], cols, &wb[m]);
+    if (st) return st;
+    if (!Y[m]) return GGUF_QK_ERR_NULL;
+    if (!aligned16(Y[m])) return GGUF_QK_ERR_ALIGN;
+  }
+  if (!X) return GGUF_QK_ERR_NULL;
   if (n_tokens < 0 || cols % kSbK) return GGUF_QK_ERR_SHAPE;
-  if (!aligned16(X) || !aligned16(Y)) return GGUF_QK_ERR_ALIGN;
-  if (n_tokens > 0 && (cols > INT64_MAX / 4 / n_tokens || rows > INT64_MAX / 4 / n_tokens))
-    return GGUF_QK_ERR_SHAPE;
-  const int64_t xb = n_tokens * cols * 4, yb = n_tokens * rows * 4;
-  if (overlap(Y, yb, W, wb) || overlap(Y, yb, X, xb)) return GGUF_QK_ERR_ALIAS;
-  if (rows == 0 || n_tokens == 0) return GGUF_QK_OK;
+  if (!aligned16(X)) return GGUF_QK_ERR_ALIGN;
+  for (int m = 0; m < n; ++m)
+    if (n_tokens > 0 && (cols > INT64_MAX / 4 / n_tokens || rows[m] > INT64_MAX / 4 / n_tokens))
+      return GGUF_QK_ERR_SHAPE;
+  const int64_t xb = n_tokens * cols * 4;
+  for (int m = 0; m < n; ++m) {
+    if (rows[m] == 0) continue;
+    const int64_t yb = n_tokens * rows[m] * 4;
+    if (overlap(Y[m], yb, X, xb)) return GGUF_QK_ERR_ALIAS;
+    for (int o = 0; o < n; ++o) {
+      if (rows[o] == 0) continue;
+      if (overlap(Y[m], yb, W[o], wb[o])) return GGUF_QK_ERR_ALIAS;
+      if (o != m && overlap(Y[m], yb, Y[o], n_tokens * rows[o] * 4)) return GGUF_QK_ERR_ALIAS;
+    }
+  }
+  if (n_tokens == 0) return GGUF_QK_OK;
   const int64_t steps = cols / kSbK;
   if (row_bytes_of(type, cols) * kSbRows > INT32_MAX || n_tokens > INT32_MAX || steps > INT32_MAX)
     return GGUF_QK_ERR_LIMIT;   // 32-bit offsets inside a block's rows
+  SbGroup G{};
+  int64_t gx = 0;
+  for (int m = 0; m < n; ++m) {
+    if (rows[m] == 0) continue;
+    G.W[G.n] = static_cast<const uint8_t*>(W[m]);
+    G.Y[G.n] = Y[m];
+    G.rows[G.n] = rows[m];
+    G.tile_begin[G.n] = (int)gx;
+    ++G.n;
+    gx += (rows[m] + kSbRows - 1) / kSbRows;
+    if (gx > INT32_MAX) return GGUF_QK_ERR_LIMIT;
+  }
+  if (G.n == 0) return GGUF_QK_OK;
+  const int64_t gy = (n_tokens + kSbTokens - 1) / kSbTokens;
+  if (gy > 65535) return GGUF_QK_ERR_LIMIT;
   ScratchArea* scratch = nullptr;
-  st = current_device(&scratch);
+  const int st = current_device(&scratch);
   if (st) return st;
-  const int64_t gx = (rows + kSbRows - 1) / kSbRows, gy = (n_tokens + kSbTokens - 1) / kSbTokens;
-  if (gx > INT32_MAX || gy > 65535) return GGUF_QK_ERR_LIMIT;
   // Split K over whole steps when the tiles alone do not fill the device, as
   // far as the partial-tile scratch allows.
   const int64_t tiles = gx * gy;
@@ -1066,16 +1101,18 @@ static int small_batch_common(int type, const void* W, const float* X, float* Y,
   while (S > 1 && S * tiles * kSbTileFloats > kGemmScratchFloats) --S;
   if (S < 1 || tiles > kGemmMaxTiles) S = 1;
   const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)S), block(256);
-  const uint8_t* w = static_cast<const uint8_t*>(W);
   if (type == GGUF_QK_TYPE_Q4_K)
-    hipLaunchKernelGGL(gemv_small_batch_kernel<true>, grid, block, 0, stream, w, X, Y,
-                       (int)n_tokens, rows, (int)steps, scratch->gemm_partials,
-                       scratch->gemm_counters);
+    hipLaunchKernelGGL(gemv_small_batch_kernel<true>, grid, block, 0, stream, G, X, (int)n_tokens,
+                       (int)steps, scratch->gemm_partials, scratch->gemm_counters);
   else
-    hipLaunchKernelGGL(gemv_small_batch_kernel<false>, grid, block, 0, stream, w, X, Y,
-                       (int)n_tokens, rows, (int)steps, scratch->gemm_partials,
-                       scratch->gemm_counters);
+    hipLaunchKernelGGL(gemv_small_batch_kernel<false>, grid, block, 0, stream, G, X, (int)n_tokens,
+                       (int)steps, scratch->gemm_partials, scratch->gemm_counters);
   return launch_status();
+}
+
+static int small_batch_common(int type, const void* W, const float* X, float* Y, int64_t n_tokens,
+                              int64_t rows, int64_t cols, hipStream_t stream) {
+  return small_batch_group(type, &W, &Y, &rows, 1, X, n_tokens, cols, stream);
 }
 
 int gguf_qmatmul_f32_q8_0(const void* W, const float* X, float* Y, int64_t n_tokens, int64_t rows,
@@ -1086,6 +1123,16 @@ int gguf_qmatmul_f32_q8_0(const void* W, const float* X, float* Y, int64_t n_tok
 int gguf_qmatmul_f32_q4_k(const void* W, const float* X, float* Y, int64_t n_tokens, int64_t rows,
                           int64_t cols, hipStream_t stream) {
   return small_batch_common(GGUF_QK_TYPE_Q4_K, W, X, Y, n_tokens, rows, cols, stream);
+}
+
+int gguf_qmatmul_f32_q8_0_multi(const void* const* W, float* const* Y, const int64_t* rows, int32_t n,
+                                const float* X, int64_t n_tokens, int64_t cols, hipStream_t stream) {
+  return small_batch_group(GGUF_QK_TYPE_Q8_0, W, Y, rows, n, X, n_tokens, cols, stream);
+}
+
+int gguf_qmatmul_f32_q4_k_multi(const void* const* W, float* const* Y, const int64_t* rows, int32_t n,
+                                const float* X, int64_t n_tokens, int64_t cols, hipStream_t stream) {
+  return small_batch_group(GGUF_QK_TYPE_Q4_K, W, Y, rows, n, X, n_tokens, cols, stream);
 }
 
 // Standalone layer steps (vectors of n fp32).

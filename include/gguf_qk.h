@@ -266,6 +266,19 @@ int gguf_qmatmul_f32_q8_0(const void* W, const float* X, float* Y, int64_t n_tok
 int gguf_qmatmul_f32_q4_k(const void* W, const float* X, float* Y, int64_t n_tokens,
                           int64_t rows, int64_t cols, hipStream_t stream);
 
+/* The same for n (1 .. 4) matrices of one type that multiply one X (as for
+ * the prefill above: q, k, v, or gate and up, read the same input), in one
+ * launch: Y[m] fp32 [n_tokens x rows[m]]. W, Y and rows are host arrays of
+ * n entries, with the single-matrix rules per matrix and no output
+ * overlapping another; all are validated before anything is launched.
+ * rows[m] = 0 skips matrix m (with n > 1 its W[m] and Y[m] may be null).
+ * Results are within the same bar as the single-matrix call (the K split is
+ * chosen for the whole group). */
+int gguf_qmatmul_f32_q8_0_multi(const void* const* W, float* const* Y, const int64_t* rows, int32_t n,
+                                const float* X, int64_t n_tokens, int64_t cols, hipStream_t stream);
+int gguf_qmatmul_f32_q4_k_multi(const void* const* W, float* const* Y, const int64_t* rows, int32_t n,
+                                const float* X, int64_t n_tokens, int64_t cols, hipStream_t stream);
+
 /* --- measurement ---------------------------------------------------------- */
 
 /* Streaming-read probe: reads `bytes` (a multiple of 16) from device buffer

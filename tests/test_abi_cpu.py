@@ -171,6 +171,20 @@ def test_matmul_multi_validation():
     assert f(W2, Y2, (I64 * 2)(0, 0), 2, B, 8, 256, None) == g.OK    # no rows: nothing to do
 
 
+@pytest.mark.parametrize("name", ["gguf_qmatmul_f32_q8_0_multi", "gguf_qmatmul_f32_q4_k_multi"])
+def test_small_batch_multi_validation(name):
+    f = getattr(g.lib(), name)
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    W2, Y2, R2 = (P * 2)(A, A + 8192), (P * 2)(C, C + (1 << 20)), (I64 * 2)(4, 8)
+    assert f(None, Y2, R2, 2, B, 8, 256, None) == g.ERR_NULL
+    assert f(W2, Y2, R2, 0, B, 8, 256, None) == g.ERR_SHAPE
+    assert f(W2, Y2, R2, 5, B, 8, 256, None) == g.ERR_SHAPE
+    assert f(W2, Y2, R2, 2, B, 8, 288, None) == g.ERR_SHAPE          # K % 256
+    assert f(W2, (P * 2)(C, C + 16), R2, 2, B, 8, 256, None) == g.ERR_ALIAS   # Y1 overlaps Y0
+    assert f(W2, Y2, R2, 2, B, 0, 256, None) == g.OK
+    assert f((P * 2)(A, None), (P * 2)(C, None), (I64 * 2)(4, 0), 2, B, 0, 256, None) == g.OK
+
+
 @pytest.mark.parametrize("name", ["gguf_qmatmul_f32_q8_0", "gguf_qmatmul_f32_q4_k"])
 def test_small_batch_validation(name):
     f = getattr(g.lib(), name)

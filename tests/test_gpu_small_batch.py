@@ -195,3 +195,24 @@ def test_small_batch_few_tokens_integer_cases_are_exact(n, cols):
     Y8 = host(g.gguf_qmatmul_f32_q8_0(dev(w8), dev(X), rows=rows))
     assert np.array_equal(Y8.astype(np.float64),
                           X.astype(np.float64) @ oracle.dequant_q8_0_f32(w8, rows, cols).astype(np.float64).T)
+
+
+@pytest.mark.parametrize("fmt,rows,cols,n", [("q4_k", (2048, 512, 512), 2048, 8),
+                                             ("q4_k", (11008, 11008), 2048, 32),
+                                             ("q4_k", (300, 0, 129, 64), 1024, 5),
+                                             ("q8_0", (777, 33), 2048, 3)])
+def test_small_batch_multi_matches_oracle(fmt, rows, cols, n):
+    """Up to four matrices of one X in one launch (q/k/v and gate/up shapes,
+    ragged rows, a matrix of no rows): every Y against the oracle."""
+    rng = np.random.default_rng([sum(rows), cols, n, 3])
+    ws = [_weights(fmt, rng, r, cols) if r else (None, None) for r in rows]
+    X = np.stack([synth.activations_f32(rng, cols) for _ in range(n)])
+    say("small batch multi", fmt, rows, cols, n)
+    f = g.gguf_qmatmul_f32_q8_0_multi if fmt == "q8_0" else g.gguf_qmatmul_f32_q4_k_multi
+    Wd = [dev(w) if w is not None else torch.empty(0, dtype=torch.uint8, device=DEV) for w, _ in ws]
+    Ys = f(Wd, dev(X), rows=list(rows))
+    for (w, w32), r, Y in zip(ws, rows, Ys):
+        if r == 0:
+            continue
+        e, ok = oracle.floored_rel_err(host(Y), oracle.matmul_f32_x_f64(X, w32))
+        assert ok and e <= TOL_F32, (r, e)
