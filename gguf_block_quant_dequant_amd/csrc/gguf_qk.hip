@@ -63,6 +63,7 @@ struct Tuning {
   int q4k_lk = 1;            // Q4_K GEMVs without epilogue: lanes-along-K kernels
   int lk_waves = 1024;       // waves a lanes-along-K launch aims for
   int lkx_waves = 2048;      // the same for rows longer than 16 super-blocks
+  int lkx_waves_q6 = 1024;   // the same for Q6_K rows longer than 16 super-blocks
   int lk_single = 1;         // one-GEMV launches take their descriptor as scalar arguments
   int lk_bw = 4;             // waves per block, rows of <= 16 super-blocks (4 or 8)
   int lkx_bw = 8;            // waves per block, longer rows (4 or 8)
@@ -95,6 +96,7 @@ static const Tuning& tuning() {
       if (key == "q4k_lk" && (v == 0 || v == 1)) r.q4k_lk = v;
       if (key == "lk_waves" && v > 0) r.lk_waves = v;
       if (key == "lkx_waves" && v > 0) r.lkx_waves = v;
+      if (key == "lkx_waves_q6" && v > 0) r.lkx_waves_q6 = v;
       if (key == "lk_single" && (v == 0 || v == 1)) r.lk_single = v;
       if (key == "lk_bw" && (v == 4 || v == 8)) r.lk_bw = v;
       if (key == "lkx_bw" && (v == 4 || v == 8)) r.lkx_bw = v;
@@ -483,7 +485,9 @@ static int launch_lk(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e,
   grp.n = n;
   int64_t total_rows = 0;
   for (int i = 0; i < n; ++i) total_rows += v[i]->rows;
-  const int64_t target_blocks = ((longrow ? tuning().lkx_waves : tuning().lk_waves) + bw - 1) / bw;
+  // (Q6_K long rows: two rows per wave halve the x staging of 4-wave blocks)
+  const int lkx_waves = type == GGUF_QK_TYPE_Q6_K ? tuning().lkx_waves_q6 : tuning().lkx_waves;
+  const int64_t target_blocks = ((longrow ? lkx_waves : tuning().lk_waves) + bw - 1) / bw;
   // gate/up pairs computed in the same wave (the gate's rows in lanes 0..31,
   // the up's in 32..63): the gate's descriptor takes both matrices' blocks,
   // the up's gets none
