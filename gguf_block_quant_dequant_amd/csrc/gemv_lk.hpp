@@ -442,6 +442,29 @@ __device__ __forceinline__ LkBlock lk_block_two(const uint8_t* W0, const uint8_t
                              second ? b - bb1 : b, wave);
 }
 
+// Three GEMVs of one x (the q, k and v of a layer) in the same 14 dwords:
+// W1 and W2 as signed 32-bit byte offsets from W0, y1 and y2 as signed
+// 32-bit float offsets from y0, rows1 | rows2 << 16 and bb1 | bb2 << 16
+// packed (the host takes this form only where all of them fit). Blocks
+// [0, bb1) take GEMV 0, [bb1, bb2) GEMV 1, [bb2, nb) GEMV 2, each with at
+// least one block.
+template <int kW, int kRps>
+__device__ __forceinline__ LkBlock lk_block_three(const uint8_t* W0, int dW1, int dW2, const float* x,
+                                                  float* y0, int dy1, int dy2, int rows0, int rows12,
+                                                  int bb12, int nb, int nsb, int b, int wave) {
+  const uint32_t bb1 = (uint32_t)bb12 & 0xFFFFu, bb2 = (uint32_t)bb12 >> 16;
+  const uint32_t ub = (uint32_t)b;
+  const int m = ub >= bb2 ? 2 : ub >= bb1 ? 1 : 0;
+  const uint32_t rows = m == 0 ? (uint32_t)rows0 : m == 1 ? ((uint32_t)rows12 & 0xFFFFu) : ((uint32_t)rows12 >> 16);
+  const uint32_t b0 = m == 0 ? 0u : m == 1 ? bb1 : bb2;
+  const uint32_t nbm = (m == 0 ? bb1 : m == 1 ? bb2 : (uint32_t)nb) - b0;
+  const uint32_t steps = (rows + kRps - 1) / kRps;
+  const uint32_t q = steps / nbm, r = steps - q * nbm;
+  const int64_t dw = m == 0 ? 0 : m == 1 ? (int64_t)dW1 : (int64_t)dW2;
+  const int64_t dy = m == 0 ? 0 : m == 1 ? (int64_t)dy1 : (int64_t)dy2;
+  return lk_block_single<kW>(W0 + dw, x, y0 + dy, (int)rows, (int)q, (int)r, nsb, (int)(ub - b0), wave);
+}
+
 // LDS float index of x's float4 i in the staged layout: lane slice u (64
 // floats) at 68 u, four floats of padding after each. Slice u holds weights
 // 64 u .. 64 u + 63 in order, except for Q6_K, whose unit u holds weights
@@ -482,6 +505,20 @@ __global__ __launch_bounds__(kW * 64) void gemv_lk1_kernel(const uint8_t* W, con
   __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   lk_run<kNsb, kDepth, kW, false, kType>(lk_block_single<kW>(W, x, y, rows, q, r, kNsb, (int)blockIdx.x, wave),
+                                         xl, nullptr);
+}
+
+// Three GEMVs of one x (stages without epilogues), the descriptors packed into
+// preloaded scalar arguments.
+template <int kType, int kNsb, int kDepth, int kW>
+__global__ __launch_bounds__(kW * 64) void gemv_lk3_kernel(const uint8_t* W0, int dW1, int dW2,
+                                                           const float* x, float* y0, int dy1, int dy2,
+                                                           int rows0, int rows12, int bb12, int nb) {
+  __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  lk_run<kNsb, kDepth, kW, false, kType>(lk_block_three<kW, 16 / kNsb>(W0, dW1, dW2, x, y0, dy1, dy2, rows0,
+                                                                       rows12, bb12, nb, kNsb,
+                                                                       (int)blockIdx.x, wave),
                                          xl, nullptr);
 }
 

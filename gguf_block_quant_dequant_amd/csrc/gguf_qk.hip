@@ -69,6 +69,7 @@ struct Tuning {
   int lkx_bw = 8;            // waves per block, longer rows (4 or 8)
   int lk_pair_in_wave = 1;   // gate/up pairs: both rows of an index in one wave
   int lk_two = 1;            // two GEMVs of one x: descriptors as scalar arguments
+  int lk_three = 1;          // three GEMVs of one x: packed descriptors as scalar arguments
   int q4_0_lk = 1;           // Q4_0 rows of 256 .. 12288 weights: lanes-along-K kernels
   int q8_0_lk = 1;           // Q8_0 rows of 256 .. 4096 weights: lanes-along-K kernels
   int q6_k_lk = 1;           // Q6_K rows of 256 .. 12288 weights: lanes-along-K kernels
@@ -102,6 +103,7 @@ static const Tuning& tuning() {
       if (key == "lkx_bw" && (v == 4 || v == 8)) r.lkx_bw = v;
       if (key == "lk_pair_in_wave" && (v == 0 || v == 1)) r.lk_pair_in_wave = v;
       if (key == "lk_two" && (v == 0 || v == 1)) r.lk_two = v;
+      if (key == "lk_three" && (v == 0 || v == 1)) r.lk_three = v;
       if (key == "q4_0_lk" && (v == 0 || v == 1)) r.q4_0_lk = v;
       if (key == "q8_0_lk" && (v == 0 || v == 1)) r.q8_0_lk = v;
       if (key == "q6_k_lk" && (v == 0 || v == 1)) r.q6_k_lk = v;
@@ -351,6 +353,48 @@ static bool lk_two(const LkGroup& grp) {
          grp.d[1].block_begin < grp.total_blocks && tuning().lk_two;
 }
 
+// Three GEMVs of one x without epilogues, every one with blocks, whose
+// packed descriptors fit (see lk_block_three).
+struct Lk3Args {
+  int dW1, dW2, dy1, dy2, rows12, bb12;
+};
+static bool fits_i32(int64_t v) { return v >= INT32_MIN && v <= INT32_MAX; }
+static bool lk_three(const LkGroup& grp, Lk3Args* a) {
+  if (grp.n != 3 || !tuning().lk_three) return false;
+  const LkDesc *d = grp.d;
+  if (d[1].x != d[0].x || d[2].x != d[0].x) return false;
+  const int bb1 = d[1].block_begin, bb2 = d[2].block_begin;
+  if (!(0 < bb1 && bb1 < bb2 && bb2 < grp.total_blocks && bb2 < 65536)) return false;
+  if (d[1].rows >= 65536 || d[2].rows >= 65536) return false;
+  const int64_t w0 = (int64_t)reinterpret_cast<intptr_t>(d[0].W);
+  const int64_t dW1 = (int64_t)reinterpret_cast<intptr_t>(d[1].W) - w0;
+  const int64_t dW2 = (int64_t)reinterpret_cast<intptr_t>(d[2].W) - w0;
+  const int64_t y0 = (int64_t)reinterpret_cast<intptr_t>(d[0].y);
+  const int64_t by1 = (int64_t)reinterpret_cast<intptr_t>(d[1].y) - y0;
+  const int64_t by2 = (int64_t)reinterpret_cast<intptr_t>(d[2].y) - y0;
+  if (!fits_i32(dW1) || !fits_i32(dW2) || by1 % 4 || by2 % 4 || !fits_i32(by1 / 4) || !fits_i32(by2 / 4))
+    return false;
+  a->dW1 = (int)dW1;
+  a->dW2 = (int)dW2;
+  a->dy1 = (int)(by1 / 4);
+  a->dy2 = (int)(by2 / 4);
+  a->rows12 = (int)((uint32_t)d[1].rows | ((uint32_t)d[2].rows << 16));
+  a->bb12 = (int)((uint32_t)bb1 | ((uint32_t)bb2 << 16));
+  return true;
+}
+
+template <int kType, int kNsb, int kW>
+static void launch_lk3(const LkGroup& grp, const Lk3Args& a, int depth, hipStream_t stream) {
+  const dim3 grid((unsigned)grp.total_blocks), block(kW * 64);
+  const LkDesc& d = grp.d[0];
+  if (depth <= 2)
+    hipLaunchKernelGGL((gemv_lk3_kernel<kType, kNsb, 2, kW>), grid, block, 0, stream, d.W, a.dW1, a.dW2, d.x,
+                       d.y, a.dy1, a.dy2, d.rows, a.rows12, a.bb12, grp.total_blocks);
+  else
+    hipLaunchKernelGGL((gemv_lk3_kernel<kType, kNsb, 4, kW>), grid, block, 0, stream, d.W, a.dW1, a.dW2, d.x,
+                       d.y, a.dy1, a.dy2, d.rows, a.rows12, a.bb12, grp.total_blocks);
+}
+
 template <int kType, int kNsb, int kW>
 static void launch_lk2(const LkGroup& grp, int depth, hipStream_t stream) {
   const dim3 grid((unsigned)grp.total_blocks), block(kW * 64);
@@ -380,6 +424,11 @@ static void launch_lk_nsb(const LkGroup& grp, int depth, hipStream_t stream) {
   }
   if (!kEp && lk_two(grp)) {
     launch_lk2<kType, kNsb, kW>(grp, depth, stream);
+    return;
+  }
+  Lk3Args a3;
+  if (!kEp && lk_three(grp, &a3)) {
+    launch_lk3<kType, kNsb, kW>(grp, a3, depth, stream);
     return;
   }
   if (depth <= 2)
