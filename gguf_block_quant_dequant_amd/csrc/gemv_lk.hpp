@@ -443,8 +443,9 @@ __device__ __forceinline__ LkBlock lk_block_two(const uint8_t* W0, const uint8_t
 }
 
 // Three GEMVs of one x (the q, k and v of a layer) in the same 14 dwords:
-// W1 and W2 as signed 32-bit byte offsets from W0, y1 and y2 as signed
-// 32-bit float offsets from y0, rows1 | rows2 << 16 and bb1 | bb2 << 16
+// W1 and W2 as signed 32-bit offsets from W0 and y1 and y2 from y0, in
+// 16-byte units (all of them 16-byte aligned; the allocator's pools for small
+// and large tensors can lie gigabytes apart), rows1 | rows2 << 16 and bb1 | bb2 << 16
 // packed (the host takes this form only where all of them fit). Blocks
 // [0, bb1) take GEMV 0, [bb1, bb2) GEMV 1, [bb2, nb) GEMV 2, each with at
 // least one block.
@@ -460,8 +461,8 @@ __device__ __forceinline__ LkBlock lk_block_three(const uint8_t* W0, int dW1, in
   const uint32_t nbm = (m == 0 ? bb1 : m == 1 ? bb2 : (uint32_t)nb) - b0;
   const uint32_t steps = (rows + kRps - 1) / kRps;
   const uint32_t q = steps / nbm, r = steps - q * nbm;
-  const int64_t dw = m == 0 ? 0 : m == 1 ? (int64_t)dW1 : (int64_t)dW2;
-  const int64_t dy = m == 0 ? 0 : m == 1 ? (int64_t)dy1 : (int64_t)dy2;
+  const int64_t dw = 16 * (m == 0 ? 0 : m == 1 ? (int64_t)dW1 : (int64_t)dW2);
+  const int64_t dy = 4 * (m == 0 ? 0 : m == 1 ? (int64_t)dy1 : (int64_t)dy2);
   return lk_block_single<kW>(W0 + dw, x, y0 + dy, (int)rows, (int)q, (int)r, nsb, (int)(ub - b0), wave);
 }
 

@@ -372,12 +372,13 @@ static bool lk_three(const LkGroup& grp, Lk3Args* a) {
   const int64_t y0 = (int64_t)reinterpret_cast<intptr_t>(d[0].y);
   const int64_t by1 = (int64_t)reinterpret_cast<intptr_t>(d[1].y) - y0;
   const int64_t by2 = (int64_t)reinterpret_cast<intptr_t>(d[2].y) - y0;
-  if (!fits_i32(dW1) || !fits_i32(dW2) || by1 % 4 || by2 % 4 || !fits_i32(by1 / 4) || !fits_i32(by2 / 4))
-    return false;
-  a->dW1 = (int)dW1;
-  a->dW2 = (int)dW2;
-  a->dy1 = (int)(by1 / 4);
-  a->dy2 = (int)(by2 / 4);
+  // offsets in 16-byte units
+  if ((w0 | dW1 | dW2 | y0 | by1 | by2) & 15) return false;
+  if (!fits_i32(dW1 / 16) || !fits_i32(dW2 / 16) || !fits_i32(by1 / 16) || !fits_i32(by2 / 16)) return false;
+  a->dW1 = (int)(dW1 / 16);
+  a->dW2 = (int)(dW2 / 16);
+  a->dy1 = (int)(by1 / 16);
+  a->dy2 = (int)(by2 / 16);
   a->rows12 = (int)((uint32_t)d[1].rows | ((uint32_t)d[2].rows << 16));
   a->bb12 = (int)((uint32_t)bb1 | ((uint32_t)bb2 << 16));
   return true;
