@@ -1,7 +1,7 @@
 """gguf_qmatvec_batch against the oracle: the full 36-layer decode pass in the
 launch configuration the benchmark times (sampled rows of every GEMV, two calls
 bit-identical, HIP-graph replays identical to the eager call), a pass whose
-steps read the previous step's outputs, and ragged shapes over many steps."""
+steps read the previous step's outputs, and ragged shapes over many steps, and three GEMVs of one x on both launch forms."""
 
 import numpy as np
 import pytest
@@ -137,3 +137,29 @@ def test_batch_ragged_shapes_many_steps():
     for y, ref in refs:
         e, ok = oracle.floored_rel_err(host(y), ref)
         assert ok and e <= TOL_F32, e
+
+
+@pytest.mark.parametrize("rows,cols", [((2048, 512, 512), 2048), ((1, 1, 1), 256), ((65535, 7, 300), 256),
+                                       ((70000, 5, 129), 512), ((5, 70000, 5), 256), ((300, 64, 65536), 256)])
+def test_three_gemvs_of_one_x(rows, cols):
+    """One step of three Q4_K GEMVs of one x (the q/k/v launch: packed
+    descriptors where k's and v's rows fit 16 bits, the descriptor batch
+    otherwise), every row against the oracle, twice."""
+    rng = np.random.default_rng(sum(rows) + cols)
+    x = synth.activations_f32(rng, cols)
+    X = dev(x)
+    entries, refs = [], []
+    for r in rows:
+        w = synth.q4_k_weights(rng, r, cols)
+        y = torch.empty(r, dtype=torch.float32, device=DEV)
+        entries.append((g.TYPE_Q4_K, dev(w), X, y, 0))
+        refs.append((y, oracle.matvec_f64(oracle.dequant_q4_k_f32(w, r, cols), x)))
+    say("three GEMVs:", rows, cols)
+    b = g.GemvBatch(entries)
+    for _ in range(2):
+        for y, _ in refs:
+            y.fill_(float("nan"))
+        g.gguf_qmatvec_batch(b)
+        for y, ref in refs:
+            e, ok = oracle.floored_rel_err(host(y), ref)
+            assert ok and e <= TOL_F32, e
