@@ -1,7 +1,8 @@
 """gguf_qmatvec_batch against the oracle: the full 36-layer decode pass in the
 launch configuration the benchmark times (sampled rows of every GEMV, two calls
 bit-identical, HIP-graph replays identical to the eager call), a pass whose
-steps read the previous step's outputs, and ragged shapes over many steps, and three GEMVs of one x on both launch forms."""
+steps read the previous step's outputs, ragged shapes over many steps, and
+three GEMVs of one x on both of their launch forms."""
 
 import numpy as np
 import pytest
