@@ -13,14 +13,22 @@ are resident in HBM before timing starts.
 
 Prints one JSON line: weight-stream GB/s (whole pass), % of the 8 TB/s HBM
 peak, tokens/s-equivalent (1 / pass time), a roofline record for the
-dominant kernel (the Q4_K lanes-along-K GEMV), the CPU oracle timed on a bounded
-sample of the same workload, and labelled extras: the pass time distribution,
-an unordered upper bound (all GEMVs of the pass as one step), the bf16
-MFMA prefill pass over the same 36-layer weights (N = 512 tokens), and the
-fp32 small-batch passes (the same 253 matrices times 8, 32 and 64 activation
+dominant kernel (the Q4_K lanes-along-K GEMV), the CPU oracle timed on bounded
+samples of the same workloads, and labelled extras: the pass time
+distribution, the streaming-read probe (whole-device read ceiling) and the
+same probe run as the pass runs (one launch per stage: the floor of a
+launch-per-stage pass), the single-matrix GEMVs (256x512, 2048x2048,
+11008x2048 Q8_0; 11008x2048, 2048x11008 Q4_K) streamed from HBM, the bf16
+MFMA prefill pass over the same 36-layer weights (N = 512 tokens), the fp32
+small-batch passes (the same 253 matrices times 8, 32 and 64 activation
 vectors), batch-1 GEMV passes over the same shapes stored as Q4_0 and Q6_K,
 and the 36 layers as decode layers with RMSN, SiLU(gate) * up and the
 residual adds fused into the GEMVs against the same steps as separate kernels.
+
+    python bench.py --timeline
+
+prints per-stage wave timelines of the decode pass instead (the instrumented
+library libgguf_qk_timeline.so, built with `build --timeline`).
 
     python bench.py --copy-calibration
 
@@ -74,6 +82,17 @@ def parse():
                     help="only the Q4_0 and Q6_K GEMV passes")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the prefill pass over the 36-layer weights (for counter runs)")
+    ap.add_argument("--single-only", action="store_true",
+                    help="only the single-matrix GEMVs (256x512, 2048x2048, 11008x2048 Q8_0; "
+                         "11008x2048, 2048x11008 Q4_K)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-wave stage timeline of the decode pass (needs the instrumented "
+                         "library, libgguf_qk_timeline.so)")
+    ap.add_argument("--stage-times", action="store_true",
+                    help="per stage kind (q+k+v, o, gate+up, down, head): the 36 launches of that kind "
+                         "alone, back to back in a HIP graph, microseconds per launch")
+    ap.add_argument("--timeline-raw", default=None,
+                    help="with --timeline: also save the raw per-wave records of the pass (.npz)")
     return ap.parse_args()
 
 
@@ -404,36 +423,291 @@ def other_types_pass(torch, g, synth, reps=5):
     return out
 
 
-def cpu_baseline():
-    """The oracle as it stands, on a bounded sample of the same workload:
-    layers 0..7's seven Q4_K GEMVs each and the first 32768 rows of the Q8_0
-    head (about 13 s of work on one core), decoded to fp32 and multiplied in
-    fp64 with NumPy, one BLAS thread."""
-    from threadpoolctl import threadpool_limits
+def stage_floor(torch, g, meta, total_bytes, stream, reps=10):
+    """The streaming-read probe run as the pass runs: one probe launch per
+    stage over that stage's weight bytes (distinct ranges of one buffer as
+    large as the whole stream), in pass order, as a HIP graph. It bounds what
+    a pass of one launch per stage can reach on this device: launch gaps and
+    each launch's ramp-up and tail with no decoding or arithmetic at all."""
+    buf = torch.zeros(total_bytes, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    ranges, off = [], 0
+    for (_, _, nb) in meta:
+        ranges.append((off, nb))
+        off += nb
+
+    def run():
+        for o, nb in ranges:
+            g.gguf_qk_probe_read(buf[o:o + nb], sink, stream=stream)
+
+    graph = capture(torch, run, stream)
+    t = time_replays(torch, graph, stream, reps)
+    ms = sorted(t)[len(t) // 2]
+    del graph, buf
+    gbps = total_bytes / (ms / 1e3) / 1e9
+    return {"label": "read probe over the pass's stage sizes (36 x {3.5, 2.4, 25.4, 12.7} MB + the "
+                     "279 MB head), one launch per stage, HIP graph: the floor of a launch-per-stage pass",
+            "launches": len(ranges), "ms_per_pass": round(ms, 4), "GBps": round(gbps, 1),
+            "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2)}
+
+
+def single_matrix_pass(torch, g, synth, reps=5):
+    """Single GEMVs (256x512, 2048x2048, 11008x2048 Q8_0; 11008x2048 and
+    2048x11008 Q4_K): each matrix copied to enough byte-identical copies at
+    distinct addresses to pass 1 GiB (at most 4096 copies, always more than the
+    256 MB Infinity Cache), one launch per copy back to back in a HIP graph, so
+    every launch streams its matrix from HBM. Also a labelled cache-resident
+    figure (one copy, launched repeatedly). Returns (records, outputs of copy 0
+    with their inputs, for the CPU leg's error check)."""
+    dev = "cuda:0"
+    recs, outs = [], []
+    stream = torch.cuda.Stream()
+    for m in synth.SINGLE_MATRICES:
+        w, x = synth.single_matrix(m)
+        nb = w.nbytes
+        copies = min(4096, -(-(1 << 30) // nb))
+        big = torch.empty(copies * nb, dtype=torch.uint8, device=dev)
+        W0 = torch.from_numpy(w.reshape(-1)).to(dev)
+        big.view(copies, nb).copy_(W0.unsqueeze(0).expand(copies, nb))
+        X = torch.from_numpy(x).to(dev)
+        Y = torch.empty(m.rows, dtype=torch.float32, device=dev)
+        f = g.gguf_qmatvec_q8_0 if m.fmt == synth.Q8_0 else g.gguf_qmatvec_q4_k
+        views = [big[i * nb:(i + 1) * nb].view(m.rows, nb // m.rows) for i in range(copies)]
+
+        def run_cold():
+            for V in views:
+                f(V, X, Y, stream=stream)
+
+        gc = capture(torch, run_cold, stream)
+        tc = time_replays(torch, gc, stream, reps)
+        us = sorted(tc)[len(tc) // 2] * 1e3 / copies
+        del gc
+        hot_n = 256
+
+        def run_hot():
+            for _ in range(hot_n):
+                f(views[0], X, Y, stream=stream)
+
+        gh = capture(torch, run_hot, stream)
+        th = time_replays(torch, gh, stream, reps)
+        hot_us = sorted(th)[len(th) // 2] * 1e3 / hot_n
+        del gh
+        f(views[0], X, Y, stream=stream)
+        torch.cuda.synchronize()
+        outs.append((m, w, x, Y.cpu().numpy()))
+        gbps = nb / (us / 1e6) / 1e9
+        recs.append({"label": m.label, "bytes": nb, "copies": copies, "us_per_gemv": round(us, 3),
+                     "GBps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+                     "tokens_per_s_equiv_note": "single matrix: 1 / us_per_gemv",
+                     "cache_resident": {"label": "one copy launched repeatedly (L2 / Infinity Cache)",
+                                        "us_per_gemv": round(hot_us, 3),
+                                        "GBps": round(nb / (hot_us / 1e6) / 1e9, 1)}})
+        del big, views, W0
+        torch.cuda.empty_cache()
+    return recs, outs
+
+
+def stage_times(torch, g, entries, meta, stream, reps=10):
+    """Microseconds per launch of each stage kind, its launches of the pass
+    alone back to back in a HIP graph (events on the replay stream), beside
+    the streaming-read probe over the same stage sizes (the floor of a launch
+    of that size)."""
+    kinds = {}
+    for tid, W, x, y, si in entries:
+        layer, names, nb = meta[si]
+        kind = "head" if layer < 0 else "+".join(names)
+        kinds.setdefault(kind, {}).setdefault(si, []).append((tid, W, x, y, si))
+    out = {}
+    for kind, stages in kinds.items():
+        ents = [e for si in sorted(stages) for e in stages[si]]
+        batch = g.GemvBatch(ents)
+        graph = capture(torch, lambda: g.gguf_qmatvec_batch(batch, stream), stream)
+        t = time_replays(torch, graph, stream, reps)
+        ms = sorted(t)[len(t) // 2]
+        nb = sum(e[1].numel() for e in ents)
+        # the read probe over the same stage sizes, one launch per stage
+        sizes = [sum(e[1].numel() for e in stages[si]) for si in sorted(stages)]
+        buf = torch.zeros(sum(sizes), dtype=torch.uint8, device="cuda:0")
+        sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+        offs = [sum(sizes[:i]) for i in range(len(sizes))]
+
+        def probe():
+            for o, n in zip(offs, sizes):
+                g.gguf_qk_probe_read(buf[o:o + n], sink, stream=stream)
+
+        pg = capture(torch, probe, stream)
+        tp = time_replays(torch, pg, stream, reps)
+        pms = sorted(tp)[len(tp) // 2]
+        out[kind] = {"launches": len(stages), "us_per_launch": round(ms * 1e3 / len(stages), 3),
+                     "GBps": round(nb / (ms / 1e3) / 1e9, 1),
+                     "probe_us_per_launch": round(pms * 1e3 / len(stages), 3)}
+        del graph, pg, buf
+    return out
+
+
+def stage_timeline(torch, g, entries, meta, stream, reps=3, raw_path=None):
+    """Per-wave time stamps of the decode pass's kernels (instrumented build):
+    per stage kind, medians over the layers of the launch gap, the wave start
+    skew and the times (from the kernel's first wave) at which the waves had
+    issued their loads, staged x, stored their first row step, computed their
+    last one, and ended."""
+    import numpy as np
+    first_w = {}
+    for tid, W, x, y, si in entries:
+        first_w.setdefault(si, W.data_ptr())
+    slot = g.gguf_qk_timeline_setup(first_w.values())
+    batch = g.GemvBatch(entries)
+    graph = capture(torch, lambda: g.gguf_qmatvec_batch(batch, stream), stream)
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            graph.replay()
+    torch.cuda.synchronize()
+    recs_u32 = g.gguf_qk_timeline_fetch()
+    if raw_path:
+        order = sorted(first_w)
+        np.savez_compressed(raw_path, recs=recs_u32[[slot[first_w[si]] for si in order]],
+                            stage=np.array(order), layer=np.array([meta[si][0] for si in order]),
+                            kind=np.array(["head" if meta[si][0] < 0 else "+".join(meta[si][1]) for si in order]))
+    recs = recs_u32.astype(np.int64)
+    del graph
+    base = None
+    rows = []
+    for si in sorted(first_w):
+        r = recs[slot[first_w[si]]]
+        live = r[:, 0] != 0
+        t = r[live][:, :6]
+        if base is None:
+            base = int(t[:, 0].min())
+        t = (t - base) % (1 << 32)
+        start, end = int(t[:, 0].min()), int(t[:, 5].max())
+        layer, names, nb = meta[si]
+        kind = "head" if layer < 0 else "+".join(names)
+        rows.append((si, kind, start, end, t, int(live.sum()), nb))
+    out = {}
+    for i, (si, kind, start, end, t, waves, nb) in enumerate(rows):
+        prev_end = rows[i - 1][3] if i else None
+        rel = t - start
+        d = out.setdefault(kind, {"waves": waves, "weight_bytes": nb, "gap": [], "span": [], "skew_p50": [],
+                                  "skew_max": [], "issued": [], "staged": [], "first": [], "last": [],
+                                  "last_max": [], "end": []})
+        if prev_end is not None:
+            d["gap"].append(start - prev_end)
+        d["span"].append(end - start)
+        d["skew_p50"].append(np.median(rel[:, 0]))
+        d["skew_max"].append(rel[:, 0].max())
+        d["issued"].append(np.median(rel[:, 1]))
+        d["staged"].append(np.median(rel[:, 2]))
+        d["first"].append(np.median(rel[:, 3]))
+        d["last"].append(np.median(rel[:, 4]))
+        d["last_max"].append(rel[:, 4].max())
+        d["end"].append(rel[:, 5].max())
+    res = {}
+    for kind, d in out.items():
+        res[kind] = {"waves": d["waves"], "weight_bytes": d["weight_bytes"], "launches": len(d["span"])}
+        for k, v in d.items():
+            if isinstance(v, list) and v:
+                res[kind][k + "_us"] = round(float(np.median(v)) * 0.01, 3)   # 100 MHz clock
+    return {"timeline": res, "unit": "us from the kernel's first wave (gap: from the previous "
+                                      "kernel's last wave); medians over the launches of each kind",
+            "clock": "s_memrealtime, 100 MHz"}
+
+
+def cpu_baseline(single_outs=None):
+    """The oracle as it stands (oracle/: NumPy, weights decoded to fp64, fp64
+    products; not tuned) on this host's cores, on bounded samples:
+    - decode (the headline workload): layers 0..3's seven Q4_K GEMVs and head
+      rows 0..16383 (Q8_0), once on one thread and once spread over every core
+      this process may use (one GEMV per task, one BLAS thread per task);
+      weight bytes per second, and tokens/s-equivalent of the whole pass at
+      that rate;
+    - the single matrices in full on one thread, with the GPU result's
+      floored error against the oracle's;
+    - prefill: rows 0..255 of layer 0's seven tensors times 512 bf16 tokens on
+      every core, linearly extrapolated to the 36-layer pass (labelled)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle
     import synth
 
-    n_layers = 8
+    ncpu = os.cpu_count()
+    cores = len(os.sched_getaffinity(0))
+    blas = [{"api": i.get("internal_api"), "threads": i.get("num_threads")} for i in threadpool_info()]
+    n_layers, head_rows = 4, 16384
     stages = synth.decode_stream(n_layers=n_layers, head=False, threads=4)
-    head_rows = 32768
     hw = synth.q8_0_weights(synth.rng_for(synth.DECODE_CFG_ID, 1000, synth.TENSOR_IDS["head"]),
                             head_rows, synth.HIDDEN)
     hx = synth.activations_f32(synth.rng_for(synth.DECODE_CFG_ID, 1000, 100), synth.HIDDEN)
-    nbytes = sum(w.nbytes for st in stages for w in st.weights) + hw.nbytes
+    tasks = [(gm.fmt, w, gm.rows, gm.cols, st.x) for st in stages for gm, w in zip(st.gemvs, st.weights)]
+    tasks.append((synth.Q8_0, hw, head_rows, synth.HIDDEN, hx))
+    nbytes = sum(t[1].nbytes for t in tasks)
+
+    def one(t):
+        fmt, w, rows, cols, x = t
+        deq = oracle.dequant_q8_0_f32 if fmt == synth.Q8_0 else oracle.dequant_q4_k_f32
+        return oracle.matvec_f64(deq(w, rows, cols), x)
+
     with threadpool_limits(1):
         t0 = time.perf_counter()
-        for st in stages:
-            for gm, w in zip(st.gemvs, st.weights):
-                oracle.matvec_f64(oracle.dequant_q4_k_f32(w, gm.rows, gm.cols), st.x)
-        oracle.matvec_f64(oracle.dequant_q8_0_f32(hw, head_rows, synth.HIDDEN), hx)
-        dt = time.perf_counter() - t0
-    gbps = nbytes / dt / 1e9
-    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"layers 0..{n_layers - 1} q,k,v,o,gate,up,down (Q4_K) + head rows 0..{head_rows - 1} "
-                      f"(Q8_0): "
-                      f"{nbytes} weight bytes in {dt:.2f} s; tokens/s-equiv "
-                      f"{gbps * 1e9 / synth.decode_stream_bytes():.4f}"}
+        for t in tasks:
+            one(t)
+        dt1 = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=cores) as ex:
+            list(ex.map(one, sorted(tasks, key=lambda t: -t[1].nbytes)))
+        dtn = time.perf_counter() - t0
+    pass_bytes = synth.decode_stream_bytes()
+    g1, gn = nbytes / dt1 / 1e9, nbytes / dtn / 1e9
+
+    singles = []
+    if single_outs:
+        with threadpool_limits(1):
+            for m, w, x, y_gpu in single_outs:
+                t0 = time.perf_counter()
+                ref = one((m.fmt, w, m.rows, m.cols, x))
+                dt = time.perf_counter() - t0
+                err, finite = oracle.floored_rel_err(y_gpu, ref)
+                singles.append({"label": m.label, "oracle_s_1thread": round(dt, 3),
+                                "oracle_GBps_1thread": round(w.nbytes / dt / 1e9, 4),
+                                "gpu_max_floored_err": float(f"{err:.3e}"), "gpu_finite": bool(finite)})
+
+    # prefill sample: 256 rows of each of layer 0's tensors x 512 bf16 tokens
+    pf_rows, pf_tokens = 256, 512
+    gen_rows = {}
+    for st in stages[:4]:
+        for gm, w in zip(st.gemvs, st.weights):
+            gen_rows[gm.name] = (gm, w[:pf_rows])
+    xb = {c: synth.activations_bf16_bits(synth.rng_for(synth.PREFILL_CFG_ID, 0, c), pf_tokens, c)
+          for c in (synth.HIDDEN, synth.FFN)}
+
+    def pf(item):
+        gm, w = item
+        return oracle.matmul_bf16_x_f64(xb[gm.cols], oracle.dequant_q4_k_f32(w, pf_rows, gm.cols))
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=cores) as ex:
+        list(ex.map(pf, gen_rows.values()))
+    dtp = time.perf_counter() - t0
+    sample_flop = sum(2.0 * pf_tokens * pf_rows * gm.cols for gm, _ in gen_rows.values())
+    pass_flop = 2.0 * pf_tokens * synth.N_LAYERS * sum(gm.rows * gm.cols for st in synth.LAYER_STAGES
+                                                        for gm in st)
+    pf_s = dtp * pass_flop / sample_flop
+    return {"value": round(gn, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"decode: layers 0..{n_layers - 1} q,k,v,o,gate,up,down (Q4_K) + head rows "
+                      f"0..{head_rows - 1} (Q8_0), {nbytes} weight bytes, one GEMV per task over {cores} "
+                      f"threads in {dtn:.2f} s",
+            "tokens_per_s_equiv": round(gn * 1e9 / pass_bytes, 5),
+            "one_thread": {"GBps": round(g1, 4), "s": round(dt1, 2),
+                           "tokens_per_s_equiv": round(g1 * 1e9 / pass_bytes, 5)},
+            "host": {"os_cpu_count": ncpu, "sched_getaffinity": cores, "blas": blas},
+            "single_matrices": singles,
+            "prefill": {"label": f"oracle prefill, rows 0..{pf_rows - 1} of layer 0's 7 tensors x "
+                                 f"{pf_tokens} bf16 tokens on {cores} threads, linearly extrapolated to "
+                                 "the 36-layer pass (extrapolated, not measured whole)",
+                        "sample_s": round(dtp, 3), "pass_s_extrapolated": round(pf_s, 1),
+                        "TFLOPs": round(pass_flop / pf_s / 1e12, 5)}}
 
 
 def copy_calibration():
@@ -449,6 +723,8 @@ def copy_calibration():
 
 def main():
     args = parse()
+    if args.timeline:
+        os.environ["GGUF_QK_TIMELINE"] = "1"   # the instrumented library
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the workload fits one MI355X); --gpus {args.gpus} "
               "is not supported", file=sys.stderr)
@@ -474,6 +750,16 @@ def main():
         return
     if args.other_types_only:
         print(json.dumps(other_types_pass(torch, g, synth)), flush=True)
+        return
+    if args.single_only:
+        recs, _ = single_matrix_pass(torch, g, synth)
+        print(json.dumps(recs), flush=True)
+        return
+    if args.timeline:
+        print(json.dumps(stage_timeline(torch, g, entries, meta, stream, raw_path=args.timeline_raw)), flush=True)
+        return
+    if args.stage_times:
+        print(json.dumps(stage_times(torch, g, entries, meta, stream)), flush=True)
         return
     if args.small_batch_only:
         print(json.dumps([small_batch_pass(torch, g, synth, entries, stream, n)
@@ -565,28 +851,20 @@ def main():
     rec["head"] = {"ms": round(head_ms, 4), "GBps": round(head_bytes / (head_ms / 1e3) / 1e9, 1)}
     del gh
 
-    # Labelled upper bound: every GEMV of the pass in one step (no stage order),
-    # grouped four to a launch.
-    ub = g.GemvBatch([(tid, W, x, y, 0) for tid, W, x, y, si in entries])
-    gu = capture(torch, lambda: g.gguf_qmatvec_batch(ub, stream), stream)
-    tu = time_replays(torch, gu, stream, 10)
-    ums = sorted(tu)[len(tu) // 2]
-    rec["unordered_upper_bound"] = {
-        "label": "all 253 GEMVs of the pass as one unordered step (not the headline)",
-        "ms": round(ums, 4), "GBps": round(total_bytes / (ums / 1e3) / 1e9, 1),
-        "pct_hbm_peak": round(100 * total_bytes / (ums / 1e3) / 1e9 / HBM_PEAK_GBPS, 2)}
-    del gu
-
     ceiling = probe_ceiling(torch, g)
     rec["read_probe_GBps"] = round(ceiling, 1)
     rec["pct_of_read_probe"] = round(100 * gbps / ceiling, 2)
+    rec["stage_floor"] = stage_floor(torch, g, meta, total_bytes, stream)
+    rec["pct_of_stage_floor"] = round(100 * rec["stage_floor"]["ms_per_pass"] / ms, 2)
+    singles, single_outs = single_matrix_pass(torch, g, synth)
+    rec["single_matrices"] = singles
     rec["prefill"] = prefill_pass(torch, g, synth, entries, meta, stream)
     rec["small_batch"] = [small_batch_pass(torch, g, synth, entries, stream, n)
                           for n in SMALL_BATCH_TOKENS]
     rec["fused_layers"] = fused_layer_pass(torch, g, synth, entries, stream)
     rec["other_types"] = other_types_pass(torch, g, synth)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline()
+        rec["cpu_baseline"] = cpu_baseline(single_outs)
     print(json.dumps(rec), flush=True)
 
 

@@ -16,7 +16,7 @@ import struct
 
 import torch
 
-from .build import LIB_PATH
+from .build import LIB_PATH, TIMELINE_LIB_PATH
 
 TYPE_Q8_0 = 8
 TYPE_Q4_K = 12
@@ -59,6 +59,8 @@ _SIGS = {
     "gguf_qmatmul_f32_q8_0_multi": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _I64, _I64, _P]),
     "gguf_qmatmul_f32_q4_k_multi": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _I64, _I64, _P]),
     "gguf_qk_probe_read": (ctypes.c_int, [_P, _I64, _P, _P]),
+    "gguf_qk_timeline_setup": (ctypes.c_int, [ctypes.c_uint64]),
+    "gguf_qk_timeline_fetch": (ctypes.c_int, [_P, _I64]),
     "gguf_qmatvec_batch": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
     "gguf_qmatvec_batch_ep": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P]),
     "gguf_rmsnorm_prep_f32": (ctypes.c_int, [_P, _P, _P, _P, _I64, _P]),
@@ -108,10 +110,15 @@ def lib() -> ctypes.CDLL:
     """The loaded libgguf_qk.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+        # GGUF_QK_TIMELINE=1 loads the instrumented build (stage timelines);
+        # GGUF_QK_LIBRARY=<path> another build of the same library (measurement
+        # of build variants)
+        path = TIMELINE_LIB_PATH if os.environ.get("GGUF_QK_TIMELINE") == "1" else LIB_PATH
+        path = os.environ.get("GGUF_QK_LIBRARY", path)
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
                                "`python -m gguf_block_quant_dequant_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(path)
         for name, (res, args) in _SIGS.items():
             f = getattr(L, name)
             f.restype = res
@@ -365,6 +372,39 @@ def gguf_qk_probe_read(buf, sink=None, stream=None):
     _check(lib().gguf_qk_probe_read(_dev(buf, "buf"), nbytes, _dev(sink, "sink", torch.int32),
                                     _stream(stream)), "gguf_qk_probe_read")
     return sink
+
+
+TIMELINE_SLOTS, TIMELINE_WAVES, TIMELINE_REC_BYTES = 4096, 2048, 32
+
+
+def timeline_slot(key: int, mult: int) -> int:
+    """Record slot of a launch key (its first weight pointer) under `mult`."""
+    return ((key * mult) & ((1 << 64) - 1)) >> 52
+
+
+def gguf_qk_timeline_setup(keys, seed=1):
+    """Arm the instrumented build's per-wave stage records; picks an odd
+    multiplier under which the launch keys `keys` take distinct slots and
+    returns {key: slot}."""
+    import random
+    ks = sorted(set(int(k) for k in keys))
+    rnd = random.Random(seed)
+    for _ in range(100000):
+        mult = rnd.getrandbits(64) | 1
+        slots = [timeline_slot(k, mult) for k in ks]
+        if len(set(slots)) == len(slots):
+            _check(lib().gguf_qk_timeline_setup(mult), "gguf_qk_timeline_setup")
+            return dict(zip(ks, slots))
+    raise GgufQkError(ERR_LIMIT, "gguf_qk_timeline_setup: no multiplier separates the keys")
+
+
+def gguf_qk_timeline_fetch():
+    """The record array as a numpy uint32 array [4096, 2048, 8] (six time stamps,
+    HW_ID, XCD id per wave)."""
+    import numpy as np
+    out = np.zeros((TIMELINE_SLOTS, TIMELINE_WAVES, TIMELINE_REC_BYTES // 4), dtype=np.uint32)
+    _check(lib().gguf_qk_timeline_fetch(out.ctypes.data, out.nbytes), "gguf_qk_timeline_fetch")
+    return out
 
 
 class GemvEpEntry(ctypes.Structure):

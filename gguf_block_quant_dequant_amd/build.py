@@ -1,6 +1,12 @@
 """Build libgguf_qk.so in-tree with hipcc for gfx950 only.
 
-    python -m gguf_block_quant_dequant_amd.build
+    python -m gguf_block_quant_dequant_amd.build [-v] [--timeline]
+
+Each source is compiled to an object file in parallel (one hipcc process per
+translation unit), then the objects are linked into the shared library.
+--timeline builds libgguf_qk_timeline.so instead: the same library with
+per-wave time stamps recorded by the decode GEMV kernels (GQK_TIMELINE), for
+stage timelines; it is never the default library.
 """
 
 from __future__ import annotations
@@ -8,12 +14,15 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libgguf_qk.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+TIMELINE_LIB_PATH = os.path.join(PKG_DIR, "libgguf_qk_timeline.so")
+OBJ_DIR = os.path.join(PKG_DIR, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -22,7 +31,6 @@ HIP_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
-    "-shared",
     "-fPIC",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -32,14 +40,26 @@ HIP_FLAGS = [
 ]
 
 
+# (source, extra defines, object tag): the lanes-along-K launches are compiled
+# once per block type (GGUF ids 12 Q4_K, 2 Q4_0, 14 Q6_K, 8 Q8_0; Q4_K also
+# with the fused epilogues) so that the heavy kernel families build in parallel.
+UNITS = [
+    ("gguf_qk.hip", [], "abi"),
+    ("lk.hip", [], "lkplan"),
+    ("lk_typed.hip", ["-DGQK_LK_TYPE=12", "-DGQK_LK_EP=0"], "lk_q4k"),
+    ("lk_typed.hip", ["-DGQK_LK_TYPE=12", "-DGQK_LK_EP=1"], "lk_q4k_ep"),
+    ("lk_typed.hip", ["-DGQK_LK_TYPE=2", "-DGQK_LK_EP=0"], "lk_q4_0"),
+    ("lk_typed.hip", ["-DGQK_LK_TYPE=14", "-DGQK_LK_EP=0"], "lk_q6_k"),
+    ("lk_typed.hip", ["-DGQK_LK_TYPE=8", "-DGQK_LK_EP=0"], "lk_q8_0"),
+    ("gguf_file.cpp", [], "file"),
+]
+
+
 def sources() -> list[str]:
-    return [os.path.join(CSRC, "gguf_qk.hip"), os.path.join(CSRC, "gguf_file.cpp")]
+    return sorted({os.path.join(CSRC, f) for f, _, _ in UNITS})
 
 
-def build_library(verbose: bool = False) -> str:
-    """Compile the HIP sources into LIB_PATH (always recompiles)."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), *sources(), "-o", tmp]
+def _run(cmd: list[str], verbose: bool) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,11 +67,33 @@ def build_library(verbose: bool = False) -> str:
                      if "packed-fp32-ops" not in l and l.strip())
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
+    return msgs
+
+
+def build_library(verbose: bool = False, timeline: bool = False) -> str:
+    """Compile the sources and link them into LIB_PATH (or TIMELINE_LIB_PATH);
+    always recompiles."""
+    out = TIMELINE_LIB_PATH if timeline else LIB_PATH
+    tag = "tl" if timeline else "rel"
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    defs = ["-DGQK_TIMELINE=1"] if timeline else []
+    jobs = []
+    for f, extra, name in UNITS:
+        src = os.path.join(CSRC, f)
+        obj = os.path.join(OBJ_DIR, f"{name}.{tag}.o")
+        jobs.append(([HIPCC, *HIP_FLAGS, *defs, *extra, "-I", os.path.join(ROOT, "include"), "-c", src, "-o",
+                      obj], obj))
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        outs = list(ex.map(lambda j: _run(j[0], verbose), jobs))
+    tmp = out + ".tmp"
+    outs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for _, o in jobs], "-o", tmp],
+                     verbose))
+    msgs = "\n".join(m for m in outs if m)
     if verbose and msgs:
         print(msgs, flush=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build_library(verbose="-v" in sys.argv))
+    print(build_library(verbose="-v" in sys.argv, timeline="--timeline" in sys.argv))

@@ -26,7 +26,8 @@
 #pragma once
 
 #include "device_common.hpp"
-#include "gemv.hpp"
+#include "gemv_types.hpp"
+#include "timeline.hpp"
 
 namespace gqk {
 
@@ -59,6 +60,23 @@ struct LkGroup {
   int total_blocks;
   GemvEpilogue ep[kLkMaxGroup];   // read by the kernel variants with epilogues only
 };
+
+// Host side: how a group is launched (rows of 256 nsb weights; long rows are
+// those of more than 16 super-blocks) and the launch of one block type,
+// instantiated per type in lk_typed.hip.
+struct LkPlan {
+  int nsb;
+  bool longrow;
+  int depth;     // load ring depth: 2 or 4
+  int bw;        // waves per block: 4 or 8
+  size_t lds;    // dynamic LDS bytes of the long-row kernel
+};
+template <int kType, bool kEp>
+void launch_lk_typed(const LkGroup& grp, const LkPlan& p, hipStream_t stream);
+struct LksGroup;
+template <int kType>
+void launch_lks_typed(const LksGroup& grp, int nsb, int R, int nw, int rps, int depth, int blocks,
+                      hipStream_t stream);
 
 // The block's share of a launch: its GEMV (pointers, rows, super-blocks per
 // row) and the wave's row steps [st0, st0 + n).
@@ -299,6 +317,77 @@ __device__ __forceinline__ float q6k_unit_dot(const LkLoad6& L, uint32_t h, XAt 
   return half_lo(L.d) * r;
 }
 
+// A lane's quarter (64 weights: sub-blocks 2 gq and 2 gq + 1 of one Q4_K
+// super-block) against its 64 activations xv and their two sub-block sums:
+// sum_j (d sc_j) sum_i q_i x_i - (dmin m_j) sum_i x_i over the two
+// sub-blocks. L: the super-block header and the 32 quant bytes of the
+// quarter; sh and hi_mask as q4k_pair_scales takes them for gq.
+__device__ __forceinline__ float q4k_quarter_dot(const LkLoad& L, uint32_t sh, uint32_t hi_mask,
+                                                 const float (&xv)[64], float xs0, float xs1) {
+  float dsc0, dsc1, dmm0, dmm1;
+  q4k_pair_scales(L.h.x, L.h.y, L.h.z, L.h.w, sh, hi_mask, dsc0, dsc1, dmm0, dmm1);
+  const uint32_t qw[8] = {L.qa.x, L.qa.y, L.qa.z, L.qa.w, L.qb.x, L.qb.y, L.qb.z, L.qb.w};
+  float la0 = 0.f, la1 = 0.f, ha0 = 0.f, ha1 = 0.f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    // byte 4t + e: low nibble = weight 4t + e of sub-block 2 gq,
+    // high nibble = weight 4t + e of sub-block 2 gq + 1
+    float ql[4], qh[4];
+    nibbles_div512(opaque(qw[t] & 0x0F0F0F0Fu), ql);
+    nibbles_div512(opaque((qw[t] >> 4) & 0x0F0F0F0Fu), qh);
+    float& la = (t & 1) ? la1 : la0;
+    float& ha = (t & 1) ? ha1 : ha0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      la = fmaf(ql[e], xv[4 * t + e], la);
+      ha = fmaf(qh[e], xv[32 + 4 * t + e], ha);
+    }
+  }
+  float r = dsc0 * (la0 + la1);
+  r = fmaf(dsc1, ha0 + ha1, r);
+  r = fmaf(-dmm0, xs0, r);
+  r = fmaf(-dmm1, xs1, r);
+  return r;
+}
+
+// A lane's Q4_0 quarter (two 18-byte blocks read as nine aligned words: d0 |
+// codes 0..1, codes 2..5, 6..9, 10..13, codes 14..15 | d1, then block 1's 16
+// code bytes) against its 64 activations: w = (code - 8) d, so each block adds
+// 512 d sum(code / 512 x) - 8 d sum(x); byte j of a block holds the code of
+// weight j (low nibble) and of weight j + 16 (high nibble).
+__device__ __forceinline__ float q40_quarter_dot(const LkLoad& L, const float (&xv)[64], float xs0,
+                                                 float xs1) {
+  const uint32_t w[9] = {L.h.x, L.h.y, L.h.z, L.h.w, L.qa.x, L.qa.y, L.qa.z, L.qa.w, L.qb.x};
+  const float d0 = half_lo(w[0]), d1 = half_hi(w[4]);
+  uint32_t c[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    c[k] = __builtin_amdgcn_alignbyte(w[k + 1], w[k], 2);   // block 0, codes 4k .. 4k + 3
+    c[4 + k] = w[5 + k];                                     // block 1
+  }
+  float s0a = 0.f, s0b = 0.f, s1a = 0.f, s1b = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float l0[4], h0[4], l1[4], h1[4];
+    nibbles_div512(opaque(c[k] & 0x0F0F0F0Fu), l0);
+    nibbles_div512(opaque((c[k] >> 4) & 0x0F0F0F0Fu), h0);
+    nibbles_div512(opaque(c[4 + k] & 0x0F0F0F0Fu), l1);
+    nibbles_div512(opaque((c[4 + k] >> 4) & 0x0F0F0F0Fu), h1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s0a = fmaf(l0[e], xv[4 * k + e], s0a);
+      s0b = fmaf(h0[e], xv[16 + 4 * k + e], s0b);
+      s1a = fmaf(l1[e], xv[32 + 4 * k + e], s1a);
+      s1b = fmaf(h1[e], xv[48 + 4 * k + e], s1b);
+    }
+  }
+  float r = (d0 * 512.0f) * (s0a + s0b);
+  r = fmaf(d1 * 512.0f, s1a + s1b, r);
+  r = fmaf(-8.0f * d0, xs0, r);
+  r = fmaf(-8.0f * d1, xs1, r);
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // The neighbouring steps of a decode layer fused into these GEMVs (the same
 // epilogues as the lane-per-row kernels, see GemvEpilogue): per row, in the
@@ -483,7 +572,8 @@ __device__ __forceinline__ int lk_x_slot(int i) {
 }
 
 template <int kNsb, int kDepth, int kW, bool kEp, int kType = 12>
-__device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGroup* grp);
+__device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGroup* grp, TlStamps& tl,
+                                       const void* tl_key);
 
 // kType is the row format, a GGUF type id: 12 (Q4_K), 2 (Q4_0: the same
 // 0.5625 bytes per weight, a lane's quarter two 18-byte blocks read as nine
@@ -495,8 +585,10 @@ __global__ __launch_bounds__(kW * 64) void gemv_lk_kernel(LkGroup grp) {
   // x in LDS with 4 floats of padding after every 64: the slice of lane u
   // starts at float 68 u, i.e. on bank 4 u mod 32 (16-byte reads conflict-free)
   __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
+  TlStamps tl;
+  tl.stamp(0);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  lk_run<kNsb, kDepth, kW, kEp, kType>(lk_block<kW>(grp, (int)blockIdx.x, wave), xl, &grp);
+  lk_run<kNsb, kDepth, kW, kEp, kType>(lk_block<kW>(grp, (int)blockIdx.x, wave), xl, &grp, tl, grp.d[0].W);
 }
 
 // One GEMV, its descriptor as (preloaded) scalar arguments.
@@ -504,9 +596,11 @@ template <int kType, int kNsb, int kDepth, int kW>
 __global__ __launch_bounds__(kW * 64) void gemv_lk1_kernel(const uint8_t* W, const float* x, float* y,
                                                            int rows, int q, int r) {
   __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
+  TlStamps tl;
+  tl.stamp(0);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   lk_run<kNsb, kDepth, kW, false, kType>(lk_block_single<kW>(W, x, y, rows, q, r, kNsb, (int)blockIdx.x, wave),
-                                         xl, nullptr);
+                                         xl, nullptr, tl, W);
 }
 
 // Three GEMVs of one x (stages without epilogues), the descriptors packed into
@@ -516,11 +610,13 @@ __global__ __launch_bounds__(kW * 64) void gemv_lk3_kernel(const uint8_t* W0, in
                                                            const float* x, float* y0, int dy1, int dy2,
                                                            int rows0, int rows12, int bb12, int nb) {
   __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
+  TlStamps tl;
+  tl.stamp(0);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   lk_run<kNsb, kDepth, kW, false, kType>(lk_block_three<kW, 16 / kNsb>(W0, dW1, dW2, x, y0, dy1, dy2, rows0,
                                                                        rows12, bb12, nb, kNsb,
                                                                        (int)blockIdx.x, wave),
-                                         xl, nullptr);
+                                         xl, nullptr, tl, W0);
 }
 
 // Two GEMVs of one x (stages without epilogues), the descriptors as preloaded
@@ -530,14 +626,17 @@ __global__ __launch_bounds__(kW * 64) void gemv_lk2_kernel(const uint8_t* W0, co
                                                            const float* x, float* y0, float* y1,
                                                            int rows0, int rows1, int bb1, int nb1) {
   __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
+  TlStamps tl;
+  tl.stamp(0);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   lk_run<kNsb, kDepth, kW, false, kType>(
       lk_block_two<kW, 16 / kNsb>(W0, W1, x, y0, y1, rows0, rows1, bb1, nb1, kNsb, (int)blockIdx.x, wave),
-      xl, nullptr);
+      xl, nullptr, tl, W0);
 }
 
 template <int kNsb, int kDepth, int kW, bool kEp, int kType>
-__device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGroup* grp) {
+__device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGroup* grp, TlStamps& tl,
+                                       const void* tl_key) {
   static_assert(kType == 12 || kType == 2 || kType == 8 || kType == 14, "Q4_K, Q4_0, Q8_0 or Q6_K rows");
   static_assert(kType == 12 || !kEp, "epilogues on Q4_K only");
   constexpr bool kQ40 = kType == 2, kQ80 = kType == 8, kQ6 = kType == 14;
@@ -629,6 +728,7 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
   Load ring[kDepth];
 #pragma unroll
   for (int p = 0; p < kDepth; ++p) issue(st0 + p, ring[p]);
+  tl.stamp(1);
 
 #pragma unroll
   for (int j = 0; j < kXIt; ++j) {
@@ -637,6 +737,7 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
       *reinterpret_cast<lk_f32x4*>(&xl[lk_x_slot<kType>(i)]) = xg[j];
   }
   __syncthreads();
+  tl.stamp(2);
   LkEp E;
   if constexpr (kEp) E = lk_ep(epl, ss_share);
   if (n > 0) {
@@ -696,64 +797,9 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
       }
       return fmaf(d1, s1a + s1b, d0 * (s0a + s0b));
     } else if constexpr (kQ40) {
-      // words: d0 | codes 0..1, codes 2..5, 6..9, 10..13, codes 14..15 | d1,
-      // then block 1's 16 codes; w = (code - 8) d, so each block adds
-      // 512 d sum(code / 512 x) - 8 d sum(x)
-      const uint32_t w[9] = {L.h.x, L.h.y, L.h.z, L.h.w, L.qa.x, L.qa.y, L.qa.z, L.qa.w, L.qb.x};
-      const float d0 = half_lo(w[0]), d1 = half_hi(w[4]);
-      uint32_t c[8];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        c[k] = __builtin_amdgcn_alignbyte(w[k + 1], w[k], 2);   // block 0, codes 4k .. 4k + 3
-        c[4 + k] = w[5 + k];                                     // block 1
-      }
-      float s0a = 0.f, s0b = 0.f, s1a = 0.f, s1b = 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        // byte j of a block: low nibble = weight j, high nibble = weight j + 16
-        float l0[4], h0[4], l1[4], h1[4];
-        nibbles_div512(opaque(c[k] & 0x0F0F0F0Fu), l0);
-        nibbles_div512(opaque((c[k] >> 4) & 0x0F0F0F0Fu), h0);
-        nibbles_div512(opaque(c[4 + k] & 0x0F0F0F0Fu), l1);
-        nibbles_div512(opaque((c[4 + k] >> 4) & 0x0F0F0F0Fu), h1);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          s0a = fmaf(l0[e], xv[4 * k + e], s0a);
-          s0b = fmaf(h0[e], xv[16 + 4 * k + e], s0b);
-          s1a = fmaf(l1[e], xv[32 + 4 * k + e], s1a);
-          s1b = fmaf(h1[e], xv[48 + 4 * k + e], s1b);
-        }
-      }
-      float r = (d0 * 512.0f) * (s0a + s0b);
-      r = fmaf(d1 * 512.0f, s1a + s1b, r);
-      r = fmaf(-8.0f * d0, xs0, r);
-      r = fmaf(-8.0f * d1, xs1, r);
-      return r;
+      return q40_quarter_dot(L, xv, xs0, xs1);
     } else {
-      float dsc0, dsc1, dmm0, dmm1;
-      q4k_pair_scales(L.h.x, L.h.y, L.h.z, L.h.w, sh, hi_mask, dsc0, dsc1, dmm0, dmm1);
-      const uint32_t qw[8] = {L.qa.x, L.qa.y, L.qa.z, L.qa.w, L.qb.x, L.qb.y, L.qb.z, L.qb.w};
-      float la0 = 0.f, la1 = 0.f, ha0 = 0.f, ha1 = 0.f;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        // byte 4t + e: low nibble = weight 4t + e of sub-block 2 gq,
-        // high nibble = weight 4t + e of sub-block 2 gq + 1
-        float ql[4], qh[4];
-        nibbles_div512(opaque(qw[t] & 0x0F0F0F0Fu), ql);
-        nibbles_div512(opaque((qw[t] >> 4) & 0x0F0F0F0Fu), qh);
-        float& la = (t & 1) ? la1 : la0;
-        float& ha = (t & 1) ? ha1 : ha0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          la = fmaf(ql[e], xv[4 * t + e], la);
-          ha = fmaf(qh[e], xv[32 + 4 * t + e], ha);
-        }
-      }
-      float r = dsc0 * (la0 + la1);
-      r = fmaf(dsc1, ha0 + ha1, r);
-      r = fmaf(-dmm0, xs0, r);
-      r = fmaf(-dmm1, xs1, r);
-      return r;
+      return q4k_quarter_dot(L, sh, hi_mask, xv, xs0, xs1);
     }
   };
   auto finish = [&](float r, int i) {
@@ -781,6 +827,7 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
       else
         y[row] = r;
     }
+    if (i == 0) tl.stamp(3);
   };
 
   // Whole groups of kDepth steps: step i consumes ring slot i mod kDepth and
@@ -801,11 +848,221 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
   for (int p = 0; p < kDepth - 1; ++p)
     if (i0 + p < n) finish(step(ring[p]), i0 + p);
   }   // n > 0
+  tl.stamp(4);
   if constexpr (kEp) {
     const int64_t rb0 = (int64_t)B.bs0 * rpm;
     const int64_t re = (int64_t)(B.bs0 + B.bn) * rpm;
     lk_ep_groups(E, rb0, re < rows ? re : rows, rows, y, __builtin_amdgcn_readfirstlane(tid >> 6), lane);
   }
+  tl.stamp(5);
+  tl_put(tl_key, tl);
+}
+
+// ---------------------------------------------------------------------------
+// Rows of any number of super-blocks up to 128 (K up to 32768), Q4_K or Q4_0,
+// with K split over the waves of a block: wave w of nw takes super-blocks
+// [w nsb / nw, (w + 1) nsb / nw) of every row, and the block takes R
+// consecutive rows of one GEMV. Within its slice a wave works as the
+// lanes-along-K kernel above with 64 / kRps lanes per row and kRps rows per
+// step: kRps = 4 (slices of at most 4 super-blocks), 2 (at most 8) or 1 (at
+// most 16). Lane u of a row holds quarter u of the slice (lanes past the
+// slice hold nothing and add zero), its 64 activations and their two
+// sub-block sums kept in VGPRs for every row of the block. The wave stages
+// only its own slice of x (through its own LDS window, no block barrier), so
+// no lane reads x per row. Each step's slice sums (a fixed butterfly) go to
+// LDS; after the last step the block adds the nw slice sums of each row in
+// wave order and stores y. Nothing leaves the block but y: no scratch, no
+// counters. The host picks kRps and nw so that the waves spread evenly over
+// the four SIMDs (nw a multiple of 4 where it can) with the fewest row steps
+// per SIMD; blocks of at most 12 waves (kRps 4 or 2) or 8 (kRps 1).
+// ---------------------------------------------------------------------------
+constexpr int kLksMaxNsb = 128;         // K up to 32768
+constexpr int kLksMaxRows = 128;        // rows per block
+
+// Super-blocks per slice at most, waves per block at most, and the LDS
+// floats of one wave's padded x window, for kRps rows per step.
+constexpr int lks_max_slice(int rps) { return 16 / rps; }
+constexpr int lks_max_waves(int rps) { return rps == 1 ? 8 : 12; }
+constexpr int lks_x_floats(int rps) { return lks_max_slice(rps) * 4 * 68; }
+
+struct LksDesc {
+  const uint8_t* W;
+  float* y;
+  int rows;
+  int block_begin;   // first block of this GEMV in the launch
+};
+
+struct LksGroup {
+  LksDesc d[kLkMaxGroup];
+  const float* x;   // the one input of the group's GEMVs
+  int n;
+};
+
+// Dynamic LDS bytes of a launch with nw waves and R rows per block.
+constexpr size_t lks_lds_bytes(int rps, int nw, int R) {
+  return (size_t)nw * lks_x_floats(rps) * 4 + (size_t)R * nw * 4;
+}
+
+// kType: GGUF type 12 (Q4_K) or 2 (Q4_0); both store 144 bytes per 256
+// weights. kSingle: one GEMV whose pointers and rows come in the leading
+// scalar arguments (preloaded into SGPRs), else the block's GEMV from grp.
+template <int kType, int kDepth, bool kSingle, int kRps>
+__global__ __launch_bounds__(lks_max_waves(kRps) * 64) void gemv_lks_kernel(const uint8_t* W1, const float* x,
+                                                                     float* y1, int rows1, int nsb, int R,
+                                                                     LksGroup grp) {
+  static_assert(kType == 12 || kType == 2, "Q4_K or Q4_0 rows");
+  static_assert(kRps == 1 || kRps == 2 || kRps == 4, "one, two or four rows per step");
+  constexpr bool kQ40 = kType == 2;
+  constexpr int kU = 64 / kRps;                 // lanes per row
+  constexpr int kMaxSlice = lks_max_slice(kRps);
+  constexpr int kXFloats = lks_x_floats(kRps);
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  TlStamps tl;
+  tl.stamp(0);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nw = (int)(blockDim.x >> 6);
+  const GQK_GLOBAL uint8_t* W;
+  GQK_GLOBAL float* y;
+  int rows, lb;
+  if constexpr (kSingle) {
+    W = (const GQK_GLOBAL uint8_t*)W1;
+    y = (GQK_GLOBAL float*)y1;
+    rows = rows1;
+    lb = (int)blockIdx.x;
+  } else {
+    const int b = (int)blockIdx.x;
+    const int g = (grp.n > 1 && b >= grp.d[1].block_begin) + (grp.n > 2 && b >= grp.d[2].block_begin) +
+                  (grp.n > 3 && b >= grp.d[3].block_begin);
+    const LksDesc& d = grp.d[g];
+    W = (const GQK_GLOBAL uint8_t*)d.W;
+    y = (GQK_GLOBAL float*)d.y;
+    rows = d.rows;
+    lb = b - d.block_begin;
+  }
+  const int64_t r0 = (int64_t)lb * R;
+  const int nrows = (int)(rows - r0 < R ? rows - r0 : R);   // >= 1: the host gives no empty block
+  const int n = (nrows + kRps - 1) / kRps;                 // row steps
+  const int sa = (wave * nsb) / nw, sb = ((wave + 1) * nsb) / nw;
+  const int S = sb - sa;                                   // 1 .. kMaxSlice super-blocks
+  const int half = lane / kU;                              // row of the step
+  const int u = lane % kU;
+  const bool valid = u < 4 * S;
+  const int uq = valid ? u : 4 * S - 1;                    // lanes past the slice re-read its last quarter
+  const uint32_t row_bytes = (uint32_t)nsb * kQ4KBlockBytes;
+  const uint32_t gq = (uint32_t)uq & 3u;
+  const uint32_t hoff = kQ40 ? 36u * (uint32_t)(4 * sa + uq) : (uint32_t)(sa + (uq >> 2)) * kQ4KBlockBytes;
+  const uint32_t qoff = hoff + 16u + 32u * gq;
+  const uint32_t sh = 16u * (gq & 1u);
+  const uint32_t hi_mask = gq >= 2 ? 0xFFFFFFFFu : 0u;
+
+  // x: the wave's slice, S * 64 float4, lane l taking float4s l + 64 j. All
+  // kMaxSlice loads are issued (those past the slice re-read its last float4
+  // and land in the unread tail of the window): loads under a branch made the
+  // compiler wait for each one in turn.
+  const GQK_GLOBAL lk_f32x4* xs4 = (const GQK_GLOBAL lk_f32x4*)x + 64 * sa;
+  lk_f32x4 xg[kMaxSlice];
+#pragma unroll
+  for (int j = 0; j < kMaxSlice; ++j) {
+    const int i = lane + 64 * j;
+    xg[j] = xs4[i < 64 * S ? i : 64 * S - 1];
+  }
+
+  // Step i reads rows r0 + kRps i + half (a row past the block's last
+  // re-reads the last one; steps past the wave's last re-read that step:
+  // every ring slot issues the same loads, so the in-order wait counts stay
+  // exact).
+  const int last = n - 1;
+  auto issue = [&](int i, LkLoad& L) {
+    i = i < last ? i : last;
+    int rr = kRps * i + half;
+    rr = rr < nrows ? rr : nrows - 1;
+    const GQK_GLOBAL uint8_t* base = W + (r0 + rr) * (int64_t)row_bytes;
+    if constexpr (kQ40) {
+      const GQK_GLOBAL uint32_t* w = reinterpret_cast<const GQK_GLOBAL uint32_t*>(base + hoff);
+      L.h = lk_u32x4{w[0], w[1], w[2], w[3]};
+      L.qa = lk_u32x4{w[4], w[5], w[6], w[7]};
+      L.qb = lk_u32x4{w[8], 0u, 0u, 0u};
+    } else {
+      L.h = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + hoff);
+      L.qa = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + qoff);
+      L.qb = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + (qoff + 16));
+    }
+  };
+  // The whole ring goes out with x (as in lk_run): the weights are in flight
+  // from the start and x's wait overlaps them.
+  LkLoad ring[kDepth];
+#pragma unroll
+  for (int p = 0; p < kDepth; ++p) issue(p, ring[p]);
+  tl.stamp(1);
+
+  // stage the slice in the wave's own LDS window (quarter v at float 68 v)
+  // and take this lane's quarter back: a wave-level exchange, no block barrier
+  float* xw = lds + wave * kXFloats;
+#pragma unroll
+  for (int j = 0; j < kMaxSlice; ++j) {
+    const int i = lane + 64 * j;
+    *reinterpret_cast<lk_f32x4*>(&xw[68 * (i >> 4) + 4 * (i & 15)]) = xg[j];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float xv[64];
+  {
+    const float4* xp = reinterpret_cast<const float4*>(&xw[68 * uq]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float4 t = xp[i];
+      xv[4 * i + 0] = t.x;
+      xv[4 * i + 1] = t.y;
+      xv[4 * i + 2] = t.z;
+      xv[4 * i + 3] = t.w;
+    }
+  }
+  float xs0 = 0.f, xs1 = 0.f;   // sums of x over the quarter's two halves of 32
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    xs0 += xv[i];
+    xs1 += xv[32 + i];
+  }
+  tl.stamp(2);
+
+  float* part = lds + nw * kXFloats;   // [row of the block][wave]
+  auto step = [&](const LkLoad& L) {
+    const float r = kQ40 ? q40_quarter_dot(L, xv, xs0, xs1) : q4k_quarter_dot(L, sh, hi_mask, xv, xs0, xs1);
+    return valid ? r : 0.f;
+  };
+  auto finish = [&](float r, int i) {
+    r = lk_segment_sum<kU>(r);
+    const int rr = kRps * i + half;
+    if (u == kU - 1 && rr < nrows) part[rr * nw + wave] = r;
+    if (i == 0) tl.stamp(3);
+  };
+  int i0 = 0;
+  for (; i0 + kDepth <= n; i0 += kDepth) {
+#pragma unroll
+    for (int p = 0; p < kDepth; ++p) {
+      const float r = step(ring[p]);
+      issue(i0 + p + kDepth, ring[p]);
+      finish(r, i0 + p);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < kDepth - 1; ++p)
+    if (i0 + p < n) finish(step(ring[p]), i0 + p);
+  tl.stamp(4);
+
+  // the rows' slice sums, added in wave order
+  __syncthreads();
+  if (wave == 0) {
+    for (int rr = lane; rr < nrows; rr += 64) {
+      float v = 0.f;
+      for (int w = 0; w < nw; ++w) v += part[rr * nw + w];
+      y[r0 + rr] = v;
+    }
+  }
+  tl.stamp(5);
+  tl_put(kSingle ? (const void*)W1 : (const void*)grp.d[0].W, tl);
 }
 
 // ---------------------------------------------------------------------------
@@ -851,6 +1108,8 @@ __global__ __launch_bounds__(kW * 64) void gemv_lkx_kernel(const uint8_t* W1, co
   // [K + K/16] padded x, then [K/32] sub-block sums ([K/16] sums of runs of
   // 16 for Q6_K)
   extern __shared__ __attribute__((aligned(16))) float xl[];
+  TlStamps tl;
+  tl.stamp(0);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -922,6 +1181,7 @@ __global__ __launch_bounds__(kW * 64) void gemv_lkx_kernel(const uint8_t* W1, co
   XLoad ring[kDepth][kQ];
 #pragma unroll
   for (int p = 0; p < kDepth; ++p) issue(st0 + p, ring[p]);
+  tl.stamp(1);
 
   // store x; the eight threads 8m .. 8m + 7 hold the 32 values of
   // sub-block i / 8 (i = their float4 index) and add them with a fixed
@@ -948,6 +1208,7 @@ __global__ __launch_bounds__(kW * 64) void gemv_lkx_kernel(const uint8_t* W1, co
     }
   }
   __syncthreads();
+  tl.stamp(2);
   LkEp E;
   if constexpr (kEp) E = lk_ep(epl, ss_share);
   if (n > 0) {
@@ -1049,6 +1310,7 @@ __global__ __launch_bounds__(kW * 64) void gemv_lkx_kernel(const uint8_t* W1, co
       else
         B.y[st0 + i] = r;
     }
+    if (i == 0) tl.stamp(3);
   };
 
   int i0 = 0;
@@ -1064,10 +1326,13 @@ __global__ __launch_bounds__(kW * 64) void gemv_lkx_kernel(const uint8_t* W1, co
   for (int p = 0; p < kDepth - 1; ++p)
     if (i0 + p < n) finish(step(ring[p]), i0 + p);
   }   // n > 0
+  tl.stamp(4);
   if constexpr (kEp) {
     const int64_t rb0 = B.bs0;
     lk_ep_groups(E, rb0, rb0 + B.bn, B.rows, B.y, wave, lane);
   }
+  tl.stamp(5);
+  tl_put(kSingle ? (const void*)W1 : (const void*)grp.d[0].W, tl);
 }
 
 }  // namespace gqk

@@ -30,11 +30,10 @@
 #pragma once
 
 #include "device_common.hpp"
+#include "gemv_types.hpp"
 
 namespace gqk {
 
-constexpr int kQ40BlockBytes = 18;
-constexpr int kQ40BlockWeights = 32;
 constexpr int kOtherRows = 4;      // rows per wave
 constexpr int kOtherWaves = 4;     // waves per block
 

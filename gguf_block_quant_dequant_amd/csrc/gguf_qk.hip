@@ -14,14 +14,15 @@
 
 #include "../../include/gguf_file.h"
 #include "../../include/gguf_qk.h"
+#include "launch.hpp"
 #include "dequant.hpp"
 #include "gemm.hpp"
 #include "gemv.hpp"
-#include "gemv_lk.hpp"
 #include "gemv_other.hpp"
 #include "gemv_small_batch.hpp"
 #include "layer_ops.hpp"
 #include "probe.hpp"
+#include "timeline.hpp"
 
 namespace gqk {
 
@@ -49,73 +50,6 @@ struct ScratchArea {
 static __device__ __attribute__((aligned(256))) ScratchArea g_scratch;
 
 constexpr int kMaxDevices = 64;
-
-// Launch-shape knobs. Defaults are the measured best; GGUF_QK_TUNE (for
-// sweeps, e.g. "tasks=2048,q4k_slots=1,q80_slots=1") overrides them.
-struct Tuning {
-  int target_tasks = 2048;   // wave tasks a split-K GEMV aims for
-  int gemm_blocks = 0;       // blocks a prefill GEMM aims for (0: by K, see gguf_qmatmul_q4_k)
-  int gemm_max_split = 0;    // largest K split of a prefill GEMM (0: by K)
-  int sb_blocks = 512;       // blocks a small-batch product aims for
-  int sb_max_split = 8;      // largest K split of a small-batch product
-  int q4k_slots = 1;         // LDS chunks in flight per wave, Q4_K
-  int q80_slots = 1;         // LDS chunks in flight per wave, Q8_0
-  int q4k_lk = 1;            // Q4_K GEMVs without epilogue: lanes-along-K kernels
-  int lk_waves = 1024;       // waves a lanes-along-K launch aims for
-  int lkx_waves = 2048;      // the same for rows longer than 16 super-blocks
-  int lkx_waves_q6 = 1024;   // the same for Q6_K rows longer than 16 super-blocks
-  int lk_single = 1;         // one-GEMV launches take their descriptor as scalar arguments
-  int lk_bw = 4;             // waves per block, rows of <= 16 super-blocks (4 or 8)
-  int lkx_bw = 8;            // waves per block, longer rows (4 or 8)
-  int lk_pair_in_wave = 1;   // gate/up pairs: both rows of an index in one wave
-  int lk_two = 1;            // two GEMVs of one x: descriptors as scalar arguments
-  int lk_three = 1;          // three GEMVs of one x: packed descriptors as scalar arguments
-  int q4_0_lk = 1;           // Q4_0 rows of 256 .. 12288 weights: lanes-along-K kernels
-  int q8_0_lk = 1;           // Q8_0 rows of 256 .. 4096 weights: lanes-along-K kernels
-  int q6_k_lk = 1;           // Q6_K rows of 256 .. 12288 weights: lanes-along-K kernels
-  int gemm_db = 1;           // prefill: the double-buffered GEMM
-};
-
-static const Tuning& tuning() {
-  static const Tuning t = [] {
-    Tuning r;
-    const char* e = std::getenv("GGUF_QK_TUNE");
-    if (!e) return r;
-    const char* p = e;
-    while (*p) {
-      const char* eq = std::strchr(p, '=');
-      if (!eq) break;
-      const std::string key(p, eq - p);
-      const int v = std::atoi(eq + 1);
-      if (key == "tasks" && v > 0) r.target_tasks = v;
-      if (key == "gemm_blocks" && v >= 0) r.gemm_blocks = v;
-      if (key == "gemm_max_split" && v >= 0 && v <= kGemmMaxSplits) r.gemm_max_split = v;
-      if (key == "sb_blocks" && v > 0) r.sb_blocks = v;
-      if (key == "sb_max_split" && v > 0 && v <= 8) r.sb_max_split = v;
-      if (key == "q4k_slots" && (v == 1 || v == 2)) r.q4k_slots = v;
-      if (key == "q80_slots" && (v == 1 || v == 2)) r.q80_slots = v;
-      if (key == "q4k_lk" && (v == 0 || v == 1)) r.q4k_lk = v;
-      if (key == "lk_waves" && v > 0) r.lk_waves = v;
-      if (key == "lkx_waves" && v > 0) r.lkx_waves = v;
-      if (key == "lkx_waves_q6" && v > 0) r.lkx_waves_q6 = v;
-      if (key == "lk_single" && (v == 0 || v == 1)) r.lk_single = v;
-      if (key == "lk_bw" && (v == 4 || v == 8)) r.lk_bw = v;
-      if (key == "lkx_bw" && (v == 4 || v == 8)) r.lkx_bw = v;
-      if (key == "lk_pair_in_wave" && (v == 0 || v == 1)) r.lk_pair_in_wave = v;
-      if (key == "lk_two" && (v == 0 || v == 1)) r.lk_two = v;
-      if (key == "lk_three" && (v == 0 || v == 1)) r.lk_three = v;
-      if (key == "q4_0_lk" && (v == 0 || v == 1)) r.q4_0_lk = v;
-      if (key == "q8_0_lk" && (v == 0 || v == 1)) r.q8_0_lk = v;
-      if (key == "q6_k_lk" && (v == 0 || v == 1)) r.q6_k_lk = v;
-      if (key == "gemm_db" && (v == 0 || v == 1)) r.gemm_db = v;
-      const char* comma = std::strchr(eq, ',');
-      if (!comma) break;
-      p = comma + 1;
-    }
-    return r;
-  }();
-  return t;
-}
 
 struct DeviceState {
   std::atomic<int> checked{0};   // 0 unknown, 1 gfx950, -1 unsupported
@@ -151,10 +85,6 @@ static int current_device(ScratchArea** scratch) {
   if (c != 1) return GGUF_QK_ERR_DEVICE;
   if (scratch) *scratch = st.scratch;
   return GGUF_QK_OK;
-}
-
-static int launch_status() {
-  return hipGetLastError() == hipSuccess ? GGUF_QK_OK : GGUF_QK_ERR_LAUNCH;
 }
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -344,273 +274,6 @@ static int64_t plan_group(int type, const gguf_qk_gemv* const* v, const GemvEpil
   return tasks;
 }
 
-extern "C++" {
-// Two GEMVs of one x without epilogues: both descriptors as scalar arguments.
-// (The kernel re-forms each GEMV's q and r from its rows and block count, so
-// both GEMVs must have blocks.)
-static bool lk_two(const LkGroup& grp) {
-  return grp.n == 2 && grp.d[0].x == grp.d[1].x && grp.d[1].block_begin > 0 &&
-         grp.d[1].block_begin < grp.total_blocks && tuning().lk_two;
-}
-
-// Three GEMVs of one x without epilogues, every one with blocks, whose
-// packed descriptors fit (see lk_block_three).
-struct Lk3Args {
-  int dW1, dW2, dy1, dy2, rows12, bb12;
-};
-static bool fits_i32(int64_t v) { return v >= INT32_MIN && v <= INT32_MAX; }
-static bool lk_three(const LkGroup& grp, Lk3Args* a) {
-  if (grp.n != 3 || !tuning().lk_three) return false;
-  const LkDesc *d = grp.d;
-  if (d[1].x != d[0].x || d[2].x != d[0].x) return false;
-  const int bb1 = d[1].block_begin, bb2 = d[2].block_begin;
-  if (!(0 < bb1 && bb1 < bb2 && bb2 < grp.total_blocks && bb2 < 65536)) return false;
-  if (d[1].rows >= 65536 || d[2].rows >= 65536) return false;
-  const int64_t w0 = (int64_t)reinterpret_cast<intptr_t>(d[0].W);
-  const int64_t dW1 = (int64_t)reinterpret_cast<intptr_t>(d[1].W) - w0;
-  const int64_t dW2 = (int64_t)reinterpret_cast<intptr_t>(d[2].W) - w0;
-  const int64_t y0 = (int64_t)reinterpret_cast<intptr_t>(d[0].y);
-  const int64_t by1 = (int64_t)reinterpret_cast<intptr_t>(d[1].y) - y0;
-  const int64_t by2 = (int64_t)reinterpret_cast<intptr_t>(d[2].y) - y0;
-  // offsets in 16-byte units
-  if ((w0 | dW1 | dW2 | y0 | by1 | by2) & 15) return false;
-  if (!fits_i32(dW1 / 16) || !fits_i32(dW2 / 16) || !fits_i32(by1 / 16) || !fits_i32(by2 / 16)) return false;
-  a->dW1 = (int)(dW1 / 16);
-  a->dW2 = (int)(dW2 / 16);
-  a->dy1 = (int)(by1 / 16);
-  a->dy2 = (int)(by2 / 16);
-  a->rows12 = (int)((uint32_t)d[1].rows | ((uint32_t)d[2].rows << 16));
-  a->bb12 = (int)((uint32_t)bb1 | ((uint32_t)bb2 << 16));
-  return true;
-}
-
-template <int kType, int kNsb, int kW>
-static void launch_lk3(const LkGroup& grp, const Lk3Args& a, int depth, hipStream_t stream) {
-  const dim3 grid((unsigned)grp.total_blocks), block(kW * 64);
-  const LkDesc& d = grp.d[0];
-  if (depth <= 2)
-    hipLaunchKernelGGL((gemv_lk3_kernel<kType, kNsb, 2, kW>), grid, block, 0, stream, d.W, a.dW1, a.dW2, d.x,
-                       d.y, a.dy1, a.dy2, d.rows, a.rows12, a.bb12, grp.total_blocks);
-  else
-    hipLaunchKernelGGL((gemv_lk3_kernel<kType, kNsb, 4, kW>), grid, block, 0, stream, d.W, a.dW1, a.dW2, d.x,
-                       d.y, a.dy1, a.dy2, d.rows, a.rows12, a.bb12, grp.total_blocks);
-}
-
-template <int kType, int kNsb, int kW>
-static void launch_lk2(const LkGroup& grp, int depth, hipStream_t stream) {
-  const dim3 grid((unsigned)grp.total_blocks), block(kW * 64);
-  const LkDesc &a = grp.d[0], &b = grp.d[1];
-  if (depth <= 2)
-    hipLaunchKernelGGL((gemv_lk2_kernel<kType, kNsb, 2, kW>), grid, block, 0, stream, a.W, b.W, a.x, a.y, b.y,
-                       a.rows, b.rows, b.block_begin, grp.total_blocks - b.block_begin);
-  else
-    hipLaunchKernelGGL((gemv_lk2_kernel<kType, kNsb, 4, kW>), grid, block, 0, stream, a.W, b.W, a.x, a.y, b.y,
-                       a.rows, b.rows, b.block_begin, grp.total_blocks - b.block_begin);
-}
-
-// One launch of the lanes-along-K kernels for rows of 256 kNsb weights of
-// type kType: one GEMV, two of one x, or a group from the descriptors.
-template <int kType, int kNsb, int kW, bool kEp>
-static void launch_lk_nsb(const LkGroup& grp, int depth, hipStream_t stream) {
-  const dim3 grid((unsigned)grp.total_blocks), block(kW * 64);
-  if (!kEp && grp.n == 1 && tuning().lk_single) {
-    const LkDesc& d = grp.d[0];
-    if (depth <= 2)
-      hipLaunchKernelGGL((gemv_lk1_kernel<kType, kNsb, 2, kW>), grid, block, 0, stream, d.W, d.x, d.y,
-                         d.rows, d.q, d.r);
-    else
-      hipLaunchKernelGGL((gemv_lk1_kernel<kType, kNsb, 4, kW>), grid, block, 0, stream, d.W, d.x, d.y,
-                         d.rows, d.q, d.r);
-    return;
-  }
-  if (!kEp && lk_two(grp)) {
-    launch_lk2<kType, kNsb, kW>(grp, depth, stream);
-    return;
-  }
-  Lk3Args a3;
-  if (!kEp && lk_three(grp, &a3)) {
-    launch_lk3<kType, kNsb, kW>(grp, a3, depth, stream);
-    return;
-  }
-  if (depth <= 2)
-    hipLaunchKernelGGL((gemv_lk_kernel<kType, kNsb, 2, kW, kEp>), grid, block, 0, stream, grp);
-  else
-    hipLaunchKernelGGL((gemv_lk_kernel<kType, kNsb, 4, kW, kEp>), grid, block, 0, stream, grp);
-}
-
-template <int kNsb>
-static void launch_lk_nsb(const LkGroup& grp, int depth, int waves, bool ep, int type,
-                          hipStream_t stream) {
-  if (type == GGUF_QK_TYPE_Q4_0)
-    launch_lk_nsb<GGUF_QK_TYPE_Q4_0, kNsb, 4, false>(grp, depth, stream);
-  else if (type == GGUF_QK_TYPE_Q6_K)
-    launch_lk_nsb<GGUF_QK_TYPE_Q6_K, kNsb, 4, false>(grp, depth, stream);
-  else if (type == GGUF_QK_TYPE_Q8_0)
-    launch_lk_nsb<GGUF_QK_TYPE_Q8_0, kNsb, 4, false>(grp, depth, stream);
-  else if (ep)
-    launch_lk_nsb<GGUF_QK_TYPE_Q4_K, kNsb, 4, true>(grp, depth, stream);
-  else if (waves == 8)
-    launch_lk_nsb<GGUF_QK_TYPE_Q4_K, kNsb, 8, false>(grp, depth, stream);
-  else
-    launch_lk_nsb<GGUF_QK_TYPE_Q4_K, kNsb, 4, false>(grp, depth, stream);
-}
-
-template <int kQ, int kW>
-static void launch_lkx(const LkGroup& grp, size_t lds, bool ep, int type, hipStream_t stream) {
-  const bool q40 = type == GGUF_QK_TYPE_Q4_0, q6 = type == GGUF_QK_TYPE_Q6_K;
-  const dim3 grid((unsigned)grp.total_blocks), block(kW * 64);
-  // one GEMV without epilogue: its descriptor as (preloaded) scalar arguments
-  const bool single = grp.n == 1 && !ep && tuning().lk_single;
-  const LkDesc& d = grp.d[0];
-  const uint8_t* W = single ? d.W : nullptr;
-  const float* x = single ? d.x : nullptr;
-  float* y = single ? d.y : nullptr;
-  const int rows = single ? d.rows : 0, q = single ? d.q : 0, r = single ? d.r : 0;
-  const int nsb = single ? d.nsb : 0;
-  if (q6) {
-    // (three rounds of Q6_K quarters run in 4-wave blocks only)
-    if constexpr (!(kQ == 3 && kW == 8)) {
-      if (single)
-        hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q6_K, kQ, 2, kW, false, true>), grid, block, lds,
-                           stream, W, x, y, rows, q, r, nsb, grp);
-      else
-        hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q6_K, kQ, 2, kW, false, false>), grid, block, lds,
-                           stream, W, x, y, rows, q, r, nsb, grp);
-    }
-    return;
-  }
-  if (q40 && single)
-    hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q4_0, kQ, 2, kW, false, true>), grid, block, lds, stream,
-                       W, x, y, rows, q, r, nsb, grp);
-  else if (q40)
-    hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q4_0, kQ, 2, kW, false, false>), grid, block, lds, stream,
-                       W, x, y, rows, q, r, nsb, grp);
-  else if (single)
-    hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q4_K, kQ, 2, kW, false, true>), grid, block, lds, stream,
-                       W, x, y, rows, q, r, nsb, grp);
-  else if (ep)
-    hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q4_K, kQ, 2, kW, true, false>), grid, block, lds, stream,
-                       W, x, y, rows, q, r, nsb, grp);
-  else
-    hipLaunchKernelGGL((gemv_lkx_kernel<GGUF_QK_TYPE_Q4_K, kQ, 2, kW, false, false>), grid, block, lds, stream,
-                       W, x, y, rows, q, r, nsb, grp);
-}
-}
-
-// Q4_K GEMVs whose rows hold 1, 2, 4, 8 or 16 super-blocks (lanes hold x), or
-// 17 to 48 (x read from LDS), all the same: the lanes-along-K kernels take
-// them, with any epilogue except norm preparation and a gate/up pair together
-// on one GEMV, and at most 256 partial sums for an input RMSN.
-static bool lk_fits(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n) {
-  const int64_t c = v[0]->cols;
-  if (c % 256 || (c != 256 && c != 512 && c != 1024 && c != 2048 && c != 4096 && (c <= 4096 || c > kLkxMaxK)))
-    return false;
-  for (int i = 0; i < n; ++i) {
-    if (v[i]->cols != c || v[i]->rows > (int64_t(1) << 30)) return false;
-    if (e && e[i]) {
-      const int f = e[i]->flags;
-      if ((f & kEpNorm) && (f & kEpPair)) return false;
-      if ((f & kEpScale) && e[i]->scale_n > 256) return false;
-      if ((f & kEpNorm) && !e[i]->norm_cnt) return false;
-    }
-  }
-  return true;
-}
-
-// Lanes-along-K launch: blocks go to the GEMVs in proportion to their rows
-// (at least one, at most one per row step); a shallow load ring when a wave
-// has only a few steps.
-static int launch_lk(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n,
-                     hipStream_t stream, int type = GGUF_QK_TYPE_Q4_K) {
-  const int nsb = (int)(v[0]->cols / 256);
-  const bool longrow = nsb > 16;
-  const int rps = longrow ? 1 : 64 / (4 * nsb);
-  bool ep = false;
-  for (int i = 0; i < n; ++i) ep = ep || (e && e[i] && e[i]->flags != 0);
-  int bw = longrow ? tuning().lkx_bw : (ep || type != GGUF_QK_TYPE_Q4_K) ? 4 : tuning().lk_bw;
-  // Q6_K rows of three rounds hold 20 words per quarter in the load ring:
-  // only 4-wave blocks (512 registers a lane) fit them without scratch
-  if (longrow && type == GGUF_QK_TYPE_Q6_K && nsb > 32) bw = 4;
-  LkGroup grp{};
-  grp.n = n;
-  int64_t total_rows = 0;
-  for (int i = 0; i < n; ++i) total_rows += v[i]->rows;
-  // (Q6_K long rows: two rows per wave halve the x staging of 4-wave blocks)
-  const int lkx_waves = type == GGUF_QK_TYPE_Q6_K ? tuning().lkx_waves_q6 : tuning().lkx_waves;
-  const int64_t target_blocks = ((longrow ? lkx_waves : tuning().lk_waves) + bw - 1) / bw;
-  // gate/up pairs computed in the same wave (the gate's rows in lanes 0..31,
-  // the up's in 32..63): the gate's descriptor takes both matrices' blocks,
-  // the up's gets none
-  bool in_wave[kLkMaxGroup] = {false, false, false, false};
-  for (int i = 0; i + 1 < n; ++i)
-    if (!longrow && rps >= 2 && e && e[i] && e[i + 1] && (e[i]->flags & kEpPair) && e[i]->role == 0 &&
-        (e[i + 1]->flags & kEpPair) && e[i + 1]->role == 1 &&
-        !((e[i]->flags | e[i + 1]->flags) & (kEpNorm | kEpResidual)) &&
-        (e[i]->flags & kEpScale) == (e[i + 1]->flags & kEpScale) &&
-        e[i]->scale_ss == e[i + 1]->scale_ss && e[i]->scale_n == e[i + 1]->scale_n &&
-        e[i]->eps == e[i + 1]->eps && v[i]->x == v[i + 1]->x && v[i + 1]->rows == v[i]->rows &&
-        tuning().lk_pair_in_wave)
-      in_wave[i] = true;
-  int64_t bb = 0, max_wave_steps = 0;
-  for (int i = 0; i < n; ++i) {
-    const bool up_half = i > 0 && in_wave[i - 1];
-    const int rpm = in_wave[i] ? rps / 2 : rps;
-    const int64_t steps = (v[i]->rows + rpm - 1) / rpm;
-    const double share = (in_wave[i] ? 2.0 : 1.0) * (double)v[i]->rows / (double)total_rows;
-    int64_t want = (int64_t)((double)target_blocks * share + 0.5);
-    if (want < 1) want = 1;
-    if (want > steps) want = steps;
-    if (up_half) want = 0;
-    LkDesc& d = grp.d[i];
-    d.W = static_cast<const uint8_t*>(v[i]->W);
-    d.x = v[i]->x;
-    d.y = v[i]->y;
-    d.rows = (int)v[i]->rows;
-    d.block_begin = (int)bb;
-    d.q = want ? (int)(steps / want) : 0;
-    d.r = want ? (int)(steps % want) : 0;
-    d.nsb = nsb;
-    if (e && e[i]) {
-      grp.ep[i] = *e[i];
-      if (in_wave[i]) grp.ep[i].flags |= kEpPairInWave;
-      d.ep_flags = grp.ep[i].flags;
-      d.scale_ss = e[i]->scale_ss;
-      d.scale_n = e[i]->scale_n;
-    }
-    bb += want;
-    if (want) {
-      const int64_t ws = ((steps + want - 1) / want + bw - 1) / bw;
-      if (ws > max_wave_steps) max_wave_steps = ws;
-    }
-  }
-  grp.total_blocks = (int)bb;
-  const int depth = max_wave_steps <= 2 ? 2 : 4;
-  if (longrow) {
-    const int kq = (4 * nsb + 63) / 64;
-    // x padded, then the sums of x per 32-weight sub-block (per run of 16 for Q6_K)
-    const size_t lds = (size_t)(256 * nsb) * 4 * (type == GGUF_QK_TYPE_Q6_K ? 36 : 35) / 32;
-    if (bw == 8) {
-      if (kq == 2)
-        launch_lkx<2, 8>(grp, lds, ep, type, stream);
-      else
-        launch_lkx<3, 8>(grp, lds, ep, type, stream);
-    } else {
-      if (kq == 2)
-        launch_lkx<2, 4>(grp, lds, ep, type, stream);
-      else
-        launch_lkx<3, 4>(grp, lds, ep, type, stream);
-    }
-    return launch_status();
-  }
-  switch (nsb) {
-    case 1: launch_lk_nsb<1>(grp, depth, bw, ep, type, stream); break;
-    case 2: launch_lk_nsb<2>(grp, depth, bw, ep, type, stream); break;
-    case 4: launch_lk_nsb<4>(grp, depth, bw, ep, type, stream); break;
-    case 8: launch_lk_nsb<8>(grp, depth, bw, ep, type, stream); break;
-    default: launch_lk_nsb<16>(grp, depth, bw, ep, type, stream); break;
-  }
-  return launch_status();
-}
 
 static int launch_other(int type, const void* W, const float* x, float* y, int64_t rows,
                         int64_t cols, hipStream_t stream);
@@ -618,7 +281,8 @@ static int launch_other(int type, const void* W, const float* x, float* y, int64
 // Launches one planned group.
 static int launch_group(int type, const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n,
                         const ScratchArea* scratch, hipStream_t stream) {
-  if (type == GGUF_QK_TYPE_Q4_K && tuning().q4k_lk && lk_fits(v, e, n)) return launch_lk(v, e, n, stream);
+  if (lks_fits(v, e, n, type)) return launch_lks(v, n, stream, type);
+  if (type == GGUF_QK_TYPE_Q4_K && tuning().q4k_lk && lk_fits(v, e, n)) return launch_lk(v, e, n, stream, GGUF_QK_TYPE_Q4_K);
   if (type == GGUF_QK_TYPE_Q4_0 || type == GGUF_QK_TYPE_Q6_K) {
     // rows of 256 .. 12288 weights in multiples of 256 (no epilogues on
     // these types): the lanes-along-K kernels; else the lane-quad kernel, one
@@ -1256,6 +920,60 @@ int gguf_swiglu_f32(const float* g, const float* u, float* out, int64_t n, hipSt
 
 int gguf_add_f32(const float* a, const float* b, float* out, int64_t n, hipStream_t stream) {
   return elementwise2(1, a, b, out, n, stream);
+}
+
+#if GQK_TIMELINE
+extern "C++" {
+namespace gqk {
+std::vector<TlBindFn>& tl_registry() {
+  static std::vector<TlBindFn> r;
+  return r;
+}
+}  // namespace gqk
+}
+static TlRec* g_tl_recs_dev = nullptr;
+#endif
+
+int gguf_qk_timeline_setup(uint64_t mult) {
+#if GQK_TIMELINE
+  if (mult && !(mult & 1u)) return GGUF_QK_ERR_SHAPE;
+  int st = current_device(nullptr);
+  if (st) return st;
+  const size_t bytes = sizeof(TlRec) * (size_t)kTlSlots * kTlWaves;
+  // the instrumented build's own record buffer (the default build allocates nothing)
+  if (!g_tl_recs_dev && hipMalloc(&g_tl_recs_dev, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return GGUF_QK_ERR_DEVICE;
+  }
+  if (hipMemset(g_tl_recs_dev, 0, bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    (void)hipGetLastError();
+    return GGUF_QK_ERR_DEVICE;
+  }
+  const TlState s{mult, g_tl_recs_dev};
+  for (TlBindFn f : tl_registry())
+    if (f(s)) return GGUF_QK_ERR_DEVICE;
+  return GGUF_QK_OK;
+#else
+  (void)mult;
+  return GGUF_QK_ERR_LIMIT;
+#endif
+}
+
+int gguf_qk_timeline_fetch(void* host_out, int64_t bytes) {
+#if GQK_TIMELINE
+  if (!host_out) return GGUF_QK_ERR_NULL;
+  if (bytes != (int64_t)(sizeof(TlRec) * (size_t)kTlSlots * kTlWaves)) return GGUF_QK_ERR_SHAPE;
+  if (!g_tl_recs_dev) return GGUF_QK_ERR_LIMIT;
+  if (hipMemcpy(host_out, g_tl_recs_dev, (size_t)bytes, hipMemcpyDeviceToHost) != hipSuccess) {
+    (void)hipGetLastError();
+    return GGUF_QK_ERR_DEVICE;
+  }
+  return GGUF_QK_OK;
+#else
+  (void)host_out;
+  (void)bytes;
+  return GGUF_QK_ERR_LIMIT;
+#endif
 }
 
 int gguf_qk_probe_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream) {

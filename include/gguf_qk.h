@@ -288,6 +288,23 @@ int gguf_qmatmul_f32_q4_k_multi(const void* const* W, float* const* Y, const int
  * bandwidth, the practical ceiling for the weight stream. */
 int gguf_qk_probe_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
 
+/* Stage timelines of the decode GEMV kernels (measurement; the instrumented
+ * build libgguf_qk_timeline.so only, compiled with GQK_TIMELINE: in the
+ * default library both calls return GGUF_QK_ERR_LIMIT and do nothing).
+ * gguf_qk_timeline_setup(mult) clears the record buffer and arms the kernels
+ * (mult odd; 0 disarms): from then on every wave of a lanes-along-K launch
+ * writes a 32-byte record {six uint32 time stamps of the 100 MHz device
+ * clock: entry, loads issued, activations staged, first row step stored, last
+ * row step computed, end; HW_ID; XCD id} at [slot][wave index in the grid] of
+ * a [4096][2048] array, slot = (key * mult mod 2^64) >> 52 with key the
+ * launch's first weight pointer (waves past 2048 are not recorded; the
+ * caller picks mult so that the launches it traces take distinct slots).
+ * gguf_qk_timeline_fetch copies that whole array (bytes must be
+ * 4096 * 2048 * 32) to host memory, synchronously. The instrumented build
+ * allocates its record buffer (256 MiB) on the first setup call. */
+int gguf_qk_timeline_setup(uint64_t mult);
+int gguf_qk_timeline_fetch(void* host_out, int64_t bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -237,3 +237,36 @@ def decode_stream_bytes(n_layers: int = N_LAYERS, head: bool = True) -> int:
     if head:
         total += HEAD.rows * row_bytes(HEAD.fmt, HEAD.cols)
     return total
+
+
+# ---------------------------------------------------------------------------
+# Single-matrix configurations: the 256x512 Q8_0 GEMV (seed stream cfg 1), the
+# Q8_0 GEMVs at decode shapes (cfg 2) and the Q4_K ffn_up-like and
+# ffn_down-like GEMVs (cfg 3), batch 1. Weights from rng_for(cfg, 0, tensor),
+# the input vector from rng_for(cfg, 0, 100 + tensor).
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class SingleMatrix:
+    label: str
+    fmt: str
+    rows: int
+    cols: int
+    cfg: int
+    tensor: int
+
+
+SINGLE_MATRICES: tuple[SingleMatrix, ...] = (
+    SingleMatrix("cfg1 Q8_0 256x512", Q8_0, 256, 512, 1, 0),
+    SingleMatrix("cfg2 Q8_0 2048x2048", Q8_0, 2048, 2048, 2, 0),
+    SingleMatrix("cfg2 Q8_0 11008x2048", Q8_0, 11008, 2048, 2, 1),
+    SingleMatrix("cfg3 Q4_K 11008x2048 (ffn_up-like)", Q4_K, 11008, 2048, 3, 0),
+    SingleMatrix("cfg3 Q4_K 2048x11008 (ffn_down-like)", Q4_K, 2048, 11008, 3, 1),
+)
+
+
+def single_matrix(m: SingleMatrix) -> tuple[np.ndarray, np.ndarray]:
+    """(weights uint8 [rows, row_bytes], x fp32 [cols]) of a single-matrix case."""
+    w = gemv_weights(rng_for(m.cfg, 0, m.tensor), Gemv(m.label, m.fmt, m.rows, m.cols))
+    x = activations_f32(rng_for(m.cfg, 0, 100 + m.tensor), m.cols)
+    return w, x

@@ -208,10 +208,12 @@ def test_matvec_q8_0_ragged(rows, cols):
     assert ok and e <= TOL_F32, e
 
 
-# Every row length the lanes-along-K kernels take (a row of 1 to 16
-# super-blocks held by lanes, 17 to 48 read in rounds from LDS) and the first
-# past them (lane-per-row kernel), with row counts that leave a partial step.
-@pytest.mark.parametrize("cols", [256, 1024, 4096, 4352, 5120, 8192, 12288, 12544])
+# Row lengths of every kernel form: 1, 2, 4, 8, 16 super-blocks (lanes hold
+# x), other lengths up to 128 super-blocks (K split over the waves of a block:
+# 3, 9, 17, 20, 32, 48, 49 and 128, i.e. 1 to 16 waves) and the first past
+# them (129: the lane-per-row kernel), with row counts that leave a partial
+# step.
+@pytest.mark.parametrize("cols", [256, 768, 1024, 2304, 4096, 4352, 5120, 8192, 12288, 12544, 32768, 33024])
 @pytest.mark.parametrize("rows", [1, 3, 130])
 def test_matvec_q4_k_every_row_length(rows, cols):
     y, ref, _, _ = _matvec_case("q4_k", rows, cols, 11)
