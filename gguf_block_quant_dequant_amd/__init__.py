@@ -59,6 +59,7 @@ _SIGS = {
     "gguf_qmatmul_f32_q8_0_multi": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _I64, _I64, _P]),
     "gguf_qmatmul_f32_q4_k_multi": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _I64, _I64, _P]),
     "gguf_qk_probe_read": (ctypes.c_int, [_P, _I64, _P, _P]),
+    "gguf_qk_stream_release": (ctypes.c_int, [_P]),
     "gguf_qk_timeline_setup": (ctypes.c_int, [ctypes.c_uint64]),
     "gguf_qk_timeline_fetch": (ctypes.c_int, [_P, _I64]),
     "gguf_qmatvec_batch": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
@@ -372,6 +373,14 @@ def gguf_qk_probe_read(buf, sink=None, stream=None):
     _check(lib().gguf_qk_probe_read(_dev(buf, "buf"), nbytes, _dev(sink, "sink", torch.int32),
                                     _stream(stream)), "gguf_qk_probe_read")
     return sink
+
+
+STREAM_SLOTS = 8   # GGUF_QK_STREAM_SLOTS: scratch slots per device
+
+
+def gguf_qk_stream_release(stream=None):
+    """Give back the scratch slot `stream` holds (synchronize the stream first)."""
+    _check(lib().gguf_qk_stream_release(_stream(stream)), "gguf_qk_stream_release")
 
 
 TIMELINE_SLOTS, TIMELINE_WAVES, TIMELINE_REC_BYTES = 4096, 2048, 32

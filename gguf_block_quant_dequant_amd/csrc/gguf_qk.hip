@@ -10,6 +10,7 @@
 #include <initializer_list>
 #include <mutex>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "../../include/gguf_file.h"
@@ -26,10 +27,13 @@
 
 namespace gqk {
 
-// Per-device scratch for split-K partial sums and row-group counters. It is a
-// static device array (each GPU the library runs on holds its own copy for the
-// life of the process); nothing is allocated at call time. Counters are zero
-// at load and every kernel that uses one returns it to zero.
+// Scratch for split-K partial sums and row-group counters, in slots: each
+// stream that runs kernels needing scratch holds one slot of the device for
+// the life of the process (or until gguf_qk_stream_release), so calls on
+// different streams may overlap in time. The slots are a static device array
+// (each GPU the library runs on holds its own copy for the life of the
+// process); nothing is allocated at call time. Counters are zero at load and
+// every kernel that uses one returns it to zero.
 constexpr int64_t kScratchPartials = int64_t(2) << 20;   // floats (8 MiB)
 constexpr int64_t kScratchCounters = int64_t(1) << 14;   // row-group counters
 constexpr int kMaxSplits = 16;                            // K ranges per row group
@@ -47,19 +51,25 @@ struct ScratchArea {
   int gemm_counters[kGemmMaxTiles * kGemmCounterStride];
   int pair_counters[kPairCounters * kCounterStride];
 };
-static __device__ __attribute__((aligned(256))) ScratchArea g_scratch;
+static_assert(GGUF_QK_STREAM_SLOTS >= 1, "at least one scratch slot");
+static __device__ __attribute__((aligned(256))) ScratchArea g_scratch[GGUF_QK_STREAM_SLOTS];
 
 constexpr int kMaxDevices = 64;
 
 struct DeviceState {
   std::atomic<int> checked{0};   // 0 unknown, 1 gfx950, -1 unsupported
-  ScratchArea* scratch = nullptr;
+  ScratchArea* scratch = nullptr;   // this device's slot array
   std::mutex mu;
+  // slot i is held by (stream[i], thread[i]) when held[i]; thread is only
+  // part of the key for the per-thread default stream
+  bool held[GGUF_QK_STREAM_SLOTS] = {};
+  hipStream_t stream[GGUF_QK_STREAM_SLOTS] = {};
+  std::thread::id thread[GGUF_QK_STREAM_SLOTS];
 };
 static DeviceState g_dev[kMaxDevices];
 
-// Returns GGUF_QK_OK and the scratch of the current device, or an error.
-static int current_device(ScratchArea** scratch) {
+// Returns GGUF_QK_OK and the current device's index, or an error.
+static int current_device(int* dev_out = nullptr) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
     (void)hipGetLastError();
@@ -83,7 +93,37 @@ static int current_device(ScratchArea** scratch) {
     }
   }
   if (c != 1) return GGUF_QK_ERR_DEVICE;
-  if (scratch) *scratch = st.scratch;
+  if (dev_out) *dev_out = dev;
+  return GGUF_QK_OK;
+}
+
+static bool same_holder(const DeviceState& st, int i, hipStream_t stream) {
+  return st.held[i] && st.stream[i] == stream &&
+         (stream != hipStreamPerThread || st.thread[i] == std::this_thread::get_id());
+}
+
+// The scratch slot of `stream` on the current device: the slot the stream
+// already holds, else a free one (taken for it). GGUF_QK_ERR_LIMIT when every
+// slot is held by another stream.
+static int stream_scratch(hipStream_t stream, ScratchArea** out) {
+  int dev = -1;
+  const int st0 = current_device(&dev);
+  if (st0) return st0;
+  DeviceState& st = g_dev[dev];
+  std::lock_guard<std::mutex> lk(st.mu);
+  int free_slot = -1;
+  for (int i = 0; i < GGUF_QK_STREAM_SLOTS; ++i) {
+    if (same_holder(st, i, stream)) {
+      *out = st.scratch + i;
+      return GGUF_QK_OK;
+    }
+    if (!st.held[i] && free_slot < 0) free_slot = i;
+  }
+  if (free_slot < 0) return GGUF_QK_ERR_LIMIT;
+  st.held[free_slot] = true;
+  st.stream[free_slot] = stream;
+  st.thread[free_slot] = std::this_thread::get_id();
+  *out = st.scratch + free_slot;
   return GGUF_QK_OK;
 }
 
@@ -179,7 +219,7 @@ static int dequant_common(int type, const void* W, void* out, int64_t out_elem_b
   const int64_t ob = rows * cols * out_elem_bytes;
   if (overlap(W, wb, out, ob)) return GGUF_QK_ERR_ALIAS;
   if (rows == 0) return GGUF_QK_OK;
-  st = current_device(nullptr);
+  st = current_device();
   if (st) return st;
   const int64_t quads = rows * cols / 4;
   if (grid_1d(quads, 256) <= 0 || quads / 256 >= INT32_MAX) return GGUF_QK_ERR_LIMIT;
@@ -278,34 +318,50 @@ static int64_t plan_group(int type, const gguf_qk_gemv* const* v, const GemvEpil
 static int launch_other(int type, const void* W, const float* x, float* y, int64_t rows,
                         int64_t cols, hipStream_t stream);
 
-// Launches one planned group.
-static int launch_group(int type, const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n,
-                        const ScratchArea* scratch, hipStream_t stream) {
-  if (lks_fits(v, e, n, type)) return launch_lks(v, n, stream, type);
-  if (type == GGUF_QK_TYPE_Q4_K && tuning().q4k_lk && lk_fits(v, e, n)) return launch_lk(v, e, n, stream, GGUF_QK_TYPE_Q4_K);
+// Kernel family of one group: the lanes-along-K launches (no scratch) or the
+// fallback GEMV kernels (split-K partials and counters in scratch).
+enum class GroupKind { kLks, kLk, kOther, kFallback };
+
+static GroupKind group_kind(int type, const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n) {
+  if (lks_fits(v, e, n, type)) return GroupKind::kLks;
+  if (type == GGUF_QK_TYPE_Q4_K && tuning().q4k_lk && lk_fits(v, e, n)) return GroupKind::kLk;
   if (type == GGUF_QK_TYPE_Q4_0 || type == GGUF_QK_TYPE_Q6_K) {
     // rows of 256 .. 12288 weights in multiples of 256 (no epilogues on
     // these types): the lanes-along-K kernels; else the lane-quad kernel, one
     // launch each
     const bool on = type == GGUF_QK_TYPE_Q4_0 ? tuning().q4_0_lk : tuning().q6_k_lk;
-    if (on && lk_fits(v, nullptr, n)) return launch_lk(v, nullptr, n, stream, type);
-    for (int i = 0; i < n; ++i) {
-      const int st = launch_other(type, v[i]->W, v[i]->x, v[i]->y, v[i]->rows, v[i]->cols, stream);
-      if (st) return st;
-    }
-    return GGUF_QK_OK;
+    return on && lk_fits(v, nullptr, n) ? GroupKind::kLk : GroupKind::kOther;
   }
   if (type == GGUF_QK_TYPE_Q8_0 && tuning().q8_0_lk && v[0]->cols <= 4096 && lk_fits(v, nullptr, n)) {
     // Q8_0 rows of 256 .. 4096 weights (multiples of 256) without epilogues:
-    // the lanes-along-K kernels; else the lane-per-row kernel below
+    // the lanes-along-K kernels; else the lane-per-row kernel
     bool ep = false;
     for (int i = 0; i < n; ++i) ep = ep || (e && e[i] && e[i]->flags != 0);
-    if (!ep) return launch_lk(v, nullptr, n, stream, type);
+    if (!ep) return GroupKind::kLk;
   }
+  return GroupKind::kFallback;
+}
+
+// Launches one planned group. scratch: the stream's slot; only the fallback
+// kernels use it (null where no group of the call needs it).
+static int launch_group(int type, const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n,
+                        ScratchArea* scratch, hipStream_t stream) {
+  switch (group_kind(type, v, e, n)) {
+    case GroupKind::kLks: return launch_lks(v, n, stream, type);
+    case GroupKind::kLk: return launch_lk(v, type == GGUF_QK_TYPE_Q4_K ? e : nullptr, n, stream, type);
+    case GroupKind::kOther:
+      for (int i = 0; i < n; ++i) {
+        const int st = launch_other(type, v[i]->W, v[i]->x, v[i]->y, v[i]->rows, v[i]->cols, stream);
+        if (st) return st;
+      }
+      return GGUF_QK_OK;
+    case GroupKind::kFallback: break;
+  }
+  if (!scratch) return GGUF_QK_ERR_LIMIT;
   GemvGroup grp;
   const int64_t tasks = plan_group(type, v, e, n, &grp);
-  float* partials = const_cast<float*>(scratch->partials);
-  int* counters = const_cast<int*>(scratch->counters);
+  float* partials = scratch->partials;
+  int* counters = scratch->counters;
   const int64_t blocks = type == GGUF_QK_TYPE_Q4_K ? tasks : (tasks + kGemvWaves - 1) / kGemvWaves;
   if (blocks > INT32_MAX) return GGUF_QK_ERR_LIMIT;
   bool ep = false;   // any epilogue in this launch: the kernel variant that has them
@@ -341,13 +397,14 @@ static int launch_rowwise_q8_0(const gguf_qk_gemv& g, hipStream_t stream) {
   return launch_status();
 }
 
-// Launches the GEMVs of one step: same-format GEMVs go together, kMaxGroup at
-// a time; each launch follows the previous one on the stream.
-static int launch_other(int type, const void* W, const float* x, float* y, int64_t rows,
-                        int64_t cols, hipStream_t stream);
-
-static int launch_step(const gguf_qk_gemv* list, const GemvEpilogue* eps, int n,
-                       const ScratchArea* scratch, hipStream_t stream) {
+// Groups the GEMVs of one step: same-format GEMVs go together, kMaxGroup at a
+// time, in a fixed order; fn(type, group, epilogues, count) is called per
+// group and single(g) for each Q8_0 GEMV whose rows are not a multiple of
+// 256 weights. Stops at the first nonzero status.
+extern "C++" {
+template <class GroupFn, class SingleFn>
+static int for_each_group(const gguf_qk_gemv* list, const GemvEpilogue* eps, int n, GroupFn&& fn,
+                          SingleFn&& single) {
   for (int type : {GGUF_QK_TYPE_Q4_K, GGUF_QK_TYPE_Q4_0, GGUF_QK_TYPE_Q6_K, GGUF_QK_TYPE_Q8_0}) {
     const gguf_qk_gemv* grp[kMaxGroup];
     const GemvEpilogue* ge[kMaxGroup];
@@ -356,31 +413,69 @@ static int launch_step(const gguf_qk_gemv* list, const GemvEpilogue* eps, int n,
       const gguf_qk_gemv& g = list[i];
       if (g.type != type || g.rows == 0) continue;
       if (type == GGUF_QK_TYPE_Q8_0 && g.cols % 256) {
-        const int st = launch_rowwise_q8_0(g, stream);
+        const int st = single(g);
         if (st) return st;
         continue;
       }
       // the two GEMVs of a gate/up pair go into one launch: a gate that would
       // take the last place of a group opens the next one
       if (k == kMaxGroup - 1 && eps && (eps[i].flags & kEpPair) && eps[i].role == 0) {
-        const int st = launch_group(type, grp, ge, k, scratch, stream);
+        const int st = fn(type, grp, ge, k);
         if (st) return st;
         k = 0;
       }
       ge[k] = eps ? &eps[i] : nullptr;
       grp[k++] = &g;
       if (k == kMaxGroup) {
-        const int st = launch_group(type, grp, ge, k, scratch, stream);
+        const int st = fn(type, grp, ge, k);
         if (st) return st;
         k = 0;
       }
     }
     if (k) {
-      const int st = launch_group(type, grp, ge, k, scratch, stream);
+      const int st = fn(type, grp, ge, k);
       if (st) return st;
     }
   }
   return GGUF_QK_OK;
+}
+
+}  // extern "C++"
+
+// Whether any group of the step runs a kernel that needs scratch.
+static bool step_needs_scratch(const gguf_qk_gemv* list, const GemvEpilogue* eps, int n) {
+  bool need = false;
+  for_each_group(
+      list, eps, n,
+      [&](int type, const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int k) {
+        need = need || group_kind(type, v, e, k) == GroupKind::kFallback;
+        return GGUF_QK_OK;
+      },
+      [](const gguf_qk_gemv&) { return GGUF_QK_OK; });
+  return need;
+}
+
+// Launches the GEMVs of one step, each launch after the previous one on the
+// stream. scratch: the stream's slot, or null when step_needs_scratch is false.
+static int launch_step(const gguf_qk_gemv* list, const GemvEpilogue* eps, int n, ScratchArea* scratch,
+                       hipStream_t stream) {
+  return for_each_group(
+      list, eps, n,
+      [&](int type, const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int k) {
+        return launch_group(type, v, e, k, scratch, stream);
+      },
+      [&](const gguf_qk_gemv& g) { return launch_rowwise_q8_0(g, stream); });
+}
+
+// Launches one step, taking the stream's scratch slot first when a kernel of
+// the step needs it (so a step that cannot get one enqueues nothing).
+static int run_step(const gguf_qk_gemv* list, const GemvEpilogue* eps, int n, ScratchArea* scratch,
+                    hipStream_t stream) {
+  if (!scratch && step_needs_scratch(list, eps, n)) {
+    const int st = stream_scratch(stream, &scratch);
+    if (st) return st;
+  }
+  return launch_step(list, eps, n, scratch, stream);
 }
 
 static int matvec_common(int type, const void* W, const float* x, float* y, int64_t rows,
@@ -389,11 +484,10 @@ static int matvec_common(int type, const void* W, const float* x, float* y, int6
   int st = check_gemv(type, W, x, y, rows, cols, &wb);
   if (st) return st;
   if (rows == 0) return GGUF_QK_OK;
-  ScratchArea* scratch = nullptr;
-  st = current_device(&scratch);
+  st = current_device();
   if (st) return st;
   const gguf_qk_gemv g{W, x, y, rows, cols, type, 0, {0}};
-  return launch_step(&g, nullptr, 1, scratch, stream);
+  return run_step(&g, nullptr, 1, nullptr, stream);
 }
 
 // Validates entry i's epilogue (the whole list is in view for pairs) and
@@ -528,9 +622,23 @@ static int batch_common(const gguf_qk_gemv* list, const gguf_qk_gemv_ep* ep, int
       if (ep[i].pair == 2) pair_rg[i] = pair_rg[i - 1];   // the gate's counters
     }
   }
-  ScratchArea* scratch = nullptr;
-  int st = current_device(&scratch);
+  int st = current_device();
   if (st) return st;
+  // the stream's scratch slot, taken before anything is enqueued when a pair
+  // or norm epilogue counts row groups or a step runs a fallback kernel
+  bool need = false;
+  for (int32_t i = 0; i < (int32_t)eps.size(); ++i) need = need || pair_rg[i] >= 0 || norm_rg[i] >= 0;
+  for (int32_t i = 0; i < n && !need;) {
+    int32_t j = i;
+    while (j < n && list[j].stage == list[i].stage) ++j;
+    need = step_needs_scratch(list + i, ep ? eps.data() + i : nullptr, j - i);
+    i = j;
+  }
+  ScratchArea* scratch = nullptr;
+  if (need) {
+    st = stream_scratch(stream, &scratch);
+    if (st) return st;
+  }
   for (int32_t i = 0; i < (int32_t)eps.size(); ++i) {
     if (pair_rg[i] >= 0) eps[i].pair_cnt = scratch->pair_counters + pair_rg[i] * kCounterStride;
     if (norm_rg[i] >= 0) eps[i].norm_cnt = scratch->pair_counters + norm_rg[i] * kCounterStride;
@@ -576,7 +684,7 @@ static int dequant_other(int type, const void* W, float* out, int64_t rows, int6
   if (rows > 0 && cols > INT64_MAX / 4 / rows) return GGUF_QK_ERR_SHAPE;
   if (overlap(W, wb, out, rows * cols * 4)) return GGUF_QK_ERR_ALIAS;
   if (rows == 0) return GGUF_QK_OK;
-  st = current_device(nullptr);
+  st = current_device();
   if (st) return st;
   const uint8_t* w = static_cast<const uint8_t*>(W);
   if (type == GGUF_QK_TYPE_Q4_0) {
@@ -602,14 +710,11 @@ static int matvec_other(int type, const void* W, const float* x, float* y, int64
   int st = check_gemv(type, W, x, y, rows, cols, &wb);
   if (st) return st;
   if (rows == 0) return GGUF_QK_OK;
-  st = current_device(nullptr);
+  st = current_device();
   if (st) return st;
   if (type == GGUF_QK_TYPE_Q4_0 || type == GGUF_QK_TYPE_Q6_K) {
-    ScratchArea* scratch = nullptr;
-    st = current_device(&scratch);
-    if (st) return st;
     const gguf_qk_gemv g{W, x, y, rows, cols, type, 0, {0}};
-    return launch_step(&g, nullptr, 1, scratch, stream);
+    return run_step(&g, nullptr, 1, nullptr, stream);
   }
   return launch_other(type, W, x, y, rows, cols, stream);
 }
@@ -701,7 +806,7 @@ static int matmul_q4_k_group(const void* const* W, uint16_t* const* Y, const int
   if (G.n == 0) return GGUF_QK_OK;
   if (gy > 65535) return GGUF_QK_ERR_LIMIT;
   ScratchArea* scratch = nullptr;
-  int st = current_device(&scratch);
+  int st = stream_scratch(stream, &scratch);
   if (st) return st;
   // Split K over whole super-blocks when there are too few tiles to fill the
   // device, as far as the scratch for the fp32 partial tiles allows.
@@ -808,7 +913,7 @@ static int small_batch_group(int type, const void* const* W, float* const* Y, co
   const int64_t gy = (n_tokens + kSbTokens - 1) / kSbTokens;
   if (gy > 65535) return GGUF_QK_ERR_LIMIT;
   ScratchArea* scratch = nullptr;
-  const int st = current_device(&scratch);
+  const int st = stream_scratch(stream, &scratch);
   if (st) return st;
   // Split K over whole steps when the tiles alone do not fill the device, as
   // far as the partial-tile scratch allows.
@@ -873,7 +978,7 @@ int gguf_rmsnorm_prep_f32(const float* v, const float* norm_w, float* vw, float*
       overlap(ss, groups * 4, vw, n * 4))
     return GGUF_QK_ERR_ALIAS;
   if (n == 0) return GGUF_QK_OK;
-  st = current_device(nullptr);
+  st = current_device();
   if (st) return st;
   if ((groups + 3) / 4 > INT32_MAX) return GGUF_QK_ERR_LIMIT;
   hipLaunchKernelGGL(rmsnorm_prep_kernel, dim3((unsigned)((groups + 3) / 4)), dim3(256), 0, stream,
@@ -888,7 +993,7 @@ int gguf_rmsnorm_f32(const float* v, const float* norm_w, float eps, float* out,
   if (!(eps >= 0.f) || eps > 3.0e38f) return GGUF_QK_ERR_SHAPE;
   if (overlap(out, n * 4, v, n * 4) || overlap(out, n * 4, norm_w, n * 4)) return GGUF_QK_ERR_ALIAS;
   if (n == 0) return GGUF_QK_OK;
-  st = current_device(nullptr);
+  st = current_device();
   if (st) return st;
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(1), dim3(1024), 0, stream, v, norm_w, eps, out, n);
   return launch_status();
@@ -903,7 +1008,7 @@ static int elementwise2(int kind, const float* a, const float* b, float* out, in
   if ((out != a && overlap(out, n * 4, a, n * 4)) || (out != b && overlap(out, n * 4, b, n * 4)))
     return GGUF_QK_ERR_ALIAS;
   if (n == 0) return GGUF_QK_OK;
-  st = current_device(nullptr);
+  st = current_device();
   if (st) return st;
   if ((n + 255) / 256 > INT32_MAX) return GGUF_QK_ERR_LIMIT;
   const dim3 grid((unsigned)((n + 255) / 256)), block(256);
@@ -937,7 +1042,7 @@ static TlRec* g_tl_recs_dev = nullptr;
 int gguf_qk_timeline_setup(uint64_t mult) {
 #if GQK_TIMELINE
   if (mult && !(mult & 1u)) return GGUF_QK_ERR_SHAPE;
-  int st = current_device(nullptr);
+  int st = current_device();
   if (st) return st;
   const size_t bytes = sizeof(TlRec) * (size_t)kTlSlots * kTlWaves;
   // the instrumented build's own record buffer (the default build allocates nothing)
@@ -976,13 +1081,24 @@ int gguf_qk_timeline_fetch(void* host_out, int64_t bytes) {
 #endif
 }
 
+int gguf_qk_stream_release(hipStream_t stream) {
+  int dev = -1;
+  const int st = current_device(&dev);
+  if (st) return st;
+  DeviceState& ds = g_dev[dev];
+  std::lock_guard<std::mutex> lk(ds.mu);
+  for (int i = 0; i < GGUF_QK_STREAM_SLOTS; ++i)
+    if (same_holder(ds, i, stream)) ds.held[i] = false;
+  return GGUF_QK_OK;
+}
+
 int gguf_qk_probe_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream) {
   if (!buf || !sink) return GGUF_QK_ERR_NULL;
   if (bytes < 0 || bytes % 16) return GGUF_QK_ERR_SHAPE;
   if (!aligned16(buf) || !aligned16(sink)) return GGUF_QK_ERR_ALIGN;
   if (overlap(sink, 4, buf, bytes)) return GGUF_QK_ERR_ALIAS;
   if (bytes == 0) return GGUF_QK_OK;
-  int st = current_device(nullptr);
+  int st = current_device();
   if (st) return st;
   int cus = 0, dev = 0;
   if (hipGetDevice(&dev) != hipSuccess ||

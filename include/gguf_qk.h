@@ -40,11 +40,21 @@
  *    returns GGUF_QK_OK without launching anything.
  *  - Outputs are fully overwritten (never accumulated into).
  *  - W needs 16-byte alignment; x, y, X, Y need 16-byte alignment.
- *  - The multiply entry points and the decode-stream entry points share one
- *    per-device scratch area inside the library (partial sums and counters,
- *    a static device array: nothing is allocated at call time). Calls that
- *    run concurrently on one device (different streams overlapping in time)
- *    race on it; issue them on one stream, or serialize them.
+ *  - Scratch: kernels that split K over blocks or count row groups (the
+ *    prefill and small-batch multiplies, the fused gate/up and norm
+ *    epilogues, the fallback GEMV kernels) keep partial sums and counters in
+ *    a scratch slot inside the library: a static device array of
+ *    GGUF_QK_STREAM_SLOTS slots per device, nothing allocated at call time.
+ *    The first such call on a stream takes a free slot for that stream and
+ *    the stream keeps it until gguf_qk_stream_release; later calls on the
+ *    stream reuse it. Calls on one stream run in stream order and calls on
+ *    different streams use different slots, so calls on any streams may
+ *    overlap in time. A call that needs a slot when every slot of the device
+ *    is held by other streams returns GGUF_QK_ERR_LIMIT and enqueues
+ *    nothing. The per-thread default stream (hipStreamPerThread) is one
+ *    stream per calling thread. A HIP graph captured from a stream keeps
+ *    that stream's slot in its kernels: do not replay it while other work
+ *    that uses the same slot may run.
  */
 #ifndef GGUF_QK_H
 #define GGUF_QK_H
@@ -59,6 +69,9 @@ extern "C" {
 #endif
 
 #define GGUF_QK_ABI_VERSION 1
+
+/* Scratch slots per device (streams that may hold scratch at one time). */
+#define GGUF_QK_STREAM_SLOTS 8
 
 /* Status codes. */
 #define GGUF_QK_OK 0
@@ -280,6 +293,13 @@ int gguf_qmatmul_f32_q4_k_multi(const void* const* W, float* const* Y, const int
                                 const float* X, int64_t n_tokens, int64_t cols, hipStream_t stream);
 
 /* --- measurement ---------------------------------------------------------- */
+
+/* Releases the scratch slot held by `stream` on the current device (for
+ * hipStreamPerThread: the calling thread's), so that another stream can take
+ * it. The caller guarantees that no work of this library enqueued on the
+ * stream is still pending (synchronize the stream first). Releasing a stream
+ * that holds no slot does nothing. Returns GGUF_QK_OK, or GGUF_QK_ERR_DEVICE. */
+int gguf_qk_stream_release(hipStream_t stream);
 
 /* Streaming-read probe: reads `bytes` (a multiple of 16) from device buffer
  * `buf` once with 16-byte vector loads spread over every compute unit, and

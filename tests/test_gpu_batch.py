@@ -81,6 +81,7 @@ def test_batch_full_decode_pass_sampled_rows():
         torch.cuda.synchronize()
         for (y, _, _), a in zip(checks, first):
             assert np.array_equal(host(y).view(np.uint32), a.view(np.uint32))
+    g.gguf_qk_stream_release(s)
 
 
 def test_batch_chained_layers_read_previous_outputs():

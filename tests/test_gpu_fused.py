@@ -256,3 +256,4 @@ def test_fused_layers_stage_by_stage():
         torch.cuda.synchronize()
         for k, v in T[1].items():
             assert np.array_equal(host(v).view(np.uint32), first[k].view(np.uint32)), k
+    g.gguf_qk_stream_release(s)

@@ -477,6 +477,7 @@ def test_batch_in_hip_graph_replays_match_eager():
         torch.cuda.synchronize()
         for y, e in zip(ys, eager):
             assert np.array_equal(host(y).view(np.uint32), e.view(np.uint32))
+    g.gguf_qk_stream_release(s)
 
 
 # (Each token's output over a matrix is one vector of the floored metric; a
