@@ -201,14 +201,16 @@ __device__ __forceinline__ void sb_q80_step(const uint8_t* ws, const uint8_t* xh
 // per token row, at k0 of each row).
 // (Plain vector types, not HIP's uint4 struct: a struct copy is a memcpy that
 // would keep the staging array in private memory.)
+// Only the wave's first nvx token rows (the valid tokens) are loaded.
 template <int N>
 __device__ __forceinline__ void sb_load(i32x4 (&wreg)[N], float4 (&xr)[8], const uint8_t* wb,
                                         const uint32_t (&woff)[N], const float* const (&xrow)[8],
-                                        int64_t k0, int xlane) {
+                                        int64_t k0, int xlane, int nvx) {
 #pragma unroll
   for (int i = 0; i < N; ++i) wreg[i] = *reinterpret_cast<const i32x4*>(wb + woff[i]);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) xr[i] = *reinterpret_cast<const float4*>(xrow[i] + k0 + xlane);
+  for (int i = 0; i < 8; ++i)
+    if (i < nvx) xr[i] = *reinterpret_cast<const float4*>(xrow[i] + k0 + xlane);
 }
 
 // Partial tile layout in scratch: [wave][e][lane] floats.
@@ -281,8 +283,10 @@ __global__ __launch_bounds__(256, 2) void gemv_small_batch_kernel(
     woff[i] = (uint32_t)(rr * row_bytes + 16 * col);
   }
   // X staging: wave w, i = 0..7 stages token w + 4 i, lane l its values
-  // k = 4 l .. 4 l + 3 of the step (one 1 KiB row per wave load). Tokens past
-  // the end are clamped (read, results never stored).
+  // k = 4 l .. 4 l + 3 of the step (one 1 KiB row per wave load). Only the
+  // valid tokens (i < nvx) are loaded and staged: the LDS rows of tokens past
+  // the end hold stale values, which reach only outputs that are never stored
+  // (each output element belongs to one token).
   // (row bases are wave-uniform: scalar registers; the lane offset is common)
   const float* xrow[8];
 #pragma unroll
@@ -292,6 +296,10 @@ __global__ __launch_bounds__(256, 2) void gemv_small_batch_kernel(
     xrow[i] = X + (int64_t)n * K;
   }
   const int xlane = 4 * lane;
+  int nvx = (n_tokens - n0 - wave + 3) / 4;   // valid token rows of this wave
+  nvx = nvx < 0 ? 0 : nvx > 8 ? 8 : nvx;
+  // token groups of 8 holding a valid token: partial tiles carry only these
+  const int ng = (n_tokens - n0 < kSbTokens ? n_tokens - n0 + 7 : kSbTokens) / 8;
 
   i32x4 wreg[F::kPiecesPerThread];
   float4 xr[8];
@@ -299,7 +307,7 @@ __global__ __launch_bounds__(256, 2) void gemv_small_batch_kernel(
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 
-  sb_load(wreg, xr, Wb + (int64_t)st_begin * F::kStepBytes, woff, xrow, (int64_t)st_begin * kSbK, xlane);
+  sb_load(wreg, xr, Wb + (int64_t)st_begin * F::kStepBytes, woff, xrow, (int64_t)st_begin * kSbK, xlane, nvx);
   for (int st = st_begin; st < st_end; ++st) {
     __syncthreads();   // the previous step's LDS reads are done
 #pragma unroll
@@ -310,6 +318,7 @@ __global__ __launch_bounds__(256, 2) void gemv_small_batch_kernel(
           wreg[F::kPiecesPerThread - 1];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      if (i >= nvx) break;
       const int t = wave + 4 * i;
       const float4 v = xr[i];
       const uint32_t h01 = pack_bf16x2(v.x, v.y), h23 = pack_bf16x2(v.z, v.w);
@@ -336,7 +345,8 @@ __global__ __launch_bounds__(256, 2) void gemv_small_batch_kernel(
     }
     __syncthreads();
     if (st + 1 < st_end)
-      sb_load(wreg, xr, Wb + (int64_t)(st + 1) * F::kStepBytes, woff, xrow, (int64_t)(st + 1) * kSbK, xlane);
+      sb_load(wreg, xr, Wb + (int64_t)(st + 1) * F::kStepBytes, woff, xrow, (int64_t)(st + 1) * kSbK, xlane,
+              nvx);
     if (Q4K)
       sb_q4k_step(ws, xh, xl, wave, lane, acc);
     else
@@ -350,10 +360,12 @@ __global__ __launch_bounds__(256, 2) void gemv_small_batch_kernel(
   const int64_t tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
   const int64_t ntiles = (int64_t)gridDim.x * gridDim.y;
   float* mine = partials + ((int64_t)split * ntiles + tile) * kSbTileFloats;
+  // element e holds token 8 (e / 4) + ...: only groups with a valid token
 #pragma unroll
   for (int e = 0; e < 16; ++e)
-    __hip_atomic_store(sb_partial_slot(mine, wave, e, lane), acc[e], __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    if ((e >> 2) < ng)
+      __hip_atomic_store(sb_partial_slot(mine, wave, e, lane), acc[e], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   // every wave's partial stores have completed before thread 0 signals
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   GQK_WAIT_VMCNT(0);
@@ -379,8 +391,9 @@ __global__ __launch_bounds__(256, 2) void gemv_small_batch_kernel(
       float* p = partials + ((int64_t)s * ntiles + tile) * kSbTileFloats;
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        v[i][e] = __hip_atomic_load(sb_partial_slot(p, wave, e, lane), __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
+        v[i][e] = (e >> 2) < ng ? __hip_atomic_load(sb_partial_slot(p, wave, e, lane), __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT)
+                                : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
