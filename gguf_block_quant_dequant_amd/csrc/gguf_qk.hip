@@ -21,6 +21,7 @@
 #include "gemv.hpp"
 #include "gemv_other.hpp"
 #include "gemv_small_batch.hpp"
+#include "gemv_sbw.hpp"
 #include "layer_ops.hpp"
 #include "probe.hpp"
 #include "timeline.hpp"
@@ -859,6 +860,81 @@ int gguf_qmatmul_q4_k_multi(const void* const* W, uint16_t* const* Y, const int6
 // 256). Shares the prefill GEMM's partial-tile scratch and tile counters.
 static_assert(kSbCounterStride == kGemmCounterStride, "shared tile counters");
 
+extern "C++" {
+// Q4_K small batch on the matrix-core kernel of gemv_sbw.hpp: up to 16
+// tokens per block (grid y past 16), one wave per super-block of a K range
+// (K split over blocks so that a range has at most kSbwMaxWaves
+// super-blocks), the split and the row tiles per block chosen below.
+static int launch_sbw(const SbGroup& G, const float* X, int64_t n_tokens, int64_t nsb, hipStream_t stream) {
+  int64_t tiles_of[kSbMaxGroup], tiles = 0;
+  for (int m = 0; m < G.n; ++m) {
+    if (G.rows[m] > INT32_MAX) return GGUF_QK_ERR_LIMIT;
+    tiles_of[m] = (G.rows[m] + 15) / 16;
+    tiles += tiles_of[m];
+  }
+  const int64_t gy = (n_tokens + kSbwMaxTokens - 1) / kSbwMaxTokens;
+  if (gy > 65535) return GGUF_QK_ERR_LIMIT;
+  // K ranges: as few as the waves of a block allow (a split costs a round
+  // trip of partial tiles through memory that is coherent across the XCDs,
+  // several microseconds); row tiles per block rt by a cost model of the
+  // launch's time: rounds of blocks (a compute unit holds 8 / nw blocks of nw
+  // waves) times a block's bytes per wave (rt tiles of 2304 weight bytes, the
+  // super-block's activations at 1 KiB per token), scaled up when fewer than
+  // 256 blocks or 1024 waves leave compute units or load slots idle; ties to
+  // fewer tiles
+  const int64_t s_min = (nsb + kSbwMaxWaves - 1) / kSbwMaxWaves;
+  const int64_t ntok = n_tokens < kSbwMaxTokens ? n_tokens : kSbwMaxTokens;
+  int64_t S = s_min, rt = 1;
+  {
+    const int64_t nw = (nsb + S - 1) / S, per_cu = kSbwMaxWaves / nw;
+    double best = -1.0;
+    for (int64_t r = 1; r <= kSbwMaxTiles; ++r) {
+      int64_t blocks = 0;
+      for (int m = 0; m < G.n; ++m) blocks += (tiles_of[m] + r - 1) / r;
+      blocks *= gy * S;
+      const int64_t rounds = (blocks + 256 * per_cu - 1) / (256 * per_cu);
+      double cost = (double)rounds * (double)(23 * r + 10 * ntok);
+      if (blocks < 256) cost *= 256.0 / (double)blocks;
+      if (blocks * nw < 1024) cost *= 1024.0 / (double)(blocks * nw);
+      if (best < 0 || cost < best) {
+        best = cost;
+        rt = r;
+      }
+    }
+  }
+  if (S > 65535) return GGUF_QK_ERR_LIMIT;
+  SbwGroup g{};
+  int64_t gx = 0;
+  for (int m = 0; m < G.n; ++m) {
+    g.W[m] = G.W[m];
+    g.Y[m] = G.Y[m];
+    g.rows[m] = (int)G.rows[m];
+    g.tile_begin[m] = (int)gx;
+    gx += (tiles_of[m] + rt - 1) / rt;
+  }
+  g.n = G.n;
+  g.rt = (int)rt;
+  if (gx > INT32_MAX) return GGUF_QK_ERR_LIMIT;
+  const int64_t ntiles = gx * gy, tile_floats = rt * 256;
+  if (S > 1 && (S * ntiles * tile_floats > kGemmScratchFloats || ntiles > kGemmMaxTiles)) return GGUF_QK_ERR_LIMIT;
+  const int nw = (int)((nsb + S - 1) / S);   // the longest range
+  ScratchArea* scratch = nullptr;
+  if (S > 1) {
+    const int st = stream_scratch(stream, &scratch);
+    if (st) return st;
+  }
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_sbw_kernel),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)sbw_lds_bytes(kSbwMaxTiles, kSbwMaxWaves, 16));
+  (void)attr;
+  // (the scratch is only touched when S > 1)
+  hipLaunchKernelGGL(gemv_sbw_kernel, dim3((unsigned)gx, (unsigned)gy, (unsigned)S), dim3(64 * nw),
+                     sbw_lds_bytes((int)rt, nw, ntok <= 8 ? 8 : 16), stream, g, X, (int)n_tokens, (int)nsb,
+                     scratch ? scratch->gemm_partials : nullptr, scratch ? scratch->gemm_counters : nullptr);
+  return launch_status();
+}
+}  // extern "C++"
+
 static int small_batch_group(int type, const void* const* W, float* const* Y, const int64_t* rows, int n,
                              const float* X, int64_t n_tokens, int64_t cols, hipStream_t stream) {
   if (!W || !Y || !rows) return GGUF_QK_ERR_NULL;
@@ -910,6 +986,7 @@ static int small_batch_group(int type, const void* const* W, float* const* Y, co
     if (gx > INT32_MAX) return GGUF_QK_ERR_LIMIT;
   }
   if (G.n == 0) return GGUF_QK_OK;
+  if (type == GGUF_QK_TYPE_Q4_K && n_tokens <= kSbwMaxTokens) return launch_sbw(G, X, n_tokens, steps, stream);
   const int64_t gy = (n_tokens + kSbTokens - 1) / kSbTokens;
   if (gy > 65535) return GGUF_QK_ERR_LIMIT;
   ScratchArea* scratch = nullptr;

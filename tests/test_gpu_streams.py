@@ -86,9 +86,11 @@ def test_scratch_slots_are_limited_and_released():
     """Streams take scratch slots up to GGUF_QK_STREAM_SLOTS per device; a call
     on one more stream fails with GGUF_QK_ERR_LIMIT and enqueues nothing, and
     succeeds once the other streams release their slots."""
+    # rows of 9 super-blocks: the small-batch multiply splits K over blocks
+    # (partial tiles in the stream's scratch slot)
     rng = synth.rng_for(42, 0, 0)
-    w = dev(synth.q4_k_weights(rng, 64, 256))
-    x = dev(rng.standard_normal((2, 256)).astype(np.float32))
+    w = dev(synth.q4_k_weights(rng, 64, 2304))
+    x = dev(rng.standard_normal((2, 2304)).astype(np.float32))
     torch.cuda.synchronize()
     held, refused = [], None
     for _ in range(g.STREAM_SLOTS + 1):
