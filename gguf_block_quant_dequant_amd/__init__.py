@@ -60,6 +60,7 @@ _SIGS = {
     "gguf_qmatmul_f32_q4_k_multi": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _I64, _I64, _P]),
     "gguf_qk_probe_read": (ctypes.c_int, [_P, _I64, _P, _P]),
     "gguf_qk_stream_release": (ctypes.c_int, [_P]),
+    "gguf_qk_last_launch": (ctypes.c_int, []),
     "gguf_qk_timeline_setup": (ctypes.c_int, [ctypes.c_uint64]),
     "gguf_qk_timeline_fetch": (ctypes.c_int, [_P, _I64]),
     "gguf_qmatvec_batch": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
@@ -107,15 +108,20 @@ class GemvEntry(ctypes.Structure):
                 ("stage", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
 
 
+def library_path() -> str:
+    """The build of libgguf_qk.so that lib() loads: GGUF_QK_LIBRARY=<path> (another
+    build of the same library: the sanitized host build, measurement of build
+    variants), else with GGUF_QK_TIMELINE=1 the instrumented build (stage
+    timelines), else the default build."""
+    path = TIMELINE_LIB_PATH if os.environ.get("GGUF_QK_TIMELINE") == "1" else LIB_PATH
+    return os.environ.get("GGUF_QK_LIBRARY", path)
+
+
 def lib() -> ctypes.CDLL:
     """The loaded libgguf_qk.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        # GGUF_QK_TIMELINE=1 loads the instrumented build (stage timelines);
-        # GGUF_QK_LIBRARY=<path> another build of the same library (measurement
-        # of build variants)
-        path = TIMELINE_LIB_PATH if os.environ.get("GGUF_QK_TIMELINE") == "1" else LIB_PATH
-        path = os.environ.get("GGUF_QK_LIBRARY", path)
+        path = library_path()
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: build it with "
                                "`python -m gguf_block_quant_dequant_amd.build`")
@@ -376,6 +382,14 @@ def gguf_qk_probe_read(buf, sink=None, stream=None):
 
 
 STREAM_SLOTS = 8   # GGUF_QK_STREAM_SLOTS: scratch slots per device
+# GGUF_QK_LAUNCH_*: kernel families reported by gguf_qk_last_launch
+(LAUNCH_NONE, LAUNCH_LK_SINGLE, LAUNCH_LK_TWO, LAUNCH_LK_THREE, LAUNCH_LK_GROUP, LAUNCH_LK_LONG, LAUNCH_LKS,
+ LAUNCH_SPLIT_K, LAUNCH_OTHER, LAUNCH_ROWWISE) = range(10)
+
+
+def gguf_qk_last_launch() -> int:
+    """Kernel family (LAUNCH_*) of this thread's most recent GEMV launch."""
+    return lib().gguf_qk_last_launch()
 
 
 def gguf_qk_stream_release(stream=None):
@@ -436,7 +450,21 @@ class GemvBatch:
     norm_out, ss_out, act; tensors for the vectors); the batch then runs through
     gguf_qmatvec_batch_ep."""
 
+    # floats each epilogue vector holds at least, for an entry of `rows` rows
+    # (the C ABI takes these pointers without lengths)
+    _EP_SIZES = {"residual": lambda r: r, "norm_w": lambda r: r, "norm_out": lambda r: r,
+                 "act": lambda r: r, "ss_out": lambda r: (r + 63) // 64}
+
     def __init__(self, entries, epilogues=None):
+        if epilogues is not None:
+            if len(epilogues) != len(entries):
+                raise ValueError("one epilogue (or None) per entry")
+            for (_, _, _, y, _), e in zip(entries, epilogues):
+                for key, need in self._EP_SIZES.items():
+                    t = (e or {}).get(key)
+                    if t is not None and t.numel() < need(y.numel()):
+                        raise ValueError(f"epilogue {key} holds {t.numel()} floats, the entry needs "
+                                         f"{need(y.numel())}")
         self._keep = []
         arr = (GemvEntry * len(entries))()
         for i, (type_id, W, x, y, stage) in enumerate(entries):
@@ -449,8 +477,6 @@ class GemvBatch:
         self.n = len(entries)
         self.ep = None
         if epilogues is not None:
-            if len(epilogues) != len(entries):
-                raise ValueError("one epilogue (or None) per entry")
             ep = (GemvEpEntry * len(entries))()
             for i, e in enumerate(epilogues):
                 if not e:

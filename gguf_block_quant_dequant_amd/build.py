@@ -6,7 +6,11 @@ Each source is compiled to an object file in parallel (one hipcc process per
 translation unit), then the objects are linked into the shared library.
 --timeline builds libgguf_qk_timeline.so instead: the same library with
 per-wave time stamps recorded by the decode GEMV kernels (GQK_TIMELINE), for
-stage timelines; it is never the default library.
+stage timelines; it is never the default library. --sanitize builds
+_build/libgguf_qk_asan.so: the host code under AddressSanitizer and
+UndefinedBehaviorSanitizer (device code unchanged), for the CPU tests of the
+file reader and of argument validation (load it with the sanitizer runtime
+preloaded, see tests/test_host_sanitizers.py).
 """
 
 from __future__ import annotations
@@ -23,6 +27,11 @@ LIB_NAME = "libgguf_qk.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 TIMELINE_LIB_PATH = os.path.join(PKG_DIR, "libgguf_qk_timeline.so")
 OBJ_DIR = os.path.join(PKG_DIR, "_build")
+ASAN_LIB_PATH = os.path.join(OBJ_DIR, "libgguf_qk_asan.so")
+# host-only sanitizers (each -fsanitize= applies to the host pass only)
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                  "-Xarch_host", "-g"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -70,13 +79,13 @@ def _run(cmd: list[str], verbose: bool) -> str:
     return msgs
 
 
-def build_library(verbose: bool = False, timeline: bool = False) -> str:
-    """Compile the sources and link them into LIB_PATH (or TIMELINE_LIB_PATH);
-    always recompiles."""
-    out = TIMELINE_LIB_PATH if timeline else LIB_PATH
-    tag = "tl" if timeline else "rel"
+def build_library(verbose: bool = False, timeline: bool = False, sanitize: bool = False) -> str:
+    """Compile the sources and link them into LIB_PATH (or TIMELINE_LIB_PATH,
+    ASAN_LIB_PATH); always recompiles."""
+    out = TIMELINE_LIB_PATH if timeline else ASAN_LIB_PATH if sanitize else LIB_PATH
+    tag = "tl" if timeline else "asan" if sanitize else "rel"
     os.makedirs(OBJ_DIR, exist_ok=True)
-    defs = ["-DGQK_TIMELINE=1"] if timeline else []
+    defs = (["-DGQK_TIMELINE=1"] if timeline else []) + (SANITIZE_FLAGS if sanitize else [])
     jobs = []
     for f, extra, name in UNITS:
         src = os.path.join(CSRC, f)
@@ -86,8 +95,10 @@ def build_library(verbose: bool = False, timeline: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         outs = list(ex.map(lambda j: _run(j[0], verbose), jobs))
     tmp = out + ".tmp"
-    outs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for _, o in jobs], "-o", tmp],
-                     verbose))
+    link_san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                "-shared-libasan"] if sanitize else []
+    outs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *link_san, *[o for _, o in jobs], "-o",
+                      tmp], verbose))
     msgs = "\n".join(m for m in outs if m)
     if verbose and msgs:
         print(msgs, flush=True)
@@ -96,4 +107,5 @@ def build_library(verbose: bool = False, timeline: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build_library(verbose="-v" in sys.argv, timeline="--timeline" in sys.argv))
+    print(build_library(verbose="-v" in sys.argv, timeline="--timeline" in sys.argv,
+                        sanitize="--sanitize" in sys.argv))

@@ -369,8 +369,11 @@ int gguf_file_upload_tensor(const gguf_file* f, int64_t i, void* dst, hipStream_
   const auto& t = f->tensors[i];
   if (t.nbytes < 0) return GGUF_QK_ERR_FORMAT;
   if (t.nbytes == 0) return GGUF_QK_OK;
+  // the source is the file mapping: wait for the copy on the stream, so that
+  // the file may be closed (and unmapped) as soon as this returns
   if (hipMemcpyAsync(dst, f->map + t.offset, (size_t)t.nbytes, hipMemcpyHostToDevice, stream) !=
-      hipSuccess) {
+          hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess) {
     (void)hipGetLastError();
     return GGUF_QK_ERR_LAUNCH;
   }

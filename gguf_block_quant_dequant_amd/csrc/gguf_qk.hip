@@ -69,6 +69,8 @@ struct DeviceState {
 };
 static DeviceState g_dev[kMaxDevices];
 
+thread_local int g_last_launch = GGUF_QK_LAUNCH_NONE;
+
 // Returns GGUF_QK_OK and the current device's index, or an error.
 static int current_device(int* dev_out = nullptr) {
   int dev = -1;
@@ -351,6 +353,7 @@ static int launch_group(int type, const gguf_qk_gemv* const* v, const GemvEpilog
     case GroupKind::kLks: return launch_lks(v, n, stream, type);
     case GroupKind::kLk: return launch_lk(v, type == GGUF_QK_TYPE_Q4_K ? e : nullptr, n, stream, type);
     case GroupKind::kOther:
+      g_last_launch = GGUF_QK_LAUNCH_OTHER;
       for (int i = 0; i < n; ++i) {
         const int st = launch_other(type, v[i]->W, v[i]->x, v[i]->y, v[i]->rows, v[i]->cols, stream);
         if (st) return st;
@@ -359,6 +362,7 @@ static int launch_group(int type, const gguf_qk_gemv* const* v, const GemvEpilog
     case GroupKind::kFallback: break;
   }
   if (!scratch) return GGUF_QK_ERR_LIMIT;
+  g_last_launch = GGUF_QK_LAUNCH_SPLIT_K;
   GemvGroup grp;
   const int64_t tasks = plan_group(type, v, e, n, &grp);
   float* partials = scratch->partials;
@@ -390,6 +394,7 @@ static int launch_group(int type, const gguf_qk_gemv* const* v, const GemvEpilog
 }
 
 static int launch_rowwise_q8_0(const gguf_qk_gemv& g, hipStream_t stream) {
+  g_last_launch = GGUF_QK_LAUNCH_ROWWISE;
   const int64_t blocks = (g.rows + 3) / 4;
   if (blocks > INT32_MAX || g.cols / kQ80BlockWeights > INT32_MAX) return GGUF_QK_ERR_LIMIT;
   hipLaunchKernelGGL(gemv_q8_0_rowwise_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
@@ -1157,6 +1162,8 @@ int gguf_qk_timeline_fetch(void* host_out, int64_t bytes) {
   return GGUF_QK_ERR_LIMIT;
 #endif
 }
+
+int gguf_qk_last_launch(void) { return g_last_launch; }
 
 int gguf_qk_stream_release(hipStream_t stream) {
   int dev = -1;

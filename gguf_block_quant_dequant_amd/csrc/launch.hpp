@@ -41,6 +41,10 @@ inline const Tuning& tuning() {
   return t;
 }
 
+// Kernel family of the calling thread's most recent GEMV launch (the values of
+// GGUF_QK_LAUNCH_* in include/gguf_qk.h), for gguf_qk_last_launch.
+extern thread_local int g_last_launch;
+
 inline int launch_status() {
   return hipGetLastError() == hipSuccess ? GGUF_QK_OK : GGUF_QK_ERR_LAUNCH;
 }

@@ -84,6 +84,7 @@ template <int kType, int kNsb, int kW, bool kEp>
 static void launch_lk_nsb(const LkGroup& grp, int depth, hipStream_t stream) {
   const dim3 grid((unsigned)grp.total_blocks), block(kW * 64);
   if (!kEp && grp.n == 1 && tuning().lk_single) {
+    g_last_launch = GGUF_QK_LAUNCH_LK_SINGLE;
     const LkDesc& d = grp.d[0];
     if (depth <= 2)
       hipLaunchKernelGGL((gemv_lk1_kernel<kType, kNsb, 2, kW>), grid, block, 0, stream, d.W, d.x, d.y,
@@ -94,14 +95,17 @@ static void launch_lk_nsb(const LkGroup& grp, int depth, hipStream_t stream) {
     return;
   }
   if (!kEp && lk_two(grp)) {
+    g_last_launch = GGUF_QK_LAUNCH_LK_TWO;
     launch_lk2<kType, kNsb, kW>(grp, depth, stream);
     return;
   }
   Lk3Args a3;
   if (!kEp && lk_three(grp, &a3)) {
+    g_last_launch = GGUF_QK_LAUNCH_LK_THREE;
     launch_lk3<kType, kNsb, kW>(grp, a3, depth, stream);
     return;
   }
+  g_last_launch = GGUF_QK_LAUNCH_LK_GROUP;
   if (depth <= 2)
     hipLaunchKernelGGL((gemv_lk_kernel<kType, kNsb, 2, kW, kEp>), grid, block, 0, stream, grp);
   else
@@ -110,6 +114,7 @@ static void launch_lk_nsb(const LkGroup& grp, int depth, hipStream_t stream) {
 
 template <int kType, bool kEp, int kQ, int kW>
 static void launch_lkx_t(const LkGroup& grp, size_t lds, hipStream_t stream) {
+  g_last_launch = GGUF_QK_LAUNCH_LK_LONG;
   const dim3 grid((unsigned)grp.total_blocks), block(kW * 64);
   // one GEMV without epilogue: its descriptor as (preloaded) scalar arguments
   const bool single = grp.n == 1 && !kEp && tuning().lk_single;
@@ -177,6 +182,7 @@ template void launch_lk_typed<GQK_LK_TYPE, (GQK_LK_EP != 0)>(const LkGroup&, con
 
 template <int kType, int kDepth, bool kSingle, int kRps>
 static void launch_lks_k(const LksGroup& grp, int nsb, int R, int nw, int blocks, hipStream_t stream) {
+  g_last_launch = GGUF_QK_LAUNCH_LKS;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&gemv_lks_kernel<kType, kDepth, kSingle, kRps>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lks_lds_bytes(kRps, lks_max_waves(kRps), kLksMaxRows));

@@ -136,9 +136,11 @@ int gguf_file_kv_array_string(const gguf_file* f, int64_t i, int64_t j, const ch
                               int64_t* len);
 
 /* Copies tensor i's bytes to device memory `dst` (at least nbytes, 16-byte
- * aligned) on `stream`; returns after the copy has been issued (the source is
- * pageable memory of the mapping, so the runtime may stage it). Fails with
- * GGUF_QK_ERR_FORMAT for a tensor of unknown size. */
+ * aligned) on `stream` and returns once the copy has completed: the call
+ * synchronizes `stream` (work queued on it before the call finishes too), so
+ * the mapping it reads from may be closed as soon as the call returns. Fails
+ * with GGUF_QK_ERR_FORMAT for a tensor of unknown size, GGUF_QK_ERR_LAUNCH if
+ * the copy or the synchronization fails. */
 int gguf_file_upload_tensor(const gguf_file* f, int64_t i, void* dst, hipStream_t stream);
 
 #ifdef __cplusplus

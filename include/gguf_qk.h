@@ -294,6 +294,21 @@ int gguf_qmatmul_f32_q4_k_multi(const void* const* W, float* const* Y, const int
 
 /* --- measurement ---------------------------------------------------------- */
 
+/* Kernel family of the calling thread's most recent GEMV launch through this
+ * library (gguf_qmatvec_*, gguf_qmatvec_batch*), for tests and diagnostics:
+ * which launch form a call actually took (0 before any). Host state only. */
+#define GGUF_QK_LAUNCH_NONE 0
+#define GGUF_QK_LAUNCH_LK_SINGLE 1   /* lanes along K, one GEMV, descriptor as scalar arguments */
+#define GGUF_QK_LAUNCH_LK_TWO 2      /* lanes along K, two GEMVs of one x, scalar arguments */
+#define GGUF_QK_LAUNCH_LK_THREE 3    /* lanes along K, three GEMVs of one x, packed scalar arguments */
+#define GGUF_QK_LAUNCH_LK_GROUP 4    /* lanes along K, up to four GEMVs from a descriptor array */
+#define GGUF_QK_LAUNCH_LK_LONG 5     /* lanes along K, rows of more than 16 super-blocks */
+#define GGUF_QK_LAUNCH_LKS 6         /* K split over the waves of a block (odd and long rows) */
+#define GGUF_QK_LAUNCH_SPLIT_K 7     /* split-K block or lane-per-row kernels (scratch) */
+#define GGUF_QK_LAUNCH_OTHER 8       /* Q4_0 / Q6_K lane-quad kernel */
+#define GGUF_QK_LAUNCH_ROWWISE 9     /* Q8_0 rows that are not whole 256-weight chunks */
+int gguf_qk_last_launch(void);
+
 /* Releases the scratch slot held by `stream` on the current device (for
  * hipStreamPerThread: the calling thread's), so that another stream can take
  * it. The caller guarantees that no work of this library enqueued on the

@@ -14,8 +14,17 @@ from gguf_block_quant_dequant_amd.build import LIB_PATH
 INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
 HEADERS = [os.path.join(INCLUDE, h) for h in sorted(os.listdir(INCLUDE)) if h.endswith(".h")]
 
-pytestmark = pytest.mark.skipif(not os.path.exists(LIB_PATH),
-                                reason="libgguf_qk.so not built (run the build step first)")
+def _gpu_visible():
+    import torch
+    return torch.cuda.device_count() > 0   # (counting does not initialize a device)
+
+
+# Well-formed calls here carry made-up addresses and rely on the missing
+# device to stop them: where a GPU is visible they would launch, so the module
+# runs only where none is.
+pytestmark = [pytest.mark.skipif(not os.path.exists(LIB_PATH),
+                                 reason="libgguf_qk.so not built (run the build step first)"),
+              pytest.mark.skipif(_gpu_visible(), reason="made-up device addresses: only where no GPU is visible")]
 
 
 def _declared_functions():
@@ -41,7 +50,7 @@ def test_header_declares_the_entry_points():
 
 
 def test_every_declared_symbol_is_exported():
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(g.library_path())
     missing = [n for n in _declared_functions() if not hasattr(L, n)]
     assert not missing, missing
 
@@ -319,3 +328,23 @@ def test_layer_ops_validation():
         assert f(A, B, A, 64, None) == g.ERR_DEVICE           # in place is allowed
         assert f(A, B, C, -1, None) == g.ERR_SHAPE
         assert f(A, B, C, 0, None) == g.OK
+
+
+def test_batch_binding_rejects_short_epilogue_vectors():
+    """The C ABI takes the epilogue vectors without lengths: the binding checks
+    each against the entry's rows (ss_out: one float per 64 rows) before
+    anything is built or launched."""
+    import torch
+    rows, cols = 130, 256
+    W = torch.zeros((rows, 144), dtype=torch.uint8)
+    x, y = torch.zeros(cols), torch.zeros(rows)
+    entries = [(g.TYPE_Q4_K, W, x, y, 0)]
+    for key, short in (("residual", rows - 1), ("norm_w", rows - 1), ("norm_out", 1), ("act", rows - 1),
+                       ("ss_out", 2)):
+        with pytest.raises(ValueError, match=key):
+            g.GemvBatch(entries, [{key: torch.zeros(short)}])
+    with pytest.raises(ValueError, match="one epilogue"):
+        g.GemvBatch(entries, [None, None])
+    # sizes that fit pass this check (host tensors are then refused as such)
+    with pytest.raises(ValueError, match="device tensor"):
+        g.GemvBatch(entries, [{"residual": torch.zeros(rows), "ss_out": torch.zeros(3)}])

@@ -160,6 +160,31 @@ def test_lookups(tmp_path):
             f.tensor("nope")
 
 
+def _gpu_visible():
+    import torch
+    return torch.cuda.device_count() > 0   # (counting does not initialize a device)
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="a made-up device address: only where no GPU is visible")
+def test_upload_validation_and_close_after_a_failed_upload(tmp_path):
+    """Without a device (or with bad arguments) upload fails before or at the
+    copy, enqueues nothing that reads the mapping, and the file closes
+    normally afterwards."""
+    import ctypes
+    _, blob, _ = tiny_file()
+    h = ctypes.c_void_p()
+    assert g.lib().gguf_file_open(write(tmp_path, blob).encode(), ctypes.byref(h)) == 0
+    L = g.lib()
+    assert L.gguf_file_upload_tensor(None, 0, 0x10000, None) == g.ERR_NULL
+    assert L.gguf_file_upload_tensor(h, 0, None, None) == g.ERR_NULL
+    assert L.gguf_file_upload_tensor(h, 1, 0x10000, None) == g.ERR_NOT_FOUND
+    assert L.gguf_file_upload_tensor(h, -1, 0x10000, None) == g.ERR_NOT_FOUND
+    assert L.gguf_file_upload_tensor(h, 0, 0x10008, None) == g.ERR_ALIGN
+    # a well-formed call on this host: the copy cannot run (no device)
+    assert L.gguf_file_upload_tensor(h, 0, 0x10000, None) == g.ERR_LAUNCH
+    L.gguf_file_close(h)
+
+
 def test_open_errors(tmp_path):
     assert open_status(str(tmp_path / "missing.gguf")) == g.ERR_IO
     assert open_status(str(tmp_path)) == g.ERR_IO

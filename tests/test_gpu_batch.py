@@ -162,6 +162,43 @@ def test_three_gemvs_of_one_x(rows, cols):
         for y, _ in refs:
             y.fill_(float("nan"))
         g.gguf_qmatvec_batch(b)
+        assert g.gguf_qk_last_launch() == _expected_three_form(entries)
         for y, ref in refs:
             e, ok = oracle.floored_rel_err(host(y), ref)
             assert ok and e <= TOL_F32, e
+
+
+def _expected_three_form(entries):
+    """The launch form three GEMVs of one x take: the packed scalar
+    descriptors when the second and third row counts fit 16 bits and every W
+    and y lies within a signed 32-bit count of 16-byte units of the first,
+    else the descriptor array."""
+    W = [e[1].data_ptr() for e in entries]
+    Y = [e[3].data_ptr() for e in entries]
+    rows = [e[3].numel() for e in entries]
+    fits = all(abs(p - ps[0]) // 16 < 2 ** 31 for ps in (W, Y) for p in ps)
+    return g.LAUNCH_LK_THREE if fits and rows[1] < 65536 and rows[2] < 65536 else g.LAUNCH_LK_GROUP
+
+
+@pytest.mark.parametrize("n,cols", [(2, 256), (2, 4096), (3, 512), (3, 2048), (4, 1024), (4, 4096)])
+def test_q8_0_gemvs_of_one_x(n, cols):
+    """One step of 2, 3 or 4 Q8_0 GEMVs of one x (rows of 256 .. 4096
+    weights take the lanes-along-K launches: two or three GEMVs as scalar
+    descriptors, four from the descriptor array), ragged row counts, every
+    row against the oracle; the launch form taken is checked."""
+    rng = np.random.default_rng(97 + n + cols)
+    x = synth.activations_f32(rng, cols)
+    X = dev(x)
+    entries, refs = [], []
+    for r in [2048, 511, 65, 1][:n]:
+        w = synth.q8_0_weights(rng, r, cols)
+        y = torch.full((r,), float("nan"), dtype=torch.float32, device=DEV)
+        entries.append((g.TYPE_Q8_0, dev(w), X, y, 0))
+        refs.append((y, oracle.matvec_f64(oracle.dequant_q8_0_f32(w, r, cols), x)))
+    say("Q8_0 GEMVs of one x:", n, cols)
+    g.gguf_qmatvec_batch(g.GemvBatch(entries))
+    expected = g.LAUNCH_LK_TWO if n == 2 else _expected_three_form(entries) if n == 3 else g.LAUNCH_LK_GROUP
+    assert g.gguf_qk_last_launch() == expected
+    for y, ref in refs:
+        e, ok = oracle.floored_rel_err(host(y), ref)
+        assert ok and e <= TOL_F32, e

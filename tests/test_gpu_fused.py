@@ -209,9 +209,12 @@ def _unfused(layers, h0, H, F, KV):
     return out
 
 
-def test_fused_layers_stage_by_stage():
-    H, F, KV = 2048, 5632, 512
-    layers, rng = _layers(2, H, F, KV)
+@pytest.mark.parametrize("n_layers,F", [(2, 5632), (1, 11008)])
+def test_fused_layers_stage_by_stage(n_layers, F):
+    """Two chained layers at a narrower FFN, and one at the workload's FFN
+    width (gate/up rows and down columns of 11008)."""
+    H, KV = 2048, 512
+    layers, rng = _layers(n_layers, H, F, KV)
     h0 = dev(synth.activations_f32(rng, H))
     batch, T = _fused_entries(layers, h0, H, F, KV)
     nw0, hw, ss = T["prep"]
@@ -237,10 +240,11 @@ def test_fused_layers_stage_by_stage():
         for k in ("q", "h1", "g", "u", "act", "h2"):
             check(host(U[li][k]), host(T[li][k]).astype(np.float64), f"fused vs unfused L{li} {k}")
     # repeat: bit-identical; graph replays: identical
-    first = {k: host(v).copy() for k, v in T[1].items()}
+    last = n_layers - 1
+    first = {k: host(v).copy() for k, v in T[last].items()}
     g.gguf_rmsnorm_prep_f32(h0, nw0, hw, ss)
     g.gguf_qmatvec_batch(batch)
-    for k, v in T[1].items():
+    for k, v in T[last].items():
         assert np.array_equal(host(v).view(np.uint32), first[k].view(np.uint32)), k
     s = torch.cuda.Stream()
     torch.cuda.synchronize()
@@ -249,11 +253,11 @@ def test_fused_layers_stage_by_stage():
         g.gguf_rmsnorm_prep_f32(h0, nw0, hw, ss, stream=s)
         g.gguf_qmatvec_batch(batch, s)
     for _ in range(2):
-        for v in T[1].values():
+        for v in T[last].values():
             v.fill_(float("nan"))
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        for k, v in T[1].items():
+        for k, v in T[last].items():
             assert np.array_equal(host(v).view(np.uint32), first[k].view(np.uint32)), k
     g.gguf_qk_stream_release(s)

@@ -51,3 +51,21 @@ def test_file_to_products(tmp_path):
         ref = oracle.matmul_f32_x_f64(X, oracle.dequant_q8_0_f32(q8, 300, 512))
         e, ok = oracle.floored_rel_err(Y.cpu().numpy(), ref)
         assert ok and e <= TOL_F32, e
+
+
+def test_close_right_after_upload_keeps_the_bytes(tmp_path):
+    """upload returns once its copy has completed, so closing the file (which
+    unmaps it) right after, with no synchronization of our own, cannot cut a
+    copy short: a 64 MiB tensor arrives whole."""
+    rng = np.random.default_rng(78)
+    big = rng.integers(0, 256, size=64 << 20, dtype=np.uint8)
+    tensors = [("big.weight", [big.size // 4], g.TENSOR_F32, big.tobytes())]
+    blob, _, _ = gguf_bytes([("general.architecture", STRING, "test")], tensors)
+    path = tmp_path / "big.gguf"
+    path.write_bytes(blob)
+    del blob
+    print("upload then close", flush=True)
+    with g.GgufFile(path) as f:
+        W = f.upload("big.weight")
+    torch.cuda.synchronize()
+    assert np.array_equal(W.cpu().numpy(), big)
