@@ -889,11 +889,13 @@ static int launch_sbw(const SbGroup& G, const float* X, int64_t n_tokens, int64_
   // fewer tiles
   const int64_t s_min = (nsb + kSbwMaxWaves - 1) / kSbwMaxWaves;
   const int64_t ntok = n_tokens < kSbwMaxTokens ? n_tokens : kSbwMaxTokens;
+  const bool pair = ntok <= 8;   // the paired layout (staging and sums side by side in LDS)
   int64_t S = s_min, rt = 1;
   {
     const int64_t nw = (nsb + S - 1) / S, per_cu = kSbwMaxWaves / nw;
     double best = -1.0;
     for (int64_t r = 1; r <= kSbwMaxTiles; ++r) {
+      if (sbw_lds_bytes((int)r, (int)nw, pair ? 8 : 16, pair) > kSbwLdsLimit) break;
       int64_t blocks = 0;
       for (int m = 0; m < G.n; ++m) blocks += (tiles_of[m] + r - 1) / r;
       blocks *= gy * S;
@@ -908,18 +910,19 @@ static int launch_sbw(const SbGroup& G, const float* X, int64_t n_tokens, int64_
     }
   }
   if (S > 65535) return GGUF_QK_ERR_LIMIT;
-  SbwGroup g{};
-  int64_t gx = 0;
+  const uint8_t* Wm[kSbMaxGroup] = {nullptr, nullptr, nullptr, nullptr};
+  int rows_m[kSbMaxGroup] = {0, 0, 0, 0};
+  SbwRest rest{};
+  int64_t gx = 0;   // (the kernel finds each matrix's first block the same way)
   for (int m = 0; m < G.n; ++m) {
-    g.W[m] = G.W[m];
-    g.Y[m] = G.Y[m];
-    g.rows[m] = (int)G.rows[m];
-    g.tile_begin[m] = (int)gx;
+    Wm[m] = static_cast<const uint8_t*>(G.W[m]);
+    rest.Y[m] = G.Y[m];
+    rows_m[m] = (int)G.rows[m];
     gx += (tiles_of[m] + rt - 1) / rt;
+    if (gx > INT32_MAX) return GGUF_QK_ERR_LIMIT;
   }
-  g.n = G.n;
-  g.rt = (int)rt;
-  if (gx > INT32_MAX) return GGUF_QK_ERR_LIMIT;
+  rest.W3 = Wm[3];
+  rest.rows3 = rows_m[3];
   const int64_t ntiles = gx * gy, tile_floats = rt * 256;
   if (S > 1 && (S * ntiles * tile_floats > kGemmScratchFloats || ntiles > kGemmMaxTiles)) return GGUF_QK_ERR_LIMIT;
   const int nw = (int)((nsb + S - 1) / S);   // the longest range
@@ -928,14 +931,26 @@ static int launch_sbw(const SbGroup& G, const float* X, int64_t n_tokens, int64_
     const int st = stream_scratch(stream, &scratch);
     if (st) return st;
   }
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_sbw_kernel),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     (int)sbw_lds_bytes(kSbwMaxTiles, kSbwMaxWaves, 16));
-  (void)attr;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_sbw_kernel<false>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSbwLdsLimit);
+  static const hipError_t attr_pair = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_sbw_kernel<true>),
+                                                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                          (int)kSbwLdsLimit);
+  if (attr != hipSuccess || attr_pair != hipSuccess) return GGUF_QK_ERR_LAUNCH;
   // (the scratch is only touched when S > 1)
-  hipLaunchKernelGGL(gemv_sbw_kernel, dim3((unsigned)gx, (unsigned)gy, (unsigned)S), dim3(64 * nw),
-                     sbw_lds_bytes((int)rt, nw, ntok <= 8 ? 8 : 16), stream, g, X, (int)n_tokens, (int)nsb,
-                     scratch ? scratch->gemm_partials : nullptr, scratch ? scratch->gemm_counters : nullptr);
+  rest.partials = scratch ? scratch->gemm_partials : nullptr;
+  rest.counters = scratch ? scratch->gemm_counters : nullptr;
+  const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)S), block(64 * nw);
+  const size_t lds = sbw_lds_bytes((int)rt, nw, pair ? 8 : 16, pair);
+  static_assert(sbw_lds_bytes(kSbwMaxTiles, kSbwMaxWaves, 16, false) <= kSbwLdsLimit, "shared staging fits");
+  if (lds > kSbwLdsLimit) return GGUF_QK_ERR_LIMIT;
+  const uint32_t shape = sbw_shape(nw, (int)rt, G.n, (int)S);
+  if (pair)
+    hipLaunchKernelGGL(gemv_sbw_kernel<true>, grid, block, lds, stream, Wm[0], Wm[1], Wm[2], X, (int)nsb,
+                       (int)n_tokens, shape, rows_m[0], rows_m[1], rows_m[2], rest);
+  else
+    hipLaunchKernelGGL(gemv_sbw_kernel<false>, grid, block, lds, stream, Wm[0], Wm[1], Wm[2], X, (int)nsb,
+                       (int)n_tokens, shape, rows_m[0], rows_m[1], rows_m[2], rest);
   return launch_status();
 }
 }  // extern "C++"
