@@ -52,10 +52,20 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 BF16_DENSE_PEAK_TFLOPS = 2500.0
 DOMINANT_KERNEL = "gemv_lk_kernel"
-KERNEL_SOURCES = ["gguf_block_quant_dequant_amd/csrc/gemv_lk.hpp",
-                  "gguf_block_quant_dequant_amd/csrc/device_common.hpp"]
+_CSRC = "gguf_block_quant_dequant_amd/csrc/"
+# Counter summaries under profiles/ that bench.py reads HBM traffic from, and
+# the sources each was measured on: a summary counts only while their hash
+# matches (its "source_sha256:" line), else the traffic field is null.
+PROFILES = {
+    "decode": ("gemv_lk_kernel_decode_stream_traffic.md",
+               ["gemv_lk.hpp", "device_common.hpp", "lk.hip", "lk_typed.hip"]),
+    "other": ("other_types_lk_traffic.md",
+              ["gemv_lk.hpp", "device_common.hpp", "lk.hip", "lk_typed.hip"]),
+    "small_batch": ("small_batch_traffic.md",
+                    ["gemv_sbw.hpp", "gemv_small_batch.hpp", "device_common.hpp", "gguf_qk.hip"]),
+    "prefill": ("gemm_q4_k_db_kernel_prefill_mfma.md", ["gemm.hpp", "device_common.hpp", "gguf_qk.hip"]),
+}
 SMALL_BATCH_TOKENS = (8, 32, 64)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_lk_kernel_decode_stream_traffic.md")
 
 
 def log(*a):
@@ -96,26 +106,27 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_sha():
+def kernel_source_sha(sources):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
+    for p in sources:
+        with open(os.path.join(ROOT, _CSRC + p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, if it was taken on the current kernel sources; else None."""
+def recorded_traffic(profile, key):
+    """HBM bytes (`key` of the committed counter summary of `profile`), if the
+    summary was taken on the current sources; else None."""
+    name, sources = PROFILES[profile]
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(os.path.join(ROOT, "profiles", name)).read()
     except OSError:
         return None
     kv = dict(re.findall(r"^([a-z_0-9]+):\s*(\S+)\s*$", text, flags=re.M))
-    if kv.get("source_sha256") != kernel_source_sha():
+    if kv.get("source_sha256") != kernel_source_sha(sources):
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
 
@@ -238,7 +249,8 @@ def prefill_pass(torch, g, synth, entries, meta, stream, n_tokens=512, reps=3):
             "gemms": gemms, "launches": len(calls), "flop": flops, "ms_per_pass": round(ms, 4),
             "roofline": {"bound": "mfma", "kernel": "gemm_q4_k_db_kernel", "achieved": round(tflops, 1),
                          "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tflops / BF16_DENSE_PEAK_TFLOPS, 4), "traffic": None}}
+                         "frac": round(tflops / BF16_DENSE_PEAK_TFLOPS, 4),
+                         "traffic": recorded_traffic("prefill", "hbm_bytes_per_launch")}}
 
 
 def small_batch_pass(torch, g, synth, entries, stream, n_tokens, reps=5):
@@ -284,9 +296,14 @@ def small_batch_pass(torch, g, synth, entries, stream, n_tokens, reps=5):
             "weight_GBps": round(gbps, 1),
             "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
             "tokens_per_s": round(n_tokens * 1e3 / ms, 1),
-            "roofline": {"bound": "hbm", "kernel": "gemv_small_batch_kernel",
+            # (per pass: achieved = the pass's weight bytes / its time, traffic =
+            # the pass's HBM bytes)
+            "roofline": {"bound": "hbm",
+                         "kernel": "gemv_sbw_kernel" if n_tokens <= 16 else "gemv_small_batch_kernel",
+                         "basis": "pass",
                          "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}}
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                         "traffic": recorded_traffic("small_batch", f"hbm_bytes_per_pass_{n_tokens}")}}
 
 
 def fused_layer_pass(torch, g, synth, entries, stream, reps=10):
@@ -416,7 +433,8 @@ def other_types_pass(torch, g, synth, reps=5):
                                  "kernel": f"gemv_lk_kernel ({name.upper()})",
                                  "achieved": round(gbps, 1),
                                  "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}})
+                                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "basis": "pass",
+                                 "traffic": recorded_traffic("other", f"hbm_bytes_per_pass_{name}")}})
         del graph, batch, ents, keep, layer
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
@@ -833,7 +851,7 @@ def main():
     avg_launch_s = q4k_ms / 1e3 / q4k_launches
     bytes_per_launch = q4k_bytes / q4k_launches
     achieved = bytes_per_launch / avg_launch_s / 1e9
-    traffic = recorded_traffic()
+    traffic = recorded_traffic("decode", "hbm_bytes_per_launch")
     rec["roofline"] = {"bound": "hbm", "kernel": DOMINANT_KERNEL, "achieved": round(achieved, 1),
                        "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                        "frac": round(achieved / HBM_PEAK_GBPS, 4),
