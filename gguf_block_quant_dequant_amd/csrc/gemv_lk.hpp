@@ -906,10 +906,13 @@ constexpr size_t lks_lds_bytes(int rps, int nw, int R) {
 // kType: GGUF type 12 (Q4_K) or 2 (Q4_0); both store 144 bytes per 256
 // weights. kSingle: one GEMV whose pointers and rows come in the leading
 // scalar arguments (preloaded into SGPRs), else the block's GEMV from grp.
+// nw: the waves per block (blockDim.x / 64, passed so that it is preloaded
+// too: blockDim.x is a kernel argument in memory, and its fetch held the
+// first loads back by a round trip).
 template <int kType, int kDepth, bool kSingle, int kRps>
 __global__ __launch_bounds__(lks_max_waves(kRps) * 64) void gemv_lks_kernel(const uint8_t* W1, const float* x,
                                                                      float* y1, int rows1, int nsb, int R,
-                                                                     LksGroup grp) {
+                                                                     int nw, LksGroup grp) {
   static_assert(kType == 12 || kType == 2, "Q4_K or Q4_0 rows");
   static_assert(kRps == 1 || kRps == 2 || kRps == 4, "one, two or four rows per step");
   constexpr bool kQ40 = kType == 2;
@@ -921,7 +924,6 @@ __global__ __launch_bounds__(lks_max_waves(kRps) * 64) void gemv_lks_kernel(cons
   tl.stamp(0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nw = (int)(blockDim.x >> 6);
   const GQK_GLOBAL uint8_t* W;
   GQK_GLOBAL float* y;
   int rows, lb;

@@ -189,7 +189,7 @@ static void launch_lks_k(const LksGroup& grp, int nsb, int R, int nw, int blocks
   (void)attr;
   const LksDesc& d = grp.d[0];
   hipLaunchKernelGGL((gemv_lks_kernel<kType, kDepth, kSingle, kRps>), dim3((unsigned)blocks), dim3(64 * nw),
-                     lks_lds_bytes(kRps, nw, R), stream, d.W, grp.x, d.y, d.rows, nsb, R, grp);
+                     lks_lds_bytes(kRps, nw, R), stream, d.W, grp.x, d.y, d.rows, nsb, R, nw, grp);
 }
 
 template <int kType, int kRps>
