@@ -299,7 +299,7 @@ def small_batch_pass(torch, g, synth, entries, stream, n_tokens, reps=5):
             # (per pass: achieved = the pass's weight bytes / its time, traffic =
             # the pass's HBM bytes)
             "roofline": {"bound": "hbm",
-                         "kernel": "gemv_sbw_kernel" if n_tokens <= 16 else "gemv_small_batch_kernel",
+                         "kernel": "gemv_sbw_kernel" if n_tokens <= 32 else "gemv_small_batch_kernel",
                          "basis": "pass",
                          "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(gbps / HBM_PEAK_GBPS, 4),

@@ -725,9 +725,14 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
       L.qb = *reinterpret_cast<const GQK_GLOBAL lk_u32x4*>(base + (off + qoff + 16));
     }
   };
+  // At most two steps go out before x is staged, the rest right after: the
+  // block's x loads then queue behind at most two steps of every wave's
+  // weight loads (with a four-step ring x arrived 1.2 us later), and the
+  // loads keep their order, so the in-order waits stay exact.
+  constexpr int kEarly = kDepth < 2 ? kDepth : 2;
   Load ring[kDepth];
 #pragma unroll
-  for (int p = 0; p < kDepth; ++p) issue(st0 + p, ring[p]);
+  for (int p = 0; p < kEarly; ++p) issue(st0 + p, ring[p]);
   tl.stamp(1);
 
 #pragma unroll
@@ -737,6 +742,8 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
       *reinterpret_cast<lk_f32x4*>(&xl[lk_x_slot<kType>(i)]) = xg[j];
   }
   __syncthreads();
+#pragma unroll
+  for (int p = kEarly; p < kDepth; ++p) issue(st0 + p, ring[p]);
   tl.stamp(2);
   LkEp E;
   if constexpr (kEp) E = lk_ep(epl, ss_share);

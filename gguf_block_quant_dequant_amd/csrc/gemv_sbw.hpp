@@ -65,6 +65,7 @@ typedef uint32_t sbw_u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t sbw_u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSbwMaxTokens = 16;   // tokens per block (grid y covers more)
+constexpr int kSbwRouteTokens = 32; // token counts the small-batch calls send here
 constexpr int kSbwMaxWaves = 8;     // super-blocks of one K range at most
 constexpr int kSbwMaxTiles = 16;    // row tiles of 16 per block at most
 constexpr int kSbwDepth = 4;        // weight ring (row tiles in flight per wave)

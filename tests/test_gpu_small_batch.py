@@ -58,6 +58,8 @@ SHAPES = [
     ("q4_k", 511, 768, 33),
     ("q4_k", 257, 256, 64),
     ("q4_k", 2048, 11008, 16),
+    ("q4_k", 300, 2048, 20),     # two token chunks of the Q4_K kernel up to 32 tokens, the second ragged
+    ("q4_k", 520, 11008, 27),    # the same with K split over blocks
     ("q4_k", 11008, 2048, 5),
     ("q8_0", 128, 256, 1),
     ("q8_0", 257, 512, 5),
