@@ -404,16 +404,34 @@ struct LkEp {
 };
 
 // The lane's share of the input RMSN's partial sums (kEpScale; at most 256
-// of them): scale_ss[lane + 64 k], k = 0..3, added in k order.
-__device__ __forceinline__ float lk_ep_ss(const LkBlock& B, int lane) {
+// of them): scale_ss[lane + 64 k], k = 0..3, added in k order. The four loads
+// go out unconditionally before the block's other loads (indices past the
+// end re-read the last sum; without kEpScale they read the block's x), and
+// they are added only where the scale is formed: loads under a condition went
+// out one at a time, each waited for before the next, ahead of every
+// activation and weight load of the launch.
+struct LkSsLoads {
+  float v[4];
+};
+
+__device__ __forceinline__ LkSsLoads lk_ep_ss_issue(const LkBlock& B, int lane) {
+  const bool on = (B.ep_flags & kEpScale) && B.scale_n > 0;
+  const GQK_GLOBAL float* const p = on ? B.scale_ss : B.x;
+  const int last = on ? B.scale_n - 1 : 0;
+  LkSsLoads r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = lane + 64 * k;
+    r.v[k] = p[i < last ? i : last];
+  }
+  return r;
+}
+
+__device__ __forceinline__ float lk_ep_ss_sum(const LkBlock& B, int lane, const LkSsLoads& r) {
   float t = 0.f;
   if (B.ep_flags & kEpScale) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = lane + 64 * k;
-      const float v = i < B.scale_n ? B.scale_ss[i] : 0.f;
-      t += v;
-    }
+    for (int k = 0; k < 4; ++k) t += lane + 64 * k < B.scale_n ? r.v[k] : 0.f;
   }
   return t;
 }
@@ -670,11 +688,11 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
   const int rpm = paired ? kRps / 2 : kRps;
   const int rsub = (lane / kU) % rpm;
   const GQK_GLOBAL uint8_t* const Wl = (paired && lane >= 32) ? B.W2 : W;
-  float ss_share = 0.f;
+  LkSsLoads ssl;
   GemvEpilogue epl;
   if constexpr (kEp) {
     epl = grp->ep[B.g];
-    ss_share = lk_ep_ss(B, lane);
+    ssl = lk_ep_ss_issue(B, lane);
   }
 
   // x: every thread loads its float4s first ...
@@ -746,7 +764,7 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
   for (int p = kEarly; p < kDepth; ++p) issue(st0 + p, ring[p]);
   tl.stamp(2);
   LkEp E;
-  if constexpr (kEp) E = lk_ep(epl, ss_share);
+  if constexpr (kEp) E = lk_ep(epl, lk_ep_ss_sum(B, lane, ssl));
   if (n > 0) {
 
   float xv[64];
@@ -1130,11 +1148,11 @@ __global__ __launch_bounds__(kW * 64) void gemv_lkx_kernel(const uint8_t* W1, co
   const int nxf4 = K / 4;
   const uint32_t row_bytes = (uint32_t)nsb * (kQ6 ? (uint32_t)kQ6KBlockBytes : (uint32_t)kQ4KBlockBytes);
   float* const xsum = xl + K + K / 16;
-  float ss_share = 0.f;
+  LkSsLoads ssl;
   GemvEpilogue epl;
   if constexpr (kEp) {
     epl = grp.ep[B.g];
-    ss_share = lk_ep_ss(B, lane);
+    ssl = lk_ep_ss_issue(B, lane);
   }
 
   // x: the block's threads load it all first (at most 16 kQ / kW float4
@@ -1219,7 +1237,7 @@ __global__ __launch_bounds__(kW * 64) void gemv_lkx_kernel(const uint8_t* W1, co
   __syncthreads();
   tl.stamp(2);
   LkEp E;
-  if constexpr (kEp) E = lk_ep(epl, ss_share);
+  if constexpr (kEp) E = lk_ep(epl, lk_ep_ss_sum(B, lane, ssl));
   if (n > 0) {
   float xs0[kQ], xs1[kQ];
   float xq6[kQ][4];
