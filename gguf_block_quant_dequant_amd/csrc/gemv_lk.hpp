@@ -75,8 +75,8 @@ template <int kType, bool kEp>
 void launch_lk_typed(const LkGroup& grp, const LkPlan& p, hipStream_t stream);
 struct LksGroup;
 template <int kType>
-void launch_lks_typed(const LksGroup& grp, int nsb, int R, int nw, int rps, int depth, int blocks,
-                      hipStream_t stream);
+void launch_lks_typed(const LksGroup& grp, const GemvEpilogue* ep, int nsb, int R, int nw, int rps, int depth,
+                      int blocks, hipStream_t stream);
 
 // The block's share of a launch: its GEMV (pointers, rows, super-blocks per
 // row) and the wave's row steps [st0, st0 + n).
@@ -933,12 +933,15 @@ constexpr size_t lks_lds_bytes(int rps, int nw, int R) {
 // scalar arguments (preloaded into SGPRs), else the block's GEMV from grp.
 // nw: the waves per block (blockDim.x / 64, passed so that it is preloaded
 // too: blockDim.x is a kernel argument in memory, and its fetch held the
-// first loads back by a round trip).
-template <int kType, int kDepth, bool kSingle, int kRps>
+// first loads back by a round trip). kEp (one Q4_K GEMV): the residual add
+// and the next norm's preparation of ep as the rows are stored (the output
+// projection of a decode layer), read only after the last step.
+template <int kType, int kDepth, bool kSingle, int kRps, bool kEp>
 __global__ __launch_bounds__(lks_max_waves(kRps) * 64) void gemv_lks_kernel(const uint8_t* W1, const float* x,
                                                                      float* y1, int rows1, int nsb, int R,
-                                                                     int nw, LksGroup grp) {
+                                                                     int nw, LksGroup grp, GemvEpilogue ep) {
   static_assert(kType == 12 || kType == 2, "Q4_K or Q4_0 rows");
+  static_assert(!kEp || (kSingle && kType == 12), "epilogues on one Q4_K GEMV");
   static_assert(kRps == 1 || kRps == 2 || kRps == 4, "one, two or four rows per step");
   constexpr bool kQ40 = kType == 2;
   constexpr int kU = 64 / kRps;                 // lanes per row
@@ -1081,11 +1084,25 @@ __global__ __launch_bounds__(lks_max_waves(kRps) * 64) void gemv_lks_kernel(cons
 
   // the rows' slice sums, added in wave order
   __syncthreads();
-  if (wave == 0) {
-    for (int rr = lane; rr < nrows; rr += 64) {
-      float v = 0.f;
-      for (int w = 0; w < nw; ++w) v += part[rr * nw + w];
-      y[r0 + rr] = v;
+  if constexpr (kEp) {
+    // residual, norm output and the 64-row groups' sums of squares, as in the
+    // kernels above (no input scale on this path)
+    const LkEp E = lk_ep(ep, 0.f);
+    if (wave == 0) {
+      for (int rr = lane; rr < nrows; rr += 64) {
+        float v = 0.f;
+        for (int w = 0; w < nw; ++w) v += part[rr * nw + w];
+        lk_ep_row(E, v, r0 + rr, y);
+      }
+    }
+    lk_ep_groups(E, r0, r0 + nrows, rows, y, wave, lane);
+  } else {
+    if (wave == 0) {
+      for (int rr = lane; rr < nrows; rr += 64) {
+        float v = 0.f;
+        for (int w = 0; w < nw; ++w) v += part[rr * nw + w];
+        y[r0 + rr] = v;
+      }
     }
   }
   tl.stamp(5);

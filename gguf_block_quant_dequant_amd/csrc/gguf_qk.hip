@@ -350,7 +350,7 @@ static GroupKind group_kind(int type, const gguf_qk_gemv* const* v, const GemvEp
 static int launch_group(int type, const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n,
                         ScratchArea* scratch, hipStream_t stream) {
   switch (group_kind(type, v, e, n)) {
-    case GroupKind::kLks: return launch_lks(v, n, stream, type);
+    case GroupKind::kLks: return launch_lks(v, type == GGUF_QK_TYPE_Q4_K ? e : nullptr, n, stream, type);
     case GroupKind::kLk: return launch_lk(v, type == GGUF_QK_TYPE_Q4_K ? e : nullptr, n, stream, type);
     case GroupKind::kOther:
       g_last_launch = GGUF_QK_LAUNCH_OTHER;

@@ -57,6 +57,7 @@ int launch_lk(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n,
 // The split-K-in-block kernel (rows of other lengths, up to 128 super-blocks;
 // Q4_K and Q4_0, no epilogues).
 bool lks_fits(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n, int type);
-int launch_lks(const gguf_qk_gemv* const* v, int n, hipStream_t stream, int type);
+int launch_lks(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n, hipStream_t stream,
+               int type);
 
 }  // namespace gqk

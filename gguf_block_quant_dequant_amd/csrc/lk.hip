@@ -26,9 +26,10 @@ bool lk_fits(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n) 
   return true;
 }
 
-// Q4_K or Q4_0 GEMVs without epilogues whose rows the kernels above do not
-// take as they are (a number of super-blocks other than 1, 2, 4, 8, 16, up
-// to 128): the split-K-in-block kernel.
+// Q4_K or Q4_0 GEMVs whose rows the kernels above do not take as they are (a
+// number of super-blocks other than 1, 2, 4, 8, 16, up to 128): the
+// split-K-in-block kernel. Epilogues: one Q4_K GEMV with a residual add and
+// norm preparation (row-group counters assigned), nothing else.
 bool lks_fits(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n, int type) {
   if (type != GGUF_QK_TYPE_Q4_K && type != GGUF_QK_TYPE_Q4_0) return false;
   const int64_t c = v[0]->cols;
@@ -37,7 +38,11 @@ bool lks_fits(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n,
   if (nsb > kLksMaxNsb || nsb == 1 || nsb == 2 || nsb == 4 || nsb == 8 || nsb == 16) return false;
   for (int i = 0; i < n; ++i) {
     if (v[i]->cols != c || v[i]->rows > (int64_t(1) << 30)) return false;
-    if (e && e[i] && e[i]->flags) return false;
+    if (e && e[i] && e[i]->flags) {
+      const int f = e[i]->flags;
+      if (n != 1 || type != GGUF_QK_TYPE_Q4_K || (f & ~(kEpResidual | kEpNorm))) return false;
+      if ((f & kEpNorm) && !e[i]->norm_cnt) return false;
+    }
   }
   return true;
 }
@@ -66,7 +71,8 @@ static void lks_shape(int nsb, int R, int* rps_out, int* nw_out) {
 // One launch per run of GEMVs of one x (at most kLkMaxGroup): each block takes
 // R rows of one GEMV, R a multiple of 4 chosen so that the launch has about
 // one block per compute unit (at most kLksMaxRows).
-int launch_lks(const gguf_qk_gemv* const* v, int n, hipStream_t stream, int type) {
+int launch_lks(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n, hipStream_t stream,
+               int type) {
   const int nsb = (int)(v[0]->cols / 256);
   for (int i0 = 0; i0 < n;) {
     int i1 = i0 + 1;
@@ -91,10 +97,12 @@ int launch_lks(const gguf_qk_gemv* const* v, int n, hipStream_t stream, int type
     }
     if (blocks > INT32_MAX) return GGUF_QK_ERR_LIMIT;
     const int depth = R / rps <= 2 ? 2 : 4;
+    // an epilogue only on a run of one GEMV (lks_fits)
+    const GemvEpilogue* ep = (e && i1 - i0 == 1 && e[i0] && e[i0]->flags) ? e[i0] : nullptr;
     if (type == GGUF_QK_TYPE_Q4_0)
-      launch_lks_typed<GGUF_QK_TYPE_Q4_0>(grp, nsb, (int)R, nw, rps, depth, (int)blocks, stream);
+      launch_lks_typed<GGUF_QK_TYPE_Q4_0>(grp, nullptr, nsb, (int)R, nw, rps, depth, (int)blocks, stream);
     else
-      launch_lks_typed<GGUF_QK_TYPE_Q4_K>(grp, nsb, (int)R, nw, rps, depth, (int)blocks, stream);
+      launch_lks_typed<GGUF_QK_TYPE_Q4_K>(grp, ep, nsb, (int)R, nw, rps, depth, (int)blocks, stream);
     const int st = launch_status();
     if (st) return st;
     i0 = i1;

@@ -180,49 +180,61 @@ void launch_lk_typed(const LkGroup& grp, const LkPlan& p, hipStream_t stream) {
 
 template void launch_lk_typed<GQK_LK_TYPE, (GQK_LK_EP != 0)>(const LkGroup&, const LkPlan&, hipStream_t);
 
-template <int kType, int kDepth, bool kSingle, int kRps>
-static void launch_lks_k(const LksGroup& grp, int nsb, int R, int nw, int blocks, hipStream_t stream) {
+template <int kType, int kDepth, bool kSingle, int kRps, bool kEp>
+static void launch_lks_k(const LksGroup& grp, const GemvEpilogue& ep, int nsb, int R, int nw, int blocks,
+                         hipStream_t stream) {
   g_last_launch = GGUF_QK_LAUNCH_LKS;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemv_lks_kernel<kType, kDepth, kSingle, kRps>),
+      reinterpret_cast<const void*>(&gemv_lks_kernel<kType, kDepth, kSingle, kRps, kEp>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lks_lds_bytes(kRps, lks_max_waves(kRps), kLksMaxRows));
   (void)attr;
   const LksDesc& d = grp.d[0];
-  hipLaunchKernelGGL((gemv_lks_kernel<kType, kDepth, kSingle, kRps>), dim3((unsigned)blocks), dim3(64 * nw),
-                     lks_lds_bytes(kRps, nw, R), stream, d.W, grp.x, d.y, d.rows, nsb, R, nw, grp);
+  hipLaunchKernelGGL((gemv_lks_kernel<kType, kDepth, kSingle, kRps, kEp>), dim3((unsigned)blocks),
+                     dim3(64 * nw), lks_lds_bytes(kRps, nw, R), stream, d.W, grp.x, d.y, d.rows, nsb, R, nw,
+                     grp, ep);
 }
 
 template <int kType, int kRps>
-static void launch_lks_r(const LksGroup& grp, int nsb, int R, int nw, int depth, int blocks,
-                         hipStream_t stream) {
-  if (grp.n == 1) {
+static void launch_lks_r(const LksGroup& grp, const GemvEpilogue* ep, int nsb, int R, int nw, int depth,
+                         int blocks, hipStream_t stream) {
+  const GemvEpilogue none{};
+  if (grp.n == 1 && ep) {
+    // (the host takes this path for one Q4_K GEMV only)
+    if constexpr (kType == GGUF_QK_TYPE_Q4_K) {
+      if (depth <= 2)
+        launch_lks_k<kType, 2, true, kRps, true>(grp, *ep, nsb, R, nw, blocks, stream);
+      else
+        launch_lks_k<kType, 4, true, kRps, true>(grp, *ep, nsb, R, nw, blocks, stream);
+    }
+  } else if (grp.n == 1) {
     if (depth <= 2)
-      launch_lks_k<kType, 2, true, kRps>(grp, nsb, R, nw, blocks, stream);
+      launch_lks_k<kType, 2, true, kRps, false>(grp, none, nsb, R, nw, blocks, stream);
     else
-      launch_lks_k<kType, 4, true, kRps>(grp, nsb, R, nw, blocks, stream);
+      launch_lks_k<kType, 4, true, kRps, false>(grp, none, nsb, R, nw, blocks, stream);
   } else {
     if (depth <= 2)
-      launch_lks_k<kType, 2, false, kRps>(grp, nsb, R, nw, blocks, stream);
+      launch_lks_k<kType, 2, false, kRps, false>(grp, none, nsb, R, nw, blocks, stream);
     else
-      launch_lks_k<kType, 4, false, kRps>(grp, nsb, R, nw, blocks, stream);
+      launch_lks_k<kType, 4, false, kRps, false>(grp, none, nsb, R, nw, blocks, stream);
   }
 }
 
 template <int kType>
-void launch_lks_typed(const LksGroup& grp, int nsb, int R, int nw, int rps, int depth, int blocks,
-                      hipStream_t stream) {
+void launch_lks_typed(const LksGroup& grp, const GemvEpilogue* ep, int nsb, int R, int nw, int rps, int depth,
+                      int blocks, hipStream_t stream) {
   if constexpr (kType == GGUF_QK_TYPE_Q4_K || kType == GGUF_QK_TYPE_Q4_0) {
     if (rps == 4)
-      launch_lks_r<kType, 4>(grp, nsb, R, nw, depth, blocks, stream);
+      launch_lks_r<kType, 4>(grp, ep, nsb, R, nw, depth, blocks, stream);
     else if (rps == 2)
-      launch_lks_r<kType, 2>(grp, nsb, R, nw, depth, blocks, stream);
+      launch_lks_r<kType, 2>(grp, ep, nsb, R, nw, depth, blocks, stream);
     else
-      launch_lks_r<kType, 1>(grp, nsb, R, nw, depth, blocks, stream);
+      launch_lks_r<kType, 1>(grp, ep, nsb, R, nw, depth, blocks, stream);
   }
 }
 
 #if GQK_LK_EP == 0
-template void launch_lks_typed<GQK_LK_TYPE>(const LksGroup&, int, int, int, int, int, int, hipStream_t);
+template void launch_lks_typed<GQK_LK_TYPE>(const LksGroup&, const GemvEpilogue*, int, int, int, int, int, int,
+                                            hipStream_t);
 #endif
 
 }  // namespace gqk

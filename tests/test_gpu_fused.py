@@ -56,6 +56,7 @@ def weights(fmt, rng, rows, cols):
 
 
 @pytest.mark.parametrize("fmt,rows,cols", [("q4_k", 2048, 2048), ("q4_k", 2048, 11008),
+                                           ("q4_k", 300, 11008), ("q4_k", 130, 2304),
                                            ("q4_k", 100, 512), ("q8_0", 2048, 2048),
                                            ("q8_0", 777, 4096)])
 def test_residual_and_norm_outputs(fmt, rows, cols):
@@ -69,6 +70,10 @@ def test_residual_and_norm_outputs(fmt, rows, cols):
     b = g.GemvBatch([(tid, dev(w), dev(x), y, 0)],
                     [{"residual": dev(r), "norm_w": dev(nw), "norm_out": no, "ss_out": ss}])
     g.gguf_qmatvec_batch(b)
+    if fmt == "q4_k" and cols // 256 not in (1, 2, 4, 8, 16):
+        # rows of other super-block counts: the split-K-in-block kernel with
+        # the epilogue, its 64-row groups spanning blocks
+        assert g.gguf_qk_last_launch() == g.LAUNCH_LKS
     yg = host(y)
     check(yg, r.astype(np.float64) + oracle.matvec_f64(w32, x), "y")
     vw, ss2 = g.gguf_rmsnorm_prep_f32(y, dev(nw))
