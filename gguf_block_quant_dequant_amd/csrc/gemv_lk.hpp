@@ -590,7 +590,7 @@ __device__ __forceinline__ int lk_x_slot(int i) {
 }
 
 template <int kNsb, int kDepth, int kW, bool kEp, int kType = 12>
-__device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGroup* grp, TlStamps& tl,
+__device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const GemvEpilogue* eps, TlStamps& tl,
                                        const void* tl_key);
 
 // kType is the row format, a GGUF type id: 12 (Q4_K), 2 (Q4_0: the same
@@ -606,7 +606,7 @@ __global__ __launch_bounds__(kW * 64) void gemv_lk_kernel(LkGroup grp) {
   TlStamps tl;
   tl.stamp(0);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  lk_run<kNsb, kDepth, kW, kEp, kType>(lk_block<kW>(grp, (int)blockIdx.x, wave), xl, &grp, tl, grp.d[0].W);
+  lk_run<kNsb, kDepth, kW, kEp, kType>(lk_block<kW>(grp, (int)blockIdx.x, wave), xl, grp.ep, tl, grp.d[0].W);
 }
 
 // One GEMV, its descriptor as (preloaded) scalar arguments.
@@ -619,6 +619,25 @@ __global__ __launch_bounds__(kW * 64) void gemv_lk1_kernel(const uint8_t* W, con
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   lk_run<kNsb, kDepth, kW, false, kType>(lk_block_single<kW>(W, x, y, rows, q, r, kNsb, (int)blockIdx.x, wave),
                                          xl, nullptr, tl, W);
+}
+
+// One Q4_K GEMV with an epilogue: the descriptor and what the first loads
+// need of the epilogue (its flags, the input RMSN's partial sums) as
+// preloaded scalar arguments (13 dwords), the rest of the epilogue in memory,
+// read after the last step.
+template <int kNsb, int kDepth, int kW>
+__global__ __launch_bounds__(kW * 64) void gemv_lk1e_kernel(const uint8_t* W, const float* x, float* y,
+                                                            int rows, int q, int r, int ep_flags, int scale_n,
+                                                            const float* scale_ss, GemvEpilogue ep) {
+  __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
+  TlStamps tl;
+  tl.stamp(0);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  LkBlock B = lk_block_single<kW>(W, x, y, rows, q, r, kNsb, (int)blockIdx.x, wave);
+  B.ep_flags = ep_flags;
+  B.scale_n = scale_n;
+  B.scale_ss = (const GQK_GLOBAL float*)scale_ss;
+  lk_run<kNsb, kDepth, kW, true, 12>(B, xl, &ep, tl, W);
 }
 
 // Three GEMVs of one x (stages without epilogues), the descriptors packed into
@@ -653,7 +672,7 @@ __global__ __launch_bounds__(kW * 64) void gemv_lk2_kernel(const uint8_t* W0, co
 }
 
 template <int kNsb, int kDepth, int kW, bool kEp, int kType>
-__device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGroup* grp, TlStamps& tl,
+__device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const GemvEpilogue* eps, TlStamps& tl,
                                        const void* tl_key) {
   static_assert(kType == 12 || kType == 2 || kType == 8 || kType == 14, "Q4_K, Q4_0, Q8_0 or Q6_K rows");
   static_assert(kType == 12 || !kEp, "epilogues on Q4_K only");
@@ -691,7 +710,7 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const LkGrou
   LkSsLoads ssl;
   GemvEpilogue epl;
   if constexpr (kEp) {
-    epl = grp->ep[B.g];
+    epl = eps[B.g];
     ssl = lk_ep_ss_issue(B, lane);
   }
 

@@ -83,6 +83,22 @@ static void launch_lk2(const LkGroup& grp, int depth, hipStream_t stream) {
 template <int kType, int kNsb, int kW, bool kEp>
 static void launch_lk_nsb(const LkGroup& grp, int depth, hipStream_t stream) {
   const dim3 grid((unsigned)grp.total_blocks), block(kW * 64);
+  if (kEp && grp.n == 1 && tuning().lk_single) {
+    // one GEMV with an epilogue (the output projection: residual add, norm
+    // preparation): descriptor and epilogue flags preloaded
+    if constexpr (kEp && kType == GGUF_QK_TYPE_Q4_K) {
+      g_last_launch = GGUF_QK_LAUNCH_LK_SINGLE;
+      const LkDesc& d = grp.d[0];
+      const GemvEpilogue& ep = grp.ep[0];
+      if (depth <= 2)
+        hipLaunchKernelGGL((gemv_lk1e_kernel<kNsb, 2, kW>), grid, block, 0, stream, d.W, d.x, d.y, d.rows, d.q,
+                           d.r, ep.flags, ep.scale_n, ep.scale_ss, ep);
+      else
+        hipLaunchKernelGGL((gemv_lk1e_kernel<kNsb, 4, kW>), grid, block, 0, stream, d.W, d.x, d.y, d.rows, d.q,
+                           d.r, ep.flags, ep.scale_n, ep.scale_ss, ep);
+      return;
+    }
+  }
   if (!kEp && grp.n == 1 && tuning().lk_single) {
     g_last_launch = GGUF_QK_LAUNCH_LK_SINGLE;
     const LkDesc& d = grp.d[0];
