@@ -414,10 +414,11 @@ struct LkSsLoads {
   float v[4];
 };
 
-__device__ __forceinline__ LkSsLoads lk_ep_ss_issue(const LkBlock& B, int lane) {
-  const bool on = (B.ep_flags & kEpScale) && B.scale_n > 0;
-  const GQK_GLOBAL float* const p = on ? B.scale_ss : B.x;
-  const int last = on ? B.scale_n - 1 : 0;
+__device__ __forceinline__ LkSsLoads lk_ep_ss_issue(int flags, int scale_n, const GQK_GLOBAL float* scale_ss,
+                                                    const GQK_GLOBAL float* x, int lane) {
+  const bool on = (flags & kEpScale) && scale_n > 0;
+  const GQK_GLOBAL float* const p = on ? scale_ss : x;
+  const int last = on ? scale_n - 1 : 0;
   LkSsLoads r;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -589,7 +590,10 @@ __device__ __forceinline__ int lk_x_slot(int i) {
   }
 }
 
-template <int kNsb, int kDepth, int kW, bool kEp, int kType = 12>
+// kPair: whether the block computes an in-wave gate/up pair (kEpPairInWave):
+// 0 from the block's flags, 1 never, 2 always (known when the kernel is
+// chosen, so that the weight addresses wait for no epilogue argument).
+template <int kNsb, int kDepth, int kW, bool kEp, int kType = 12, int kPair = 0>
 __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const GemvEpilogue* eps, TlStamps& tl,
                                        const void* tl_key);
 
@@ -640,6 +644,28 @@ __global__ __launch_bounds__(kW * 64) void gemv_lk1e_kernel(const uint8_t* W, co
   lk_run<kNsb, kDepth, kW, true, 12>(B, xl, &ep, tl, W);
 }
 
+// A gate/up pair with epilogue (input RMSN scale, SiLU(gate) up) computed in
+// one wave: gate rows in lanes 0..31, the same rows of up in lanes 32..63.
+// The descriptors as preloaded scalar arguments (13 dwords; the blocks split
+// the gate's row steps), the epilogue in memory: it is first needed by the
+// input RMSN's partial-sum loads, which go out after the first weight loads.
+template <int kNsb, int kDepth, int kW>
+__global__ __launch_bounds__(kW * 64) void gemv_lk2e_kernel(const uint8_t* W0, const uint8_t* W1, const float* x,
+                                                            float* y0, float* y1, int rows, int q, int r,
+                                                            GemvEpilogue ep) {
+  __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
+  TlStamps tl;
+  tl.stamp(0);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  LkBlock B = lk_block_single<kW>(W0, x, y0, rows, q, r, kNsb, (int)blockIdx.x, wave);
+  B.W2 = (const GQK_GLOBAL uint8_t*)W1;
+  B.y2 = (GQK_GLOBAL float*)y1;
+  B.ep_flags = ep.flags;
+  B.scale_n = ep.scale_n;
+  B.scale_ss = (const GQK_GLOBAL float*)ep.scale_ss;
+  lk_run<kNsb, kDepth, kW, true, 12, 2>(B, xl, &ep, tl, W0);
+}
+
 // Three GEMVs of one x (stages without epilogues), the descriptors packed into
 // preloaded scalar arguments.
 template <int kType, int kNsb, int kDepth, int kW>
@@ -671,7 +697,7 @@ __global__ __launch_bounds__(kW * 64) void gemv_lk2_kernel(const uint8_t* W0, co
       xl, nullptr, tl, W0);
 }
 
-template <int kNsb, int kDepth, int kW, bool kEp, int kType>
+template <int kNsb, int kDepth, int kW, bool kEp, int kType, int kPair>
 __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const GemvEpilogue* eps, TlStamps& tl,
                                        const void* tl_key) {
   static_assert(kType == 12 || kType == 2 || kType == 8 || kType == 14, "Q4_K, Q4_0, Q8_0 or Q6_K rows");
@@ -703,7 +729,7 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const GemvEp
   const uint32_t hi_mask = gq >= 2 ? 0xFFFFFFFFu : 0u;
   // rows per step of each matrix: kRps, or kRps / 2 of the gate (lanes 0..31)
   // and the same rows of the up matrix (lanes 32..63) for an in-wave pair
-  const bool paired = kEp && kRps >= 2 && (B.ep_flags & kEpPairInWave);
+  const bool paired = kEp && kRps >= 2 && (kPair == 2 || (kPair == 0 && (B.ep_flags & kEpPairInWave)));
   const int rpm = paired ? kRps / 2 : kRps;
   const int rsub = (lane / kU) % rpm;
   const GQK_GLOBAL uint8_t* const Wl = (paired && lane >= 32) ? B.W2 : W;
@@ -711,7 +737,6 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const GemvEp
   GemvEpilogue epl;
   if constexpr (kEp) {
     epl = eps[B.g];
-    ssl = lk_ep_ss_issue(B, lane);
   }
 
   // x: every thread loads its float4s first ...
@@ -770,6 +795,16 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const GemvEp
   Load ring[kDepth];
 #pragma unroll
   for (int p = 0; p < kEarly; ++p) issue(st0 + p, ring[p]);
+  // the input RMSN's partial sums after the first weight loads: where the
+  // epilogue comes from argument memory, only they wait for it (the empty asm
+  // keeps the scheduler from moving their address work, and with it the
+  // wait, above the weight loads)
+  if constexpr (kEp) {
+    int f = B.ep_flags, sn = B.scale_n;
+    const float* sp = (const float*)B.scale_ss;
+    asm volatile("" : "+s"(f), "+s"(sn), "+s"(sp));
+    ssl = lk_ep_ss_issue(f, sn, (const GQK_GLOBAL float*)sp, B.x, lane);
+  }
   tl.stamp(1);
 
 #pragma unroll
@@ -1188,7 +1223,7 @@ __global__ __launch_bounds__(kW * 64) void gemv_lkx_kernel(const uint8_t* W1, co
   GemvEpilogue epl;
   if constexpr (kEp) {
     epl = grp.ep[B.g];
-    ssl = lk_ep_ss_issue(B, lane);
+    ssl = lk_ep_ss_issue(B.ep_flags, B.scale_n, B.scale_ss, B.x, lane);
   }
 
   // x: the block's threads load it all first (at most 16 kQ / kW float4

@@ -99,6 +99,21 @@ static void launch_lk_nsb(const LkGroup& grp, int depth, hipStream_t stream) {
       return;
     }
   }
+  if (kEp && grp.n == 2 && (grp.ep[0].flags & kEpPairInWave) && tuning().lk_two) {
+    // a gate/up pair in one wave: both descriptors preloaded
+    if constexpr (kEp && kType == GGUF_QK_TYPE_Q4_K) {
+      g_last_launch = GGUF_QK_LAUNCH_LK_TWO;
+      const LkDesc& d0 = grp.d[0];
+      const LkDesc& d1 = grp.d[1];
+      if (depth <= 2)
+        hipLaunchKernelGGL((gemv_lk2e_kernel<kNsb, 2, kW>), grid, block, 0, stream, d0.W, d1.W, d0.x, d0.y, d1.y,
+                           d0.rows, d0.q, d0.r, grp.ep[0]);
+      else
+        hipLaunchKernelGGL((gemv_lk2e_kernel<kNsb, 4, kW>), grid, block, 0, stream, d0.W, d1.W, d0.x, d0.y, d1.y,
+                           d0.rows, d0.q, d0.r, grp.ep[0]);
+      return;
+    }
+  }
   if (!kEp && grp.n == 1 && tuning().lk_single) {
     g_last_launch = GGUF_QK_LAUNCH_LK_SINGLE;
     const LkDesc& d = grp.d[0];

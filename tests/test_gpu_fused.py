@@ -111,6 +111,8 @@ def test_gate_up_pair_writes_the_activation(rows, cols):
     for rep in range(2):   # the pair counters are left at zero for the next call
         act.fill_(float("nan"))
         g.gguf_qmatvec_batch(b)
+        if cols <= 4096:   # both rows of an index in one wave, descriptors preloaded
+            assert g.gguf_qk_last_launch() == g.LAUNCH_LK_TWO
         gv, uv = host(yg_), host(yu_)
         check(gv, oracle.matvec_f64(oracle.dequant_q4_k_f32(wg, rows, cols), x), "gate")
         check(uv, oracle.matvec_f64(oracle.dequant_q4_k_f32(wu, rows, cols), x), "up")
