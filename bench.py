@@ -208,6 +208,54 @@ def probe_ceiling(torch, g):
     return (2 << 30) / t / 1e9
 
 
+def latency_probe(torch, g):
+    """Dependent-load latency (gguf_qk_probe_latency): one wave whose lanes each
+    follow a chain i -> (A i + C) mod n (a single cycle over the whole buffer:
+    A = 1 mod 4, C odd, n a power of two), over buffers sized for the L2 and
+    the Infinity Cache (timed after an untimed chase over the same lines), and
+    over 2 GiB for HBM (timed cold, after a streaming read of another 2 GiB has
+    pushed the chain's lines out of the caches); then the HBM chase on a second
+    stream while streaming-read probes run on the first. ns per dependent load
+    from the kernel's own clock (100 MHz)."""
+    dev = "cuda:0"
+    A, C = 0x9E3779B1, 0x7F4A7C15
+
+    def chain(n):
+        i = torch.arange(n, dtype=torch.int64, device=dev)
+        return ((i * A + C) & (n - 1)).to(torch.int32)
+
+    def ns(out, steps):
+        torch.cuda.synchronize()
+        return round(int(out[0].item()) * 10.0 / steps, 1)
+
+    levels = []
+    for label, nbytes, steps in (("1 MiB (L2)", 1 << 20, 4096), ("64 MiB (Infinity Cache)", 64 << 20, 4096)):
+        nxt = chain(nbytes // 4)
+        g.gguf_qk_probe_latency(nxt, steps)
+        levels.append({"label": label, "bytes": nbytes, "steps": steps,
+                       "ns_per_load": ns(g.gguf_qk_probe_latency(nxt, steps), steps)})
+        del nxt
+    nbytes = 2 << 30
+    nxt = chain(nbytes // 4)
+    other = torch.zeros(2 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    g.gguf_qk_probe_read(other, sink)
+    levels.append({"label": "2 GiB (HBM), cold", "bytes": nbytes, "steps": 2048,
+                   "ns_per_load": ns(g.gguf_qk_probe_latency(nxt, 2048), 2048)})
+    # loaded: 24 read probes over the other 2 GiB on one stream, then the chase
+    # (further along the chain) on a second stream (both default priority)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(24):
+        g.gguf_qk_probe_read(other, sink, stream=s1)
+    out = g.gguf_qk_probe_latency(nxt, 512, stream=s2)
+    levels.append({"label": "2 GiB (HBM) while streaming reads run on another stream", "bytes": nbytes,
+                   "steps": 512, "ns_per_load": ns(out, 512)})
+    del nxt, other
+    return {"label": "dependent-load latency: one wave, 64 independent chains, each load waiting for the one "
+                     "before (the kernel's 100 MHz clock)", "levels": levels}
+
+
 def prefill_pass(torch, g, synth, entries, meta, stream, n_tokens=512, reps=3):
     """36 layers x 7 Q4_K GEMMs (Y = X W^T, X bf16 [n_tokens x K]) over the
     resident decode weights, as one HIP graph: the matrices of a stage that
@@ -872,6 +920,7 @@ def main():
     ceiling = probe_ceiling(torch, g)
     rec["read_probe_GBps"] = round(ceiling, 1)
     rec["pct_of_read_probe"] = round(100 * gbps / ceiling, 2)
+    rec["latency_probe"] = latency_probe(torch, g)
     rec["stage_floor"] = stage_floor(torch, g, meta, total_bytes, stream)
     rec["pct_of_stage_floor"] = round(100 * rec["stage_floor"]["ms_per_pass"] / ms, 2)
     singles, single_outs = single_matrix_pass(torch, g, synth)

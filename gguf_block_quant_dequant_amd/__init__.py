@@ -59,6 +59,7 @@ _SIGS = {
     "gguf_qmatmul_f32_q8_0_multi": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _I64, _I64, _P]),
     "gguf_qmatmul_f32_q4_k_multi": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _I64, _I64, _P]),
     "gguf_qk_probe_read": (ctypes.c_int, [_P, _I64, _P, _P]),
+    "gguf_qk_probe_latency": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
     "gguf_qk_stream_release": (ctypes.c_int, [_P]),
     "gguf_qk_last_launch": (ctypes.c_int, []),
     "gguf_qk_timeline_setup": (ctypes.c_int, [ctypes.c_uint64]),
@@ -379,6 +380,19 @@ def gguf_qk_probe_read(buf, sink=None, stream=None):
     _check(lib().gguf_qk_probe_read(_dev(buf, "buf"), nbytes, _dev(sink, "sink", torch.int32),
                                     _stream(stream)), "gguf_qk_probe_read")
     return sink
+
+
+def gguf_qk_probe_latency(next_idx, steps, out=None, stream=None):
+    """Enqueue the dependent-load chase over the int32 device tensor `next_idx`
+    (a power-of-two number of entries); returns the int64 tensor out whose
+    element 0 becomes the elapsed 100 MHz ticks of `steps` dependent loads."""
+    if next_idx.dtype != torch.int32:
+        raise TypeError("next_idx must be int32")
+    if out is None:
+        out = torch.zeros(2, dtype=torch.int64, device=next_idx.device)
+    _check(lib().gguf_qk_probe_latency(_dev(next_idx, "next_idx", torch.int32), next_idx.numel(), int(steps),
+                                       _dev(out, "out", torch.int64), _stream(stream)), "gguf_qk_probe_latency")
+    return out
 
 
 STREAM_SLOTS = 8   # GGUF_QK_STREAM_SLOTS: scratch slots per device

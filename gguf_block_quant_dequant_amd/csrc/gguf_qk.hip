@@ -1217,4 +1217,15 @@ int gguf_qk_probe_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream
   return launch_status();
 }
 
+int gguf_qk_probe_latency(const uint32_t* next, int64_t n, int64_t steps, uint64_t* out, hipStream_t stream) {
+  if (!next || !out) return GGUF_QK_ERR_NULL;
+  if (n < 64 || n > (int64_t(1) << 31) || (n & (n - 1)) || steps < 1) return GGUF_QK_ERR_SHAPE;
+  if (!aligned16(next) || !aligned16(out)) return GGUF_QK_ERR_ALIGN;
+  if (overlap(out, 16, next, n * 4)) return GGUF_QK_ERR_ALIAS;
+  const int st = current_device();
+  if (st) return st;
+  hipLaunchKernelGGL(probe_chase_kernel, dim3(1), dim3(64), 0, stream, next, (uint32_t)(n - 1), steps, out);
+  return launch_status();
+}
+
 }  // extern "C"

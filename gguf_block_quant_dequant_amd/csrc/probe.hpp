@@ -32,4 +32,22 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4* 
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+// Latency probe: one wave; lane l starts at entry l and follows the chain
+// i = next[i] & mask `steps` times, each load waiting for the one before (the
+// lanes' loads of a step go out together). The mask keeps every index inside
+// the buffer whatever it holds. out[0]: elapsed ticks of the constant 100 MHz
+// clock; out[1]: lane 0's last index (keeps the chain alive).
+__global__ __launch_bounds__(64) void probe_chase_kernel(const uint32_t* __restrict__ next, uint32_t mask,
+                                                         int64_t steps, uint64_t* __restrict__ out) {
+  uint32_t i = threadIdx.x & mask;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (int64_t s = 0; s < steps; ++s) i = next[i] & mask;
+  asm volatile("" : "+v"(i));   // the last load is complete before the second stamp
+  const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    out[0] = t1 - t0;
+    out[1] = i;
+  }
+}
+
 }  // namespace gqk

@@ -323,6 +323,17 @@ int gguf_qk_stream_release(hipStream_t stream);
  * bandwidth, the practical ceiling for the weight stream. */
 int gguf_qk_probe_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
 
+/* Latency probe: one wave of 64 lanes; lane l starts at entry l of `next` (n
+ * uint32 entries, n a power of two, 64 <= n <= 2^31, device memory) and follows
+ * i = next[i] & (n - 1) `steps` times, every load waiting for the one before.
+ * Writes out[0] = the elapsed ticks of the device's constant 100 MHz clock
+ * between the first load and the completion of the last, out[1] = lane 0's
+ * last index (out: 2 uint64 in device memory, 16-byte aligned). Entries past
+ * n are masked into range, so any buffer contents are safe. With `next` a
+ * single cycle spread over a buffer larger than a cache level, out[0] * 10 ns /
+ * steps is that level's (or HBM's) latency for a dependent load. */
+int gguf_qk_probe_latency(const uint32_t* next, int64_t n, int64_t steps, uint64_t* out, hipStream_t stream);
+
 /* Stage timelines of the decode GEMV kernels (measurement; the instrumented
  * build libgguf_qk_timeline.so only, compiled with GQK_TIMELINE: in the
  * default library both calls return GGUF_QK_ERR_LIMIT and do nothing).

@@ -348,3 +348,24 @@ def test_batch_binding_rejects_short_epilogue_vectors():
     # sizes that fit pass this check (host tensors are then refused as such)
     with pytest.raises(ValueError, match="device tensor"):
         g.GemvBatch(entries, [{"residual": torch.zeros(rows), "ss_out": torch.zeros(3)}])
+
+
+def test_probe_validation():
+    """The probes check their arguments before any HIP call: the latency
+    probe's chain length must be a power of two (its indices are masked with
+    n - 1, which then keeps every load inside the buffer) and at least one
+    wave's worth of start entries."""
+    L = g.lib()
+    assert L.gguf_qk_probe_read(None, 64, C, None) == g.ERR_NULL
+    assert L.gguf_qk_probe_read(A, 63, C, None) == g.ERR_SHAPE
+    assert L.gguf_qk_probe_read(A, 64, A + 16, None) == g.ERR_ALIAS
+    assert L.gguf_qk_probe_read(A, 64, C, None) == g.ERR_DEVICE
+    assert L.gguf_qk_probe_latency(None, 64, 1, C, None) == g.ERR_NULL
+    assert L.gguf_qk_probe_latency(A, 64, 1, None, None) == g.ERR_NULL
+    for n in (0, 32, 63, 96, 1000, (1 << 31) + 1, 1 << 32):
+        assert L.gguf_qk_probe_latency(A, n, 1, C, None) == g.ERR_SHAPE, n
+    assert L.gguf_qk_probe_latency(A, 64, 0, C, None) == g.ERR_SHAPE
+    assert L.gguf_qk_probe_latency(A + 4, 64, 1, C, None) == g.ERR_ALIGN
+    assert L.gguf_qk_probe_latency(A, 64, 1, A + 16, None) == g.ERR_ALIAS
+    assert L.gguf_qk_probe_latency(A, 64, 1, C, None) == g.ERR_DEVICE
+    assert L.gguf_qk_probe_latency(C, 1 << 31, 1, A, None) == g.ERR_DEVICE   # out below the 8 GiB chain
