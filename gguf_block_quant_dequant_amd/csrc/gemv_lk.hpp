@@ -571,7 +571,9 @@ __device__ __forceinline__ LkBlock lk_block_three(const uint8_t* W0, int dW1, in
   const uint32_t q = steps / nbm, r = steps - q * nbm;
   const int64_t dw = 16 * (m == 0 ? 0 : m == 1 ? (int64_t)dW1 : (int64_t)dW2);
   const int64_t dy = 4 * (m == 0 ? 0 : m == 1 ? (int64_t)dy1 : (int64_t)dy2);
-  return lk_block_single<kW>(W0 + dw, x, y0 + dy, (int)rows, (int)q, (int)r, nsb, (int)(ub - b0), wave);
+  LkBlock o = lk_block_single<kW>(W0 + dw, x, y0 + dy, (int)rows, (int)q, (int)r, nsb, (int)(ub - b0), wave);
+  o.g = m;
+  return o;
 }
 
 // LDS float index of x's float4 i in the staged layout: lane slice u (64
@@ -680,6 +682,31 @@ __global__ __launch_bounds__(kW * 64) void gemv_lk3_kernel(const uint8_t* W0, in
                                                                        rows12, bb12, nb, kNsb,
                                                                        (int)blockIdx.x, wave),
                                          xl, nullptr, tl, W0);
+}
+
+// Three GEMVs of one x with epilogues (the fused q/k/v: the input RMSN scale),
+// the descriptors packed into the preloaded arguments as above, the three
+// epilogues in memory (first needed by the input RMSN's partial-sum loads,
+// which go out after the first weight loads).
+struct LkEp3 {
+  GemvEpilogue e[3];
+};
+
+template <int kNsb, int kDepth, int kW>
+__global__ __launch_bounds__(kW * 64) void gemv_lk3e_kernel(const uint8_t* W0, int dW1, int dW2, const float* x,
+                                                            float* y0, int dy1, int dy2, int rows0, int rows12,
+                                                            int bb12, int nb, LkEp3 ep) {
+  __shared__ __attribute__((aligned(16))) float xl[256 * kNsb + 16 * kNsb];
+  TlStamps tl;
+  tl.stamp(0);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  LkBlock B = lk_block_three<kW, 16 / kNsb>(W0, dW1, dW2, x, y0, dy1, dy2, rows0, rows12, bb12, nb, kNsb,
+                                            (int)blockIdx.x, wave);
+  const GemvEpilogue& e = ep.e[B.g];
+  B.ep_flags = e.flags;
+  B.scale_n = e.scale_n;
+  B.scale_ss = (const GQK_GLOBAL float*)e.scale_ss;
+  lk_run<kNsb, kDepth, kW, true, 12, 1>(B, xl, ep.e, tl, W0);
 }
 
 // Two GEMVs of one x (stages without epilogues), the descriptors as preloaded

@@ -66,6 +66,20 @@ static void launch_lk3(const LkGroup& grp, const Lk3Args& a, int depth, hipStrea
                        d.y, a.dy1, a.dy2, d.rows, a.rows12, a.bb12, grp.total_blocks);
 }
 
+template <int kNsb, int kW>
+static void launch_lk3e(const LkGroup& grp, const Lk3Args& a, int depth, hipStream_t stream) {
+  const dim3 grid((unsigned)grp.total_blocks), block(kW * 64);
+  const LkDesc& d = grp.d[0];
+  LkEp3 ep;
+  for (int i = 0; i < 3; ++i) ep.e[i] = grp.ep[i];
+  if (depth <= 2)
+    hipLaunchKernelGGL((gemv_lk3e_kernel<kNsb, 2, kW>), grid, block, 0, stream, d.W, a.dW1, a.dW2, d.x, d.y,
+                       a.dy1, a.dy2, d.rows, a.rows12, a.bb12, grp.total_blocks, ep);
+  else
+    hipLaunchKernelGGL((gemv_lk3e_kernel<kNsb, 4, kW>), grid, block, 0, stream, d.W, a.dW1, a.dW2, d.x, d.y,
+                       a.dy1, a.dy2, d.rows, a.rows12, a.bb12, grp.total_blocks, ep);
+}
+
 template <int kType, int kNsb, int kW>
 static void launch_lk2(const LkGroup& grp, int depth, hipStream_t stream) {
   const dim3 grid((unsigned)grp.total_blocks), block(kW * 64);
@@ -131,6 +145,14 @@ static void launch_lk_nsb(const LkGroup& grp, int depth, hipStream_t stream) {
     return;
   }
   Lk3Args a3;
+  if (kEp && !(grp.ep[0].flags & kEpPairInWave) && !(grp.ep[1].flags & kEpPairInWave) && lk_three(grp, &a3)) {
+    // three GEMVs of one x with epilogues (the fused q/k/v)
+    if constexpr (kEp && kType == GGUF_QK_TYPE_Q4_K) {
+      g_last_launch = GGUF_QK_LAUNCH_LK_THREE;
+      launch_lk3e<kNsb, kW>(grp, a3, depth, stream);
+      return;
+    }
+  }
   if (!kEp && lk_three(grp, &a3)) {
     g_last_launch = GGUF_QK_LAUNCH_LK_THREE;
     launch_lk3<kType, kNsb, kW>(grp, a3, depth, stream);

@@ -98,6 +98,27 @@ def test_rmsnorm_scale_of_the_input(fmt, rows, cols):
     check(host(y), oracle.matvec_f64(w32, oracle.rmsnorm_f64(v, nw, EPS)), "scaled y")
 
 
+@pytest.mark.parametrize("rows,cols", [((2048, 512, 512), 2048), ((300, 100, 37), 2048),
+                                       ((64, 1, 130), 512), ((200, 70, 90), 2304)])
+def test_rmsnorm_scale_of_three_gemvs_of_one_input(rows, cols):
+    # the fused q/k/v: three matrices of one scaled x in one launch
+    rng = np.random.default_rng([sum(rows), cols, 9])
+    v = (3.0 * rng.standard_normal(cols)).astype(np.float32)
+    nw = rng.uniform(0.5, 1.5, cols).astype(np.float32)
+    vw, ss = g.gguf_rmsnorm_prep_f32(dev(v), dev(nw))
+    xn = oracle.rmsnorm_f64(v, nw, EPS)
+    ws = [synth.q4_k_weights(rng, r, cols) for r in rows]
+    ys = [empty(r) for r in rows]
+    say("three scaled GEMVs", rows, cols)
+    b = g.GemvBatch([(g.TYPE_Q4_K, dev(w), vw, y, 0) for w, y in zip(ws, ys)],
+                    [{"scale_ss": ss, "eps": EPS}] * 3)
+    g.gguf_qmatvec_batch(b)
+    if cols // 256 in (1, 2, 4, 8, 16):
+        assert g.gguf_qk_last_launch() == g.LAUNCH_LK_THREE
+    for w, y, r in zip(ws, ys, rows):
+        check(host(y), oracle.matvec_f64(oracle.dequant_q4_k_f32(w, r, cols), xn), ("scaled y", r))
+
+
 @pytest.mark.parametrize("rows,cols", [(11008, 2048), (100, 512), (300, 11008)])
 def test_gate_up_pair_writes_the_activation(rows, cols):
     rng = np.random.default_rng([rows, cols, 7])
