@@ -60,6 +60,9 @@ SHAPES = [
     ("q4_k", 2048, 11008, 16),
     ("q4_k", 300, 2048, 20),     # two token chunks of the Q4_K kernel up to 32 tokens, the second ragged
     ("q4_k", 520, 11008, 27),    # the same with K split over blocks
+    ("q4_k", 70, 20480, 5),      # K split over more than eight ranges (80 super-blocks): paired layout
+    ("q4_k", 40, 20480, 20),     # the same, two token chunks of 16
+    ("q4_k", 90, 20480, 64),     # the same on the 32-token tile kernel
     ("q4_k", 11008, 2048, 5),
     ("q8_0", 128, 256, 1),
     ("q8_0", 257, 512, 5),
