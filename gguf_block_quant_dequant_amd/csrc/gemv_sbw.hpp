@@ -25,8 +25,8 @@
 // the range's activations once (whole 1 KiB rows per load, split into bf16
 // hi and lo in the A layout in LDS) and each wave takes its super-block's
 // operands into registers; it then streams the row tiles' weights through a
-// register ring
-// of four (a header and four 8-byte quant pieces per lane and tile: bytes
+// register ring of kSbwDepth tiles (a header and four 8-byte quant pieces per
+// lane and tile: bytes
 // 32 g + 8 (l / 16) of group g, whose low nibbles are sub-block 2 g and high
 // nibbles 2 g + 1), runs each tile's MFMAs from registers and leaves its
 // sums in LDS. The waves' sums are then added in wave order. Weights are read
@@ -68,7 +68,9 @@ constexpr int kSbwMaxTokens = 16;   // tokens per block (grid y covers more)
 constexpr int kSbwRouteTokens = 32; // token counts the small-batch calls send here
 constexpr int kSbwMaxWaves = 8;     // super-blocks of one K range at most
 constexpr int kSbwMaxTiles = 16;    // row tiles of 16 per block at most
-constexpr int kSbwDepth = 4;        // weight ring (row tiles in flight per wave)
+// weight ring (row tiles in flight per wave): two measured faster than three
+// or four (8 tokens: 1.33 / 1.34 / 1.36 ms per pass)
+constexpr int kSbwDepth = 2;
 
 // LDS bytes of a block: the staged activations of its (at most nw)
 // super-blocks (token slots x 16 bytes x (64 A operand groups + 2 sums) each),
@@ -199,22 +201,29 @@ __global__ __launch_bounds__(64 * kSbwMaxWaves) void gemv_sbw_kernel(const uint8
   const uint32_t row_bytes = (uint32_t)nsb * kQ4KBlockBytes;
   const int c4 = lane >> 4, col = lane & 15;
 
-  // row tile u of the block (tiles past the last re-read it; rows past the
-  // matrix re-read its last row; neither is stored)
+  // row tile u of the block (rows past the matrix re-read its last row, which
+  // is never stored). A slot past the block's last tile loads the first 16
+  // bytes of the wave's super-block column in every lane (one cache line); the
+  // choice is made per lane, so every slot issues the same loads on every
+  // path and the in-order load counter stays exact (a uniform branch around
+  // the loads made the compiler wait for the whole ring before the
+  // activations were staged).
   const GQK_GLOBAL uint8_t* const wb = (const GQK_GLOBAL uint8_t*)W + (uint32_t)sb * kQ4KBlockBytes;
   auto issue = [&](int u, SbwUnit<kPair>& L) {
-    u = u < ntile ? u : ntile - 1;
-    int r = r0 + 16 * u + col;
+    int on = u < ntile;
+    asm volatile("" : "+v"(on));
+    int r = r0 + 16 * (u < ntile ? u : ntile - 1) + col;
     r = r < rows ? r : rows - 1;
-    const GQK_GLOBAL uint8_t* b = wb + (int64_t)r * row_bytes;
-    L.h = *reinterpret_cast<const GQK_GLOBAL sbw_u32x4*>(b);
+    const GQK_GLOBAL uint8_t* const b = wb + (int64_t)r * row_bytes;
+    auto at = [&](uint32_t off) { return on ? b + off : wb; };
+    L.h = *reinterpret_cast<const GQK_GLOBAL sbw_u32x4*>(at(0u));
     if constexpr (kPair) {
-      L.qa = *reinterpret_cast<const GQK_GLOBAL sbw_u32x4*>(b + (16u + 16u * c4));
-      L.qb = *reinterpret_cast<const GQK_GLOBAL sbw_u32x4*>(b + (80u + 16u * c4));
+      L.qa = *reinterpret_cast<const GQK_GLOBAL sbw_u32x4*>(at(16u + 16u * c4));
+      L.qb = *reinterpret_cast<const GQK_GLOBAL sbw_u32x4*>(at(80u + 16u * c4));
     } else {
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        L.q[g] = *reinterpret_cast<const GQK_GLOBAL sbw_u32x2*>(b + (16u + 32u * g + 8u * c4));
+        L.q[g] = *reinterpret_cast<const GQK_GLOBAL sbw_u32x2*>(at(16u + 32u * g + 8u * c4));
     }
   };
   SbwUnit<kPair> ring[kD];
@@ -280,12 +289,10 @@ __global__ __launch_bounds__(64 * kSbwMaxWaves) void gemv_sbw_kernel(const uint8
     }
   };
   if constexpr (kPair) {
-    // the weight ring (only real tiles: with fewer than kD tiles the loop
-    // below does not run and the tail reads just these), then the wave's rows
-    // into its own area and a wave-level exchange: no block barrier
+    // the weight ring, then the wave's rows into its own area and a
+    // wave-level exchange: no block barrier
 #pragma unroll
-    for (int p = 0; p < kD; ++p)
-      if (p < ntile) issue(p, ring[p]);
+    for (int p = 0; p < kD; ++p) issue(p, ring[p]);
     tl.stamp(1);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -296,11 +303,8 @@ __global__ __launch_bounds__(64 * kSbwMaxWaves) void gemv_sbw_kernel(const uint8
   } else {
     float4 xv[8];
     load_rows(wave, xv);
-    // (only real tiles: with fewer than kD tiles the loop below does not run
-    // and the tail reads just these)
 #pragma unroll
-    for (int p = 0; p < kD; ++p)
-      if (p < ntile) issue(p, ring[p]);
+    for (int p = 0; p < kD; ++p) issue(p, ring[p]);
     tl.stamp(1);
     if (wave < npr) stage_rows(wave, xv);
     for (int pb = wave + 8 * nw; pb < npr; pb += 8 * nw) {
