@@ -144,6 +144,40 @@ __device__ __forceinline__ float* gemm_partial_slot(float* tile, int wave, int i
   return tile + ((((wave * 2 + it) * 2 + jt) * 16 + e) * 64 + lane);
 }
 
+// The last block of a split tile: the S partial tiles summed in range order
+// and stored as bf16. Two accumulator tiles at a time: a range's 32 values per
+// lane are loaded together, so the sum costs 2 S memory round trips (4 S with
+// one tile at a time; all four tiles together took the kernel past 256
+// registers, one wave per SIMD).
+__device__ __forceinline__ void gemm_sum_partials(const float* partials, int64_t ntiles, int64_t tile, int S,
+                                                  int wave, int lane, uint16_t* Y, int64_t n_tokens, int64_t rows,
+                                                  int64_t n0, int64_t r0, int wi, int wj) {
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    f32x16 sum[2];
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sum[jt][e] = 0.f;
+    for (int sp = 0; sp < S; ++sp) {
+      float* p = const_cast<float*>(partials) + ((int64_t)sp * ntiles + tile) * kGemmTileFloats;
+      float v[2][16];
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          v[jt][e] = __hip_atomic_load(gemm_partial_slot(p, wave, it, jt, e, lane), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sum[jt][e] += v[jt][e];
+    }
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) gemm_store_bf16(sum[jt], Y, n_tokens, rows, n0, r0, wi, wj, it, jt, lane);
+  }
+}
+
 __global__ __launch_bounds__(256) void gemm_q4_k_kernel(const uint8_t* __restrict__ W,
                                                         const uint16_t* __restrict__ X,
                                                         uint16_t* __restrict__ Y, int64_t n_tokens,
@@ -222,22 +256,7 @@ __global__ __launch_bounds__(256) void gemm_q4_k_kernel(const uint8_t* __restric
   }
   __syncthreads();
   if (!last) return;
-#pragma unroll
-  for (int it = 0; it < 2; ++it)
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt) {
-      f32x16 sum;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sum[e] = 0.f;
-      for (int s = 0; s < S; ++s) {
-        float* p = partials + ((int64_t)s * ntiles + tile) * kGemmTileFloats;
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          sum[e] += __hip_atomic_load(gemm_partial_slot(p, wave, it, jt, e, lane),
-                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      gemm_store_bf16(sum, Y, n_tokens, rows, n0, r0, wi, wj, it, jt, lane);
-    }
+  gemm_sum_partials(partials, ntiles, tile, S, wave, lane, Y, n_tokens, rows, n0, r0, wi, wj);
   if (tid == 0)
     __hip_atomic_store(&counters[tile * kGemmCounterStride], 0, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
@@ -476,22 +495,7 @@ __global__ __launch_bounds__(256) void gemm_q4_k_db_kernel(GemmGroup G, const ui
   }
   __syncthreads();
   if (!last) return;
-#pragma unroll
-  for (int it = 0; it < 2; ++it)
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt) {
-      f32x16 sum;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sum[e] = 0.f;
-      for (int sp = 0; sp < S; ++sp) {
-        float* p = partials + ((int64_t)sp * ntiles + tile) * kGemmTileFloats;
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          sum[e] += __hip_atomic_load(gemm_partial_slot(p, wave, it, jt, e, lane),
-                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      gemm_store_bf16(sum, Y, n_tokens, rows, n0, r0, wi, wj, it, jt, lane);
-    }
+  gemm_sum_partials(partials, ntiles, tile, S, wave, lane, Y, n_tokens, rows, n0, r0, wi, wj);
   if (tid == 0)
     __hip_atomic_store(&counters[tile * kGemmCounterStride], 0, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);

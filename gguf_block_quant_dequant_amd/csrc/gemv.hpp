@@ -382,13 +382,14 @@ __device__ __forceinline__ void splitk_finish(float acc, float* __restrict__ y, 
       // eight loads in flight at a time (indexes past P repeat the last
       // partial and are not added), added strictly in order 0..P-1
       for (int p0 = 0; p0 < P; p0 += 8) {
-        float v[8];
+        const float* pp[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int p = (p0 + i) < P ? (p0 + i) : (P - 1);
-          v[i] = __hip_atomic_load(&sk.partials[(int64_t)p * rows + row0 + lane], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+          pp[i] = &sk.partials[(int64_t)p * rows + row0 + lane];
         }
+        float v[8];
+        coherent_load8(pp, v);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           if (p0 + i < P) s += v[i];

@@ -504,22 +504,23 @@ __global__ __launch_bounds__(64 * kSbwMaxWaves) void gemv_sbw_kernel(const uint8
     tl_put(W0, tl);
     return;
   }
-  // the partial values of an element are read eight ranges at a time
-  // (indexes past the last range re-read it and are not added) and added in
-  // range order
+  // the partial values of an element are read eight ranges at a time, all
+  // eight in flight (indexes past the last range re-read it and are not
+  // added), and added in range order
   for (int e = tid; e < ne; e += nthreads) {
     int r, t;
     coords(e, r, t);
     if (r >= rows || t >= nb) continue;
     float sum = 0.f;
     for (int s0 = 0; s0 < S; s0 += 8) {
-      float v[8];
+      const float* pp[8];
 #pragma unroll
       for (int sp = 0; sp < 8; ++sp) {
         const int spc = s0 + sp < S ? s0 + sp : S - 1;
-        v[sp] = __hip_atomic_load(partials + ((int64_t)spc * ntiles + btile) * tile_floats + e, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
+        pp[sp] = partials + ((int64_t)spc * ntiles + btile) * tile_floats + e;
       }
+      float v[8];
+      coherent_load8(pp, v);
 #pragma unroll
       for (int sp = 0; sp < 8; ++sp)
         if (s0 + sp < S) sum += v[sp];

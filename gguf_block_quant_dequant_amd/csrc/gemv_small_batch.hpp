@@ -379,7 +379,10 @@ __global__ __launch_bounds__(256, 2) void gemv_small_batch_kernel(
   __syncthreads();
   if (!last) return;
   // The partial tiles are read four ranges at a time (one round trip per four,
-  // indexes past the last range clamped and not added) and added in range order.
+  // indexes past the last range clamped and not added) and added in range
+  // order. Every load is issued, whatever the valid token groups (a group
+  // past them re-reads group 0's slot and is not added): loads under a
+  // condition went out one at a time.
   f32x16 sum;
 #pragma unroll
   for (int e = 0; e < 16; ++e) sum[e] = 0.f;
@@ -391,15 +394,14 @@ __global__ __launch_bounds__(256, 2) void gemv_small_batch_kernel(
       float* p = partials + ((int64_t)s * ntiles + tile) * kSbTileFloats;
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        v[i][e] = (e >> 2) < ng ? __hip_atomic_load(sb_partial_slot(p, wave, e, lane), __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT)
-                                : 0.f;
+        v[i][e] = __hip_atomic_load(sb_partial_slot(p, wave, (e >> 2) < ng ? e : (e & 3), lane), __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (s0 + i < S) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sum[e] += v[i][e];
+        for (int e = 0; e < 16; ++e) sum[e] += (e >> 2) < ng ? v[i][e] : 0.f;
       }
   }
   sb_store(sum, Y, n_tokens, rows, n0, r0, wave, lane);
