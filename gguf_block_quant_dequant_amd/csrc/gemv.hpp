@@ -22,6 +22,7 @@
 // that wave, leaving scratch ready for the next call.
 #pragma once
 
+#include "coherent.hpp"
 #include "device_common.hpp"
 #include "gemv_types.hpp"
 

@@ -54,6 +54,7 @@
 // does not depend on arrival order), writes Y and resets the counter.
 #pragma once
 
+#include "coherent.hpp"
 #include "device_common.hpp"
 #include "gemv_small_batch.hpp"
 #include "timeline.hpp"
