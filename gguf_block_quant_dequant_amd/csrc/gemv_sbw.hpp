@@ -335,10 +335,15 @@ __global__ __launch_bounds__(64 * kSbwMaxWaves) void gemv_sbw_kernel(const uint8
           for (int e = 0; e < 2; ++e) {
             const int sbk = 2 * (2 * q + (c4 >> 1)) + h, ck = 2 * (c4 & 1) + e;
             const uint8_t* ap = xl + (((sl * 2) * 32 + sbk * 4 + ck) * slots + ts) * 16;
-            const bf16x8 vh = *reinterpret_cast<const bf16x8*>(ap);
-            const bf16x8 vl = *reinterpret_cast<const bf16x8*>(ap + 32 * slots * 16);
-            ah[q * 4 + h * 2 + e] = on ? vh : z8;
-            al[q * 4 + h * 2 + e] = on ? vl : z8;
+            // (only the lanes whose group feeds their slot read: half the
+            // LDS traffic of reading in every lane and selecting)
+            bf16x8 vh = z8, vl = z8;
+            if (on) {
+              vh = *reinterpret_cast<const bf16x8*>(ap);
+              vl = *reinterpret_cast<const bf16x8*>(ap + 32 * slots * 16);
+            }
+            ah[q * 4 + h * 2 + e] = vh;
+            al[q * 4 + h * 2 + e] = vl;
           }
     } else {
       const uint8_t* ap = xl + (((sl * 2) * 32 + c4) * slots + ts) * 16;
