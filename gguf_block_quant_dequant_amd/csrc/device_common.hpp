@@ -33,8 +33,12 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
 __device__ __forceinline__ uint16_t to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
+// Both halves in one v_cvt_pk_bf16_f32 (the per-element form took two
+// conversions, a shift and an or); nearest-even, as to_bf16.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)to_bf16(lo) | ((uint32_t)to_bf16(hi) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // Hide a value from the optimizer so that byte-wise conversions of a masked

@@ -149,9 +149,10 @@ __device__ __forceinline__ float* gemm_partial_slot(float* tile, int wave, int i
 // lane are loaded together, so the sum costs 2 S memory round trips (4 S with
 // one tile at a time; all four tiles together took the kernel past 256
 // registers, one wave per SIMD).
-__device__ __forceinline__ void gemm_sum_partials(const float* partials, int64_t ntiles, int64_t tile, int S,
-                                                  int wave, int lane, uint16_t* Y, int64_t n_tokens, int64_t rows,
-                                                  int64_t n0, int64_t r0, int wi, int wj) {
+__device__ __forceinline__ void gemm_sum_partials(const float* partials, int64_t ntiles, int64_t tile,
+                                                  int64_t tile_floats, int S, int wave, int lane, uint16_t* Y,
+                                                  int64_t n_tokens, int64_t rows, int64_t n0, int64_t r0, int wi,
+                                                  int wj) {
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     f32x16 sum[2];
@@ -160,7 +161,7 @@ __device__ __forceinline__ void gemm_sum_partials(const float* partials, int64_t
 #pragma unroll
       for (int e = 0; e < 16; ++e) sum[jt][e] = 0.f;
     for (int sp = 0; sp < S; ++sp) {
-      float* p = const_cast<float*>(partials) + ((int64_t)sp * ntiles + tile) * kGemmTileFloats;
+      float* p = const_cast<float*>(partials) + ((int64_t)sp * ntiles + tile) * tile_floats;
       float v[2][16];
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt)
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(256) void gemm_q4_k_kernel(const uint8_t* __restric
   }
   __syncthreads();
   if (!last) return;
-  gemm_sum_partials(partials, ntiles, tile, S, wave, lane, Y, n_tokens, rows, n0, r0, wi, wj);
+  gemm_sum_partials(partials, ntiles, tile, kGemmTileFloats, S, wave, lane, Y, n_tokens, rows, n0, r0, wi, wj);
   if (tid == 0)
     __hip_atomic_store(&counters[tile * kGemmCounterStride], 0, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
@@ -265,19 +266,26 @@ __global__ __launch_bounds__(256) void gemm_q4_k_kernel(const uint8_t* __restric
 #undef GQK_GEMM_LOAD
 #undef GQK_GEMM_STEP
 
+
 // ---------------------------------------------------------------------------
-// The same product with the operand tiles double-buffered in LDS. Steps of 64
-// k (one 32-byte nibble group: sub-blocks 2 g and 2 g + 1 of a super-block);
-// each thread holds the raw bytes of the next two steps in registers (X: 16
-// bytes of 4 token rows; W: the header and the group's 32 bytes of one weight
-// row, of which it decodes one sub-block), and while a wave's MFMAs read step
-// s from one LDS buffer it decodes step s + 1 into the other: one barrier per
-// step, and the decode's VALU work and LDS stores sit between the MFMAs
-// instead of before them. The tile values are the same bits as the kernel
-// above (fma(d sc, q, -dmin m) in fp32, rounded to nearest-even bf16).
-// Block tile, wave tiles, MFMA layout, split K and the partial-tile epilogue
-// are those of the kernel above; the partial tiles and counters are indexed
-// by the grid tile, so the matrices of a group share them.
+// The same product with the operand tiles double-buffered in LDS, in two
+// block shapes: kWi = 2 (4 waves, 128 tokens x 128 weight rows) or kWi = 4
+// (8 waves, 256 tokens x 128 rows). Either way a wave computes a 64 x 64
+// sub-tile (wave w: tokens 64 (w / 2), rows 64 (w % 2)) with the MFMA layout
+// above. Steps of 64 k (one 32-byte nibble group: sub-blocks 2 g and 2 g + 1
+// of a super-block); each thread holds the raw bytes of the next steps in
+// registers (X: 16 bytes of 4 token rows; W: the super-block header and 32
+// (kWi = 2) or 16 (kWi = 4) nibble bytes of one weight row, of which it
+// decodes one nibble half: 32 or 16 weights), and while a wave's MFMAs read
+// step s from one LDS buffer it decodes step s + 1 into the other: one
+// barrier per step, and the decode's VALU work and LDS stores sit between the
+// MFMAs instead of before them. A weight is decoded once per block, so the
+// 256-token block spends half the decode work per MFMA of the 128-token one.
+// The tile values are the same bits as the kernel above (fma(d sc, q, -dmin m)
+// in fp32, rounded to nearest-even bf16). Split K and the partial-tile
+// epilogue are those of the kernel above (a partial tile is the block's 128
+// kWi x 64 fp32 values); the partial tiles and counters are indexed by the
+// grid tile, so the matrices of a group share them.
 // ---------------------------------------------------------------------------
 // Load step `step` (clamped to the block's last: every slot issues the same
 // loads, so the in-order wait counts stay exact; re-read steps are never
@@ -297,9 +305,9 @@ __global__ __launch_bounds__(256) void gemm_q4_k_kernel(const uint8_t* __restric
     const int st_ = GQK_GDB_STEP_CLAMP(step);                                                   \
     const uint8_t* sb_ = wrow + (int64_t)(st_ >> 2) * kQ4KBlockBytes;                           \
     h##G = *reinterpret_cast<const uint4*>(sb_);                                                \
-    const uint4* q_ = reinterpret_cast<const uint4*>(sb_ + 16 + 32 * (st_ & 3));                \
+    const uint4* q_ = reinterpret_cast<const uint4*>(sb_ + 16 + 32 * (st_ & 3) + qpart);        \
     qa##G = q_[0];                                                                              \
-    qb##G = q_[1];                                                                              \
+    if constexpr (kWi == 2) qb##G = q_[1];                                                      \
   } while (0)
 
 // Decodes X register set S and W register set G, a step of nibble group G (a
@@ -310,12 +318,12 @@ __global__ __launch_bounds__(256) void gemm_q4_k_kernel(const uint8_t* __restric
 // between the MFMAs.
 #define GQK_GDB_DECODE(S, G, BUF)                                                               \
   do {                                                                                          \
-    uint8_t* xs_ = lds + (BUF) * kGdbStage;                                                     \
-    uint8_t* ws_ = xs_ + kGemmBM * kGdbRow;                                                     \
-    *reinterpret_cast<uint4*>(xs_ + (xr + 0) * kGdbRow + 16 * xc) = x##S##0;                    \
-    *reinterpret_cast<uint4*>(xs_ + (xr + 32) * kGdbRow + 16 * xc) = x##S##1;                   \
-    *reinterpret_cast<uint4*>(xs_ + (xr + 64) * kGdbRow + 16 * xc) = x##S##2;                   \
-    *reinterpret_cast<uint4*>(xs_ + (xr + 96) * kGdbRow + 16 * xc) = x##S##3;                   \
+    uint8_t* xs_ = lds + (BUF) * kStage;                                                        \
+    uint8_t* ws_ = xs_ + kBM * kGdbRow;                                                         \
+    *reinterpret_cast<uint4*>(xs_ + (xr + 0 * kXRows) * kGdbRow + 16 * xc) = x##S##0;           \
+    *reinterpret_cast<uint4*>(xs_ + (xr + 1 * kXRows) * kGdbRow + 16 * xc) = x##S##1;           \
+    *reinterpret_cast<uint4*>(xs_ + (xr + 2 * kXRows) * kGdbRow + 16 * xc) = x##S##2;           \
+    *reinterpret_cast<uint4*>(xs_ + (xr + 3 * kXRows) * kGdbRow + 16 * xc) = x##S##3;           \
     const uint32_t b_ = 8u * (2u * (uint32_t)((G) & 1) + (uint32_t)half);                       \
     const uint32_t s0_ = (h##G.y >> b_) & 0xFFu, s4_ = (h##G.z >> b_) & 0xFFu;                  \
     const uint32_t s8_ = (h##G.w >> b_) & 0xFFu;                                                \
@@ -323,19 +331,26 @@ __global__ __launch_bounds__(256) void gemm_q4_k_kernel(const uint8_t* __restric
     const uint32_t mm_ = (G) >= 2 ? ((s8_ >> 4) | ((s4_ >> 6) << 4)) : (s4_ & 63u);             \
     const float dl_ = half_lo(h##G.x) * (float)sc_;                                             \
     const float ml_ = half_hi(h##G.x) * (float)mm_;                                             \
-    const uint4 qa_ = qa##G, qb_ = qb##G;                                                         \
-    const uint32_t qw_[8] = {qa_.x, qa_.y, qa_.z, qa_.w, qb_.x, qb_.y, qb_.z, qb_.w};           \
-    uint32_t o_[16];                                                                            \
-    _Pragma("unroll") for (int t_ = 0; t_ < 8; ++t_) {                                          \
+    uint32_t qw_[kQWords];                                                                      \
+    qw_[0] = qa##G.x;                                                                           \
+    qw_[1] = qa##G.y;                                                                           \
+    qw_[2] = qa##G.z;                                                                           \
+    qw_[3] = qa##G.w;                                                                           \
+    if constexpr (kWi == 2) {                                                                   \
+      qw_[4 % kQWords] = qb##G.x;                                                               \
+      qw_[5 % kQWords] = qb##G.y;                                                               \
+      qw_[6 % kQWords] = qb##G.z;                                                               \
+      qw_[7 % kQWords] = qb##G.w;                                                               \
+    }                                                                                           \
+    uint32_t o_[2 * kQWords];                                                                   \
+    _Pragma("unroll") for (int t_ = 0; t_ < kQWords; ++t_) {                                    \
       const uint32_t n4_ = opaque((qw_[t_] >> nsh) & 0x0F0F0F0Fu);                              \
       o_[2 * t_] = pack_bf16x2(fmaf(dl_, ubyte0(n4_), -ml_), fmaf(dl_, ubyte1(n4_), -ml_));      \
       o_[2 * t_ + 1] = pack_bf16x2(fmaf(dl_, ubyte2(n4_), -ml_), fmaf(dl_, ubyte3(n4_), -ml_));  \
     }                                                                                           \
-    uint4* wd_ = reinterpret_cast<uint4*>(ws_ + ld_row * kGdbRow + 64 * half);                  \
-    wd_[0] = make_uint4(o_[0], o_[1], o_[2], o_[3]);                                            \
-    wd_[1] = make_uint4(o_[4], o_[5], o_[6], o_[7]);                                            \
-    wd_[2] = make_uint4(o_[8], o_[9], o_[10], o_[11]);                                          \
-    wd_[3] = make_uint4(o_[12], o_[13], o_[14], o_[15]);                                        \
+    uint4* wd_ = reinterpret_cast<uint4*>(ws_ + ld_row * kGdbRow + 64 * half + 2 * qpart);      \
+    _Pragma("unroll") for (int t_ = 0; t_ < kQWords / 2; ++t_)                                  \
+      wd_[t_] = make_uint4(o_[4 * t_], o_[4 * t_ + 1], o_[4 * t_ + 2], o_[4 * t_ + 3]);          \
   } while (0)
 
 // Up to four Q4_K matrices of one X (q, k, v; gate, up) in one launch: their
@@ -351,26 +366,51 @@ struct GemmGroup {
 
 constexpr int kGdbBK = 64;                                   // k per step
 constexpr int kGdbRow = kGdbBK * 2 + 16;                     // 144-byte LDS rows (36 dwords)
-constexpr int kGdbStage = (kGemmBM + kGemmBN) * kGdbRow;     // one buffer: X rows, then W rows
+// tokens per block and fp32 values per partial tile of the kWi shape
+constexpr int gdb_bm(int wi) { return 64 * wi; }
+constexpr int64_t gdb_tile_floats(int wi) { return (int64_t)gdb_bm(wi) * kGemmBN; }
 
-__global__ __launch_bounds__(256) void gemm_q4_k_db_kernel(GemmGroup G, const uint16_t* __restrict__ X,
-                                                           int64_t n_tokens, int nsb, float* partials,
-                                                           int* counters) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kGdbStage];
+// Grid: one dimension. Blocks [0, nfull) take grid tiles 0 .. nfull - 1 over
+// all of K; the later tiles are split into nsplit K ranges, range-major:
+// block nfull + j nt + i takes K range j of tile nfull + i (nt split tiles),
+// so that the blocks of one range of neighbouring tiles run together (taking
+// a tile's ranges together ran the 128-token down and output GEMMs 7 and 4 us
+// slower). A grid tile is (row tile t % gx, token tile t / gx). The host
+// splits only the tiles past the last whole round of blocks, so that they
+// fill one short round instead of a mostly idle full one.
+template <int kWi>
+__global__ __launch_bounds__(128 * kWi) void gemm_q4_k_db_kernel(GemmGroup G, const uint16_t* __restrict__ X,
+                                                                 int64_t n_tokens, int nsb, int gx, int nfull,
+                                                                 int nsplit, float* partials, int* counters) {
+  static_assert(kWi == 2 || kWi == 4, "128 or 256 tokens per block");
+  constexpr int kBM = gdb_bm(kWi);                       // tokens per block
+  constexpr int kThreads = 128 * kWi;
+  constexpr int kStage = (kBM + kGemmBN) * kGdbRow;      // one buffer: X rows, then W rows
+  constexpr int kXRows = kThreads / 8;                   // token rows per X copy round
+  constexpr int kQWords = 16 / kWi;                      // nibble words a thread decodes per step
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
   __shared__ int last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wi = wave >> 1, wj = wave & 1;
-  // this block's matrix and its row tile
-  const int bx = (int)blockIdx.x;
+  // this block's grid tile and K range
+  const int b = (int)blockIdx.x;
+  const bool whole = b < nfull;
+  const int ntr = ((int)gridDim.x - nfull) / nsplit;
+  const int nt = ntr > 0 ? ntr : 1;                   // split tiles (none: 1, unused)
+  const int q = b - nfull;
+  const int qs = whole ? 0 : q / nt;
+  const int tile = whole ? b : nfull + (q - qs * nt);
+  const int S = whole ? 1 : nsplit, split = qs;
+  const int bx = tile % gx, by = tile / gx;
+  // its matrix and row tile
   const int m = (G.n > 1 && bx >= G.tile_begin[1]) + (G.n > 2 && bx >= G.tile_begin[2]) +
                 (G.n > 3 && bx >= G.tile_begin[3]);
   const uint8_t* const W = m == 0 ? G.W[0] : m == 1 ? G.W[1] : m == 2 ? G.W[2] : G.W[3];
   uint16_t* const Y = m == 0 ? G.Y[0] : m == 1 ? G.Y[1] : m == 2 ? G.Y[2] : G.Y[3];
   const int64_t rows = m == 0 ? G.rows[0] : m == 1 ? G.rows[1] : m == 2 ? G.rows[2] : G.rows[3];
   const int tb = m == 0 ? G.tile_begin[0] : m == 1 ? G.tile_begin[1] : m == 2 ? G.tile_begin[2] : G.tile_begin[3];
-  const int64_t n0 = (int64_t)blockIdx.y * kGemmBM;
+  const int64_t n0 = (int64_t)by * kBM;
   const int64_t r0 = (int64_t)(bx - tb) * kGemmBN;
-  const int S = (int)gridDim.z, split = (int)blockIdx.z;
   const int64_t K = (int64_t)nsb * kQ4KBlockWeights;
   const int64_t row_bytes = (int64_t)nsb * kQ4KBlockBytes;
   // this block's steps: super-blocks [nsb * split / S, nsb * (split + 1) / S), 4 steps each
@@ -378,35 +418,42 @@ __global__ __launch_bounds__(256) void gemm_q4_k_db_kernel(GemmGroup G, const ui
   const int step_end = 4 * (int)((int64_t)nsb * (split + 1) / S);
 
   // X: thread t copies the 16 bytes at k 8 xc .. 8 xc + 7 of the step of
-  // token rows xr + 32 j, j = 0..3 (a wave reads 8 whole 128-byte row
-  // slices). W: thread t decodes sub-block 2 g + half of weight row ld_row.
-  // Rows past the end are clamped (read, never stored).
+  // token rows xr + kXRows j, j = 0..3 (a wave reads 8 whole 128-byte row
+  // slices). W: kWi threads per weight row ld_row; thread t decodes nibble
+  // half `half` (sub-block 2 g + half) of the group's bytes [qpart, qpart +
+  // 32 / (kWi / 2)). Rows past the end are clamped (read, never stored).
   const int xc = tid & 7, xr = tid >> 3;
   uint32_t xoff[4];   // byte offsets (the host keeps X below 4 GiB for this kernel)
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int64_t n = n0 + xr + 32 * j;
+    const int64_t n = n0 + xr + kXRows * j;
     xoff[j] = (uint32_t)(((n < n_tokens ? n : n_tokens - 1) * K + 8 * xc) * 2);
   }
-  const int ld_row = tid >> 1, half = tid & 1;
+  const int ld_row = tid / kWi;
+  const int half = (tid / (kWi / 2)) & 1;
+  const int qpart = kWi == 2 ? 0 : 16 * (tid & 1);
   const int64_t wr = (r0 + ld_row) < rows ? (r0 + ld_row) : (rows - 1);
   const uint8_t* wrow = W + wr * row_bytes;
   const uint32_t nsh = 4u * (uint32_t)half;   // low (half 0) or high nibbles
 
-  // Register sets of raw step bytes: X (16 bytes of token rows xr + 32 j),
-  // sets A and B; W (the super-block header and the group's 32 nibble bytes),
+  // Register sets of raw step bytes: X (16 bytes of token rows xr + kXRows j),
+  // sets A and B; W (the super-block header and the thread's nibble bytes),
   // sets 0..3 by nibble group. Named variables (arrays captured by helpers
   // stayed in scratch memory).
   uint4 xA0, xA1, xA2, xA3, xB0, xB1, xB2, xB3;
   uint4 h0, qa0, qb0, h1, qa1, qb1, h2, qa2, qb2, h3, qa3, qb3;
+  (void)qb0;
+  (void)qb1;
+  (void)qb2;
+  (void)qb3;
   const uint8_t* const xbase = reinterpret_cast<const uint8_t*>(X);
 
   f32x16 acc00, acc01, acc10, acc11;
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc00[e] = acc01[e] = acc10[e] = acc11[e] = 0.f;
   auto mfma_step = [&](int buf) {
-    const uint8_t* xs = lds + buf * kGdbStage;
-    const uint8_t* ws = xs + kGemmBM * kGdbRow;
+    const uint8_t* xs = lds + buf * kStage;
+    const uint8_t* ws = xs + kBM * kGdbRow;
 #pragma unroll
     for (int kk = 0; kk < kGdbBK; kk += 16) {
       const int kb = (kk + 8 * (lane >> 5)) * 2;
@@ -469,9 +516,10 @@ __global__ __launch_bounds__(256) void gemm_q4_k_db_kernel(GemmGroup G, const ui
     return;
   }
 
-  const int64_t tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-  const int64_t ntiles = (int64_t)gridDim.x * gridDim.y;
-  float* mine = partials + ((int64_t)split * ntiles + tile) * kGemmTileFloats;
+  // partial tiles and counters of the split tiles only, indexed from nfull
+  const int64_t st = tile - nfull;
+  const int64_t ntiles = nt;
+  float* mine = partials + ((int64_t)split * ntiles + st) * gdb_tile_floats(kWi);
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     __hip_atomic_store(gemm_partial_slot(mine, wave, 0, 0, e, lane), acc00[e], __ATOMIC_RELAXED,
@@ -489,15 +537,16 @@ __global__ __launch_bounds__(256) void gemm_q4_k_db_kernel(GemmGroup G, const ui
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
   if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(&counters[tile * kGemmCounterStride], 1,
+    const int old = __hip_atomic_fetch_add(&counters[st * kGemmCounterStride], 1,
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     last = old == S - 1;
   }
   __syncthreads();
   if (!last) return;
-  gemm_sum_partials(partials, ntiles, tile, S, wave, lane, Y, n_tokens, rows, n0, r0, wi, wj);
+  gemm_sum_partials(partials, ntiles, st, gdb_tile_floats(kWi), S, wave, lane, Y, n_tokens, rows, n0, r0, wi,
+                    wj);
   if (tid == 0)
-    __hip_atomic_store(&counters[tile * kGemmCounterStride], 0, __ATOMIC_RELAXED,
+    __hip_atomic_store(&counters[st * kGemmCounterStride], 0, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 

@@ -796,7 +796,6 @@ static int matmul_q4_k_group(const void* const* W, uint16_t* const* Y, const int
     }
   }
   if (n_tokens == 0) return GGUF_QK_OK;
-  const int64_t gy = (n_tokens + kGemmBM - 1) / kGemmBM;
   GemmGroup G{};
   int64_t gx = 0;
   for (int m = 0; m < n; ++m) {
@@ -810,38 +809,87 @@ static int matmul_q4_k_group(const void* const* W, uint16_t* const* Y, const int
     if (gx > INT32_MAX) return GGUF_QK_ERR_LIMIT;
   }
   if (G.n == 0) return GGUF_QK_OK;
-  if (gy > 65535) return GGUF_QK_ERR_LIMIT;
   ScratchArea* scratch = nullptr;
   int st = stream_scratch(stream, &scratch);
   if (st) return st;
+  const int64_t nsb = cols / kQ4KBlockWeights;
   // Split K over whole super-blocks when there are too few tiles to fill the
-  // device, as far as the scratch for the fp32 partial tiles allows.
-  // Measured on the 2048-hidden shapes: long K (down, 43 super-blocks) gains
-  // from up to 8 ranges and two blocks per CU; short K (8 super-blocks) from
-  // at most 4 ranges and one block per CU, past which the last block's sum
-  // over the partial tiles costs more than the extra blocks save.
-  const int64_t tiles = gx * gy, nsb = cols / kQ4KBlockWeights;
+  // device, as far as the scratch for the fp32 partial tiles allows; the
+  // split is then evened out (the fewest ranges that give the same longest
+  // range). `target` blocks, at most `max_split` ranges.
+  auto split_for = [&](int64_t tiles, int64_t tile_floats, int64_t target, int64_t max_split) {
+    int64_t S = target / tiles;
+    if (S > max_split) S = max_split;
+    if (S > nsb) S = nsb;
+    while (S > 1 && S * tiles * tile_floats > kGemmScratchFloats) --S;
+    if (S < 1 || tiles > kGemmMaxTiles) S = 1;
+    if (S > 1) {
+      const int64_t per = (nsb + S - 1) / S;
+      S = (nsb + per - 1) / per;
+    }
+    return S;
+  };
+  // Measured on the 2048-hidden shapes with 128-token blocks (one block per
+  // CU: 288 registers a lane): about one round of blocks, K split into at
+  // most 8 (long K: down, 43 super-blocks) or 4 (short K: 8 super-blocks)
+  // ranges; down took 2 us less in one round of 4 ranges than in two rounds
+  // of 8, and short K slows past 4 ranges, where the last block's sum over
+  // the partial tiles costs more than the extra blocks save.
   const bool long_k = nsb >= 32;
-  const int64_t target = tuning().gemm_blocks ? tuning().gemm_blocks : (long_k ? 512 : 256);
+  const int64_t target = tuning().gemm_blocks ? tuning().gemm_blocks : 256;
   const int64_t max_split = tuning().gemm_max_split ? tuning().gemm_max_split : (long_k ? 8 : 4);
-  int64_t S = target / tiles;
-  if (S > max_split) S = max_split;
-  if (S > nsb) S = nsb;
-  while (S > 1 && S * tiles * kGemmTileFloats > kGemmScratchFloats) --S;
-  if (S < 1 || tiles > kGemmMaxTiles) S = 1;
   if (tuning().gemm_db && xb < (int64_t(1) << 32)) {   // 32-bit X offsets
-    hipLaunchKernelGGL(gemm_q4_k_db_kernel, dim3((unsigned)gx, (unsigned)gy, (unsigned)S), dim3(256), 0,
-                       stream, G, X, n_tokens, (int)nsb, scratch->gemm_partials, scratch->gemm_counters);
-    return launch_status();
+    // Tiles [0, nfull) over all of K, the rest split S ways; the fp32 partial
+    // tiles of the split ones must fit the scratch.
+    auto launch_db = [&](auto kernel, int threads, int64_t tiles, int64_t nfull, int64_t S, int64_t tile_floats) {
+      while (S > 1 && ((tiles - nfull) * S * tile_floats > kGemmScratchFloats || tiles - nfull > kGemmMaxTiles)) --S;
+      if (S <= 1) {
+        S = 1;
+        nfull = tiles;
+      }
+      const int64_t blocks = nfull + (tiles - nfull) * S;
+      if (blocks > INT32_MAX) return (int)GGUF_QK_ERR_LIMIT;
+      hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, G, X, n_tokens, (int)nsb,
+                         (int)gx, (int)nfull, (int)S, scratch->gemm_partials, scratch->gemm_counters);
+      return launch_status();
+    };
+    // The K ranges for tiles that would otherwise leave the device partly
+    // idle: as many as fill `slots` blocks (at most max_split, at most one
+    // super-block each), then evened out (the fewest ranges with the same
+    // longest range).
+    auto even_split = [&](int64_t tiles, int64_t slots) {
+      int64_t S = slots / (tiles > 0 ? tiles : 1);
+      if (S > max_split) S = max_split;
+      if (S > nsb) S = nsb;
+      if (S < 1) S = 1;
+      const int64_t per = (nsb + S - 1) / S;
+      return (nsb + per - 1) / per;
+    };
+    // 256-token blocks (half the weight decoding per MFMA of 128-token ones)
+    // where they give at least a block per CU unsplit: whole rounds of one
+    // block per CU (a 110 KB LDS tile) take all of K, and the tiles past the
+    // last whole round are split so that they fill one short round instead
+    // of a mostly idle full one (the prefill gate/up launch: 344 tiles, 256
+    // whole + 88 split in two, 1.5 rounds of a whole tile's time instead of 2)
+    const int64_t gy4 = (n_tokens + gdb_bm(4) - 1) / gdb_bm(4);
+    const int64_t slots = tuning().gemm_wide_target;
+    if (tuning().gemm_wide && n_tokens > gdb_bm(2) && gx * gy4 >= tuning().gemm_wide_tiles) {
+      const int64_t tiles = gx * gy4;
+      const int64_t nfull = tiles >= slots ? tiles / slots * slots : 0;
+      return launch_db(gemm_q4_k_db_kernel<4>, 512, tiles, nfull, even_split(tiles - nfull, slots),
+                       gdb_tile_floats(4));
+    }
+    // 128-token blocks: every tile split alike
+    const int64_t gy = (n_tokens + gdb_bm(2) - 1) / gdb_bm(2);
+    const int64_t S = split_for(gx * gy, gdb_tile_floats(2), target, max_split);
+    return launch_db(gemm_q4_k_db_kernel<2>, 256, gx * gy, S > 1 ? 0 : gx * gy, S, gdb_tile_floats(2));
   }
+  const int64_t gy = (n_tokens + kGemmBM - 1) / kGemmBM;
+  if (gy > 65535) return GGUF_QK_ERR_LIMIT;
   // the single-buffered kernel, one launch per matrix (its own split)
   for (int m = 0; m < G.n; ++m) {
     const int64_t gxm = (G.rows[m] + kGemmBN - 1) / kGemmBN, tm = gxm * gy;
-    int64_t Sm = target / tm;
-    if (Sm > max_split) Sm = max_split;
-    if (Sm > nsb) Sm = nsb;
-    while (Sm > 1 && Sm * tm * kGemmTileFloats > kGemmScratchFloats) --Sm;
-    if (Sm < 1 || tm > kGemmMaxTiles) Sm = 1;
+    const int64_t Sm = split_for(tm, kGemmTileFloats, target, max_split);
     hipLaunchKernelGGL(gemm_q4_k_kernel, dim3((unsigned)gxm, (unsigned)gy, (unsigned)Sm), dim3(256), 0,
                        stream, G.W[m], X, G.Y[m], n_tokens, G.rows[m], (int)nsb, scratch->gemm_partials,
                        scratch->gemm_counters);

@@ -14,7 +14,7 @@ namespace gqk {
 // batch shapes).
 struct Tuning {
   int target_tasks = 2048;   // wave tasks a split-K GEMV aims for
-  int gemm_blocks = 0;       // blocks a prefill GEMM aims for (0: by K, see gguf_qmatmul_q4_k)
+  int gemm_blocks = 0;       // blocks a split prefill GEMM aims for (0: 256, one per CU)
   int gemm_max_split = 0;    // largest K split of a prefill GEMM (0: by K)
   int sb_blocks = 512;       // blocks a small-batch product aims for
   int sb_max_split = 8;      // largest K split of a small-batch product
@@ -34,6 +34,9 @@ struct Tuning {
   int q8_0_lk = 1;           // Q8_0 rows of 256 .. 4096 weights: lanes-along-K kernels
   int q6_k_lk = 1;           // Q6_K rows of 256 .. 12288 weights: lanes-along-K kernels
   int gemm_db = 1;           // prefill: the double-buffered GEMM
+  int gemm_wide = 1;         // prefill: 256-token blocks where they fill the device
+  int gemm_wide_tiles = 256; // ... i.e. give at least this many tiles unsplit
+  int gemm_wide_target = 256;  // 256-token blocks resident at once (one per CU)
 };
 
 inline const Tuning& tuning() {

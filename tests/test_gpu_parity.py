@@ -483,11 +483,14 @@ def test_batch_in_hip_graph_replays_match_eager():
 # (Each token's output over a matrix is one vector of the floored metric; a
 # matrix of one row would make that floor the value itself.)
 @pytest.mark.parametrize("n,rows", [(512, (2048, 512, 512)), (100, (200, 129, 1000)), (64, (11008, 11008)),
-                                    (129, (65,)), (512, (300, 0, 700, 128))])
+                                    (129, (65,)), (512, (300, 0, 700, 128)), (512, (11008, 11008)),
+                                    (300, (16384 + 77,))])
 def test_matmul_multi_matches_oracle(n, rows):
     """Up to four matrices of one X in one launch (q/k/v and gate/up shapes,
     ragged row counts, a matrix of no rows): each Y against the oracle within
-    the bf16 bar."""
+    the bf16 bar. The prefill gate/up launch (512 tokens, 2 x 11008 rows) and
+    300 tokens over 16461 rows have enough row tiles for 256-token blocks; the
+    latter's second token tile is ragged (44 tokens)."""
     rng = synth.rng_for(19, n, len(rows))
     cols = 2048
     ws = [synth.q4_k_weights(rng, r, cols) if r else np.zeros((0, cols // 256 * 144), np.uint8)
