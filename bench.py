@@ -63,7 +63,7 @@ PROFILES = {
               ["gemv_lk.hpp", "device_common.hpp", "lk.hip", "lk_typed.hip"]),
     "small_batch": ("small_batch_traffic.md",
                     ["gemv_sbw.hpp", "gemv_small_batch.hpp", "device_common.hpp", "gguf_qk.hip"]),
-    "prefill": ("gemm_q4_k_db_kernel_prefill_mfma.md", ["gemm.hpp", "device_common.hpp", "gguf_qk.hip"]),
+    "prefill": ("gemm_q4_k_db_kernel_prefill_mfma.md", ["gemm.hpp", "device_common.hpp", "gguf_qk.hip", "launch.hpp"]),
 }
 SMALL_BATCH_TOKENS = (8, 32, 64)
 
