@@ -378,8 +378,12 @@ constexpr int64_t gdb_tile_floats(int wi) { return (int64_t)gdb_bm(wi) * kGemmBN
 // slower). A grid tile is (row tile t % gx, token tile t / gx). The host
 // splits only the tiles past the last whole round of blocks, so that they
 // fill one short round instead of a mostly idle full one.
+// (The 256-token instance is held to two waves per SIMD explicitly: with the
+// hint the compiler allocates 193 registers instead of 229, and the gate/up
+// launch ran 67.0 against 69.2 us in a trace, 70.4 against 71.7 alone; the
+// 128-token instance, one wave per SIMD at 288 registers, spills under it.)
 template <int kWi>
-__global__ __launch_bounds__(128 * kWi) void gemm_q4_k_db_kernel(GemmGroup G, const uint16_t* __restrict__ X,
+__global__ __launch_bounds__(128 * kWi, kWi == 4 ? 2 : 1) void gemm_q4_k_db_kernel(GemmGroup G, const uint16_t* __restrict__ X,
                                                                  int64_t n_tokens, int nsb, int gx, int nfull,
                                                                  int nsplit, float* partials, int* counters) {
   static_assert(kWi == 2 || kWi == 4, "128 or 256 tokens per block");
