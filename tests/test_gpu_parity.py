@@ -347,10 +347,13 @@ def _matmul_case(n, rows, cols, seed):
 @pytest.mark.parametrize("n,rows,cols", [(512, 256, 512), (1, 200, 256), (100, 129, 768),
                                          (129, 300, 2048), (512, 2048, 2048), (512, 512, 2048),
                                          (512, 2048, 11008), (512, 11008, 2048),
-                                         (64, 128, 7 * 256)])
+                                         (64, 128, 7 * 256), (129, 33000, 256), (512, 16684, 768)])
 def test_matmul_q4_k(n, rows, cols):
     """Includes the prefill shapes at N = 512 and a K of 7 super-blocks, which
-    the K split cuts into unequal ranges."""
+    the K split cuts into unequal ranges. The last two take 256-token blocks:
+    129 tokens over 258 row tiles of one super-block (127 token rows of the
+    tile past the end, every tile whole), and 512 tokens over 262 tiles of
+    three super-blocks (256 whole, the last 6 split into three ranges)."""
     Y, ref = _matmul_case(n, rows, cols, 12)
     e, ok = oracle.floored_rel_err(Y, ref)
     say("err", e)
