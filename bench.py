@@ -370,33 +370,43 @@ def fused_layer_pass(torch, g, synth, entries, stream, reps=10):
     norms = [(torch.rand(H, generator=gen) + 0.5).to(dev) for _ in range(2 * len(layers))]
     e_ = lambda n: torch.empty(n, dtype=torch.float32, device=dev)
     h0 = torch.randn(H, generator=gen).to(dev)
-    # fused
-    hw, ss = e_(H), e_(H // 64)
-    ents, eps, h = [], [], h0
-    for li, L in enumerate(layers):
-        st = 4 * li
-        q, k, v = e_(H), e_(KV), e_(KV)
-        h1, hw2, ss2, gg, uu, act = e_(H), e_(H), e_(H // 64), e_(F), e_(F), e_(F)
-        h2, hw3, ss3 = e_(H), e_(H), e_(H // 64)
-        for name, y in (("q", q), ("k", k), ("v", v)):
-            ents.append((g.TYPE_Q4_K, L[name], hw, y, st))
-            eps.append({"scale_ss": ss, "eps": EPS})
-        ents.append((g.TYPE_Q4_K, L["o"], q, h1, st + 1))
-        eps.append({"residual": h, "norm_w": norms[2 * li + 1], "norm_out": hw2, "ss_out": ss2})
-        ents.append((g.TYPE_Q4_K, L["gate"], hw2, gg, st + 2))
-        eps.append({"scale_ss": ss2, "eps": EPS, "pair": 1, "act": act})
-        ents.append((g.TYPE_Q4_K, L["up"], hw2, uu, st + 2))
-        eps.append({"scale_ss": ss2, "eps": EPS, "pair": 2, "act": act})
-        nxt = norms[2 * (li + 1)] if li + 1 < len(layers) else norms[0]
-        ents.append((g.TYPE_Q4_K, L["down"], act, h2, st + 3))
-        eps.append({"residual": h1, "norm_w": nxt, "norm_out": hw3, "ss_out": ss3})
-        h, hw, ss = h2, hw3, ss3
-    fb = g.GemvBatch(ents, eps)
-    hw0, ss0 = ents[0][2], eps[0]["scale_ss"]
+    # fused: each RMSN scale from the producer's partial sums of squares
+    # (mode "ss": ss_out -> scale_ss) or from the producer's output itself
+    # (mode "v": scale_v, no ss_out and no row-group completion)
+    def build_fused(mode):
+        hw, ss = e_(H), e_(H // 64)
+        ents, eps, h = [], [], h0
+        for li, L in enumerate(layers):
+            st = 4 * li
+            q, k, v = e_(H), e_(KV), e_(KV)
+            h1, hw2, ss2, gg, uu, act = e_(H), e_(H), e_(H // 64), e_(F), e_(F), e_(F)
+            h2, hw3, ss3 = e_(H), e_(H), e_(H // 64)
+            sc = {"scale_ss": ss, "eps": EPS} if mode == "ss" else {"scale_v": h, "eps": EPS}
+            for name, y in (("q", q), ("k", k), ("v", v)):
+                ents.append((g.TYPE_Q4_K, L[name], hw, y, st))
+                eps.append(dict(sc))
+            ents.append((g.TYPE_Q4_K, L["o"], q, h1, st + 1))
+            eps.append({"residual": h, "norm_w": norms[2 * li + 1], "norm_out": hw2,
+                        **({"ss_out": ss2} if mode == "ss" else {})})
+            sc2 = {"scale_ss": ss2, "eps": EPS} if mode == "ss" else {"scale_v": h1, "eps": EPS}
+            ents.append((g.TYPE_Q4_K, L["gate"], hw2, gg, st + 2))
+            eps.append({**sc2, "pair": 1, "act": act})
+            ents.append((g.TYPE_Q4_K, L["up"], hw2, uu, st + 2))
+            eps.append({**sc2, "pair": 2, "act": act})
+            nxt = norms[2 * (li + 1)] if li + 1 < len(layers) else norms[0]
+            ents.append((g.TYPE_Q4_K, L["down"], act, h2, st + 3))
+            eps.append({"residual": h1, "norm_w": nxt, "norm_out": hw3,
+                        **({"ss_out": ss3} if mode == "ss" else {})})
+            h, hw, ss = h2, hw3, ss3
+        fb = g.GemvBatch(ents, eps)
+        hw0, ss0 = ents[0][2], e_(H // 64) if mode == "v" else eps[0]["scale_ss"]
 
-    def fused():
-        g.gguf_rmsnorm_prep_f32(h0, norms[0], hw0, ss0, stream=stream)
-        g.gguf_qmatvec_batch(fb, stream)
+        def fused():
+            g.gguf_rmsnorm_prep_f32(h0, norms[0], hw0, ss0, stream=stream)
+            g.gguf_qmatvec_batch(fb, stream)
+        return fused
+
+    fused, fused_v = build_fused("ss"), build_fused("v")
 
     # unfused: plain grouped GEMV steps with standalone steps between them
     plan, h = [], h0
@@ -424,10 +434,13 @@ def fused_layer_pass(torch, g, synth, entries, stream, reps=10):
             g.gguf_add_f32(h1, d, h2, stream=stream)
 
     out = {"label": f"{len(layers)} decode layers (Q4_K, SmolLM3-3B shapes) with RMSN, SiLU(gate)*up "
-                    "and the residual adds; attention stood in by q (not measured); HIP graphs",
+                    "and the residual adds; attention stood in by q (not measured); HIP graphs; fused: "
+                    "RMSN scales from the producers' partial sums (ss_out), fused_scale_v: from the "
+                    "producers' output vectors (scale_v)",
            "layers": len(layers)}
     wbytes = sum(e[1].numel() for e in q4)
-    for name, fn, launches in (("fused", fused, 4 * len(layers) + 1), ("unfused", unfused, 9 * len(layers))):
+    for name, fn, launches in (("fused", fused, 4 * len(layers) + 1), ("fused_scale_v", fused_v, 4 * len(layers) + 1),
+                               ("unfused", unfused, 9 * len(layers))):
         graph = capture(torch, fn, stream)
         t = time_replays(torch, graph, stream, reps)
         ms = sorted(t)[len(t) // 2]

@@ -448,7 +448,8 @@ class GemvEpEntry(ctypes.Structure):
     """struct gguf_qk_gemv_ep of the C ABI."""
     _fields_ = [("scale_ss", ctypes.c_void_p), ("scale_n", ctypes.c_int64), ("eps", ctypes.c_float),
                 ("pair", ctypes.c_int32), ("residual", ctypes.c_void_p), ("norm_w", ctypes.c_void_p),
-                ("norm_out", ctypes.c_void_p), ("ss_out", ctypes.c_void_p), ("act", ctypes.c_void_p)]
+                ("norm_out", ctypes.c_void_p), ("ss_out", ctypes.c_void_p), ("act", ctypes.c_void_p),
+                ("scale_v", ctypes.c_void_p)]
 
 
 def _opt(t, name):
@@ -461,8 +462,8 @@ class GemvBatch:
 
     `epilogues` (optional, one per entry, None for none) are dicts with the
     gguf_qk_gemv_ep fields as keys (scale_ss, eps, pair, residual, norm_w,
-    norm_out, ss_out, act; tensors for the vectors); the batch then runs through
-    gguf_qmatvec_batch_ep."""
+    norm_out, ss_out, act, scale_v; tensors for the vectors); the batch then
+    runs through gguf_qmatvec_batch_ep."""
 
     # floats each epilogue vector holds at least, for an entry of `rows` rows
     # (the C ABI takes these pointers without lengths)
@@ -473,12 +474,15 @@ class GemvBatch:
         if epilogues is not None:
             if len(epilogues) != len(entries):
                 raise ValueError("one epilogue (or None) per entry")
-            for (_, _, _, y, _), e in zip(entries, epilogues):
+            for (_, _, x, y, _), e in zip(entries, epilogues):
                 for key, need in self._EP_SIZES.items():
                     t = (e or {}).get(key)
                     if t is not None and t.numel() < need(y.numel()):
                         raise ValueError(f"epilogue {key} holds {t.numel()} floats, the entry needs "
                                          f"{need(y.numel())}")
+                v = (e or {}).get("scale_v")
+                if v is not None and v.numel() < x.numel():
+                    raise ValueError(f"epilogue scale_v holds {v.numel()} floats, the entry needs {x.numel()}")
         self._keep = []
         arr = (GemvEntry * len(entries))()
         for i, (type_id, W, x, y, stage) in enumerate(entries):
@@ -500,7 +504,7 @@ class GemvBatch:
                                     float(e.get("eps", 0.0)), int(e.get("pair", 0)),
                                     _opt(e.get("residual"), "residual"), _opt(e.get("norm_w"), "norm_w"),
                                     _opt(e.get("norm_out"), "norm_out"), _opt(e.get("ss_out"), "ss_out"),
-                                    _opt(e.get("act"), "act"))
+                                    _opt(e.get("act"), "act"), _opt(e.get("scale_v"), "scale_v"))
                 self._keep.append(tuple(v for v in e.values() if isinstance(v, torch.Tensor)))
             self.ep = ep
 

@@ -296,7 +296,9 @@ __device__ __forceinline__ void finish_rows(const GemvEpilogue& ep, float v, flo
   const bool live = lane < valid;
   const int64_t r = row0 + (live ? lane : 0);
   if (flags & kEpScale) {
-    // the partial sums in order, eight loads in flight at a time
+    // the partial sums (or, kEpScaleV, the squares of v) in order, eight
+    // loads in flight at a time
+    const bool sq = (flags & kEpScaleV) != 0;
     float S = 0.f;
     const int n = ep.scale_n;
     for (int i0 = 0; i0 < n; i0 += 8) {
@@ -305,7 +307,7 @@ __device__ __forceinline__ void finish_rows(const GemvEpilogue& ep, float v, flo
       for (int i = 0; i < 8; ++i) t[i] = ep.scale_ss[(i0 + i) < n ? (i0 + i) : (n - 1)];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        if (i0 + i < n) S += t[i];
+        if (i0 + i < n) S += sq ? t[i] * t[i] : t[i];
     }
     v *= 1.0f / sqrtf(S * ep.inv_k + ep.eps);
   }
@@ -316,8 +318,8 @@ __device__ __forceinline__ void finish_rows(const GemvEpilogue& ep, float v, flo
     else
       y[r] = v;
   }
-  if (flags & kEpNorm) {
-    if (live) ep.norm_out[r] = v * ep.norm_w[r];
+  if ((flags & kEpNorm) && live) ep.norm_out[r] = v * ep.norm_w[r];
+  if (flags & kEpSs) {
     // the square rounded on its own (kept out of the butterfly's first add,
     // which could otherwise take it unrounded as an fma): the same bits as the
     // standalone preparation kernel

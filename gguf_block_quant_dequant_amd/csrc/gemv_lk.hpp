@@ -400,7 +400,7 @@ __device__ __forceinline__ float q40_quarter_dot(const LkLoad& L, const float (&
 struct LkEp {
   GemvEpilogue e;
   float scale;       // input RMSN factor (1 without kEpScale)
-  int gflags;        // group work: kEpNorm or kEpPair (not both), else 0
+  int gflags;        // group work: kEpSs or kEpPair (not both), else 0
 };
 
 // The lane's share of the input RMSN's partial sums (kEpScale; at most 256
@@ -438,13 +438,17 @@ __device__ __forceinline__ float lk_ep_ss_sum(const LkBlock& B, int lane, const 
 }
 
 // The block's epilogue; the scale is 1 / sqrt(S / K + eps) with S the lanes'
-// shares added by a fixed butterfly.
-__device__ __forceinline__ LkEp lk_ep(const GemvEpilogue& e, float ss_share) {
+// shares added by a fixed butterfly, or (kEpScaleV) the block's sum of v^2,
+// formed by the caller.
+__device__ __forceinline__ LkEp lk_ep(const GemvEpilogue& e, float ss_share, float v_total = 0.f) {
   LkEp o;
   o.e = e;
   o.scale = 1.f;
-  o.gflags = (o.e.flags & kEpPairInWave) ? 0 : o.e.flags & (kEpNorm | kEpPair);
-  if (o.e.flags & kEpScale) o.scale = 1.0f / sqrtf(wave_sum_fixed(ss_share) * o.e.inv_k + o.e.eps);
+  o.gflags = (o.e.flags & kEpPairInWave) ? 0 : o.e.flags & (kEpSs | kEpPair);
+  if (o.e.flags & kEpScale) {
+    const float S = (o.e.flags & kEpScaleV) ? v_total : wave_sum_fixed(ss_share);
+    o.scale = 1.0f / sqrtf(S * o.e.inv_k + o.e.eps);
+  }
   return o;
 }
 
@@ -826,11 +830,22 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const GemvEp
   // epilogue comes from argument memory, only they wait for it (the empty asm
   // keeps the scheduler from moving their address work, and with it the
   // wait, above the weight loads)
+  // (kEpScaleV) the thread's float4s of v at x's indices, for the block's
+  // sum of v^2; they read x when the flag is off, so the loads go out on
+  // every path
+  lk_f32x4 vg[kXIt];
   if constexpr (kEp) {
     int f = B.ep_flags, sn = B.scale_n;
     const float* sp = (const float*)B.scale_ss;
     asm volatile("" : "+s"(f), "+s"(sn), "+s"(sp));
     ssl = lk_ep_ss_issue(f, sn, (const GQK_GLOBAL float*)sp, B.x, lane);
+    const GQK_GLOBAL lk_f32x4* const vb =
+        reinterpret_cast<const GQK_GLOBAL lk_f32x4*>((f & kEpScaleV) ? (const GQK_GLOBAL float*)sp : B.x);
+#pragma unroll
+    for (int j = 0; j < kXIt; ++j) {
+      const int i = tid + j * kW * 64;
+      vg[j] = vb[kXF4 % (kW * 64) == 0 || i < kXF4 ? i : 0];
+    }
   }
   tl.stamp(1);
 
@@ -840,12 +855,36 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const GemvEp
     if (kXF4 % (kW * 64) == 0 || i < kXF4)
       *reinterpret_cast<lk_f32x4*>(&xl[lk_x_slot<kType>(i)]) = xg[j];
   }
+  // (kEpScaleV) the block's sum of v^2 in a fixed order: each thread its
+  // float4s in order, the wave's lanes by a fixed butterfly, the waves in
+  // wave order after the barrier
+  __shared__ float lk_vsum[kW];
+  if constexpr (kEp) {
+    float sq = 0.f;
+#pragma unroll
+    for (int j = 0; j < kXIt; ++j) {
+      const int i = tid + j * kW * 64;
+      if (kXF4 % (kW * 64) == 0 || i < kXF4) {
+        sq = fmaf(vg[j].x, vg[j].x, sq);
+        sq = fmaf(vg[j].y, vg[j].y, sq);
+        sq = fmaf(vg[j].z, vg[j].z, sq);
+        sq = fmaf(vg[j].w, vg[j].w, sq);
+      }
+    }
+    const float ws = wave_sum_fixed(sq);
+    if (lane == 0) lk_vsum[tid >> 6] = ws;
+  }
   __syncthreads();
 #pragma unroll
   for (int p = kEarly; p < kDepth; ++p) issue(st0 + p, ring[p]);
   tl.stamp(2);
   LkEp E;
-  if constexpr (kEp) E = lk_ep(epl, lk_ep_ss_sum(B, lane, ssl));
+  if constexpr (kEp) {
+    float vtot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) vtot += lk_vsum[w];
+    E = lk_ep(epl, lk_ep_ss_sum(B, lane, ssl), vtot);
+  }
   if (n > 0) {
 
   float xv[64];

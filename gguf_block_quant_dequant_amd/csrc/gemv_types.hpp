@@ -26,8 +26,11 @@ struct SplitK {
 //              RMSN of the input when x holds v * norm and scale_ss the partial
 //              sums of v^2 (the scalar factor of RMSN moves past the product)
 //  kEpResidual y += residual (the residual add)
-//  kEpNorm     also norm_out = y * norm_w and ss_out[rg] = sum of y^2 over the
-//              row group's rows (fixed butterfly order): the next RMSN's inputs
+//  kEpNorm     also norm_out = y * norm_w: the next RMSN's input
+//  kEpSs       (with kEpNorm) also ss_out[rg] = sum of y^2 over the row group's
+//              rows (fixed butterfly order): the next RMSN's partial sums
+//  kEpScaleV   (with kEpScale) scale_ss is v itself (scale_n = cols floats) and
+//              the kernel forms sum(v^2) in a fixed order
 //  kEpPair     one of a gate/up pair: the second of the pair to finish a row
 //              group writes act = SiLU(gate) * up for it (y stores and the
 //              partner's loads are agent-scope; a counter per row group)
@@ -35,6 +38,7 @@ constexpr int kEpScale = 1, kEpResidual = 2, kEpNorm = 4, kEpPair = 8;
 // A gate/up pair whose rows the lanes-along-K kernel computes in the same
 // wave (the gate's descriptor carries both; set by the host, never by users).
 constexpr int kEpPairInWave = 16;
+constexpr int kEpSs = 32, kEpScaleV = 64;
 
 struct GemvEpilogue {
   const float* scale_ss;

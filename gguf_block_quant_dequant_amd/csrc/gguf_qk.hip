@@ -41,7 +41,6 @@ constexpr int kMaxSplits = 16;                            // K ranges per row gr
 // Prefill split K: fp32 partial tiles (32 MiB) and one counter per tile.
 constexpr int64_t kGemmScratchFloats = int64_t(8) << 20;
 constexpr int64_t kGemmMaxTiles = int64_t(1) << 12;
-constexpr int kGemmMaxSplits = 8;
 // Gate/up pair counters of the fused SiLU(gate) * up epilogue (row groups of
 // the pairs of one step).
 constexpr int64_t kPairCounters = int64_t(1) << 12;
@@ -510,10 +509,20 @@ static int make_epilogue(const gguf_qk_gemv* list, const gguf_qk_gemv_ep* ep, in
   const int64_t RG = (g.rows + 63) / 64;
   auto al4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
   int flags = 0;
+  if (e.scale_ss && e.scale_v) return GGUF_QK_ERR_SHAPE;
   if (e.scale_ss) {
     if (e.scale_n < 1 || e.scale_n > INT32_MAX || !(e.eps >= 0.f) || e.eps > 3.0e38f || !al4(e.scale_ss))
       return GGUF_QK_ERR_SHAPE;
     flags |= kEpScale;
+  }
+  if (e.scale_v) {
+    if (!(e.eps >= 0.f) || e.eps > 3.0e38f || g.cols > INT32_MAX) return GGUF_QK_ERR_SHAPE;
+    if (!aligned16(e.scale_v)) return GGUF_QK_ERR_ALIGN;
+    // v is read while the step runs: no output of the step may overlap it
+    for (int32_t b = 0; b < n; ++b)
+      if (list[b].stage == g.stage && overlap(e.scale_v, g.cols * 4, list[b].y, list[b].rows * 4))
+        return GGUF_QK_ERR_ALIAS;
+    flags |= kEpScale | kEpScaleV;
   }
   if (e.residual) {
     if (!al4(e.residual)) return GGUF_QK_ERR_ALIGN;
@@ -521,14 +530,17 @@ static int make_epilogue(const gguf_qk_gemv* list, const gguf_qk_gemv_ep* ep, in
     flags |= kEpResidual;
   }
   if (e.norm_w || e.norm_out || e.ss_out) {
-    if (!e.norm_w || !e.norm_out || !e.ss_out) return GGUF_QK_ERR_NULL;
-    if (!al4(e.norm_w) || !al4(e.norm_out) || !al4(e.ss_out)) return GGUF_QK_ERR_ALIGN;
+    if (!e.norm_w || !e.norm_out) return GGUF_QK_ERR_NULL;
+    if (!al4(e.norm_w) || !al4(e.norm_out) || (e.ss_out && !al4(e.ss_out))) return GGUF_QK_ERR_ALIGN;
     flags |= kEpNorm;
-    // row-group counters for kernels whose blocks do not own whole row groups
-    // (taken from the step's group counters when there are enough left)
-    if (*pair_off + RG <= kPairCounters) {
-      *norm_rg = *pair_off;
-      *pair_off += RG;
+    if (e.ss_out) {
+      flags |= kEpSs;
+      // row-group counters for kernels whose blocks do not own whole row groups
+      // (taken from the step's group counters when there are enough left)
+      if (*pair_off + RG <= kPairCounters) {
+        *norm_rg = *pair_off;
+        *pair_off += RG;
+      }
     }
   }
   if (e.pair != 0) {
@@ -566,18 +578,19 @@ static int make_epilogue(const gguf_qk_gemv* list, const gguf_qk_gemv_ep* ep, in
     }
     if (overlap(outs[a], outn[a], e.residual, e.residual ? g.rows * 4 : 0) ||
         overlap(outs[a], outn[a], e.norm_w, e.norm_w ? g.rows * 4 : 0) ||
-        overlap(outs[a], outn[a], e.scale_ss, e.scale_ss ? e.scale_n * 4 : 0))
+        overlap(outs[a], outn[a], e.scale_ss, e.scale_ss ? e.scale_n * 4 : 0) ||
+        overlap(outs[a], outn[a], e.scale_v, e.scale_v ? g.cols * 4 : 0))
       return GGUF_QK_ERR_ALIAS;
   }
   if (flags && ((g.type == GGUF_QK_TYPE_Q8_0 && g.cols % 256) || g.type == GGUF_QK_TYPE_Q4_0 ||
                 g.type == GGUF_QK_TYPE_Q6_K))
     return GGUF_QK_ERR_SHAPE;
-  out->scale_ss = e.scale_ss;
+  out->scale_ss = e.scale_v ? e.scale_v : e.scale_ss;
   out->residual = e.residual;
   out->norm_w = e.norm_w;
   out->norm_out = e.norm_out;
   out->ss_out = e.ss_out;
-  out->scale_n = (int)e.scale_n;
+  out->scale_n = e.scale_v ? (int)g.cols : (int)e.scale_n;
   out->eps = e.eps;
   out->inv_k = 1.0f / (float)g.cols;
   out->flags = flags;
@@ -919,11 +932,10 @@ extern "C++" {
 // (K split over blocks so that a range has at most kSbwMaxWaves
 // super-blocks), the split and the row tiles per block chosen below.
 static int launch_sbw(const SbGroup& G, const float* X, int64_t n_tokens, int64_t nsb, hipStream_t stream) {
-  int64_t tiles_of[kSbMaxGroup], tiles = 0;
+  int64_t tiles_of[kSbMaxGroup];
   for (int m = 0; m < G.n; ++m) {
     if (G.rows[m] > INT32_MAX) return GGUF_QK_ERR_LIMIT;
     tiles_of[m] = (G.rows[m] + 15) / 16;
-    tiles += tiles_of[m];
   }
   const int64_t gy = (n_tokens + kSbwMaxTokens - 1) / kSbwMaxTokens;
   if (gy > 65535) return GGUF_QK_ERR_LIMIT;

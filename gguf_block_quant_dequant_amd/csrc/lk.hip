@@ -9,7 +9,8 @@ namespace gqk {
 // Q4_K GEMVs whose rows hold 1, 2, 4, 8 or 16 super-blocks (lanes hold x), or
 // 17 to 48 (x read from LDS), all the same: the lanes-along-K kernels take
 // them, with any epilogue except norm preparation and a gate/up pair together
-// on one GEMV, and at most 256 partial sums for an input RMSN.
+// on one GEMV, and at most 256 partial sums for an input RMSN (or the input
+// vector itself, rows of at most 16 super-blocks).
 bool lk_fits(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n) {
   const int64_t c = v[0]->cols;
   if (c % 256 || (c != 256 && c != 512 && c != 1024 && c != 2048 && c != 4096 && (c <= 4096 || c > kLkxMaxK)))
@@ -19,8 +20,9 @@ bool lk_fits(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n) 
     if (e && e[i]) {
       const int f = e[i]->flags;
       if ((f & kEpNorm) && (f & kEpPair)) return false;
-      if ((f & kEpScale) && e[i]->scale_n > 256) return false;
-      if ((f & kEpNorm) && !e[i]->norm_cnt) return false;
+      if ((f & kEpScale) && !(f & kEpScaleV) && e[i]->scale_n > 256) return false;
+      if ((f & kEpScaleV) && c > 4096) return false;
+      if ((f & kEpSs) && !e[i]->norm_cnt) return false;
     }
   }
   return true;
@@ -29,7 +31,7 @@ bool lk_fits(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n) 
 // Q4_K or Q4_0 GEMVs whose rows the kernels above do not take as they are (a
 // number of super-blocks other than 1, 2, 4, 8, 16, up to 128): the
 // split-K-in-block kernel. Epilogues: one Q4_K GEMV with a residual add and
-// norm preparation (row-group counters assigned), nothing else.
+// norm preparation (row-group counters assigned for the partial sums), nothing else.
 bool lks_fits(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n, int type) {
   if (type != GGUF_QK_TYPE_Q4_K && type != GGUF_QK_TYPE_Q4_0) return false;
   const int64_t c = v[0]->cols;
@@ -40,8 +42,8 @@ bool lks_fits(const gguf_qk_gemv* const* v, const GemvEpilogue* const* e, int n,
     if (v[i]->cols != c || v[i]->rows > (int64_t(1) << 30)) return false;
     if (e && e[i] && e[i]->flags) {
       const int f = e[i]->flags;
-      if (n != 1 || type != GGUF_QK_TYPE_Q4_K || (f & ~(kEpResidual | kEpNorm))) return false;
-      if ((f & kEpNorm) && !e[i]->norm_cnt) return false;
+      if (n != 1 || type != GGUF_QK_TYPE_Q4_K || (f & ~(kEpResidual | kEpNorm | kEpSs))) return false;
+      if ((f & kEpSs) && !e[i]->norm_cnt) return false;
     }
   }
   return true;

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GGUF_QK_ABI_VERSION 1
+#define GGUF_QK_ABI_VERSION 2
 
 /* Scratch slots per device (streams that may hold scratch at one time). */
 #define GGUF_QK_STREAM_SLOTS 8
@@ -204,13 +204,20 @@ typedef struct gguf_qk_gemv_ep {
   int32_t pair;
   /* y = residual + ... (rows floats; may be y itself, not a partial overlap). */
   const float* residual;
-  /* Output half of the next RMSN: norm_out = y * norm_w (rows floats) and
-   * ss_out[j] = sum of y^2 over rows 64 j .. 64 j + 63 (ceil(rows / 64) floats),
-   * the scale_ss of the GEMVs that read norm_out. All three or none. */
+  /* Output half of the next RMSN: norm_out = y * norm_w (rows floats) and,
+   * where ss_out is given, ss_out[j] = sum of y^2 over rows 64 j .. 64 j + 63
+   * (ceil(rows / 64) floats), the scale_ss of the GEMVs that read norm_out.
+   * norm_w and norm_out together or neither; ss_out only with them. */
   const float* norm_w;
   float* norm_out;
   float* ss_out;
   float* act;
+  /* Input RMSN from the vector itself, in place of scale_ss: v (cols floats,
+   * 16-byte aligned), with x = v * norm; the GEMV forms sum(v^2) in a fixed
+   * order and scales y by 1 / sqrt(sum(v^2) / cols + eps). The producer of v
+   * then needs no ss_out, and no row-group completion between its blocks.
+   * NULL: off. At most one of scale_ss and scale_v. */
+  const float* scale_v;
 } gguf_qk_gemv_ep;
 
 /* gguf_qmatvec_batch with an epilogue per entry (ep: n entries, or NULL for

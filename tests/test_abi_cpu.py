@@ -61,7 +61,7 @@ def test_binding_names_match_header():
 
 
 def test_version_and_strerror():
-    assert g.gguf_qk_abi_version() == 1
+    assert g.gguf_qk_abi_version() == 2
     for s in range(-10, 1):
         assert g.gguf_qk_strerror(s)
     assert g.gguf_qk_strerror(-99) == "unknown status"
@@ -302,6 +302,15 @@ def test_batch_ep_validation():
     assert _run_ep(_pair_entries(), [_ep(norm_w=0x9000000, norm_out=0x7000000, ss_out=0xA000000),
                                      _ep()]) == g.ERR_ALIAS                              # over the other y
     assert _run_ep(_pair_entries(), [_ep(scale_ss=0xB000000, scale_n=0), _ep()]) == g.ERR_SHAPE
+    # the input RMSN from the vector itself: alone, 16-byte aligned, not over an output of the step
+    assert _run_ep(_pair_entries(), [_ep(scale_v=0xB000000), _ep()]) == g.ERR_DEVICE
+    assert _run_ep(_pair_entries(), [_ep(scale_v=0xB000000, scale_ss=0xB100000, scale_n=4), _ep()]) == g.ERR_SHAPE
+    assert _run_ep(_pair_entries(), [_ep(scale_v=0xB000004), _ep()]) == g.ERR_ALIGN
+    assert _run_ep(_pair_entries(), [_ep(scale_v=0x7000000), _ep()]) == g.ERR_ALIAS    # the other entry's y
+    assert _run_ep(_pair_entries(), [_ep(scale_v=0xB000000, eps=-1.0), _ep()]) == g.ERR_SHAPE
+    # norm_out without the partial sums is complete; ss_out alone is not
+    assert _run_ep(_pair_entries(), [_ep(norm_w=0x9000000, norm_out=0xA000000), _ep()]) == g.ERR_DEVICE
+    assert _run_ep(_pair_entries(), [_ep(ss_out=0xA000000), _ep()]) == g.ERR_NULL
     assert _run_ep(_pair_entries(), [_ep(scale_ss=0xB000000, scale_n=4, eps=-1.0), _ep()]) == g.ERR_SHAPE
     assert _run_ep(_pair_entries(), [_ep(scale_ss=0xB000000, scale_n=4, eps=float("nan")), _ep()]) == g.ERR_SHAPE
     assert _run_ep(_pair_entries(), [_ep(residual=0xC000001), _ep()]) == g.ERR_ALIGN

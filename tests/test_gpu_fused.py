@@ -179,9 +179,12 @@ def _layers(n_layers=2, H=2048, F=5632, KV=512):
     return [Layer(rng, H, F, KV) for _ in range(n_layers)], rng
 
 
-def _fused_entries(layers, h0, H, F, KV):
+def _fused_entries(layers, h0, H, F, KV, mode="ss"):
     """The fused chain as one batch: per layer 4 steps. The attention result
-    (out of scope) is stood in by the q projection's output."""
+    (out of scope) is stood in by the q projection's output. mode "ss": each
+    RMSN's scale from the producer's partial sums of squares (ss_out ->
+    scale_ss); "v": from the producer's output vector itself (scale_v), the
+    producers writing no ss_out."""
     T = {}
     ents, eps = [], []
     h = h0
@@ -197,22 +200,25 @@ def _fused_entries(layers, h0, H, F, KV):
         if first:
             T["prep"] = (dev(L.attn_norm), hw, ss)
             first = False
-        sc = {"scale_ss": ss, "eps": EPS}
+        sc = {"scale_ss": ss, "eps": EPS} if mode == "ss" else {"scale_v": h, "eps": EPS}
         for name, y in (("q", q), ("k", k), ("v", v)):
             ents.append((g.TYPE_Q4_K, L.d[name], hw, y, stage))
             eps.append(dict(sc))
         stage += 1
         ents.append((g.TYPE_Q4_K, L.d["o"], q, h1, stage))
-        eps.append({"residual": h, "norm_w": dev(L.ffn_norm), "norm_out": hw2, "ss_out": ss2})
+        eps.append({"residual": h, "norm_w": dev(L.ffn_norm), "norm_out": hw2,
+                    **({"ss_out": ss2} if mode == "ss" else {})})
+        sc2 = {"scale_ss": ss2, "eps": EPS} if mode == "ss" else {"scale_v": h1, "eps": EPS}
         stage += 1
         ents.append((g.TYPE_Q4_K, L.d["gate"], hw2, gg, stage))
-        eps.append({"scale_ss": ss2, "eps": EPS, "pair": 1, "act": act})
+        eps.append({**sc2, "pair": 1, "act": act})
         ents.append((g.TYPE_Q4_K, L.d["up"], hw2, uu, stage))
-        eps.append({"scale_ss": ss2, "eps": EPS, "pair": 2, "act": act})
+        eps.append({**sc2, "pair": 2, "act": act})
         stage += 1
         nxt = layers[li + 1].attn_norm if li + 1 < len(layers) else layers[li].attn_norm
         ents.append((g.TYPE_Q4_K, L.d["down"], act, h2, stage))
-        eps.append({"residual": h1, "norm_w": dev(nxt), "norm_out": hw3, "ss_out": ss3})
+        eps.append({"residual": h1, "norm_w": dev(nxt), "norm_out": hw3,
+                    **({"ss_out": ss3} if mode == "ss" else {})})
         stage += 1
         T[li] = dict(q=q, k=k, v=v, h1=h1, g=gg, u=uu, act=act, h2=h2)
         h, hw, ss = h2, hw3, ss3
@@ -237,14 +243,15 @@ def _unfused(layers, h0, H, F, KV):
     return out
 
 
-@pytest.mark.parametrize("n_layers,F", [(2, 5632), (1, 11008)])
-def test_fused_layers_stage_by_stage(n_layers, F):
+@pytest.mark.parametrize("n_layers,F,mode", [(2, 5632, "ss"), (1, 11008, "ss"), (2, 5632, "v"), (1, 11008, "v")])
+def test_fused_layers_stage_by_stage(n_layers, F, mode):
     """Two chained layers at a narrower FFN, and one at the workload's FFN
-    width (gate/up rows and down columns of 11008)."""
+    width (gate/up rows and down columns of 11008); each RMSN scale from the
+    producer's partial sums (ss) or from the producer's output (v)."""
     H, KV = 2048, 512
     layers, rng = _layers(n_layers, H, F, KV)
     h0 = dev(synth.activations_f32(rng, H))
-    batch, T = _fused_entries(layers, h0, H, F, KV)
+    batch, T = _fused_entries(layers, h0, H, F, KV, mode)
     nw0, hw, ss = T["prep"]
     say("fused chain:", batch.n, "GEMVs")
     g.gguf_rmsnorm_prep_f32(h0, nw0, hw, ss)
