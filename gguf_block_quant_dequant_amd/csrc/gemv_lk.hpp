@@ -778,6 +778,20 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const GemvEp
     const int i = tid + j * kW * 64;
     if (kXF4 % (kW * 64) == 0 || i < kXF4) xg[j] = reinterpret_cast<const GQK_GLOBAL lk_f32x4*>(x)[i];
   }
+  // (kEpScaleV) and the float4s of v at the same indices, for the block's sum
+  // of v^2, right behind x: the loads complete in order, so issued after the
+  // first weight loads they held the x-staging barrier back until those
+  // arrived. They read x when the flag is off, so they go out on every path.
+  lk_f32x4 vg[kXIt];
+  if constexpr (kEp) {
+    const GQK_GLOBAL lk_f32x4* const vb = reinterpret_cast<const GQK_GLOBAL lk_f32x4*>(
+        (B.ep_flags & kEpScaleV) ? (const GQK_GLOBAL float*)B.scale_ss : x);
+#pragma unroll
+    for (int j = 0; j < kXIt; ++j) {
+      const int i = tid + j * kW * 64;
+      vg[j] = vb[kXF4 % (kW * 64) == 0 || i < kXF4 ? i : 0];
+    }
+  }
 
   // ... then the weight loads of the first kDepth steps. A wave's steps are
   // consecutive rows: step st reads rows [st kRps, st kRps + kRps) at base
@@ -830,22 +844,11 @@ __device__ __forceinline__ void lk_run(const LkBlock& B, float* xl, const GemvEp
   // epilogue comes from argument memory, only they wait for it (the empty asm
   // keeps the scheduler from moving their address work, and with it the
   // wait, above the weight loads)
-  // (kEpScaleV) the thread's float4s of v at x's indices, for the block's
-  // sum of v^2; they read x when the flag is off, so the loads go out on
-  // every path
-  lk_f32x4 vg[kXIt];
   if constexpr (kEp) {
     int f = B.ep_flags, sn = B.scale_n;
     const float* sp = (const float*)B.scale_ss;
     asm volatile("" : "+s"(f), "+s"(sn), "+s"(sp));
     ssl = lk_ep_ss_issue(f, sn, (const GQK_GLOBAL float*)sp, B.x, lane);
-    const GQK_GLOBAL lk_f32x4* const vb =
-        reinterpret_cast<const GQK_GLOBAL lk_f32x4*>((f & kEpScaleV) ? (const GQK_GLOBAL float*)sp : B.x);
-#pragma unroll
-    for (int j = 0; j < kXIt; ++j) {
-      const int i = tid + j * kW * 64;
-      vg[j] = vb[kXF4 % (kW * 64) == 0 || i < kXF4 ? i : 0];
-    }
   }
   tl.stamp(1);
 
